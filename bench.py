@@ -1,0 +1,263 @@
+"""Benchmark of the TTT-layer forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one forward pass of the layer over one batch of synthetic input (all
+chunks of every (sequence, head) unit), launched through the C ABI. Inputs are
+resident in HBM before the timed region. The default workload is TTT-Linear
+with LayerNorm+residual, bf16 Q/K/V, B=8 H=12 N=2048 d=64 b=16 with per-token
+step sizes. To keep the 256 MB Infinity Cache from serving repeated reads, the
+steps rotate over four distinct device copies of the inputs and outputs.
+
+Prints ONE JSON line (stdout). Diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from weights_ttt_layer_amd import workloads as wlm  # noqa: E402
+
+DEFAULT_WORKLOAD = "linear_ln_bf16_B8H12N2048_d64_b16"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+ROTATE = 4
+METRIC = "TTT layer fwd tokens/sec"
+
+KERNEL_SOURCES = {
+    "plain": ["smallb_linear.hip", "device_common.h"],
+    "ln": ["smallb_linear.hip", "device_common.h"],
+    "mlp": ["smallb_mlp.hip", "device_common.h"],
+    "large": ["large_chunk.hip", "device_common.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic traffic and work of one launch
+# ---------------------------------------------------------------------------
+
+def chunk_rows(N, b):
+    full, rem = divmod(N, b)
+    return [b] * full + ([rem] if rem else [])
+
+
+def algorithmic_bytes(wl: wlm.Workload) -> int:
+    """Compulsory HBM bytes: read Q,K,V (+eta), write Z (fp32), read and write the state."""
+    es = 2 if wl.dtype == "bf16" else 4
+    tok = wl.B * wl.H * wl.N
+    b = 3 * tok * wl.d * es + tok * wl.d * 4
+    if wl.eta == "sigmoid":
+        b += tok * 4
+    state = wl.d * wl.d if wl.kind != "mlp" else 2 * wl.d * wl.hidden
+    b += 2 * wl.B * wl.H * state * 4
+    if wl.kind in ("ln", "mlp"):
+        b += 2 * wl.H * wl.d * 4
+    return b
+
+
+def algorithmic_flops(wl: wlm.Workload) -> int:
+    """Per chunk of n rows: linear 6 n d^2 + 2 d n(n+1); MLP 56 n d^2 + 10 d n(n+1)
+    (the tril products counted over their causal half only)."""
+    d = wl.d
+    f = 0
+    for n in chunk_rows(wl.N, wl.b):
+        if wl.kind == "mlp":
+            f += 56 * n * d * d + 10 * d * n * (n + 1)
+        else:
+            f += 6 * n * d * d + 2 * d * n * (n + 1)
+    return f * wl.B * wl.H
+
+
+def source_digest(kind_key: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind_key]:
+        with open(os.path.join(ROOT, "weights_ttt_layer_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(wl: wlm.Workload, kind_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none for this workload or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest(kind_key):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int):
+    import torch
+    from weights_ttt_layer_amd import linear_fwd, linear_workspace_bytes, mlp_fwd
+
+    dev = torch.device("cuda:0")
+    base = wlm.to_device(inp, dev)
+    sets = [base] + [{k: (None if t is None else t.clone()) for k, t in base.items()}
+                     for _ in range(ROTATE - 1)]
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    outs = []
+    for s in sets:
+        z = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+        if wl.kind == "mlp":
+            outs.append((z, torch.empty_like(s["w1"]), torch.empty_like(s["w2"])))
+        else:
+            ws_bytes = linear_workspace_bytes(wl.kind, s["q"].dtype, B, H, N, d, wl.b)
+            ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+            outs.append((z, torch.empty_like(s["w0"]), ws))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s, o = sets[i % ROTATE], outs[i % ROTATE]
+        if wl.kind == "mlp":
+            mlp_fwd(s["q"], s["k"], s["v"], s["w1"], s["w2"], s["eta"], b=wl.b,
+                    eta_const=inp.eta_const, ln_gamma=s["gamma"], ln_beta=s["beta"],
+                    ln_eps=wl.ln_eps, z=o[0], w1_end=o[1], w2_end=o[2], stream=stream)
+        else:
+            linear_fwd(s["q"], s["k"], s["v"], s["w0"], s["eta"], b=wl.b, kind=wl.kind,
+                       eta_const=inp.eta_const, ln_gamma=s["gamma"], ln_beta=s["beta"],
+                       ln_eps=wl.ln_eps, z=o[0], w_end=o[1], workspace=o[2], stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    z = outs[(steps - 1) % ROTATE][0]
+    finite = bool(torch.isfinite(z).all().item())
+    return ms_total / steps, finite
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle as it stands
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl: wlm.Workload, inp: wlm.Inputs, max_units: int):
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    threads = min(threads, 16)
+    units = [(bi, hi) for bi in range(wl.B) for hi in range(wl.H)][:max_units]
+    sub_b = sorted({u[0] for u in units})
+    # the sample: the first `max_units` units in (b, h) order, whole sequences
+    q, k, v = inp.f64("q"), inp.f64("k"), inp.f64("v")
+    nb = len(sub_b)
+    sl = slice(0, nb)
+    eta = inp.eta_f64()[sl]
+    t0 = time.perf_counter()
+    if wl.kind == "mlp":
+        oracle.mlp(oracle.MINIBATCH, q[sl], k[sl], v[sl], eta, inp.f64("w1")[sl], inp.f64("w2")[sl],
+                   wl.b, inp.f64("gamma"), inp.f64("beta"), wl.ln_eps, nthreads=threads)
+    else:
+        kind = oracle.LN if wl.kind == "ln" else oracle.PLAIN
+        oracle.linear(oracle.MINIBATCH, kind, q[sl], k[sl], v[sl], eta, inp.f64("w0")[sl], wl.b,
+                      None if inp.gamma is None else inp.f64("gamma"),
+                      None if inp.beta is None else inp.f64("beta"), wl.ln_eps, nthreads=threads)
+    dt = time.perf_counter() - t0
+    token_heads = nb * wl.H * wl.N
+    return {
+        "value": token_heads / wl.H / dt,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"mini-batch primal fp64 oracle over {nb} of {wl.B} sequences x {wl.H} heads x "
+                  f"{wl.N} tokens ({dt:.2f} s wall)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(wlm.BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=96,
+                    help="cap on (sequence, head) units in the CPU-baseline sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the TTT forward shards "
+              f"over (sequence, head) units with no communication, so N GPUs run N independent "
+              f"copies of this benchmark.", file=sys.stderr)
+        sys.exit(2)
+
+    idx = [w.name for w in wlm.WORKLOADS].index(args.workload)
+    wl = wlm.WORKLOADS[idx]
+    inp = wlm.workload_inputs(idx)
+    log(f"[bench] workload {wl.name}: generated inputs")
+
+    ms, finite = run_gpu(wl, inp, args.steps, args.warmup)
+    if not finite:
+        log("[bench] WARNING: non-finite output")
+    sec = ms / 1e3
+    tokens = wl.B * wl.N
+    large = wl.b >= 256
+    kind_key = "large" if large else wl.kind
+    nbytes = algorithmic_bytes(wl)
+    flops = algorithmic_flops(wl)
+    if large:
+        roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(wl, kind_key)
+    log(f"[bench] {ms*1e3:.1f} us/step, {tokens/sec:.4g} tokens/s, {nbytes/sec/1e9:.1f} GB/s "
+        f"algorithmic, {flops/sec/1e12:.2f} TFLOP/s algorithmic")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, inp, args.cpu_units)
+        log(f"[bench] cpu baseline: {cpu['value']:.4g} tokens/s on {cpu['cores']} threads")
+
+    rec = {
+        "metric": METRIC,
+        "value": tokens / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "kind": wl.kind, "B": wl.B, "H": wl.H, "N": wl.N,
+                   "d": wl.d, "b": wl.b, "qkv_dtype": wl.dtype, "state_dtype": "f32",
+                   "eta": wl.eta, "token_heads_per_s": tokens * wl.H / sec,
+                   "algorithmic_bytes": nbytes, "algorithmic_flops": flops},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

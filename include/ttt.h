@@ -1,0 +1,156 @@
+/*
+ * ttt.h -- C ABI of the MI355X (gfx950) TTT-layer forward library, libttt.so.
+ *
+ * The library computes the forward pass of a Test-Time Training layer in the
+ * mini-batch dual form. The layer's recurrent state is the weight set W of a
+ * small inner model f. For every mini-batch (chunk) of b tokens the layer takes
+ * one gradient-descent step on the per-token loss ||f(k_t; W) - v_t||^2,
+ * with every gradient of the chunk taken at the chunk's starting weights W_c,
+ * and emits z_t = f(q_t; W_t), where W_t already contains the updates of the
+ * chunk's tokens up to and including t.
+ *   Web page "Test-Time Training: Linear Complexity Beyond Attention":
+ *   section "1. The Self-Supervised Inner-Loop Task" (the loss), section "2. The
+ *   Online Gradient Descent Update Rule" (the step), section "3. Forward
+ *   Evaluation and Output Projection" (z_t uses the updated W_t), section
+ *   "4. Mini-Batch Parallelism (Dual Formulation)" (chunks of b tokens computed
+ *   with matrix products that mirror causal attention, the accumulated weight
+ *   delta carried from chunk to chunk).
+ * In matrix form, per chunk with rows Q, K, V (b x d) and per-token step sizes
+ * eta:   G   = d loss / d(pre-activation) at W_c, row by row
+ *        Z   = f evaluated on the pre-activation  Q W_c - tril(Q K^T) diag(eta) G
+ *        W  <- W_c - K^T diag(eta) G
+ * with tril including the diagonal. For f(x) = x W this is
+ * Z = Q W_c - 2 tril(Q K^T) diag(eta) E and W_end = W_c - 2 K^T diag(eta) E,
+ * E = K W_c - V. The page writes f(k;W) = W k with a loss carrying a factor
+ * 1/2; this ABI uses row vectors, f(x;W) = x W, and no 1/2 (the same method
+ * with W_page = W^T and eta_page = 2 eta).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor arguments are DEVICE pointers owned by the caller. The library
+ *    allocates no memory and keeps no global state; calls are reentrant.
+ *  - Token streams Q, K, V: [B, H, N, d], contiguous, d fastest, of dtype
+ *    qkv_dtype (TTT_DTYPE_F32 = IEEE fp32, TTT_DTYPE_BF16 = bfloat16).
+ *  - eta: [B, H, N] fp32, the step size of each SOURCE token (it scales that
+ *    token's own gradient). When eta == NULL every token uses eta_const.
+ *  - State: fp32, row index = input feature (f(x) = x W). W_end may equal the
+ *    state input (in-place update); any other overlap between an output and an
+ *    input is an error.
+ *  - Z: [B, H, N, d] fp32 output.
+ *  - N need not be a multiple of b: the last chunk holds N mod b tokens.
+ *  - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
+ *    stream). Argument validation happens on the host before any HIP call; a
+ *    non-TTT_OK return means nothing was launched. Faults inside kernels surface
+ *    at the caller's next synchronisation of the stream. Nothing is printed.
+ *  - NaN/Inf in the inputs propagate by IEEE rules; there are no checks on the
+ *    hot path.
+ */
+#ifndef TTT_H_
+#define TTT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_ABI_VERSION 1
+
+typedef enum {
+    TTT_OK = 0,
+    TTT_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, bad enum, bad overlap */
+    TTT_ERR_UNSUPPORTED = 2,        /* valid arguments with no kernel for them */
+    TTT_ERR_WORKSPACE_TOO_SMALL = 3,
+    TTT_ERR_HIP = 4                 /* a HIP launch reported an error */
+} ttt_status;
+
+typedef enum { TTT_DTYPE_F32 = 0, TTT_DTYPE_BF16 = 1 } ttt_dtype;
+
+typedef enum {
+    TTT_LINEAR_PLAIN = 0,   /* f(x) = x W           (page 1, sec. 1) */
+    TTT_LINEAR_LN = 1       /* f(x) = x + LN(x W)   LayerNorm (over d, biased variance,
+                               eps inside the square root, fixed gamma/beta) and a
+                               residual placed inside the inner model; page 1 sec. 3
+                               applies the same pair to the layer output */
+} ttt_linear_kind;
+
+typedef enum {
+    TTT_PATH_NONE = 0,        /* unsupported combination */
+    TTT_PATH_SMALL_B = 1,     /* one workgroup per (sequence, head), state on chip */
+    TTT_PATH_LARGE_CHUNK = 2  /* chunk-parallel path for large b (plain f only) */
+} ttt_path;
+
+/*
+ * ttt_linear_fwd -- TTT-Linear forward, kinds PLAIN and LN.
+ *
+ *   kind        ttt_linear_kind
+ *   qkv_dtype   ttt_dtype of Q, K, V
+ *   B, H, N, d  batch, heads, tokens, head dim (all >= 1)
+ *   b           mini-batch (chunk) size, >= 1
+ *   Q, K, V     device [B,H,N,d] qkv_dtype
+ *   eta         device [B,H,N] fp32 or NULL (then eta_const for every token)
+ *   W0          device [B,H,d,d] fp32 initial state
+ *   ln_gamma    device [H,d] fp32 (kind LN; ignored, may be NULL, for PLAIN)
+ *   ln_beta     device [H,d] fp32 (kind LN; ignored, may be NULL, for PLAIN)
+ *   ln_eps      LayerNorm epsilon (kind LN), >= 0
+ *   Z           device [B,H,N,d] fp32 output
+ *   W_end       device [B,H,d,d] fp32 output, the state after the last token;
+ *               may equal W0
+ *   workspace   device scratch of at least ttt_linear_fwd_workspace_bytes(...)
+ *               bytes, 256-byte aligned (may be NULL when that size is 0)
+ *   hip_stream  hipStream_t to launch on
+ *
+ * Supported (else TTT_ERR_UNSUPPORTED):
+ *   small-b path  : kind PLAIN or LN, dtype F32 or BF16, d = 64, 1 <= b <= 16
+ *   large-chunk   : kind PLAIN, dtype BF16, d = 128, b >= 256 and b % 128 == 0
+ * ttt_linear_fwd_path() reports which path a combination takes.
+ */
+int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b,
+                   const void* Q, const void* K, const void* V,
+                   const float* eta, float eta_const, const float* W0,
+                   const float* ln_gamma, const float* ln_beta, float ln_eps,
+                   float* Z, float* W_end,
+                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of device workspace ttt_linear_fwd needs for these sizes (0 for the
+ * small-b path). Returns 0 as well for unsupported or invalid combinations. */
+size_t ttt_linear_fwd_workspace_bytes(int kind, int qkv_dtype, int B, int H, int N, int d, int b);
+
+/* Which ttt_path a (kind, dtype, d, b) combination takes; TTT_PATH_NONE if none. */
+int ttt_linear_fwd_path(int kind, int qkv_dtype, int d, int b);
+
+/*
+ * ttt_mlp_fwd -- TTT-MLP forward, f(x) = x + LN(GELU(x W1) W2), no biases, exact
+ * erf GELU. The page "How to Master Test-Time Training for Infinite Context
+ * LLMs" (section "The Math and Architecture of TTT Layers") names a small
+ * multi-layer perceptron as the inner model. The dual form is applied to both
+ * layers: with A = K W1_c, X2 = GELU(A) and the loss gradients G2 (at the
+ * second pre-activation) and G1 = (G2 W2_c^T) * GELU'(A),
+ *   A_Q = Q W1_c - tril(Q K^T) diag(eta) G1,  X2_Q = GELU(A_Q),
+ *   H_Q = X2_Q W2_c - tril(X2_Q X2^T) diag(eta) G2,  Z = Q + LN(H_Q),
+ *   W1 <- W1_c - K^T diag(eta) G1,  W2 <- W2_c - X2^T diag(eta) G2.
+ *
+ *   hidden      width of the hidden layer (4*d)
+ *   W1_0        device [B,H,d,hidden] fp32;  W2_0 device [B,H,hidden,d] fp32
+ *   W1_end, W2_end   outputs of the same shapes; may equal W1_0 / W2_0
+ *   other arguments as for ttt_linear_fwd (ln_gamma/ln_beta required).
+ * Supported: dtype F32 or BF16, d = 64, hidden = 256, 1 <= b <= 16.
+ */
+int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b,
+                const void* Q, const void* K, const void* V,
+                const float* eta, float eta_const,
+                const float* W1_0, const float* W2_0,
+                const float* ln_gamma, const float* ln_beta, float ln_eps,
+                float* Z, float* W1_end, float* W2_end, void* hip_stream);
+
+/* Static, NUL-terminated description of a ttt_status value. */
+const char* ttt_status_string(int status);
+
+/* TTT_ABI_VERSION of the built library. */
+int ttt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_H_ */

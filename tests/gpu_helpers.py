@@ -1,0 +1,73 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI and
+the fp64 oracle on the same seeded inputs, and measure the normwise error."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from weights_ttt_layer_amd import workloads as wlm
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max_i |got_i - ref_i| / max_i |ref_i| over one output tensor."""
+    den = float(np.max(np.abs(ref)))
+    num = float(np.max(np.abs(got.astype(np.float64) - ref)))
+    return num if den == 0.0 else num / den
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_linear(inp: wlm.Inputs, in_place: bool = False, **kw):
+    import torch
+    from weights_ttt_layer_amd import linear_fwd
+    t = wlm.to_device(inp)
+    wl = inp.wl
+    w_end = t["w0"] if in_place else None
+    z, w = linear_fwd(t["q"], t["k"], t["v"], t["w0"], t["eta"], b=wl.b, kind=wl.kind,
+                      eta_const=inp.eta_const, ln_gamma=t["gamma"], ln_beta=t["beta"],
+                      ln_eps=wl.ln_eps, w_end=w_end, **kw)
+    torch.cuda.synchronize()
+    return z.cpu().numpy(), w.cpu().numpy()
+
+
+def gpu_mlp(inp: wlm.Inputs):
+    import torch
+    from weights_ttt_layer_amd import mlp_fwd
+    t = wlm.to_device(inp)
+    wl = inp.wl
+    z, w1, w2 = mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], b=wl.b,
+                        eta_const=inp.eta_const, ln_gamma=t["gamma"], ln_beta=t["beta"],
+                        ln_eps=wl.ln_eps)
+    torch.cuda.synchronize()
+    return z.cpu().numpy(), w1.cpu().numpy(), w2.cpu().numpy()
+
+
+def oracle_linear(inp: wlm.Inputs, mode=oracle.MINIBATCH):
+    wl = inp.wl
+    kind = oracle.LN if wl.kind == "ln" else oracle.PLAIN
+    return oracle.linear(mode, kind, inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.eta_f64(),
+                         inp.f64("w0"), wl.b,
+                         None if inp.gamma is None else inp.f64("gamma"),
+                         None if inp.beta is None else inp.f64("beta"), wl.ln_eps)
+
+
+def oracle_mlp(inp: wlm.Inputs, mode=oracle.MINIBATCH):
+    wl = inp.wl
+    return oracle.mlp(mode, inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.eta_f64(), inp.f64("w1"),
+                      inp.f64("w2"), wl.b, inp.f64("gamma"), inp.f64("beta"), wl.ln_eps)
+
+
+def sample_units(wl: wlm.Workload, count: int, seed: int = 0):
+    """A deterministic spread of (b, h) units: the first, the last, and random ones."""
+    rng = np.random.default_rng(seed)
+    units = {(0, 0), (wl.B - 1, wl.H - 1)}
+    while len(units) < min(count, wl.B * wl.H):
+        units.add((int(rng.integers(wl.B)), int(rng.integers(wl.H))))
+    return sorted(units)

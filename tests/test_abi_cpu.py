@@ -1,0 +1,126 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+symbol include/ttt.h declares, and rejects bad arguments on the host before any
+HIP call (so nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt.h")
+
+from weights_ttt_layer_amd import binding  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "ttt_linear_fwd" in names and "ttt_mlp_fwd" in names
+    for n in names:
+        assert hasattr(lib, n), f"libttt.so does not export {n}"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ttt_abi_version() == 1
+    for s in range(5):
+        assert binding.status_string(s).startswith("TTT_")
+    assert binding.status_string(99) == "unknown ttt_status"
+
+
+def test_path_selection(lib):
+    P = lib.ttt_linear_fwd_path
+    assert P(0, 0, 64, 16) == binding.TTT_PATH_SMALL_B
+    assert P(1, 1, 64, 1) == binding.TTT_PATH_SMALL_B
+    assert P(1, 1, 64, 17) == binding.TTT_PATH_NONE
+    assert P(0, 1, 128, 2048) == binding.TTT_PATH_LARGE_CHUNK
+    assert P(1, 1, 128, 2048) == binding.TTT_PATH_NONE       # LN has no large-chunk path
+    assert P(0, 1, 128, 2000) == binding.TTT_PATH_NONE       # not a multiple of 128
+    assert P(0, 1, 32, 16) == binding.TTT_PATH_NONE
+    assert P(5, 1, 64, 16) == binding.TTT_PATH_NONE
+
+
+def test_workspace_sizes(lib):
+    W = lib.ttt_linear_fwd_workspace_bytes
+    assert W(0, 1, 8, 12, 2048, 64, 16) == 0          # small-b path needs none
+    assert W(0, 1, 1, 16, 32768, 128, 2048) > 0
+    assert W(0, 1, 0, 16, 32768, 128, 2048) == 0      # invalid sizes
+
+
+# Fake, never-dereferenced device addresses: every call below must be rejected
+# by host-side validation before anything is launched.
+A = 1 << 40
+
+
+def addr(i, size=1 << 30):
+    return ctypes.c_void_p(A + i * size)
+
+
+def lin_call(lib, kind=0, dt=1, B=1, H=1, N=64, d=64, b=16, Q=0, K=1, V=2, eta=None, W0=3,
+             gam=4, bet=5, eps=1e-6, Z=6, We=7, ws=None, wsb=0):
+    p = lambda i: None if i is None else (i if isinstance(i, ctypes.c_void_p) else addr(i))
+    return lib.ttt_linear_fwd(kind, dt, B, H, N, d, b, p(Q), p(K), p(V), p(eta), 0.1, p(W0), p(gam),
+                              p(bet), eps, p(Z), p(We), p(ws), wsb, None)
+
+
+def test_rejects_invalid_arguments(lib):
+    E = binding.TTT_ERR_INVALID_ARGUMENT
+    assert lin_call(lib, kind=7) == E
+    assert lin_call(lib, dt=3) == E
+    assert lin_call(lib, B=0) == E
+    assert lin_call(lib, N=0) == E
+    assert lin_call(lib, b=0) == E
+    assert lin_call(lib, Q=None) == E
+    assert lin_call(lib, Z=None) == E
+    assert lin_call(lib, We=None) == E
+    assert lin_call(lib, kind=1, gam=None) == E
+    assert lin_call(lib, kind=1, eps=-1.0) == E
+    assert lin_call(lib, kind=1, eps=float("nan")) == E
+    # misaligned token stream
+    assert lin_call(lib, Q=ctypes.c_void_p(A + 2)) == E
+    # Z overlapping an input
+    assert lin_call(lib, Z=ctypes.c_void_p(A + 8)) == E
+    # W_end partially overlapping W0 (equal is allowed, see below)
+    assert lin_call(lib, We=ctypes.c_void_p(A + 3 * (1 << 30) + 64)) == E
+
+
+def test_rejects_unsupported(lib):
+    U = binding.TTT_ERR_UNSUPPORTED
+    assert lin_call(lib, d=32) == U
+    assert lin_call(lib, b=17) == U
+    assert lin_call(lib, kind=1, d=128, b=2048) == U
+    assert lin_call(lib, dt=0, d=128, b=2048) == U
+
+
+def test_large_chunk_workspace_checked_before_launch(lib):
+    rc = lin_call(lib, B=1, H=16, N=32768, d=128, b=2048, ws=None, wsb=0)
+    assert rc == binding.TTT_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_mlp_rejections(lib):
+    p = addr
+    f = lib.ttt_mlp_fwd
+    E, U = binding.TTT_ERR_INVALID_ARGUMENT, binding.TTT_ERR_UNSUPPORTED
+    args = lambda **kw: dict(dict(dt=1, B=1, H=1, N=64, d=64, hid=256, b=16), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return f(a["dt"], a["B"], a["H"], a["N"], a["d"], a["hid"], a["b"], p(0), p(1), p(2), None,
+                 0.1, a.get("W1", p(3)), p(4), a.get("gam", p(5)), p(6), 1e-6, p(7), p(8), p(9), None)
+    assert call(dt=5) == E
+    assert call(hid=0) == E
+    assert call(gam=None) == E
+    assert call(W1=None) == E
+    assert call(d=32, hid=128) == U
+    assert call(hid=128) == U
+    assert call(b=32) == U

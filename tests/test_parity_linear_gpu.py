@@ -1,0 +1,130 @@
+"""GPU parity of the small-b TTT-Linear path (plain and LayerNorm+residual) with
+the fp64 oracle, through the C ABI, on identical seeded inputs.
+
+Tolerance (per output tensor, max|gpu - ref| / max|ref|): 1e-5 for fp32 token
+streams, 2e-3 for bf16 token streams with fp32 accumulation.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from weights_ttt_layer_amd import workloads as wlm
+
+from gpu_helpers import TOL, gpu_linear, oracle_linear, rel_err, sample_units, say
+
+pytestmark = pytest.mark.gpu
+
+
+def small(kind, dtype, B, H, N, b, eta="sigmoid", seed=7, **kw):
+    wl = wlm.Workload(f"edge_{kind}_{dtype}_{B}x{H}x{N}_b{b}", kind, dtype, B, H, N, 64, b, eta,
+                      0.05, qkv_std=1.0 if dtype == "bf16" else 0.125, **kw)
+    return wlm.generate(wl, seed)
+
+
+def check(inp, tol=None, in_place=False):
+    tol = tol or TOL[inp.wl.dtype]
+    z, w = gpu_linear(inp, in_place=in_place)
+    zr, wr = oracle_linear(inp)
+    ez, ew = rel_err(z, zr), rel_err(w, wr)
+    say(f"  {inp.wl.name}: err Z {ez:.2e}  W_end {ew:.2e}  (tol {tol:.0e})")
+    assert ez <= tol and ew <= tol
+    return z, w
+
+
+def test_workload_linear_f32_B1H1N256():
+    """TTT-Linear, fp32, B=1 H=1 N=256 d=64 b=16, eta = 0.1: full comparison."""
+    inp = wlm.workload_inputs(0)
+    say(f"case {inp.wl.name}")
+    check(inp)
+
+
+CASES = [
+    (kind, dtype, B, H, N, b)
+    for kind in ("plain", "ln")
+    for dtype in ("f32", "bf16")
+    for (B, H, N, b) in [(2, 3, 37, 16), (1, 2, 5, 16), (1, 1, 100, 1), (2, 1, 64, 3),
+                         (1, 1, 1, 16), (3, 2, 129, 7)]
+]
+
+
+@pytest.mark.parametrize("kind,dtype,B,H,N,b", CASES)
+def test_edge_shapes(kind, dtype, B, H, N, b):
+    """Ragged tails (N % b != 0), N < b, b = 1 (online GD), odd b, one token."""
+    inp = small(kind, dtype, B, H, N, b)
+    say(f"case {inp.wl.name}")
+    check(inp)
+
+
+@pytest.mark.parametrize("index", [1, 2])
+def test_workload_ln_bf16_sampled_units(index):
+    """Full-size LN workloads (B=8 H=12 N=2048; B=16 H=12 N=8192), launched whole
+    exactly as the benchmark launches them; every output of a spread of units is
+    compared with the oracle run on those units alone."""
+    inp = wlm.workload_inputs(index)
+    say(f"case {inp.wl.name} (full launch, sampled units)")
+    z, w = gpu_linear(inp)
+    assert np.all(np.isfinite(z)) and np.all(np.isfinite(w))
+    for (bi, hi) in sample_units(inp.wl, 4 if index == 1 else 3, seed=index):
+        u = inp.unit(bi, hi)
+        zr, wr = oracle_linear(u)
+        ez, ew = rel_err(z[bi, hi], zr[0, 0]), rel_err(w[bi, hi], wr[0, 0])
+        say(f"  unit ({bi},{hi}): err Z {ez:.2e} W_end {ew:.2e}")
+        assert ez <= TOL["bf16"] and ew <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kind,dtype", [("plain", "f32"), ("ln", "bf16")])
+def test_eta_zero_gives_f_of_q(kind, dtype):
+    """eta = 0 leaves the state untouched: W_end = W0 exactly, Z = f(Q; W0)."""
+    inp = small(kind, dtype, 2, 2, 40, 16, eta="const")
+    inp.eta_const = 0.0
+    z, w = gpu_linear(inp)
+    assert np.array_equal(w, inp.w0)
+    zr, _ = oracle_linear(inp)
+    assert rel_err(z, zr) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ln_zero_affine_gives_identity(dtype):
+    """gamma = beta = 0: LN(.) = 0, so Z = Q exactly and the state is unchanged."""
+    inp = small("ln", dtype, 1, 3, 50, 16)
+    inp.gamma = np.zeros_like(inp.gamma)
+    inp.beta = np.zeros_like(inp.beta)
+    z, w = gpu_linear(inp)
+    assert np.array_equal(z, inp.f64("q").astype(np.float32))
+    assert np.array_equal(w, inp.w0)
+
+
+@pytest.mark.parametrize("kind", ["plain", "ln"])
+def test_state_passing(kind):
+    """run(N1 + N2) equals run(N1) followed by run(N2) from the returned state."""
+    inp = small(kind, "bf16", 2, 2, 96, 16)
+    z, w = gpu_linear(inp)
+    N1 = 48
+    a = wlm.Inputs(inp.wl.replace(N=N1), inp.q[:, :, :N1], inp.k[:, :, :N1], inp.v[:, :, :N1],
+                   inp.eta[:, :, :N1], inp.eta_const, inp.w0, None, None, inp.gamma, inp.beta)
+    za, wa = gpu_linear(a)
+    b2 = wlm.Inputs(inp.wl.replace(N=96 - N1), inp.q[:, :, N1:].copy(), inp.k[:, :, N1:].copy(),
+                    inp.v[:, :, N1:].copy(), inp.eta[:, :, N1:].copy(), inp.eta_const, wa, None,
+                    None, inp.gamma, inp.beta)
+    zb, wb = gpu_linear(b2)
+    assert rel_err(np.concatenate([za, zb], 2), z) <= 1e-6
+    assert rel_err(wb, w) <= 1e-6
+
+
+def test_in_place_state_and_determinism():
+    """W_end may alias W0; two identical launches give bitwise identical outputs."""
+    inp = small("ln", "bf16", 2, 3, 77, 16)
+    z1, w1 = gpu_linear(inp)
+    z2, w2 = gpu_linear(inp, in_place=True)
+    assert np.array_equal(z1, z2) and np.array_equal(w1, w2)
+
+
+def test_units_independent():
+    """Permuting the batch permutes the outputs (units never interact)."""
+    inp = small("ln", "bf16", 3, 2, 33, 16)
+    z, w = gpu_linear(inp)
+    p = [2, 0, 1]
+    perm = wlm.Inputs(inp.wl, inp.q[p].copy(), inp.k[p].copy(), inp.v[p].copy(), inp.eta[p].copy(),
+                      inp.eta_const, inp.w0[p].copy(), None, None, inp.gamma, inp.beta)
+    zp, wp = gpu_linear(perm)
+    assert np.array_equal(zp, z[p]) and np.array_equal(wp, w[p])

@@ -1,0 +1,20 @@
+"""MI355X (gfx950) TTT-layer forward pass: HIP kernels behind a C ABI (libttt.so).
+
+    from weights_ttt_layer_amd import linear_fwd, mlp_fwd
+
+``linear_fwd`` runs TTT-Linear (plain or LayerNorm+residual inner model) and
+``mlp_fwd`` runs TTT-MLP, both in the mini-batch dual form, on device tensors.
+Build the library first with ``python -m weights_ttt_layer_amd.build``.
+"""
+from .binding import (  # noqa: F401
+    TTTError,
+    linear_fwd,
+    linear_path,
+    linear_workspace_bytes,
+    load_library,
+    mlp_fwd,
+    status_string,
+)
+
+__all__ = ["TTTError", "linear_fwd", "linear_path", "linear_workspace_bytes", "load_library",
+           "mlp_fwd", "status_string"]

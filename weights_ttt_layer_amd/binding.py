@@ -1,0 +1,181 @@
+"""Thin Python binding of libttt.so (the C ABI in include/ttt.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs are allocated with torch, and the device pointers plus the
+current HIP stream are handed to the C entry points, which run every step of
+the computation in the library's HIP kernels. There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libttt.so")
+
+TTT_OK, TTT_ERR_INVALID_ARGUMENT, TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE_TOO_SMALL, TTT_ERR_HIP = range(5)
+TTT_DTYPE_F32, TTT_DTYPE_BF16 = 0, 1
+TTT_LINEAR_PLAIN, TTT_LINEAR_LN = 0, 1
+TTT_PATH_NONE, TTT_PATH_SMALL_B, TTT_PATH_LARGE_CHUNK = 0, 1, 2
+
+KINDS = {"plain": TTT_LINEAR_PLAIN, "ln": TTT_LINEAR_LN}
+
+_lib = None
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libttt.so once and declare the C signatures. Raises if it was never built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m weights_ttt_layer_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, fp, i, f, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.ttt_linear_fwd.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, fp, f, fp, fp, fp, f, fp, fp, vp,
+                                   sz, vp]
+    lib.ttt_linear_fwd.restype = i
+    lib.ttt_linear_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.ttt_linear_fwd_workspace_bytes.restype = sz
+    lib.ttt_linear_fwd_path.argtypes = [i, i, i, i]
+    lib.ttt_linear_fwd_path.restype = i
+    lib.ttt_mlp_fwd.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, fp, f, fp, fp, fp, fp, f, fp, fp, fp,
+                                vp]
+    lib.ttt_mlp_fwd.restype = i
+    lib.ttt_status_string.argtypes = [i]
+    lib.ttt_status_string.restype = ctypes.c_char_p
+    lib.ttt_abi_version.argtypes = []
+    lib.ttt_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ttt_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _qkv_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TTT_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return TTT_DTYPE_F32
+    raise TypeError(f"Q/K/V must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def linear_path(kind: str, dtype: torch.dtype, d: int, b: int) -> int:
+    return load_library().ttt_linear_fwd_path(KINDS[kind], _qkv_dtype(torch.empty(0, dtype=dtype)), d, b)
+
+
+def linear_workspace_bytes(kind: str, dtype: torch.dtype, B: int, H: int, N: int, d: int, b: int) -> int:
+    return int(load_library().ttt_linear_fwd_workspace_bytes(
+        KINDS[kind], _qkv_dtype(torch.empty(0, dtype=dtype)), B, H, N, d, b))
+
+
+def linear_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w0: torch.Tensor,
+               eta: Optional[torch.Tensor] = None, *, b: int, kind: str = "plain",
+               eta_const: float = 0.0, ln_gamma: Optional[torch.Tensor] = None,
+               ln_beta: Optional[torch.Tensor] = None, ln_eps: float = 1e-6,
+               z: Optional[torch.Tensor] = None, w_end: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, stream=None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """TTT-Linear forward through ``ttt_linear_fwd``. Returns (Z, W_end).
+
+    q, k, v: [B,H,N,d] bf16 or fp32; w0: [B,H,d,d] fp32; eta: [B,H,N] fp32 or
+    None (then ``eta_const`` for every token); ln_gamma/ln_beta: [H,d] fp32 for
+    kind "ln". ``w_end`` may be ``w0`` for an in-place state update.
+    """
+    lib = load_library()
+    if kind not in KINDS:
+        raise ValueError(f"kind must be one of {sorted(KINDS)}")
+    B, H, N, d = q.shape
+    dt = _qkv_dtype(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, (B, H, N, d), q.dtype)
+    _check(w0, "w0", (B, H, d, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H, N), torch.float32)
+    if kind == "ln":
+        if ln_gamma is None or ln_beta is None:
+            raise ValueError("kind 'ln' needs ln_gamma and ln_beta")
+        _check(ln_gamma, "ln_gamma", (H, d), torch.float32)
+        _check(ln_beta, "ln_beta", (H, d), torch.float32)
+    if z is None:
+        z = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    else:
+        _check(z, "z", (B, H, N, d), torch.float32)
+    if w_end is None:
+        w_end = torch.empty_like(w0)
+    else:
+        _check(w_end, "w_end", (B, H, d, d), torch.float32)
+    need = int(lib.ttt_linear_fwd_workspace_bytes(KINDS[kind], dt, B, H, N, d, b))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ttt_linear_fwd(KINDS[kind], dt, B, H, N, d, int(b), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                            float(eta_const), _ptr(w0), _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps),
+                            _ptr(z), _ptr(w_end), _ptr(workspace), ws_bytes, _stream_ptr(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_linear_fwd")
+    return z, w_end
+
+
+def mlp_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
+            eta: Optional[torch.Tensor] = None, *, b: int, ln_gamma: torch.Tensor,
+            ln_beta: torch.Tensor, eta_const: float = 0.0, ln_eps: float = 1e-6,
+            z: Optional[torch.Tensor] = None, w1_end: Optional[torch.Tensor] = None,
+            w2_end: Optional[torch.Tensor] = None, stream=None
+            ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """TTT-MLP forward through ``ttt_mlp_fwd``. Returns (Z, W1_end, W2_end)."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    hid = w1.shape[-1]
+    dt = _qkv_dtype(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, (B, H, N, d), q.dtype)
+    _check(w1, "w1", (B, H, d, hid), torch.float32)
+    _check(w2, "w2", (B, H, hid, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H, N), torch.float32)
+    _check(ln_gamma, "ln_gamma", (H, d), torch.float32)
+    _check(ln_beta, "ln_beta", (H, d), torch.float32)
+    z = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if z is None else z
+    w1_end = torch.empty_like(w1) if w1_end is None else w1_end
+    w2_end = torch.empty_like(w2) if w2_end is None else w2_end
+    st = lib.ttt_mlp_fwd(dt, B, H, N, d, hid, int(b), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                         float(eta_const), _ptr(w1), _ptr(w2), _ptr(ln_gamma), _ptr(ln_beta),
+                         float(ln_eps), _ptr(z), _ptr(w1_end), _ptr(w2_end), _stream_ptr(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_mlp_fwd")
+    return z, w1_end, w2_end

@@ -1,0 +1,57 @@
+// kernels.h -- host-side launch interface between the C ABI (ttt_abi.hip) and the
+// kernel translation units. Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace ttt {
+
+struct LinearArgs {
+    int kind;          // 0 plain, 1 LayerNorm + residual
+    int dtype;         // 0 fp32, 1 bf16 token streams
+    int B, H, N, d, b;
+    const void* Q;
+    const void* K;
+    const void* V;
+    const float* eta;  // [B,H,N] or nullptr
+    float eta_const;
+    const float* W0;
+    const float* gamma;
+    const float* beta;
+    float eps;
+    float* Z;
+    float* W_end;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+struct MlpArgs {
+    int dtype;
+    int B, H, N, d, hidden, b;
+    const void* Q;
+    const void* K;
+    const void* V;
+    const float* eta;
+    float eta_const;
+    const float* W1;
+    const float* W2;
+    const float* gamma;
+    const float* beta;
+    float eps;
+    float* Z;
+    float* W1_end;
+    float* W2_end;
+};
+
+// Small-b path: one workgroup per (sequence, head); d = 64, 1 <= b <= 16.
+hipError_t launch_smallb_linear(const LinearArgs& a, hipStream_t stream);
+
+// Large-chunk path (plain f, bf16, d = 128, b % 128 == 0).
+size_t large_chunk_workspace_bytes(int B, int H, int N, int d, int b);
+hipError_t launch_large_chunk_linear(const LinearArgs& a, hipStream_t stream);
+
+// TTT-MLP small-b path: d = 64, hidden = 256, 1 <= b <= 16.
+hipError_t launch_smallb_mlp(const MlpArgs& a, hipStream_t stream);
+
+}  // namespace ttt

@@ -1,0 +1,209 @@
+// ttt_abi.hip -- the extern "C" entry points declared in include/ttt.h:
+// synchronous host-side validation, path selection and kernel launch.
+// Validation touches no HIP API, so every rejection path is testable on a
+// machine without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/ttt.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int SMALLB_D = 64;
+constexpr int SMALLB_MAX_B = 16;
+constexpr int LARGE_D = 128;
+constexpr int LARGE_MIN_B = 256;
+constexpr int LARGE_B_MULT = 128;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// [a, a+na) and [b, b+nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+int linear_path(int kind, int dtype, int d, int b)
+{
+    if ((kind == TTT_LINEAR_PLAIN || kind == TTT_LINEAR_LN) &&
+        (dtype == TTT_DTYPE_F32 || dtype == TTT_DTYPE_BF16) && d == SMALLB_D && b >= 1 &&
+        b <= SMALLB_MAX_B)
+        return TTT_PATH_SMALL_B;
+    if (kind == TTT_LINEAR_PLAIN && dtype == TTT_DTYPE_BF16 && d == LARGE_D && b >= LARGE_MIN_B &&
+        b % LARGE_B_MULT == 0)
+        return TTT_PATH_LARGE_CHUNK;
+    return TTT_PATH_NONE;
+}
+
+size_t elem_size(int dtype) { return dtype == TTT_DTYPE_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int ttt_abi_version(void) { return TTT_ABI_VERSION; }
+
+const char* ttt_status_string(int status)
+{
+    switch (status) {
+        case TTT_OK: return "TTT_OK: success";
+        case TTT_ERR_INVALID_ARGUMENT: return "TTT_ERR_INVALID_ARGUMENT: invalid argument";
+        case TTT_ERR_UNSUPPORTED: return "TTT_ERR_UNSUPPORTED: no kernel for this combination";
+        case TTT_ERR_WORKSPACE_TOO_SMALL: return "TTT_ERR_WORKSPACE_TOO_SMALL: workspace too small";
+        case TTT_ERR_HIP: return "TTT_ERR_HIP: a HIP launch failed";
+        default: return "unknown ttt_status";
+    }
+}
+
+int ttt_linear_fwd_path(int kind, int qkv_dtype, int d, int b) { return linear_path(kind, qkv_dtype, d, b); }
+
+size_t ttt_linear_fwd_workspace_bytes(int kind, int qkv_dtype, int B, int H, int N, int d, int b)
+{
+    if (B < 1 || H < 1 || N < 1 || d < 1 || b < 1) return 0;
+    if (linear_path(kind, qkv_dtype, d, b) != TTT_PATH_LARGE_CHUNK) return 0;
+    return ttt::large_chunk_workspace_bytes(B, H, N, d, b);
+}
+
+int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b, const void* Q,
+                   const void* K, const void* V, const float* eta, float eta_const, const float* W0,
+                   const float* ln_gamma, const float* ln_beta, float ln_eps, float* Z, float* W_end,
+                   void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    if (kind != TTT_LINEAR_PLAIN && kind != TTT_LINEAR_LN) return TTT_ERR_INVALID_ARGUMENT;
+    if (qkv_dtype != TTT_DTYPE_F32 && qkv_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARGUMENT;
+    if (B < 1 || H < 1 || N < 1 || d < 1 || b < 1) return TTT_ERR_INVALID_ARGUMENT;
+    if (!Q || !K || !V || !W0 || !Z || !W_end) return TTT_ERR_INVALID_ARGUMENT;
+    if (kind == TTT_LINEAR_LN && (!ln_gamma || !ln_beta || !(ln_eps >= 0.f)))
+        return TTT_ERR_INVALID_ARGUMENT;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(W0, 4) ||
+        !aligned(Z, 4) || !aligned(W_end, 4) || (eta && !aligned(eta, 4)))
+        return TTT_ERR_INVALID_ARGUMENT;
+    // size arithmetic in 64 bits; reject overflow of the int32 sizes' products
+    const size_t units = (size_t)B * (size_t)H;
+    const size_t tok = units * (size_t)N;
+    const size_t qkv_bytes = tok * (size_t)d * elem_size(qkv_dtype);
+    const size_t z_bytes = tok * (size_t)d * 4;
+    const size_t w_bytes = units * (size_t)d * (size_t)d * 4;
+    if (units > (size_t)INT32_MAX || tok / units != (size_t)N) return TTT_ERR_INVALID_ARGUMENT;
+    // Z must not overlap any input; W_end must equal W0 or not overlap it
+    if (overlaps(Z, z_bytes, Q, qkv_bytes) || overlaps(Z, z_bytes, K, qkv_bytes) ||
+        overlaps(Z, z_bytes, V, qkv_bytes) || overlaps(Z, z_bytes, W0, w_bytes) ||
+        overlaps(Z, z_bytes, W_end, w_bytes) || (eta && overlaps(Z, z_bytes, eta, tok * 4)))
+        return TTT_ERR_INVALID_ARGUMENT;
+    if (W_end != W0 && overlaps(W_end, w_bytes, W0, w_bytes)) return TTT_ERR_INVALID_ARGUMENT;
+    if (overlaps(W_end, w_bytes, Q, qkv_bytes) || overlaps(W_end, w_bytes, K, qkv_bytes) ||
+        overlaps(W_end, w_bytes, V, qkv_bytes) || (eta && overlaps(W_end, w_bytes, eta, tok * 4)))
+        return TTT_ERR_INVALID_ARGUMENT;
+
+    const int path = linear_path(kind, qkv_dtype, d, b);
+    if (path == TTT_PATH_NONE) return TTT_ERR_UNSUPPORTED;
+
+    ttt::LinearArgs a;
+    a.kind = kind;
+    a.dtype = qkv_dtype;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.d = d;
+    a.b = b;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.eta = eta;
+    a.eta_const = eta_const;
+    a.W0 = W0;
+    a.gamma = ln_gamma;
+    a.beta = ln_beta;
+    a.eps = ln_eps;
+    a.Z = Z;
+    a.W_end = W_end;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+
+    hipError_t err;
+    if (path == TTT_PATH_SMALL_B) {
+        err = ttt::launch_smallb_linear(a, stream);
+    } else {
+        const size_t need = ttt::large_chunk_workspace_bytes(B, H, N, d, b);
+        if (workspace_bytes < need || (need > 0 && !workspace)) return TTT_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned(workspace, 256)) return TTT_ERR_INVALID_ARGUMENT;
+        if (overlaps(workspace, need, Z, z_bytes) || overlaps(workspace, need, W_end, w_bytes) ||
+            overlaps(workspace, need, Q, qkv_bytes) || overlaps(workspace, need, K, qkv_bytes) ||
+            overlaps(workspace, need, V, qkv_bytes) || overlaps(workspace, need, W0, w_bytes))
+            return TTT_ERR_INVALID_ARGUMENT;
+        err = ttt::launch_large_chunk_linear(a, stream);
+    }
+    return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b, const void* Q,
+                const void* K, const void* V, const float* eta, float eta_const, const float* W1_0,
+                const float* W2_0, const float* ln_gamma, const float* ln_beta, float ln_eps,
+                float* Z, float* W1_end, float* W2_end, void* hip_stream)
+{
+    if (qkv_dtype != TTT_DTYPE_F32 && qkv_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARGUMENT;
+    if (B < 1 || H < 1 || N < 1 || d < 1 || hidden < 1 || b < 1) return TTT_ERR_INVALID_ARGUMENT;
+    if (!Q || !K || !V || !W1_0 || !W2_0 || !ln_gamma || !ln_beta || !Z || !W1_end || !W2_end)
+        return TTT_ERR_INVALID_ARGUMENT;
+    if (!(ln_eps >= 0.f)) return TTT_ERR_INVALID_ARGUMENT;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(W1_0, 16) ||
+        !aligned(W2_0, 16) || !aligned(Z, 4) || !aligned(W1_end, 16) || !aligned(W2_end, 16) ||
+        (eta && !aligned(eta, 4)))
+        return TTT_ERR_INVALID_ARGUMENT;
+    const size_t units = (size_t)B * (size_t)H;
+    const size_t tok = units * (size_t)N;
+    const size_t qkv_bytes = tok * (size_t)d * elem_size(qkv_dtype);
+    const size_t z_bytes = tok * (size_t)d * 4;
+    const size_t w_bytes = units * (size_t)d * (size_t)hidden * 4;
+    if (units > (size_t)INT32_MAX) return TTT_ERR_INVALID_ARGUMENT;
+    const void* ins[5] = {Q, K, V, W1_0, W2_0};
+    const size_t in_bytes[5] = {qkv_bytes, qkv_bytes, qkv_bytes, w_bytes, w_bytes};
+    for (int i = 0; i < 5; ++i) {
+        if (overlaps(Z, z_bytes, ins[i], in_bytes[i])) return TTT_ERR_INVALID_ARGUMENT;
+        if (i < 3 && (overlaps(W1_end, w_bytes, ins[i], in_bytes[i]) ||
+                      overlaps(W2_end, w_bytes, ins[i], in_bytes[i])))
+            return TTT_ERR_INVALID_ARGUMENT;
+    }
+    if (eta && (overlaps(Z, z_bytes, eta, tok * 4) || overlaps(W1_end, w_bytes, eta, tok * 4) ||
+                overlaps(W2_end, w_bytes, eta, tok * 4)))
+        return TTT_ERR_INVALID_ARGUMENT;
+    if (overlaps(Z, z_bytes, W1_end, w_bytes) || overlaps(Z, z_bytes, W2_end, w_bytes) ||
+        overlaps(W1_end, w_bytes, W2_end, w_bytes))
+        return TTT_ERR_INVALID_ARGUMENT;
+    if (W1_end != W1_0 && overlaps(W1_end, w_bytes, W1_0, w_bytes)) return TTT_ERR_INVALID_ARGUMENT;
+    if (W2_end != W2_0 && overlaps(W2_end, w_bytes, W2_0, w_bytes)) return TTT_ERR_INVALID_ARGUMENT;
+    if (overlaps(W1_end, w_bytes, W2_0, w_bytes) || overlaps(W2_end, w_bytes, W1_0, w_bytes))
+        return TTT_ERR_INVALID_ARGUMENT;
+
+    if (d != 64 || hidden != 4 * d || b > 16) return TTT_ERR_UNSUPPORTED;
+
+    ttt::MlpArgs a;
+    a.dtype = qkv_dtype;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.d = d;
+    a.hidden = hidden;
+    a.b = b;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.eta = eta;
+    a.eta_const = eta_const;
+    a.W1 = W1_0;
+    a.W2 = W2_0;
+    a.gamma = ln_gamma;
+    a.beta = ln_beta;
+    a.eps = ln_eps;
+    a.Z = Z;
+    a.W1_end = W1_end;
+    a.W2_end = W2_end;
+    hipError_t err = ttt::launch_smallb_mlp(a, reinterpret_cast<hipStream_t>(hip_stream));
+    return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+}  // extern "C"

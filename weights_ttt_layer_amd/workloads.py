@@ -195,3 +195,20 @@ def generate(wl: Workload, seed: int) -> Inputs:
 def workload_inputs(index: int) -> Inputs:
     """Inputs of the index-th named workload with its documented seed."""
     return generate(WORKLOADS[index], SEED_BASE + index)
+
+
+def to_device(inp: Inputs, device="cuda"):
+    """Copy rounded inputs to device tensors (bf16 streams keep their bit patterns)."""
+    import torch
+
+    def stream(a):
+        if inp.wl.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(a).to(device)
+
+    def f32(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    return dict(q=stream(inp.q), k=stream(inp.k), v=stream(inp.v), eta=f32(inp.eta),
+                w0=f32(inp.w0), w1=f32(inp.w1), w2=f32(inp.w2), gamma=f32(inp.gamma),
+                beta=f32(inp.beta))
