@@ -11,156 +11,61 @@
 //     W_{c+1} = W_c - K^T Gt
 //
 // Design (gfx950):
-//  * One workgroup (4 waves, 256 lanes) per (sequence, head) unit. Wave w owns
-//    the state columns [16w, 16w+16) as four 16x16 fp32 MFMA accumulator tiles;
-//    W never leaves the registers between the first load of W0 and the final
-//    store of W_end (the pages' "weight update in SRAM" idea, page "How to
-//    Master Test-Time Training for Infinite Context LLMs").
-//  * The accumulator layout of W is used directly as the B operand of the next
-//    K W_c and Q W_c products: the k index of a 16x16x32 B operand is taken in
-//    the permuted order (tile 2p rows 4g..4g+3, then tile 2p+1 rows 4g..4g+3)
-//    and the A operands (K, Q rows) are read from LDS in the same order.
-//  * The gradient Gt, produced in the C layout of H_K, is directly the B
-//    operand of both K^T Gt (state update) and tril(QK^T) Gt.
-//  * S^T = K Q^T is computed instead of Q K^T because its C layout is exactly
-//    the A operand layout of the 16x16x16 product tril(S) Gt.
-//  * fp32 operands (W, Gt, S) are split into bf16 terms (2 for bf16 token
-//    streams, 3 for fp32 streams); fp32 token streams use 3 terms as well.
-//  * Q/K/V/eta chunks are prefetched into registers one chunk ahead and staged
-//    through double-buffered, row-padded LDS tiles.
-//  * LayerNorm statistics are row sums over the 64 columns: a 16-lane DPP
-//    reduction inside each wave, then a 4-wave exchange through LDS.
-#include "device_common.h"
+//  * One workgroup (4 waves) per (sequence, head) unit. Wave w owns the state
+//    columns [16w, 16w+16) as four 16x16 fp32 MFMA accumulator tiles; W stays in
+//    registers from the load of W0 to the store of W_end (the pages' "weight
+//    update in SRAM" idea, page "How to Master Test-Time Training for Infinite
+//    Context LLMs").
+//  * The accumulator layout of W serves directly as the B operand of K W and
+//    Q W (k index in the permuted order tile 2p rows 4g..4g+3, then tile 2p+1).
+//    Passing the same registers as the A operand instead yields the transposed
+//    product (W^T K^T): its C layout puts ONE token per lane (lane (g, n):
+//    token n, features 16w+4g..16w+4g+3). The LayerNorm row statistics, the
+//    per-token constants and the Z stores (16-byte vectors) are all done in
+//    this "token per lane" layout: a row sum is three in-lane adds, two
+//    permlane swaps and one 4-wave exchange through LDS.
+//  * Gt is moved back to the MFMA C layout (token 4g+i, feature n) through a
+//    per-wave LDS transpose; there it is the B operand of the state update
+//    K^T Gt and (as Gt^T) the A operand of the causal term Gt^T tril(S)^T.
+//  * S^T = K Q^T is computed so that its C layout is exactly the B operand of
+//    Gt^T S^T.
+//  * fp32 operands are split into bf16 terms (2 for bf16 token streams, 3 for
+//    fp32 streams; fp32 token streams use 3 terms too).
+//  * Q/K/V/eta chunks are prefetched PF chunks ahead into a register ring and
+//    staged through double-buffered, row-padded LDS tiles. Per chunk: one
+//    workgroup barrier (plain) or two (LayerNorm: forward statistics together
+//    with the previous chunk's output statistics, then backward statistics).
 #include "kernels.h"
+#include "smallb_common.h"
 
 namespace ttt {
 namespace {
 
-constexpr int D = 64;
-constexpr int ROWS = 16;
-constexpr int THREADS = 256;
-
-template <typename S>
-struct Stor;
-template <>
-struct Stor<uint16_t> {  // bf16 bit patterns
-    static constexpr int TERMS = 1;
-    static constexpr int STRIDE = D + 8;              // elements per LDS row (144 B)
-    static constexpr int PIECES = D * 2 / 16;          // 16-byte pieces per row
-    __device__ static float f(uint16_t x) { return __builtin_bit_cast(float, (uint32_t)x << 16); }
-};
-template <>
-struct Stor<float> {
-    static constexpr int TERMS = 3;
-    static constexpr int STRIDE = D + 4;              // 272 B
-    static constexpr int PIECES = D * 4 / 16;
-    __device__ static float f(float x) { return x; }
-};
-
-// Eight consecutive-in-k operand elements given as two groups of four, p0[0..3]
-// and p1[0..3], as TERMS bf16x8 terms.
-template <typename S, int T>
-__device__ __forceinline__ void load_a8(const S* p0, const S* p1, bf16x8 (&out)[T])
-{
-    if constexpr (sizeof(S) == 2) {
-        static_assert(T == 1, "bf16 streams are exact in one term");
-        uint2 a = *reinterpret_cast<const uint2*>(p0);
-        uint2 b = *reinterpret_cast<const uint2*>(p1);
-        uint4 v = make_uint4(a.x, a.y, b.x, b.y);
-        out[0] = __builtin_bit_cast(bf16x8, v);
-    } else {
-        float4 a = *reinterpret_cast<const float4*>(p0);
-        float4 b = *reinterpret_cast<const float4*>(p1);
-        float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            __bf16 t[T];
-            split_terms<T>(x[j], t);
-#pragma unroll
-            for (int s = 0; s < T; ++s) out[s][j] = t[s];
-        }
-    }
-}
-
-// Four operand elements x[0..3] (fp32 values) as T bf16x4 terms.
-template <int T>
-__device__ __forceinline__ void terms4(const float (&x)[4], bf16x4 (&out)[T])
-{
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        __bf16 t[T];
-        split_terms<T>(x[j], t);
-#pragma unroll
-        for (int s = 0; s < T; ++s) out[s][j] = bf16_bits(t[s]);
-    }
-}
-
-template <typename S>
-struct alignas(16) Stage {
-    S q[ROWS * Stor<S>::STRIDE];
-    S k[ROWS * Stor<S>::STRIDE];
-    S v[ROWS * Stor<S>::STRIDE];
-    float eta[ROWS];
-};
+using namespace smallb;
 
 template <typename S>
 struct alignas(16) Smem {
     Stage<S> st[2];
-    float red[3][4][ROWS][2];   // [exchange][wave][row][quantity]
+    float red1[ROWS][4][4];         // [token][wave]: sum h, sum h^2 (chunk c), sum hq, sum hq^2 (chunk c-1)
+    float red2[ROWS][4][2];         // [token][wave]: LayerNorm-backward sums
+    float tp[4][ROWS][ROWS + 4];    // per-wave transpose tile [wave][feature][token]
 };
 
-
-template <typename S>
-struct Pieces {
-    static constexpr int PIECES = Stor<S>::PIECES;
-    static constexpr int ELEMS_PER_PIECE = 16 / sizeof(S);
-    static constexpr int TOTAL = 3 * ROWS * PIECES;
-};
-
-// Issue the global loads of chunk c (rows past the sequence end read as zero).
-template <typename S, int PPT>
-__device__ __forceinline__ void load_chunk(uint4 (&pf)[PPT], float& pe, int c, int b, int N, int tid,
-                                           const S* Qu, const S* Ku, const S* Vu,
-                                           const float* etau, float eta_const)
+// Output stage of the LayerNorm kind for one chunk: Z = Q + LN(H_Q).
+__device__ __forceinline__ void store_ln_out(float* __restrict__ Zu, const f32x4& hq, const float4& q,
+                                             float s1, float s2, const float (&gam)[4],
+                                             const float (&bet)[4], float eps, int c0, int bc, int n,
+                                             int fcol)
 {
-    using P = Pieces<S>;
-    const int c0 = c * b;
-    const int bc = min(b, N - c0);
+    const float mu = s1 * (1.f / D);
+    const float var = fmaxf(s2 * (1.f / D) - mu * mu, 0.f);
+    const float rs = __builtin_amdgcn_rsqf(var + eps);
+    const float qv[4] = {q.x, q.y, q.z, q.w};
+    float z[4];
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-        const int idx = tid + k * THREADS;
-        pf[k] = make_uint4(0, 0, 0, 0);
-        if (idx < P::TOTAL) {
-            const int tensor = idx / (ROWS * P::PIECES);
-            const int rem = idx - tensor * (ROWS * P::PIECES);
-            const int row = rem / P::PIECES;
-            const int piece = rem - row * P::PIECES;
-            const S* src = tensor == 0 ? Qu : (tensor == 1 ? Ku : Vu);
-            if (row < bc)
-                pf[k] = *reinterpret_cast<const uint4*>(src + (size_t)(c0 + row) * D +
-                                                         piece * P::ELEMS_PER_PIECE);
-        }
-    }
-    if (tid < ROWS) pe = tid < bc ? (etau ? etau[c0 + tid] : eta_const) : 0.f;
-}
-
-template <typename S, int PPT>
-__device__ __forceinline__ void store_chunk(Stage<S>& st, const uint4 (&pf)[PPT], float pe, int tid)
-{
-    using P = Pieces<S>;
-#pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-        const int idx = tid + k * THREADS;
-        if (idx < P::TOTAL) {
-            const int tensor = idx / (ROWS * P::PIECES);
-            const int rem = idx - tensor * (ROWS * P::PIECES);
-            const int row = rem / P::PIECES;
-            const int piece = rem - row * P::PIECES;
-            S* dst = tensor == 0 ? st.q : (tensor == 1 ? st.k : st.v);
-            *reinterpret_cast<uint4*>(dst + row * Stor<S>::STRIDE + piece * P::ELEMS_PER_PIECE) = pf[k];
-        }
-    }
-    if (tid < ROWS) st.eta[tid] = pe;
+    for (int i = 0; i < 4; ++i) z[i] = qv[i] + gam[i] * ((hq[i] - mu) * rs) + bet[i];
+    if (n < bc)
+        *reinterpret_cast<float4*>(Zu + (size_t)(c0 + n) * D + fcol) = make_float4(z[0], z[1], z[2], z[3]);
 }
 
 template <int KIND, typename S>
@@ -172,7 +77,7 @@ smallb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __r
                      float* __restrict__ Wend)
 {
     constexpr int TIN = Stor<S>::TERMS;               // terms of a token-stream operand
-    constexpr int TS = (TIN == 1) ? 2 : 3;            // terms of an fp32 state operand
+    constexpr int TS = (TIN == 1) ? 2 : 3;            // terms of an fp32 operand
     constexpr int STRIDE = Stor<S>::STRIDE;
     constexpr int PPT = (Pieces<S>::TOTAL + THREADS - 1) / THREADS;
 
@@ -183,7 +88,8 @@ smallb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __r
     const int lane = tid & 63;
     const int g = lane >> 4;
     const int n = lane & 15;
-    const int col = 16 * w + n;
+    const int col = 16 * w + n;          // feature column in the MFMA C layout
+    const int fcol = 16 * w + 4 * g;     // first of the four features in the token-per-lane layout
 
     const size_t unit = blockIdx.x;
     const int h = (int)(unit % H);
@@ -202,211 +108,237 @@ smallb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __r
 #pragma unroll
             for (int i = 0; i < 4; ++i) Wacc[r][i] = W0u[(16 * r + 4 * g + i) * D + col];
     }
-    float gam = 0.f, bet = 0.f;
+    float gam[4] = {0.f, 0.f, 0.f, 0.f}, bet[4] = {0.f, 0.f, 0.f, 0.f}, gam2x2[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (KIND == 1) {
-        gam = gamma[h * D + col];
-        bet = beta[h * D + col];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            gam[i] = gamma[h * D + fcol + i];
+            bet[i] = beta[h * D + fcol + i];
+            gam2x2[i] = 2.f * gam[i] * gam[i];
+        }
     }
 
     const int nchunks = (N + b - 1) / b;
 
-    // ---- chunk prefetch: registers -> LDS ----
-    uint4 pf[PPT];
-    float pe = 0.f;
-    if (nchunks > 0) {
-        load_chunk<S, PPT>(pf, pe, 0, b, N, tid, Qu, Ku, Vu, etau, eta_const);
-        store_chunk<S, PPT>(sm.st[0], pf, pe, tid);
+    // register ring: slot (c % PF) holds chunk c from its load until it is
+    // written to LDS buffer (c & 1) during the processing of chunk c - 1
+    uint4 pf[PF][PPT];
+    float pe[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) pe[j] = 0.f;
+    load_chunk<S, PPT>(pf[0], pe[0], 0, b, N, tid, Qu, Ku, Vu, etau, eta_const);
+    store_chunk<S, PPT>(sm.st[0], pf[0], pe[0], tid, min(b, N));
+#pragma unroll
+    for (int j = 1; j <= PF; ++j)
+        if (j < nchunks)
+            load_chunk<S, PPT>(pf[j % PF], pe[j % PF], j, b, N, tid, Qu, Ku, Vu, etau, eta_const);
+
+    // W_c as B-operand terms, permuted k order
+    bf16x8 Wb[2][TS];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) b8_from_acc<TS>(Wacc[2 * p], Wacc[2 * p + 1], Wb[p]);
+
+    // previous chunk's output, waiting for its LayerNorm statistics
+    f32x4 hq_prev = {0.f, 0.f, 0.f, 0.f};
+    float4 q_prev = make_float4(0.f, 0.f, 0.f, 0.f);
+    int c0_prev = 0, bc_prev = 0;
+
+    __syncthreads();
+
+    for (int cb = 0; cb < nchunks; cb += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            const int c = cb + j;
+            if (c < nchunks) {
+                const int c0 = c * b;
+                const int bc = min(b, N - c0);
+                const Stage<S>& st = sm.st[c & 1];
+                const int nslot = (j + 1) % PF;   // ring slot of chunk c + 1
+
+                // ======== phase A: operands and products of chunk c ========
+                bf16x8 ka[2][TIN], qa[2][TIN];
+                f32x4 sT = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int o0 = n * STRIDE + 32 * p + 4 * g;
+                    load_a8<S, TIN>(st.k + o0, st.k + o0 + 16, ka[p]);
+                    load_a8<S, TIN>(st.q + o0, st.q + o0 + 16, qa[p]);
+                    bf16x8 kn[TIN], qn[TIN];
+                    const int o1 = n * STRIDE + 32 * p + 8 * g;
+                    load_a8<S, TIN>(st.k + o1, st.k + o1 + 4, kn);
+                    load_a8<S, TIN>(st.q + o1, st.q + o1 + 4, qn);
+                    sT = mma32_terms<TIN, TIN>(sT, kn, qn);   // lane (g,n): S[n][4g+i]
+                }
+                bf16x4 kt[4][TIN];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) load_kT_tile<S, TIN>(st.k, r, g, n, kt[r]);
+                const float4 qT = load4_f32<S>(st.q + n * STRIDE + fcol);
+
+                // H_Q^T (token per lane)
+                f32x4 hqT = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < 2; ++p) hqT = mma32_terms<TS, TIN>(hqT, Wb[p], qa[p]);
+
+                float gt[4];   // diag(eta) G in the MFMA C layout (token 4g+i, feature col)
+                if constexpr (KIND == 0) {
+                    f32x4 hk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) hk = mma32_terms<TIN, TS>(hk, ka[p], Wb[p]);
+                    const float4 et = *reinterpret_cast<const float4*>(st.eta + 4 * g);
+                    const float etv[4] = {et.x, et.y, et.z, et.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float vv = Stor<S>::f(st.v[(4 * g + i) * STRIDE + col]);
+                        gt[i] = (4 * g + i < bc) ? 2.f * etv[i] * (hk[i] - vv) : 0.f;
+                    }
+                    // chunk c+1 into LDS, refill its ring slot
+                    if (c + 1 < nchunks) {
+                        store_chunk<S, PPT>(sm.st[(c + 1) & 1], pf[nslot], pe[nslot], tid,
+                                            min(b, N - (c + 1) * b));
+                        if (c + 1 + PF < nchunks)
+                            load_chunk<S, PPT>(pf[nslot], pe[nslot], c + 1 + PF, b, N, tid, Qu, Ku,
+                                               Vu, etau, eta_const);
+                    }
+                } else {
+                    // H_K^T (token per lane) and LayerNorm forward partial sums
+                    f32x4 hkT = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) hkT = mma32_terms<TS, TIN>(hkT, Wb[p], ka[p]);
+                    const float4 kT = load4_f32<S>(st.k + n * STRIDE + fcol);
+                    const float4 vT = load4_f32<S>(st.v + n * STRIDE + fcol);
+                    const float eta_n = st.eta[n];
+                    const float kv[4] = {kT.x - vT.x, kT.y - vT.y, kT.z - vT.z, kT.w - vT.w};
+                    float cpr[4];   // 2 gamma (K - V + beta): residual part of 2 E gamma
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) cpr[i] = 2.f * gam[i] * (kv[i] + bet[i]);
+
+                    float s1 = (hkT[0] + hkT[1]) + (hkT[2] + hkT[3]);
+                    float s2 = (hkT[0] * hkT[0] + hkT[1] * hkT[1]) + (hkT[2] * hkT[2] + hkT[3] * hkT[3]);
+                    float s3 = (hq_prev[0] + hq_prev[1]) + (hq_prev[2] + hq_prev[3]);
+                    float s4 = (hq_prev[0] * hq_prev[0] + hq_prev[1] * hq_prev[1]) +
+                               (hq_prev[2] * hq_prev[2] + hq_prev[3] * hq_prev[3]);
+                    s1 = xrow4_sum(s1);
+                    s2 = xrow4_sum(s2);
+                    s3 = xrow4_sum(s3);
+                    s4 = xrow4_sum(s4);
+                    if (g == 0)
+                        *reinterpret_cast<float4*>(&sm.red1[n][w][0]) = make_float4(s1, s2, s3, s4);
+                    // chunk c+1 into LDS, refill its ring slot
+                    if (c + 1 < nchunks) {
+                        store_chunk<S, PPT>(sm.st[(c + 1) & 1], pf[nslot], pe[nslot], tid,
+                                            min(b, N - (c + 1) * b));
+                        if (c + 1 + PF < nchunks)
+                            load_chunk<S, PPT>(pf[nslot], pe[nslot], c + 1 + PF, b, N, tid, Qu, Ku,
+                                               Vu, etau, eta_const);
+                    }
+                    __syncthreads();   // X1
+
+                    // ======== phase B: forward statistics, backward partial sums ========
+                    float t[4][4];
+#pragma unroll
+                    for (int ww = 0; ww < 4; ++ww) {
+                        const float4 v = *reinterpret_cast<const float4*>(&sm.red1[n][ww][0]);
+                        t[ww][0] = v.x;
+                        t[ww][1] = v.y;
+                        t[ww][2] = v.z;
+                        t[ww][3] = v.w;
+                    }
+                    const float S1 = (t[0][0] + t[1][0]) + (t[2][0] + t[3][0]);
+                    const float S2 = (t[0][1] + t[1][1]) + (t[2][1] + t[3][1]);
+                    const float S3 = (t[0][2] + t[1][2]) + (t[2][2] + t[3][2]);
+                    const float S4 = (t[0][3] + t[1][3]) + (t[2][3] + t[3][3]);
+                    const float mu = S1 * (1.f / D);
+                    const float rs = __builtin_amdgcn_rsqf(fmaxf(S2 * (1.f / D) - mu * mu, 0.f) + eps);
+                    float xh[4], dxh[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        xh[i] = (hkT[i] - mu) * rs;
+                        dxh[i] = cpr[i] + gam2x2[i] * xh[i];
+                    }
+                    float u1 = (dxh[0] + dxh[1]) + (dxh[2] + dxh[3]);
+                    float u2 = (dxh[0] * xh[0] + dxh[1] * xh[1]) + (dxh[2] * xh[2] + dxh[3] * xh[3]);
+                    u1 = xrow4_sum(u1);
+                    u2 = xrow4_sum(u2);
+                    if (g == 0) *reinterpret_cast<float2*>(&sm.red2[n][w][0]) = make_float2(u1, u2);
+                    if (c > 0)
+                        store_ln_out(Zu, hq_prev, q_prev, S3, S4, gam, bet, eps, c0_prev, bc_prev, n,
+                                     fcol);
+                    __syncthreads();   // X2
+
+                    // ======== phase C: gradient, moved to the MFMA C layout ========
+                    const float4 a = *reinterpret_cast<const float4*>(&sm.red2[n][0][0]);
+                    const float4 bb = *reinterpret_cast<const float4*>(&sm.red2[n][2][0]);
+                    const float m1 = ((a.x + a.z) + (bb.x + bb.z)) * (1.f / D);
+                    const float m2 = ((a.y + a.w) + (bb.y + bb.w)) * (1.f / D);
+                    const float scale = eta_n * rs;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sm.tp[w][4 * g + i][n] = (n < bc) ? scale * (dxh[i] - m1 - xh[i] * m2) : 0.f;
+                    // the tile is private to this wave: order its LDS writes before the reads
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    const float4 gv = *reinterpret_cast<const float4*>(&sm.tp[w][n][4 * g]);
+                    gt[0] = gv.x;
+                    gt[1] = gv.y;
+                    gt[2] = gv.z;
+                    gt[3] = gv.w;
+                }
+
+                // -Gt as terms: B operand of K^T Gt (k = token), A operand of Gt^T S^T
+                bf16x4 ngb[TS];
+                {
+                    float x[4] = {-gt[0], -gt[1], -gt[2], -gt[3]};
+                    terms4<TS>(x, ngb);
+                }
+                // H_Q^T -= Gt^T tril(S)^T
+                {
+                    float x[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = (4 * g + i <= n) ? sT[i] : 0.f;
+                    bf16x4 sb[TS];
+                    terms4<TS>(x, sb);
+                    hqT = mma16_terms<TS, TS>(hqT, ngb, sb);
+                }
+                // W_{c+1} = W_c - K^T Gt
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Wacc[r] = mma16_terms<TIN, TS>(Wacc[r], kt[r], ngb);
+#pragma unroll
+                for (int p = 0; p < 2; ++p) b8_from_acc<TS>(Wacc[2 * p], Wacc[2 * p + 1], Wb[p]);
+
+                if constexpr (KIND == 0) {
+                    if (n < bc)
+                        *reinterpret_cast<float4*>(Zu + (size_t)(c0 + n) * D + fcol) =
+                            make_float4(hqT[0], hqT[1], hqT[2], hqT[3]);
+                    __syncthreads();   // chunk c+1 staged
+                } else {
+                    hq_prev = hqT;
+                    q_prev = qT;
+                    c0_prev = c0;
+                    bc_prev = bc;
+                }
+            }
+        }
     }
 
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        const int c0 = c * b;
-        const int bc = min(b, N - c0);
-        if (c + 1 < nchunks) load_chunk<S, PPT>(pf, pe, c + 1, b, N, tid, Qu, Ku, Vu, etau, eta_const);
+    if constexpr (KIND == 1) {
+        // output statistics of the last chunk
+        float s3 = (hq_prev[0] + hq_prev[1]) + (hq_prev[2] + hq_prev[3]);
+        float s4 = (hq_prev[0] * hq_prev[0] + hq_prev[1] * hq_prev[1]) +
+                   (hq_prev[2] * hq_prev[2] + hq_prev[3] * hq_prev[3]);
+        s3 = xrow4_sum(s3);
+        s4 = xrow4_sum(s4);
+        // red1 is free: every wave has passed the last chunk's X2 barrier
+        if (g == 0) *reinterpret_cast<float2*>(&sm.red1[n][w][0]) = make_float2(s3, s4);
         __syncthreads();
-        const Stage<S>& st = sm.st[buf];
-
-        // ---- W_c as B operand terms (permuted k order) ----
-        bf16x8 Wb[2][TS];
+        float S3 = 0.f, S4 = 0.f;
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float x = j < 4 ? Wacc[2 * p][j] : Wacc[2 * p + 1][j - 4];
-                __bf16 t[TS];
-                split_terms<TS>(x, t);
-#pragma unroll
-                for (int s = 0; s < TS; ++s) Wb[p][s][j] = t[s];
-            }
-
-        // ---- H_K = K W_c, H_Q = Q W_c (row n of the A operand is token n) ----
-        f32x4 hk = {0.f, 0.f, 0.f, 0.f};
-        f32x4 hq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            bf16x8 ka[TIN], qa[TIN];
-            const int o0 = n * STRIDE + 32 * p + 4 * g;
-            load_a8<S, TIN>(st.k + o0, st.k + o0 + 16, ka);
-            load_a8<S, TIN>(st.q + o0, st.q + o0 + 16, qa);
-            hk = mma32_terms<TIN, TS>(hk, ka, Wb[p]);
-            hq = mma32_terms<TIN, TS>(hq, qa, Wb[p]);
+        for (int ww = 0; ww < 4; ++ww) {
+            const float2 v = *reinterpret_cast<const float2*>(&sm.red1[n][ww][0]);
+            S3 += v.x;
+            S4 += v.y;
         }
-
-        // ---- S^T = K Q^T: lane (g, n) gets S[n][4g+i] = q_n . k_{4g+i} ----
-        f32x4 sT = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            bf16x8 ka[TIN], qb[TIN];
-            const int o = n * STRIDE + 32 * p + 8 * g;
-            load_a8<S, TIN>(st.k + o, st.k + o + 4, ka);
-            load_a8<S, TIN>(st.q + o, st.q + o + 4, qb);
-            sT = mma32_terms<TIN, TIN>(sT, ka, qb);
-        }
-
-        // ---- per-element values in the C layout: row 4g+i, column col ----
-        float vv[4], et[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            vv[i] = Stor<S>::f(st.v[(4 * g + i) * STRIDE + col]);
-            et[i] = st.eta[4 * g + i];
-        }
-
-        float gt[4];
-        if constexpr (KIND == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gt[i] = et[i] * 2.f * (hk[i] - vv[i]);
-        } else {
-            // LayerNorm forward statistics of H_K rows
-            float s1[4], s2[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s1[i] = row16_sum(hk[i]);
-                s2[i] = row16_sum(hk[i] * hk[i]);
-            }
-            if (n == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sm.red[0][w][4 * g + i][0] = s1[i];
-                    sm.red[0][w][4 * g + i][1] = s2[i];
-                }
-            }
-            __syncthreads();
-            float mu[4], rs[4], xh[4], dxh[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float a = 0.f, q2 = 0.f;
-#pragma unroll
-                for (int ww = 0; ww < 4; ++ww) {
-                    a += sm.red[0][ww][4 * g + i][0];
-                    q2 += sm.red[0][ww][4 * g + i][1];
-                }
-                mu[i] = a * (1.f / D);
-                const float var = fmaxf(q2 * (1.f / D) - mu[i] * mu[i], 0.f);
-                rs[i] = 1.f / sqrtf(var + eps);
-                xh[i] = (hk[i] - mu[i]) * rs[i];
-                const float kk = Stor<S>::f(st.k[(4 * g + i) * STRIDE + col]);
-                const float e = kk + gam * xh[i] + bet - vv[i];
-                dxh[i] = 2.f * e * gam;
-            }
-            // LayerNorm backward: means of dxh and dxh*xh over the row
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s1[i] = row16_sum(dxh[i]);
-                s2[i] = row16_sum(dxh[i] * xh[i]);
-            }
-            if (n == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sm.red[1][w][4 * g + i][0] = s1[i];
-                    sm.red[1][w][4 * g + i][1] = s2[i];
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float m1 = 0.f, m2 = 0.f;
-#pragma unroll
-                for (int ww = 0; ww < 4; ++ww) {
-                    m1 += sm.red[1][ww][4 * g + i][0];
-                    m2 += sm.red[1][ww][4 * g + i][1];
-                }
-                const float gg = rs[i] * (dxh[i] - m1 * (1.f / D) - xh[i] * (m2 * (1.f / D)));
-                gt[i] = et[i] * gg;
-            }
-        }
-        // padded rows contribute nothing (guards eps = 0 on all-zero rows)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * g + i >= bc) gt[i] = 0.f;
-
-        // ---- -Gt as B operand terms (k index = token 4g+i) ----
-        bf16x4 gb[TS];
-        {
-            float x[4] = {-gt[0], -gt[1], -gt[2], -gt[3]};
-            terms4<TS>(x, gb);
-        }
-
-        // ---- H_Q -= tril(S) Gt  (A = S with row n, k = 4g+i) ----
-        {
-            float x[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (4 * g + i <= n) ? sT[i] : 0.f;
-            bf16x4 sa[TS];
-            terms4<TS>(x, sa);
-            hq = mma16_terms<TS, TS>(hq, sa, gb);
-        }
-
-        // ---- W_{c+1} = W_c - K^T Gt  (A = K^T tile r: row m = feature, k = token) ----
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float x[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = Stor<S>::f(st.k[(4 * g + j) * STRIDE + 16 * r + n]);
-            bf16x4 kt[TIN];
-            terms4<TIN>(x, kt);
-            Wacc[r] = mma16_terms<TIN, TS>(Wacc[r], kt, gb);
-        }
-
-        // ---- output ----
-        float z[4];
-        if constexpr (KIND == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) z[i] = hq[i];
-        } else {
-            float s1[4], s2[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s1[i] = row16_sum(hq[i]);
-                s2[i] = row16_sum(hq[i] * hq[i]);
-            }
-            if (n == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sm.red[2][w][4 * g + i][0] = s1[i];
-                    sm.red[2][w][4 * g + i][1] = s2[i];
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float a = 0.f, q2 = 0.f;
-#pragma unroll
-                for (int ww = 0; ww < 4; ++ww) {
-                    a += sm.red[2][ww][4 * g + i][0];
-                    q2 += sm.red[2][ww][4 * g + i][1];
-                }
-                const float mu = a * (1.f / D);
-                const float var = fmaxf(q2 * (1.f / D) - mu * mu, 0.f);
-                const float rs = 1.f / sqrtf(var + eps);
-                const float qq = Stor<S>::f(st.q[(4 * g + i) * STRIDE + col]);
-                z[i] = qq + gam * ((hq[i] - mu) * rs) + bet;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * g + i < bc) Zu[(size_t)(c0 + 4 * g + i) * D + col] = z[i];
-
-        if (c + 1 < nchunks) store_chunk<S, PPT>(sm.st[buf ^ 1], pf, pe, tid);
+        store_ln_out(Zu, hq_prev, q_prev, S3, S4, gam, bet, eps, c0_prev, bc_prev, n, fcol);
     }
 
     float* Wu = Wend + unit * (size_t)D * D;
