@@ -1,0 +1,85 @@
+"""GPU parity of the large-chunk TTT-Linear path (plain f, d = 128, b >= 256)
+with the fp64 oracle, through the C ABI, on identical seeded inputs.
+
+Tolerance per output tensor (max|gpu - ref| / max|ref|): 2e-3 (bf16 token
+streams with fp32 accumulation).
+"""
+import numpy as np
+import pytest
+
+from weights_ttt_layer_amd import workloads as wlm
+
+from gpu_helpers import TOL, gpu_linear, oracle_linear, rel_err, sample_units, say
+
+pytestmark = pytest.mark.gpu
+
+
+def lc(B, H, N, b, eta="const", eta_const=0.01, seed=5):
+    wl = wlm.Workload(f"lc_{B}x{H}x{N}_b{b}_{eta}", "plain", "bf16", B, H, N, 128, b, eta, eta_const,
+                      l2_rows=True)
+    return wlm.generate(wl, seed)
+
+
+def check(inp):
+    z, w = gpu_linear(inp)
+    zr, wr = oracle_linear(inp)
+    ez, ew = rel_err(z, zr), rel_err(w, wr)
+    say(f"  {inp.wl.name}: err Z {ez:.2e}  W_end {ew:.2e}  (tol 2e-03)")
+    assert ez <= TOL["bf16"] and ew <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,H,N,b,eta", [
+    (1, 2, 1024, 256, "const"),      # 4 chunks of 8 query blocks... of 2 blocks each
+    (2, 1, 768, 256, "sigmoid"),     # per-token step sizes
+    (1, 1, 640, 256, "const"),       # short last chunk (128 tokens)
+    (1, 2, 2048, 512, "const"),      # 4 blocks per chunk
+    (1, 1, 256, 256, "const"),       # a single chunk
+])
+def test_large_chunk_shapes(B, H, N, b, eta):
+    inp = lc(B, H, N, b, eta)
+    say(f"case {inp.wl.name}")
+    check(inp)
+
+
+def test_large_chunk_single_chunk_is_causal_linear_attention():
+    """W0 = 0, one chunk: Z = 2 tril(Q K^T) diag(eta) V exactly (unnormalised
+    causal linear attention), W_end = 2 K^T diag(eta) V; checked through the
+    oracle of record and the closed form."""
+    inp = lc(1, 1, 512, 512, "const", 0.02)
+    inp.w0 = np.zeros_like(inp.w0)
+    z, w = gpu_linear(inp)
+    Q, K, V = (inp.f64(n)[0, 0] for n in ("q", "k", "v"))
+    eta = float(np.float32(0.02))
+    zc = 2 * eta * np.tril(Q @ K.T) @ V
+    wc = 2 * eta * K.T @ V
+    assert rel_err(z[0, 0], zc) <= TOL["bf16"]
+    assert rel_err(w[0, 0], wc) <= TOL["bf16"]
+
+
+def test_large_chunk_workload_sampled_units():
+    """The full large-chunk workload (B=1 H=16 N=32768 d=128 b=2048, eta = 0.01),
+    launched whole; two heads compared with the oracle run on them alone."""
+    inp = wlm.workload_inputs(4)
+    say(f"case {inp.wl.name} (full launch, sampled units)")
+    z, w = gpu_linear(inp)
+    assert np.all(np.isfinite(z)) and np.all(np.isfinite(w))
+    for (bi, hi) in sample_units(inp.wl, 2, seed=4):
+        zr, wr = oracle_linear(inp.unit(bi, hi))
+        ez, ew = rel_err(z[bi, hi], zr[0, 0]), rel_err(w[bi, hi], wr[0, 0])
+        say(f"  unit ({bi},{hi}): err Z {ez:.2e} W_end {ew:.2e}")
+        assert ez <= TOL["bf16"] and ew <= TOL["bf16"]
+
+
+def test_large_chunk_state_passing():
+    """run(N1 + N2) equals run(N1) then run(N2) from the returned state (N1 % b == 0)."""
+    inp = lc(1, 2, 1024, 256, "const")
+    z, w = gpu_linear(inp)
+    N1 = 512
+    a = wlm.Inputs(inp.wl.replace(N=N1), inp.q[:, :, :N1].copy(), inp.k[:, :, :N1].copy(),
+                   inp.v[:, :, :N1].copy(), None, inp.eta_const, inp.w0)
+    za, wa = gpu_linear(a)
+    b2 = wlm.Inputs(inp.wl.replace(N=1024 - N1), inp.q[:, :, N1:].copy(), inp.k[:, :, N1:].copy(),
+                    inp.v[:, :, N1:].copy(), None, inp.eta_const, wa)
+    zb, wb = gpu_linear(b2)
+    assert rel_err(np.concatenate([za, zb], 2), z) <= 1e-6
+    assert rel_err(wb, w) <= 1e-6

@@ -47,6 +47,14 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma_32x32x16_f16(const f16x8& a, const f16x8& b, const f32x16& c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ short bf16_bits(__bf16 x) { return __builtin_bit_cast(short, x); }
 __device__ __forceinline__ __bf16 bits_bf16(uint16_t x) { return __builtin_bit_cast(__bf16, x); }
 __device__ __forceinline__ float bf16_to_f32(__bf16 x) { return (float)x; }
@@ -60,6 +68,61 @@ __device__ __forceinline__ void split_terms(float x, __bf16 (&t)[T])
         t[i] = (__bf16)x;
         x -= (float)t[i];
     }
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 and packed into one register (element 0 in
+// the low half): one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Two fp32 values rounded to fp16 (nearest even) and packed into one register.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b)
+{
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// Split the pair (a, b) into T packed bf16 pairs: out[0] = bf16(a, b),
+// out[1] = bf16 of the remainders, ...
+template <int T>
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t (&out)[T])
+{
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+        out[i] = pack_bf16x2(a, b);
+        if (i + 1 < T) {
+            a -= __builtin_bit_cast(float, out[i] << 16);
+            b -= __builtin_bit_cast(float, out[i] & 0xFFFF0000u);
+        }
+    }
+}
+
+// Eight fp32 values as T bf16x8 operand terms.
+template <int T>
+__device__ __forceinline__ void terms8(const float (&x)[8], bf16x8 (&out)[T])
+{
+    uint32_t p[4][T];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split_pair<T>(x[2 * q], x[2 * q + 1], p[q]);
+#pragma unroll
+    for (int s = 0; s < T; ++s) out[s] = __builtin_bit_cast(bf16x8, make_uint4(p[0][s], p[1][s], p[2][s], p[3][s]));
+}
+
+// Four fp32 values as T bf16x4 (16x16x16) operand terms.
+template <int T>
+__device__ __forceinline__ void terms4(const float (&x)[4], bf16x4 (&out)[T])
+{
+    uint32_t p[2][T];
+    split_pair<T>(x[0], x[1], p[0]);
+    split_pair<T>(x[2], x[3], p[1]);
+#pragma unroll
+    for (int s = 0; s < T; ++s) out[s] = __builtin_bit_cast(bf16x4, make_uint2(p[0][s], p[1][s]));
 }
 
 // acc += sum over kept term pairs of A_i * B_j (16x16x32 shape).

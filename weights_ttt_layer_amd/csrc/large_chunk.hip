@@ -1,6 +1,545 @@
-// large_chunk.hip -- placeholder until the large-chunk path lands.
+// large_chunk.hip -- TTT-Linear forward, plain f(x) = x W, for large mini-batches
+// (b >= 256, b % 128 == 0, d = 128, N % 128 == 0), bf16 token streams.
+//
+// Large chunks are what the page "Test-Time Training Done Right" (abstract)
+// proposes against the low utilisation of small mini-batches; the computation
+// is the same mini-batch dual form (page "Test-Time Training: Linear Complexity
+// Beyond Attention", section "4. Mini-Batch Parallelism (Dual Formulation)"):
+//     E_c = K_c W_c - V_c,   W_{c+1} = W_c - 2 K_c^T diag(eta) E_c,
+//     Z_c = Q_c W_c - 2 tril(Q_c K_c^T) diag(eta) E_c.
+// For plain f the chunk update is affine in W:
+//     W_{c+1} = W_c - M_c W_c + B_c,   M_c = K_c^T D K_c,  B_c = K_c^T D V_c,
+// D = diag(2 eta). The path runs four kernels on one stream:
+//   lc_gram : M_c and B_c for every (unit, chunk) at once (no dependence on W);
+//   lc_scan : the 16-step recurrence W_c -> W_{c+1} (one workgroup per
+//             (unit, 32-column block)); writes every W_c^T as two bf16 terms;
+//   lc_grad : Gneg^T = -(D (K W_c - V))^T per 128-token block, stored fp16;
+//   lc_out  : Z = Q W_c - tril(Q K^T) diag(...) E in 128x128 blocks: for every
+//             query block, the causal key blocks j <= i of its chunk.
+// Workspace (caller-provided): M, B (fp32), W_c^T terms (bf16), Gneg^T (fp16).
+//
+// Precision: every product involving the fp32 state uses two bf16 terms (16
+// significant bits). The causal term tril(Q K^T) Gneg takes single fp16
+// operands for P = Q K^T and Gneg (11 significant bits, eight times finer than
+// bf16, at the same MFMA rate); this requires |q.k| and |2 eta (k W - v)| to
+// stay below the fp16 range (6.5e4), e.g. L2-normalised keys.
+//
+// MFMA v_mfma_f32_32x32x16_bf16 throughout. Token-major operands (the token
+// index contracted in K^T K, K^T V) are read from row-major LDS tiles with the
+// gfx950 transpose read ds_read_b64_tr_b16.
+#include "device_common.h"
 #include "kernels.h"
+
 namespace ttt {
-size_t large_chunk_workspace_bytes(int, int, int, int, int) { return 0; }
-hipError_t launch_large_chunk_linear(const LinearArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int LD = 128;          // head dim of this path
+constexpr int LT = 256;          // threads per workgroup
+constexpr int TB = 128;          // token block of lc_grad / lc_out
+
+// Row of a 32x32 C-layout tile held by lane half h = lane / 32 at slot i.
+__device__ __forceinline__ int crow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+struct LcLayout {
+    size_t m_off, b_off, wt_off, g_off, total;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline LcLayout lc_layout(int units, int N, int b)
+{
+    const size_t C = (size_t)((N + b - 1) / b);
+    LcLayout L;
+    L.m_off = 0;
+    L.b_off = align256(L.m_off + (size_t)units * C * LD * LD * 4);
+    L.wt_off = align256(L.b_off + (size_t)units * C * LD * LD * 4);
+    L.g_off = align256(L.wt_off + (size_t)units * C * 2 * LD * LD * 2);
+    L.total = align256(L.g_off + (size_t)units * N * LD * 2);
+    return L;
+}
+
+__device__ __forceinline__ uint32_t f16_bits_f(float x) { return pack_f16x2(x, 0.f) & 0xFFFFu; }
+
+// ===========================================================================
+// lc_gram: M_c = K^T D K (symmetric: upper 32x32 tiles computed, mirrored on
+// store) and B_c = K^T D V for one (unit, chunk) per workgroup.
+// ===========================================================================
+constexpr int GR_TOK = 64;              // tokens per LDS stage
+constexpr int GR_STRIDE = LD + 8;       // bf16 elements per LDS row (272 B)
+
+struct GramSmem {
+    uint16_t k[2][GR_TOK * GR_STRIDE];
+    uint16_t v[2][GR_TOK * GR_STRIDE];
+    float eta[2][GR_TOK];
+};
+
+// Token-major operand fragment of a [tokens x 128] bf16 LDS tile: lane l gets
+// the 8 tokens t0 + 8*(l/32) + 0..7 of feature 32*f + l%32 (two transpose reads).
+__device__ __forceinline__ bf16x8 tok_major_frag(const uint16_t* tile, int t0, int f, int lane)
+{
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const int q = lane >> 4, r = lane & 15;
+    const int row = t0 + 8 * (q >> 1) + (r >> 2);
+    const int colm = 32 * f + 16 * (q & 1) + 4 * (r & 3);
+    const uint16_t* p0 = tile + row * GR_STRIDE + colm;
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(p0));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(p0 + 4 * GR_STRIDE));
+    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    return __builtin_bit_cast(bf16x8, make_uint4(ua.x, ua.y, ub.x, ub.y));
+}
+
+// staging of one 64-token stage of K and V: 2 x 1024 16-byte pieces
+constexpr int GR_PIECES = 2 * GR_TOK * LD * 2 / 16;
+constexpr int GR_PPT = GR_PIECES / LT;
+
+template <bool PER_TOKEN>
+__device__ __forceinline__ void gram_issue(uint4 (&pf)[GR_PPT], float& pe, int s, int tid,
+                                           const uint16_t* Ku, const uint16_t* Vu, const float* etau)
+{
+#pragma unroll
+    for (int k = 0; k < GR_PPT; ++k) {
+        const int idx = tid + k * LT;
+        const int tensor = idx / (GR_PIECES / 2);
+        const int rem = idx % (GR_PIECES / 2);
+        const int row = rem / (LD / 8), piece = rem % (LD / 8);
+        const uint16_t* src = (tensor == 0 ? Ku : Vu) + (size_t)(s * GR_TOK + row) * LD + piece * 8;
+        pf[k] = *reinterpret_cast<const uint4*>(src);
+    }
+    if (PER_TOKEN) pe = etau[s * GR_TOK + (tid & (GR_TOK - 1))];
+}
+
+template <bool PER_TOKEN>
+__device__ __forceinline__ void gram_commit(GramSmem& sm, int buf, const uint4 (&pf)[GR_PPT], float pe,
+                                            int tid)
+{
+#pragma unroll
+    for (int k = 0; k < GR_PPT; ++k) {
+        const int idx = tid + k * LT;
+        const int tensor = idx / (GR_PIECES / 2);
+        const int rem = idx % (GR_PIECES / 2);
+        const int row = rem / (LD / 8), piece = rem % (LD / 8);
+        uint16_t* dst = (tensor == 0 ? sm.k[buf] : sm.v[buf]) + row * GR_STRIDE + piece * 8;
+        *reinterpret_cast<uint4*>(dst) = pf[k];
+    }
+    if (PER_TOKEN && tid < GR_TOK) sm.eta[buf][tid] = 2.f * pe;
+}
+
+// A operand of K^T D: the fragment itself (constant eta, D applied after the
+// sum) or, with per-token eta, each token's entry times 2 eta_t as TA terms.
+template <bool PER_TOKEN, int TA>
+__device__ __forceinline__ void scaled_frag(const bf16x8& f, const float* eta8, bf16x8 (&out)[TA])
+{
+    if constexpr (PER_TOKEN) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = eta8[j] * (float)f[j];
+        terms8<TA>(x, out);
+    } else {
+        out[0] = f;
+    }
+}
+
+// The 10 upper tiles of M and the 16 tiles of B, spread over 4 waves.
+__device__ __constant__ const int kGramM[4][3][2] = {
+    {{0, 0}, {0, 1}, {0, 2}}, {{0, 3}, {1, 1}, {1, 2}}, {{1, 3}, {2, 2}, {-1, -1}}, {{2, 3}, {3, 3}, {-1, -1}}};
+
+template <bool PER_TOKEN>
+__global__ void __launch_bounds__(LT)
+lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
+               const float* __restrict__ etag, float eta_const, float* __restrict__ Mout,
+               float* __restrict__ Bout)
+{
+    constexpr int TA = PER_TOKEN ? 2 : 1;    // terms of the D-scaled operand
+    __shared__ GramSmem sm;
+    const int C = (N + b - 1) / b;
+    const int unit = blockIdx.x / C, c = blockIdx.x % C;
+    const int c0 = c * b, nt = min(b, N - c0);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const uint16_t* Ku = Kg + ((size_t)unit * N + c0) * LD;
+    const uint16_t* Vu = Vg + ((size_t)unit * N + c0) * LD;
+    const float* etau = PER_TOKEN ? etag + (size_t)unit * N + c0 : nullptr;
+
+    // wave w: B row tile w (4 tiles) + up to 3 upper M tiles
+    f32x16 accB[4], accM[3];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) accB[t] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < 3; ++t) accM[t] = f32x16{};
+
+    const int nstage = nt / GR_TOK;
+    uint4 pf[GR_PPT];
+    float pe = 0.f;
+    gram_issue<PER_TOKEN>(pf, pe, 0, tid, Ku, Vu, etau);
+    gram_commit<PER_TOKEN>(sm, 0, pf, pe, tid);
+    gram_issue<PER_TOKEN>(pf, pe, min(1, nstage - 1), tid, Ku, Vu, etau);   // unconditional: no branch around loads
+    __syncthreads();
+    for (int s = 0; s < nstage; ++s) {
+        const int buf = s & 1;
+        const uint16_t* kt = sm.k[buf];
+        const uint16_t* vt = sm.v[buf];
+#pragma unroll
+        for (int ks = 0; ks < GR_TOK / 16; ++ks) {
+            const float* er = sm.eta[buf] + 16 * ks + 8 * h;
+            bf16x8 aw[TA];
+            scaled_frag<PER_TOKEN, TA>(tok_major_frag(kt, 16 * ks, w, lane), er, aw);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bf16x8 bv = tok_major_frag(vt, 16 * ks, t, lane);
+#pragma unroll
+                for (int s2 = TA - 1; s2 >= 0; --s2) accB[t] = mfma_32x32x16(aw[s2], bv, accB[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const int r = kGramM[w][t][0], cc = kGramM[w][t][1];
+                if (r >= 0) {
+                    bf16x8 ar[TA];
+                    scaled_frag<PER_TOKEN, TA>(tok_major_frag(kt, 16 * ks, r, lane), er, ar);
+                    const bf16x8 bk = tok_major_frag(kt, 16 * ks, cc, lane);
+#pragma unroll
+                    for (int s2 = TA - 1; s2 >= 0; --s2) accM[t] = mfma_32x32x16(ar[s2], bk, accM[t]);
+                }
+            }
+        }
+        if (s + 1 < nstage) {
+            __syncthreads();            // everyone done with buffer buf ^ 1 (stage s - 1)
+            gram_commit<PER_TOKEN>(sm, buf ^ 1, pf, pe, tid);
+            gram_issue<PER_TOKEN>(pf, pe, min(s + 2, nstage - 1), tid, Ku, Vu, etau);
+            __syncthreads();
+        }
+    }
+
+    const float scale = PER_TOKEN ? 1.f : 2.f * eta_const;
+    const size_t base = ((size_t)unit * C + c) * LD * LD;
+    float* Mo = Mout + base;
+    float* Bo = Bout + base;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Bo[(32 * w + crow(i, h)) * LD + 32 * t + l32] = scale * accB[t][i];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+        const int r = kGramM[w][t][0], cc = kGramM[w][t][1];
+        if (r >= 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float v = scale * accM[t][i];
+                Mo[(32 * r + crow(i, h)) * LD + 32 * cc + l32] = v;
+                if (r != cc) Mo[(32 * cc + l32) * LD + 32 * r + crow(i, h)] = v;
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// lc_scan: W_{c+1} = W_c - M_c W_c + B_c for one (unit, 32-column block).
+// Wave w holds rows [32w, 32w+32) of the block as one 32x32 C tile.
+// ===========================================================================
+constexpr int SC_STRIDE = LD + 4;   // floats per column of the column-major LDS block
+
+__global__ void __launch_bounds__(LT)
+lc_scan_kernel(int N, int b, const float* __restrict__ W0, const float* __restrict__ Mg,
+               const float* __restrict__ Bg, uint16_t* __restrict__ WT, float* __restrict__ Wend)
+{
+    __shared__ __attribute__((aligned(16))) float wcol[32 * SC_STRIDE];   // [column][row]
+    const int C = (N + b - 1) / b;
+    const int unit = blockIdx.x >> 2, cb = blockIdx.x & 3;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int colg = 32 * cb + l32;   // global column of this lane
+
+    f32x16 acc;
+    const float* W0u = W0 + (size_t)unit * LD * LD;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = W0u[(32 * w + crow(i, h)) * LD + colg];
+
+    for (int c = 0; c < C; ++c) {
+        // publish W_c: column-major block in LDS, W_c^T terms in the workspace
+        uint16_t* wt = WT + ((size_t)unit * C + c) * 2 * LD * LD;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+            const int row0 = 32 * w + 8 * q + 4 * h;
+            *reinterpret_cast<float4*>(&wcol[l32 * SC_STRIDE + row0]) = v;
+            uint32_t p01[2], p23[2];   // [term] packed bf16 pairs of rows row0, row0+1 / row0+2, row0+3
+            split_pair<2>(v.x, v.y, p01);
+            split_pair<2>(v.z, v.w, p23);
+            // W_c^T[col][row0..row0+3], term 0 and term 1
+            *reinterpret_cast<uint2*>(wt + (size_t)colg * LD + row0) = make_uint2(p01[0], p23[0]);
+            *reinterpret_cast<uint2*>(wt + (size_t)LD * LD + (size_t)colg * LD + row0) =
+                make_uint2(p01[1], p23[1]);
+        }
+        __syncthreads();
+        const float* Mc = Mg + ((size_t)unit * C + c) * LD * LD;
+        const float* Bc = Bg + ((size_t)unit * C + c) * LD * LD;
+        f32x16 t = {};
+#pragma unroll
+        for (int ks = 0; ks < LD / 16; ++ks) {
+            // A = M_c rows 32w + l32, k = 16ks + 8h + 0..7 ; B = W_c rows k, column colg
+            const float4 a0 = *reinterpret_cast<const float4*>(Mc + (size_t)(32 * w + l32) * LD + 16 * ks + 8 * h);
+            const float4 a1 = *reinterpret_cast<const float4*>(Mc + (size_t)(32 * w + l32) * LD + 16 * ks + 8 * h + 4);
+            const float4 b0 = *reinterpret_cast<const float4*>(&wcol[l32 * SC_STRIDE + 16 * ks + 8 * h]);
+            const float4 b1 = *reinterpret_cast<const float4*>(&wcol[l32 * SC_STRIDE + 16 * ks + 8 * h + 4]);
+            const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float xb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            bf16x8 ta[2], tb[2];
+            terms8<2>(xa, ta);
+            terms8<2>(xb, tb);
+            t = mfma_32x32x16(ta[1], tb[0], t);
+            t = mfma_32x32x16(ta[0], tb[1], t);
+            t = mfma_32x32x16(ta[0], tb[0], t);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = (acc[i] - t[i]) + Bc[(size_t)(32 * w + crow(i, h)) * LD + colg];
+        __syncthreads();   // wcol is rewritten next step
+    }
+    float* We = Wend + (size_t)unit * LD * LD;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) We[(32 * w + crow(i, h)) * LD + colg] = acc[i];
+}
+
+// ===========================================================================
+// lc_grad: Gneg^T[d][t] = -D_t (K W_c - V)[t][d] for a 128-token block.
+// Wave w computes output rows d in [32w, 32w+32) for the 128 tokens.
+// ===========================================================================
+template <bool PER_TOKEN>
+__global__ void __launch_bounds__(LT)
+lc_grad_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
+               const float* __restrict__ etag, float eta_const, const uint16_t* __restrict__ WT,
+               uint16_t* __restrict__ GT)
+{
+    const int C = (N + b - 1) / b;
+    const int nblk = N / TB;
+    const int unit = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+    const int t0 = blk * TB, c = t0 / b;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const uint16_t* Ku = Kg + (size_t)unit * N * LD;
+    const uint16_t* Vu = Vg + (size_t)unit * N * LD;
+    const uint16_t* wt = WT + ((size_t)unit * C + c) * 2 * LD * LD;
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < LD / 16; ++ks) {
+        // A = W_c^T rows d = 32w + l32 (two terms), k = 16ks + 8h..
+        bf16x8 a[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            a[s] = *reinterpret_cast<const bf16x8*>(wt + (size_t)s * LD * LD + (size_t)(32 * w + l32) * LD +
+                                                     16 * ks + 8 * h);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            // B = K^T: column = token t0 + 32t + l32, k = feature
+            const bf16x8 bk = *reinterpret_cast<const bf16x8*>(Ku + (size_t)(t0 + 32 * t + l32) * LD + 16 * ks + 8 * h);
+            acc[t] = mfma_32x32x16(a[1], bk, acc[t]);
+            acc[t] = mfma_32x32x16(a[0], bk, acc[t]);
+        }
+    }
+    uint16_t* Gu = GT + (size_t)unit * LD * N;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int tok = t0 + 32 * t + l32;
+        const float dt = 2.f * (PER_TOKEN ? etag[(size_t)unit * N + tok] : eta_const);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int d0 = 32 * w + 8 * q + 4 * h;
+            const uint2 vv = *reinterpret_cast<const uint2*>(Vu + (size_t)tok * LD + d0);
+            const float v4[4] = {__builtin_bit_cast(float, vv.x << 16), __builtin_bit_cast(float, vv.x & 0xFFFF0000u),
+                                 __builtin_bit_cast(float, vv.y << 16), __builtin_bit_cast(float, vv.y & 0xFFFF0000u)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float gneg = -dt * (acc[t][4 * q + e] - v4[e]);
+                Gu[(size_t)(d0 + e) * N + tok] = (uint16_t)f16_bits_f(gneg);
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// lc_out: Z rows of one 128-query block: Z = Q W_c + sum_{key blocks j <= i}
+// mask(Q K_j^T) Gneg_j. Wave w owns queries [32w, 32w+32) of the block and all
+// 128 output features (four 32x32 C tiles).
+// ===========================================================================
+constexpr int OT_STRIDE = LD + 8;      // bf16 elements per LDS row
+
+struct OutSmem {
+    uint16_t k[TB * OT_STRIDE];        // K_j  [key][feature]
+    uint16_t g[LD * OT_STRIDE];        // Gneg_j^T [feature][key], fp16
+};
+
+// staging of one key block: K_j tile and Gneg_j^T tile, 16-byte pieces
+constexpr int OT_PIECES = 2 * TB * LD * 2 / 16;   // 4096
+constexpr int OT_PPT = OT_PIECES / LT;            // 16
+
+__device__ __forceinline__ void out_issue(uint4 (&pf)[OT_PPT], int kb, int tid, int N, const uint16_t* Ku,
+                                          const uint16_t* Gu)
+{
+#pragma unroll
+    for (int k = 0; k < OT_PPT; ++k) {
+        const int idx = tid + k * LT;
+        const int tensor = idx / (OT_PIECES / 2);
+        const int rem = idx % (OT_PIECES / 2);
+        const int row = rem / (LD / 8), piece = rem % (LD / 8);
+        const uint16_t* src = tensor == 0 ? Ku + (size_t)(kb * TB + row) * LD + piece * 8
+                                          : Gu + (size_t)row * N + kb * TB + piece * 8;
+        pf[k] = *reinterpret_cast<const uint4*>(src);
+    }
+}
+
+__device__ __forceinline__ void out_commit(OutSmem& sm, const uint4 (&pf)[OT_PPT], int tid)
+{
+#pragma unroll
+    for (int k = 0; k < OT_PPT; ++k) {
+        const int idx = tid + k * LT;
+        const int tensor = idx / (OT_PIECES / 2);
+        const int rem = idx % (OT_PIECES / 2);
+        const int row = rem / (LD / 8), piece = rem % (LD / 8);
+        uint16_t* dst = (tensor == 0 ? sm.k : sm.g) + row * OT_STRIDE + piece * 8;
+        *reinterpret_cast<uint4*>(dst) = pf[k];
+    }
+}
+
+__global__ void __launch_bounds__(LT)
+lc_out_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+              const uint16_t* __restrict__ WT, const uint16_t* __restrict__ GT, float* __restrict__ Zg)
+{
+    __shared__ OutSmem sm;
+    const int C = (N + b - 1) / b;
+    const int bpc = b / TB;                              // query blocks per chunk
+    const int units = gridDim.x / (C * bpc);
+    // heaviest blocks (largest in-chunk index, most key blocks) first
+    const int unit = blockIdx.x % units;
+    const int rank = blockIdx.x / units;
+    const int iin = bpc - 1 - rank / C;                  // block index inside the chunk
+    const int c = rank % C;
+    const int qblk = c * bpc + iin;
+    const int q0 = qblk * TB;
+    if (q0 >= N) return;                                 // past a short last chunk
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const uint16_t* Qu = Qg + (size_t)unit * N * LD;
+    const uint16_t* Ku = Kg + (size_t)unit * N * LD;
+    const uint16_t* Gu = GT + (size_t)unit * LD * N;
+    const uint16_t* wt = WT + ((size_t)unit * C + c) * 2 * LD * LD;
+    const int myq = q0 + 32 * w + l32;                   // query row of this lane (A operand / P column)
+
+    // Q rows as operands: A of Q W_c and B of K_j Q^T share the registers
+    bf16x8 qa[LD / 16];
+#pragma unroll
+    for (int ks = 0; ks < LD / 16; ++ks)
+        qa[ks] = *reinterpret_cast<const bf16x8*>(Qu + (size_t)myq * LD + 16 * ks + 8 * h);
+
+    // Z = Q W_c  (B = W_c: row k = input feature, column n = 32t + l32 -> W_c^T row n)
+    f32x16 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        acc[t] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < LD / 16; ++ks) {
+            const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(wt + (size_t)(32 * t + l32) * LD + 16 * ks + 8 * h);
+            const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(wt + (size_t)LD * LD + (size_t)(32 * t + l32) * LD +
+                                                               16 * ks + 8 * h);
+            acc[t] = mfma_32x32x16(qa[ks], b1, acc[t]);
+            acc[t] = mfma_32x32x16(qa[ks], b0, acc[t]);
+        }
+    }
+
+    // causal key blocks of the chunk
+    const int kb0 = c * bpc;
+    uint4 pf[OT_PPT];
+    out_issue(pf, kb0, tid, N, Ku, Gu);
+    for (int j = 0; j <= iin; ++j) {
+        __syncthreads();                 // previous tiles consumed
+        out_commit(sm, pf, tid);
+        out_issue(pf, kb0 + min(j + 1, iin), tid, N, Ku, Gu);   // unconditional: no branch around loads
+        __syncthreads();
+        const bool diag = (j == iin);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            // P^T = K_j Q^T for 32 keys: C layout lane l holds keys crow(i,h), query l32
+            f32x16 pt = {};
+#pragma unroll
+            for (int ks = 0; ks < LD / 16; ++ks) {
+                const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.k[(32 * kt + l32) * OT_STRIDE + 16 * ks + 8 * h]);
+                pt = mfma_32x32x16(ak, qa[ks], pt);
+            }
+            // Z += P Gneg_j with P as the A operand (row = query l32), keys in
+            // the permuted order of the C layout
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                float x[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int i = 8 * half + jj;
+                    const int key = 32 * kt + crow(i, h);             // key index inside the block
+                    const bool keep = !diag || key <= 32 * w + l32;
+                    x[jj] = keep ? pt[i] : 0.f;
+                }
+                const f16x8 pa = __builtin_bit_cast(
+                    f16x8, make_uint4(pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(x[4], x[5]),
+                                      pack_f16x2(x[6], x[7])));
+                const int kbase = 32 * kt + 16 * half;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint16_t* grow = &sm.g[(32 * t + l32) * OT_STRIDE + kbase];
+                    const uint2 lo = *reinterpret_cast<const uint2*>(grow + 4 * h);
+                    const uint2 hi = *reinterpret_cast<const uint2*>(grow + 8 + 4 * h);
+                    const f16x8 gb = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    acc[t] = mfma_32x32x16_f16(pa, gb, acc[t]);
+                }
+            }
+        }
+    }
+
+    float* Zu = Zg + (size_t)unit * N * LD;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Zu[(size_t)(q0 + 32 * w + crow(i, h)) * LD + 32 * t + l32] = acc[t][i];
+}
+
+}  // namespace
+
+size_t large_chunk_workspace_bytes(int B, int H, int N, int d, int b)
+{
+    if (d != LD || b % TB != 0 || N % TB != 0) return 0;
+    return lc_layout(B * H, N, b).total;
+}
+
+hipError_t launch_large_chunk_linear(const LinearArgs& a, hipStream_t stream)
+{
+    const int units = a.B * a.H;
+    const int C = (a.N + a.b - 1) / a.b;
+    const LcLayout L = lc_layout(units, a.N, a.b);
+    char* ws = static_cast<char*>(a.workspace);
+    float* M = reinterpret_cast<float*>(ws + L.m_off);
+    float* Bm = reinterpret_cast<float*>(ws + L.b_off);
+    uint16_t* WT = reinterpret_cast<uint16_t*>(ws + L.wt_off);
+    uint16_t* GT = reinterpret_cast<uint16_t*>(ws + L.g_off);
+    const uint16_t* Q = static_cast<const uint16_t*>(a.Q);
+    const uint16_t* K = static_cast<const uint16_t*>(a.K);
+    const uint16_t* V = static_cast<const uint16_t*>(a.V);
+    const bool per_token = a.eta != nullptr;
+
+    if (per_token)
+        hipLaunchKernelGGL((lc_gram_kernel<true>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, K, V, a.eta,
+                           a.eta_const, M, Bm);
+    else
+        hipLaunchKernelGGL((lc_gram_kernel<false>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, K, V, a.eta,
+                           a.eta_const, M, Bm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lc_scan_kernel, dim3(units * 4), dim3(LT), 0, stream, a.N, a.b, a.W0, M, Bm, WT, a.W_end);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int nblk = a.N / TB;
+    if (per_token)
+        hipLaunchKernelGGL((lc_grad_kernel<true>), dim3(units * nblk), dim3(LT), 0, stream, a.N, a.b, K, V, a.eta,
+                           a.eta_const, WT, GT);
+    else
+        hipLaunchKernelGGL((lc_grad_kernel<false>), dim3(units * nblk), dim3(LT), 0, stream, a.N, a.b, K, V, a.eta,
+                           a.eta_const, WT, GT);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(lc_out_kernel, dim3(units * C * (a.b / TB)), dim3(LT), 0, stream, a.N, a.b, Q, K, WT, GT,
+                       a.Z);
+    return hipGetLastError();
+}
+
 }  // namespace ttt

@@ -45,27 +45,8 @@ __device__ __forceinline__ void load_a8(const S* p0, const S* p1, bf16x8 (&out)[
     } else {
         float4 a = *reinterpret_cast<const float4*>(p0);
         float4 b = *reinterpret_cast<const float4*>(p1);
-        float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            __bf16 t[T];
-            split_terms<T>(x[j], t);
-#pragma unroll
-            for (int s = 0; s < T; ++s) out[s][j] = t[s];
-        }
-    }
-}
-
-// Four operand elements x[0..3] (fp32 values) as T bf16x4 terms.
-template <int T>
-__device__ __forceinline__ void terms4(const float (&x)[4], bf16x4 (&out)[T])
-{
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        __bf16 t[T];
-        split_terms<T>(x[j], t);
-#pragma unroll
-        for (int s = 0; s < T; ++s) out[s][j] = bf16_bits(t[s]);
+        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        terms8<T>(x, out);
     }
 }
 
@@ -184,14 +165,8 @@ __device__ __forceinline__ void xwave_row_sums(float (&a)[4], float (&b)[4], flo
 template <int T>
 __device__ __forceinline__ void b8_from_acc(const f32x4& t0, const f32x4& t1, bf16x8 (&out)[T])
 {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float x = j < 4 ? t0[j] : t1[j - 4];
-        __bf16 t[T];
-        split_terms<T>(x, t);
-#pragma unroll
-        for (int s = 0; s < T; ++s) out[s][j] = t[s];
-    }
+    const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+    terms8<T>(x, out);
 }
 
 }  // namespace smallb
