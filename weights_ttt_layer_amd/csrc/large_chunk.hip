@@ -65,12 +65,15 @@ __device__ __forceinline__ uint32_t f16_bits_f(float x) { return pack_f16x2(x, 0
 // store) and B_c = K^T D V for one (unit, chunk) per workgroup.
 // ===========================================================================
 constexpr int GR_TOK = 64;              // tokens per LDS stage
-constexpr int GR_STRIDE = LD + 8;       // bf16 elements per LDS row (272 B)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// byte offset of piece p (16 B) of row r in a 256-byte-row tile whose pieces
+// are XOR-swizzled (piece p of row r at slot p ^ (r % 16))
+__device__ __forceinline__ int swz(int r, int p) { return r * 256 + ((p ^ (r & 15)) << 4); }
 
 struct GramSmem {
-    uint16_t k[2][GR_TOK * GR_STRIDE];
-    uint16_t v[2][GR_TOK * GR_STRIDE];
-    float eta[2][GR_TOK];
+    uint16_t k[2][GR_TOK * LD];         // [token][feature], swizzled pieces
+    uint16_t v[2][GR_TOK * LD];
 };
 
 // Token-major operand fragment of a [tokens x 128] bf16 LDS tile: lane l gets
@@ -81,47 +84,30 @@ __device__ __forceinline__ bf16x8 tok_major_frag(const uint16_t* tile, int t0, i
     const int q = lane >> 4, r = lane & 15;
     const int row = t0 + 8 * (q >> 1) + (r >> 2);
     const int colm = 32 * f + 16 * (q & 1) + 4 * (r & 3);
-    const uint16_t* p0 = tile + row * GR_STRIDE + colm;
+    const char* base = reinterpret_cast<const char*>(tile);
+    const char* p0 = base + swz(row, colm >> 3) + (colm & 7) * 2;
+    const char* p1 = base + swz(row + 4, colm >> 3) + (colm & 7) * 2;
     const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(p0));
-    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(p0 + 4 * GR_STRIDE));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(p1));
     const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
     return __builtin_bit_cast(bf16x8, make_uint4(ua.x, ua.y, ub.x, ub.y));
 }
 
-// staging of one 64-token stage of K and V: 2 x 1024 16-byte pieces
-constexpr int GR_PIECES = 2 * GR_TOK * LD * 2 / 16;
-constexpr int GR_PPT = GR_PIECES / LT;
-
-template <bool PER_TOKEN>
-__device__ __forceinline__ void gram_issue(uint4 (&pf)[GR_PPT], float& pe, int s, int tid,
-                                           const uint16_t* Ku, const uint16_t* Vu, const float* etau)
+// Fill the K and V tiles of stage s with direct LDS loads: each tile is 16
+// wave instructions of 1 KB; wave w issues instructions 4w .. 4w+3 of each.
+__device__ __forceinline__ void gram_dma(GramSmem& sm, int buf, int s, int w, int lane, const uint16_t* Ku,
+                                         const uint16_t* Vu)
 {
 #pragma unroll
-    for (int k = 0; k < GR_PPT; ++k) {
-        const int idx = tid + k * LT;
-        const int tensor = idx / (GR_PIECES / 2);
-        const int rem = idx % (GR_PIECES / 2);
-        const int row = rem / (LD / 8), piece = rem % (LD / 8);
-        const uint16_t* src = (tensor == 0 ? Ku : Vu) + (size_t)(s * GR_TOK + row) * LD + piece * 8;
-        pf[k] = *reinterpret_cast<const uint4*>(src);
+    for (int k = 0; k < 4; ++k) {
+        const int sl = (4 * w + k) * 64 + lane;
+        const int r = sl >> 4, p = (sl & 15) ^ (r & 15);
+        const size_t off = (size_t)(s * GR_TOK + r) * LD + p * 8;
+        __builtin_amdgcn_global_load_lds(Ku + off, (lds_void*)(reinterpret_cast<char*>(sm.k[buf]) + (4 * w + k) * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(Vu + off, (lds_void*)(reinterpret_cast<char*>(sm.v[buf]) + (4 * w + k) * 1024),
+                                         16, 0, 0);
     }
-    if (PER_TOKEN) pe = etau[s * GR_TOK + (tid & (GR_TOK - 1))];
-}
-
-template <bool PER_TOKEN>
-__device__ __forceinline__ void gram_commit(GramSmem& sm, int buf, const uint4 (&pf)[GR_PPT], float pe,
-                                            int tid)
-{
-#pragma unroll
-    for (int k = 0; k < GR_PPT; ++k) {
-        const int idx = tid + k * LT;
-        const int tensor = idx / (GR_PIECES / 2);
-        const int rem = idx % (GR_PIECES / 2);
-        const int row = rem / (LD / 8), piece = rem % (LD / 8);
-        uint16_t* dst = (tensor == 0 ? sm.k[buf] : sm.v[buf]) + row * GR_STRIDE + piece * 8;
-        *reinterpret_cast<uint4*>(dst) = pf[k];
-    }
-    if (PER_TOKEN && tid < GR_TOK) sm.eta[buf][tid] = 2.f * pe;
 }
 
 // A operand of K^T D: the fragment itself (constant eta, D applied after the
@@ -130,9 +116,12 @@ template <bool PER_TOKEN, int TA>
 __device__ __forceinline__ void scaled_frag(const bf16x8& f, const float* eta8, bf16x8 (&out)[TA])
 {
     if constexpr (PER_TOKEN) {
+        const float4 e0 = *reinterpret_cast<const float4*>(eta8);
+        const float4 e1 = *reinterpret_cast<const float4*>(eta8 + 4);
+        const float e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
         float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = eta8[j] * (float)f[j];
+        for (int j = 0; j < 8; ++j) x[j] = 2.f * e[j] * (float)f[j];
         terms8<TA>(x, out);
     } else {
         out[0] = f;
@@ -167,19 +156,16 @@ lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
     for (int t = 0; t < 3; ++t) accM[t] = f32x16{};
 
     const int nstage = nt / GR_TOK;
-    uint4 pf[GR_PPT];
-    float pe = 0.f;
-    gram_issue<PER_TOKEN>(pf, pe, 0, tid, Ku, Vu, etau);
-    gram_commit<PER_TOKEN>(sm, 0, pf, pe, tid);
-    gram_issue<PER_TOKEN>(pf, pe, min(1, nstage - 1), tid, Ku, Vu, etau);   // unconditional: no branch around loads
-    __syncthreads();
+    gram_dma(sm, 0, 0, w, lane, Ku, Vu);
     for (int s = 0; s < nstage; ++s) {
         const int buf = s & 1;
+        __syncthreads();                                 // stage s landed; stage s-1 consumed
+        if (s + 1 < nstage) gram_dma(sm, buf ^ 1, s + 1, w, lane, Ku, Vu);
         const uint16_t* kt = sm.k[buf];
         const uint16_t* vt = sm.v[buf];
 #pragma unroll
         for (int ks = 0; ks < GR_TOK / 16; ++ks) {
-            const float* er = sm.eta[buf] + 16 * ks + 8 * h;
+            const float* er = PER_TOKEN ? etau + s * GR_TOK + 16 * ks + 8 * h : nullptr;
             bf16x8 aw[TA];
             scaled_frag<PER_TOKEN, TA>(tok_major_frag(kt, 16 * ks, w, lane), er, aw);
 #pragma unroll
@@ -199,12 +185,6 @@ lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
                     for (int s2 = TA - 1; s2 >= 0; --s2) accM[t] = mfma_32x32x16(ar[s2], bk, accM[t]);
                 }
             }
-        }
-        if (s + 1 < nstage) {
-            __syncthreads();            // everyone done with buffer buf ^ 1 (stage s - 1)
-            gram_commit<PER_TOKEN>(sm, buf ^ 1, pf, pe, tid);
-            gram_issue<PER_TOKEN>(pf, pe, min(s + 2, nstage - 1), tid, Ku, Vu, etau);
-            __syncthreads();
         }
     }
 
@@ -355,46 +335,37 @@ lc_grad_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
 }
 
 // ===========================================================================
-// lc_out: Z rows of one 128-query block: Z = Q W_c + sum_{key blocks j <= i}
-// mask(Q K_j^T) Gneg_j. Wave w owns queries [32w, 32w+32) of the block and all
-// 128 output features (four 32x32 C tiles).
+// lc_out: Z rows of one 256-query block: Z = Q W_c + sum_{key blocks j}
+// mask(Q K_j^T) Gneg_j over the causal 128-key blocks of the chunk. Wave w owns
+// queries [64w, 64w+64) of the block (two 32-query tiles) and all 128 output
+// features (four 32x32 C tiles per query tile), so every operand read from LDS
+// feeds two MFMAs. K_j and Gneg_j^T tiles (32 KB each) are double-buffered in
+// LDS and filled by direct global->LDS loads (no registers): one 16-byte piece
+// per lane, 1 KB per wave instruction. Rows are 256 B; the 16 pieces of row r
+// are stored XOR-swizzled (piece p at slot p ^ (r % 16)) so that 32 lanes
+// reading the same piece of 32 different rows hit distinct banks.
 // ===========================================================================
-constexpr int OT_STRIDE = LD + 8;      // bf16 elements per LDS row
+constexpr int QB = 256;                 // queries per lc_out workgroup
 
 struct OutSmem {
-    uint16_t k[TB * OT_STRIDE];        // K_j  [key][feature]
-    uint16_t g[LD * OT_STRIDE];        // Gneg_j^T [feature][key], fp16
+    uint16_t k[2][TB * LD];             // K_j [key][feature], swizzled pieces
+    uint16_t g[2][LD * TB];             // Gneg_j^T [feature][key], fp16, swizzled pieces
 };
 
-// staging of one key block: K_j tile and Gneg_j^T tile, 16-byte pieces
-constexpr int OT_PIECES = 2 * TB * LD * 2 / 16;   // 4096
-constexpr int OT_PPT = OT_PIECES / LT;            // 16
 
-__device__ __forceinline__ void out_issue(uint4 (&pf)[OT_PPT], int kb, int tid, int N, const uint16_t* Ku,
-                                          const uint16_t* Gu)
+// Fill one K tile and one Gneg^T tile (key block kb) with direct LDS loads:
+// wave w writes LDS pieces [(8w + k) * 64, +64) of each tile.
+__device__ __forceinline__ void out_dma(OutSmem& sm, int buf, int kb, int w, int lane, int N,
+                                        const uint16_t* Ku, const uint16_t* Gu)
 {
 #pragma unroll
-    for (int k = 0; k < OT_PPT; ++k) {
-        const int idx = tid + k * LT;
-        const int tensor = idx / (OT_PIECES / 2);
-        const int rem = idx % (OT_PIECES / 2);
-        const int row = rem / (LD / 8), piece = rem % (LD / 8);
-        const uint16_t* src = tensor == 0 ? Ku + (size_t)(kb * TB + row) * LD + piece * 8
-                                          : Gu + (size_t)row * N + kb * TB + piece * 8;
-        pf[k] = *reinterpret_cast<const uint4*>(src);
-    }
-}
-
-__device__ __forceinline__ void out_commit(OutSmem& sm, const uint4 (&pf)[OT_PPT], int tid)
-{
-#pragma unroll
-    for (int k = 0; k < OT_PPT; ++k) {
-        const int idx = tid + k * LT;
-        const int tensor = idx / (OT_PIECES / 2);
-        const int rem = idx % (OT_PIECES / 2);
-        const int row = rem / (LD / 8), piece = rem % (LD / 8);
-        uint16_t* dst = (tensor == 0 ? sm.k : sm.g) + row * OT_STRIDE + piece * 8;
-        *reinterpret_cast<uint4*>(dst) = pf[k];
+    for (int k = 0; k < 8; ++k) {
+        const int sl = (8 * w + k) * 64 + lane;          // 16-byte slot in the tile
+        const int r = sl >> 4, p = (sl & 15) ^ (r & 15); // row and the piece that lives there
+        char* kdst = reinterpret_cast<char*>(sm.k[buf]) + (8 * w + k) * 1024;
+        char* gdst = reinterpret_cast<char*>(sm.g[buf]) + (8 * w + k) * 1024;
+        __builtin_amdgcn_global_load_lds(Ku + (size_t)(kb * TB + r) * LD + p * 8, (lds_void*)kdst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(Gu + (size_t)r * N + kb * TB + p * 8, (lds_void*)gdst, 16, 0, 0);
     }
 }
 
@@ -404,96 +375,119 @@ lc_out_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* __r
 {
     __shared__ OutSmem sm;
     const int C = (N + b - 1) / b;
-    const int bpc = b / TB;                              // query blocks per chunk
+    const int bpc = (b + QB - 1) / QB;                   // query blocks per (full) chunk
     const int units = gridDim.x / (C * bpc);
     // heaviest blocks (largest in-chunk index, most key blocks) first
     const int unit = blockIdx.x % units;
     const int rank = blockIdx.x / units;
-    const int iin = bpc - 1 - rank / C;                  // block index inside the chunk
+    const int iin = bpc - 1 - rank / C;                  // query block index inside the chunk
     const int c = rank % C;
-    const int qblk = c * bpc + iin;
-    const int q0 = qblk * TB;
-    if (q0 >= N) return;                                 // past a short last chunk
+    const int c0 = c * b;
+    const int q0 = c0 + iin * QB;                        // first query of the block
+    const int cend = min(c0 + b, N);                     // end of the chunk
+    if (q0 >= cend) return;                              // past a short chunk
+    const int nq = min(QB, cend - q0);                   // 128 or 256
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const uint16_t* Qu = Qg + (size_t)unit * N * LD;
     const uint16_t* Ku = Kg + (size_t)unit * N * LD;
     const uint16_t* Gu = GT + (size_t)unit * LD * N;
     const uint16_t* wt = WT + ((size_t)unit * C + c) * 2 * LD * LD;
-    const int myq = q0 + 32 * w + l32;                   // query row of this lane (A operand / P column)
+    const bool active = 64 * w < nq;                     // this wave has queries
+    const int qw = q0 + 64 * w;                          // first query of this wave
+
+    // causal key blocks of the chunk visible to this query block
+    const int kb0 = c0 / TB;
+    const int nkb = (iin * QB + nq) / TB;
+    out_dma(sm, 0, kb0, w, lane, N, Ku, Gu);
 
     // Q rows as operands: A of Q W_c and B of K_j Q^T share the registers
-    bf16x8 qa[LD / 16];
+    bf16x8 qa[2][LD / 16];
 #pragma unroll
-    for (int ks = 0; ks < LD / 16; ++ks)
-        qa[ks] = *reinterpret_cast<const bf16x8*>(Qu + (size_t)myq * LD + 16 * ks + 8 * h);
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int ks = 0; ks < LD / 16; ++ks) {
+            const int q = active ? qw + 32 * qt + l32 : q0;
+            qa[qt][ks] = *reinterpret_cast<const bf16x8*>(Qu + (size_t)q * LD + 16 * ks + 8 * h);
+        }
 
-    // Z = Q W_c  (B = W_c: row k = input feature, column n = 32t + l32 -> W_c^T row n)
-    f32x16 acc[4];
+    // Z = Q W_c  (B = W_c: row k = input feature, column n -> W_c^T row n, two terms)
+    f32x16 acc[2][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        acc[t] = f32x16{};
+        acc[0][t] = f32x16{};
+        acc[1][t] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < LD / 16; ++ks) {
             const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(wt + (size_t)(32 * t + l32) * LD + 16 * ks + 8 * h);
             const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(wt + (size_t)LD * LD + (size_t)(32 * t + l32) * LD +
                                                                16 * ks + 8 * h);
-            acc[t] = mfma_32x32x16(qa[ks], b1, acc[t]);
-            acc[t] = mfma_32x32x16(qa[ks], b0, acc[t]);
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                acc[qt][t] = mfma_32x32x16(qa[qt][ks], b1, acc[qt][t]);
+                acc[qt][t] = mfma_32x32x16(qa[qt][ks], b0, acc[qt][t]);
+            }
         }
     }
 
-    // causal key blocks of the chunk
-    const int kb0 = c * bpc;
-    uint4 pf[OT_PPT];
-    out_issue(pf, kb0, tid, N, Ku, Gu);
-    for (int j = 0; j <= iin; ++j) {
-        __syncthreads();                 // previous tiles consumed
-        out_commit(sm, pf, tid);
-        out_issue(pf, kb0 + min(j + 1, iin), tid, N, Ku, Gu);   // unconditional: no branch around loads
-        __syncthreads();
-        const bool diag = (j == iin);
+    const int qin = iin * QB + 64 * w;                   // first query of the wave inside the chunk
+    for (int j = 0; j < nkb; ++j) {
+        __syncthreads();                                 // tile j landed; tile j-1 consumed
+        if (j + 1 < nkb) out_dma(sm, (j + 1) & 1, kb0 + j + 1, w, lane, N, Ku, Gu);
+        if (!active || TB * j > qin + 63) continue;      // every key of the block is after every query
+        const char* kt_base = reinterpret_cast<const char*>(sm.k[j & 1]);
+        const char* gt_base = reinterpret_cast<const char*>(sm.g[j & 1]);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-            // P^T = K_j Q^T for 32 keys: C layout lane l holds keys crow(i,h), query l32
-            f32x16 pt = {};
+            const int kmin = TB * j + 32 * kt;           // first key of the tile inside the chunk
+            if (kmin > qin + 63) continue;
+            // P^T = K Q^T for 32 keys x 64 queries
+            f32x16 pt[2] = {f32x16{}, f32x16{}};
 #pragma unroll
             for (int ks = 0; ks < LD / 16; ++ks) {
-                const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.k[(32 * kt + l32) * OT_STRIDE + 16 * ks + 8 * h]);
-                pt = mfma_32x32x16(ak, qa[ks], pt);
+                const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt_base + swz(32 * kt + l32, 2 * ks + h));
+                pt[0] = mfma_32x32x16(ak, qa[0][ks], pt[0]);
+                pt[1] = mfma_32x32x16(ak, qa[1][ks], pt[1]);
             }
-            // Z += P Gneg_j with P as the A operand (row = query l32), keys in
-            // the permuted order of the C layout
+            const bool need_mask = kmin + 31 > qin;      // some key of the tile is after some query
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                float x[8];
+                f16x8 pa[2];
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int i = 8 * half + jj;
-                    const int key = 32 * kt + crow(i, h);             // key index inside the block
-                    const bool keep = !diag || key <= 32 * w + l32;
-                    x[jj] = keep ? pt[i] : 0.f;
+                for (int qt = 0; qt < 2; ++qt) {
+                    float x[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const int i = 8 * half + jj;
+                        const bool keep = !need_mask || kmin + crow(i, h) <= qin + 32 * qt + l32;
+                        x[jj] = keep ? pt[qt][i] : 0.f;
+                    }
+                    pa[qt] = __builtin_bit_cast(
+                        f16x8, make_uint4(pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]),
+                                          pack_f16x2(x[4], x[5]), pack_f16x2(x[6], x[7])));
                 }
-                const f16x8 pa = __builtin_bit_cast(
-                    f16x8, make_uint4(pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(x[4], x[5]),
-                                      pack_f16x2(x[6], x[7])));
-                const int kbase = 32 * kt + 16 * half;
+                const int piece = 4 * kt + 2 * half;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const uint16_t* grow = &sm.g[(32 * t + l32) * OT_STRIDE + kbase];
-                    const uint2 lo = *reinterpret_cast<const uint2*>(grow + 4 * h);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(grow + 8 + 4 * h);
+                    const int row = 32 * t + l32;
+                    const uint2 lo = *reinterpret_cast<const uint2*>(gt_base + swz(row, piece) + 8 * h);
+                    const uint2 hi = *reinterpret_cast<const uint2*>(gt_base + swz(row, piece + 1) + 8 * h);
                     const f16x8 gb = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                    acc[t] = mfma_32x32x16_f16(pa, gb, acc[t]);
+                    acc[0][t] = mfma_32x32x16_f16(pa[0], gb, acc[0][t]);
+                    acc[1][t] = mfma_32x32x16_f16(pa[1], gb, acc[1][t]);
                 }
             }
         }
     }
 
+    if (!active) return;
     float* Zu = Zg + (size_t)unit * N * LD;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Zu[(size_t)(q0 + 32 * w + crow(i, h)) * LD + 32 * t + l32] = acc[t][i];
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                Zu[(size_t)(qw + 32 * qt + crow(i, h)) * LD + 32 * t + l32] = acc[qt][t][i];
 }
 
 }  // namespace
@@ -537,8 +531,8 @@ hipError_t launch_large_chunk_linear(const LinearArgs& a, hipStream_t stream)
         hipLaunchKernelGGL((lc_grad_kernel<false>), dim3(units * nblk), dim3(LT), 0, stream, a.N, a.b, K, V, a.eta,
                            a.eta_const, WT, GT);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(lc_out_kernel, dim3(units * C * (a.b / TB)), dim3(LT), 0, stream, a.N, a.b, Q, K, WT, GT,
-                       a.Z);
+    hipLaunchKernelGGL(lc_out_kernel, dim3(units * C * ((a.b + QB - 1) / QB)), dim3(LT), 0, stream, a.N, a.b, Q,
+                       K, WT, GT, a.Z);
     return hipGetLastError();
 }
 
