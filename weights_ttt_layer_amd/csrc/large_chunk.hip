@@ -13,10 +13,10 @@
 //   lc_gram : M_c and B_c for every (unit, chunk) at once (no dependence on W);
 //   lc_scan : the 16-step recurrence W_c -> W_{c+1} (one workgroup per
 //             (unit, 32-column block)); writes every W_c^T as two bf16 terms;
-//   lc_grad : Gneg^T = -(D (K W_c - V))^T per 128-token block, stored fp16;
+//   lc_grad : Gneg = -D (K W_c - V) per chunk, stored fp16 [token][feature];
 //   lc_out  : Z = Q W_c - tril(Q K^T) diag(...) E in 128x128 blocks: for every
 //             query block, the causal key blocks j <= i of its chunk.
-// Workspace (caller-provided): M, B (fp32), W_c^T terms (bf16), Gneg^T (fp16).
+// Workspace (caller-provided): M, B (fp32), W_c^T terms (bf16), Gneg (fp16).
 //
 // Precision: every product involving the fp32 state uses two bf16 terms (16
 // significant bits). The causal term tril(Q K^T) Gneg takes single fp16
@@ -216,6 +216,22 @@ lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
 // ===========================================================================
 constexpr int SC_STRIDE = LD + 4;   // floats per column of the column-major LDS block
 
+// Operands of one scan step: this lane's A rows of M_c (row 32w + l32, the
+// 8 k values of each k-step) and its 16 entries of B_c in the C layout.
+__device__ __forceinline__ void scan_load(const float* Mg, const float* Bg, int unit, int C, int c, int w, int l32,
+                                          int h, int colg, float4 (&ma)[LD / 16][2], float (&bv)[16])
+{
+    const float* Mc = Mg + ((size_t)unit * C + c) * LD * LD;
+    const float* Bc = Bg + ((size_t)unit * C + c) * LD * LD;
+#pragma unroll
+    for (int ks = 0; ks < LD / 16; ++ks) {
+        ma[ks][0] = *reinterpret_cast<const float4*>(Mc + (size_t)(32 * w + l32) * LD + 16 * ks + 8 * h);
+        ma[ks][1] = *reinterpret_cast<const float4*>(Mc + (size_t)(32 * w + l32) * LD + 16 * ks + 8 * h + 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bv[i] = Bc[(size_t)(32 * w + crow(i, h)) * LD + colg];
+}
+
 __global__ void __launch_bounds__(LT)
 lc_scan_kernel(int N, int b, const float* __restrict__ W0, const float* __restrict__ Mg,
                const float* __restrict__ Bg, uint16_t* __restrict__ WT, float* __restrict__ Wend)
@@ -231,6 +247,9 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const float* __restri
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = W0u[(32 * w + crow(i, h)) * LD + colg];
 
+    float4 ma[LD / 16][2];
+    float bv[16];
+    scan_load(Mg, Bg, unit, C, 0, w, l32, h, colg, ma, bv);
     for (int c = 0; c < C; ++c) {
         // publish W_c: column-major block in LDS, W_c^T terms in the workspace
         uint16_t* wt = WT + ((size_t)unit * C + c) * 2 * LD * LD;
@@ -248,17 +267,18 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const float* __restri
                 make_uint2(p01[1], p23[1]);
         }
         __syncthreads();
-        const float* Mc = Mg + ((size_t)unit * C + c) * LD * LD;
-        const float* Bc = Bg + ((size_t)unit * C + c) * LD * LD;
+        // prefetch M_{c+1}, B_{c+1} (clamped: the last step reloads its own)
+        float4 mn[LD / 16][2];
+        float bn[16];
+        scan_load(Mg, Bg, unit, C, min(c + 1, C - 1), w, l32, h, colg, mn, bn);
         f32x16 t = {};
 #pragma unroll
         for (int ks = 0; ks < LD / 16; ++ks) {
             // A = M_c rows 32w + l32, k = 16ks + 8h + 0..7 ; B = W_c rows k, column colg
-            const float4 a0 = *reinterpret_cast<const float4*>(Mc + (size_t)(32 * w + l32) * LD + 16 * ks + 8 * h);
-            const float4 a1 = *reinterpret_cast<const float4*>(Mc + (size_t)(32 * w + l32) * LD + 16 * ks + 8 * h + 4);
             const float4 b0 = *reinterpret_cast<const float4*>(&wcol[l32 * SC_STRIDE + 16 * ks + 8 * h]);
             const float4 b1 = *reinterpret_cast<const float4*>(&wcol[l32 * SC_STRIDE + 16 * ks + 8 * h + 4]);
-            const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float xa[8] = {ma[ks][0].x, ma[ks][0].y, ma[ks][0].z, ma[ks][0].w,
+                                 ma[ks][1].x, ma[ks][1].y, ma[ks][1].z, ma[ks][1].w};
             const float xb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
             bf16x8 ta[2], tb[2];
             terms8<2>(xa, ta);
@@ -268,7 +288,14 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const float* __restri
             t = mfma_32x32x16(ta[0], tb[0], t);
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = (acc[i] - t[i]) + Bc[(size_t)(32 * w + crow(i, h)) * LD + colg];
+        for (int i = 0; i < 16; ++i) acc[i] = (acc[i] - t[i]) + bv[i];
+#pragma unroll
+        for (int ks = 0; ks < LD / 16; ++ks) {
+            ma[ks][0] = mn[ks][0];
+            ma[ks][1] = mn[ks][1];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bv[i] = bn[i];
         __syncthreads();   // wcol is rewritten next step
     }
     float* We = Wend + (size_t)unit * LD * LD;
@@ -277,58 +304,91 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const float* __restri
 }
 
 // ===========================================================================
-// lc_grad: Gneg^T[d][t] = -D_t (K W_c - V)[t][d] for a 128-token block.
-// Wave w computes output rows d in [32w, 32w+32) for the 128 tokens.
+// lc_grad: Gneg[t][d] = -D_t (K W_c - V)[t][d] for every token of one chunk.
+// One workgroup per (unit, chunk). W_c^T (two bf16 terms, 64 KB) is staged once
+// in LDS by direct loads and is the A operand (wave w: output features
+// [32w, 32w+32)); the B operand is K^T, i.e. K rows straight from global memory
+// (four 32-token tiles per 128-token block, prefetched a block ahead). The C
+// layout then holds, per lane, one token and four consecutive features, so V is
+// read and Gneg written as 8-byte row segments, with no barrier in the loop.
 // ===========================================================================
+struct GradSmem {
+    uint16_t wt[2][LD * LD];             // W_c^T [dout][din], term 0 and 1, swizzled rows
+};
+
 template <bool PER_TOKEN>
 __global__ void __launch_bounds__(LT)
 lc_grad_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
                const float* __restrict__ etag, float eta_const, const uint16_t* __restrict__ WT,
-               uint16_t* __restrict__ GT)
+               uint16_t* __restrict__ Gg)
 {
+    __shared__ GradSmem sm;
     const int C = (N + b - 1) / b;
-    const int nblk = N / TB;
-    const int unit = blockIdx.x / nblk, blk = blockIdx.x % nblk;
-    const int t0 = blk * TB, c = t0 / b;
+    const int unit = blockIdx.x / C, c = blockIdx.x % C;
+    const int c0 = c * b, nblk = min(b, N - c0) / TB;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const uint16_t* Ku = Kg + (size_t)unit * N * LD;
     const uint16_t* Vu = Vg + (size_t)unit * N * LD;
     const uint16_t* wt = WT + ((size_t)unit * C + c) * 2 * LD * LD;
+    uint16_t* Gu = Gg + (size_t)unit * N * LD;
 
-    f32x16 acc[4];
+    // W_c^T terms: 4096 16-byte pieces, 16 wave instructions per wave
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
+    for (int k = 0; k < 16; ++k) {
+        const int ins = 16 * w + k;
+        const int sl = ins * 64 + lane;
+        const int term = sl >> 11, rem = sl & 2047;
+        const int r = rem >> 4, pc = (rem & 15) ^ (r & 15);
+        __builtin_amdgcn_global_load_lds(wt + (size_t)term * LD * LD + r * LD + pc * 8,
+                                         (lds_void*)(reinterpret_cast<char*>(&sm.wt[0][0]) + ins * 1024), 16, 0, 0);
+    }
+    // K rows of the first block (B operand, lane: token 32tt + l32)
+    bf16x8 kb[4][LD / 16];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int ks = 0; ks < LD / 16; ++ks)
+            kb[tt][ks] = *reinterpret_cast<const bf16x8*>(Ku + (size_t)(c0 + 32 * tt + l32) * LD + 16 * ks + 8 * h);
+    __syncthreads();
+
+    // A operands (W_c^T rows 32w + l32, two terms) stay in registers for the chunk
+    const char* wtb = reinterpret_cast<const char*>(&sm.wt[0][0]);
+    bf16x8 wa[LD / 16][2];
 #pragma unroll
     for (int ks = 0; ks < LD / 16; ++ks) {
-        // A = W_c^T rows d = 32w + l32 (two terms), k = 16ks + 8h..
-        bf16x8 a[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-            a[s] = *reinterpret_cast<const bf16x8*>(wt + (size_t)s * LD * LD + (size_t)(32 * w + l32) * LD +
-                                                     16 * ks + 8 * h);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            // B = K^T: column = token t0 + 32t + l32, k = feature
-            const bf16x8 bk = *reinterpret_cast<const bf16x8*>(Ku + (size_t)(t0 + 32 * t + l32) * LD + 16 * ks + 8 * h);
-            acc[t] = mfma_32x32x16(a[1], bk, acc[t]);
-            acc[t] = mfma_32x32x16(a[0], bk, acc[t]);
-        }
+        wa[ks][0] = *reinterpret_cast<const bf16x8*>(wtb + swz(32 * w + l32, 2 * ks + h));
+        wa[ks][1] = *reinterpret_cast<const bf16x8*>(wtb + LD * LD * 2 + swz(32 * w + l32, 2 * ks + h));
     }
-    uint16_t* Gu = GT + (size_t)unit * LD * N;
+
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int tb0 = c0 + blk * TB;
+        const int tn = (blk + 1 < nblk) ? tb0 + TB : tb0;      // next block (clamped: unconditional loads)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int tok = t0 + 32 * t + l32;
-        const float dt = 2.f * (PER_TOKEN ? etag[(size_t)unit * N + tok] : eta_const);
+        for (int tt = 0; tt < 4; ++tt) {
+            // G^T tile: rows = features 32w + crow(i,h), column = token tb0 + 32tt + l32
+            f32x16 acc = {};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int d0 = 32 * w + 8 * q + 4 * h;
-            const uint2 vv = *reinterpret_cast<const uint2*>(Vu + (size_t)tok * LD + d0);
-            const float v4[4] = {__builtin_bit_cast(float, vv.x << 16), __builtin_bit_cast(float, vv.x & 0xFFFF0000u),
-                                 __builtin_bit_cast(float, vv.y << 16), __builtin_bit_cast(float, vv.y & 0xFFFF0000u)};
+            for (int ks = 0; ks < LD / 16; ++ks) {
+                acc = mfma_32x32x16(wa[ks][1], kb[tt][ks], acc);
+                acc = mfma_32x32x16(wa[ks][0], kb[tt][ks], acc);
+            }
+            const int tok = tb0 + 32 * tt + l32;
+            // prefetch this tile's rows of the next block
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float gneg = -dt * (acc[t][4 * q + e] - v4[e]);
-                Gu[(size_t)(d0 + e) * N + tok] = (uint16_t)f16_bits_f(gneg);
+            for (int ks = 0; ks < LD / 16; ++ks)
+                kb[tt][ks] = *reinterpret_cast<const bf16x8*>(Ku + (size_t)(tn + 32 * tt + l32) * LD + 16 * ks + 8 * h);
+            const float dt = 2.f * (PER_TOKEN ? etag[(size_t)unit * N + tok] : eta_const);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d0 = 32 * w + 8 * q4 + 4 * h;
+                const uint2 vv = *reinterpret_cast<const uint2*>(Vu + (size_t)tok * LD + d0);
+                const float v4[4] = {__builtin_bit_cast(float, vv.x << 16), __builtin_bit_cast(float, vv.x & 0xFFFF0000u),
+                                     __builtin_bit_cast(float, vv.y << 16), __builtin_bit_cast(float, vv.y & 0xFFFF0000u)};
+                float g[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) g[e] = -dt * (acc[4 * q4 + e] - v4[e]);
+                *reinterpret_cast<uint2*>(Gu + (size_t)tok * LD + d0) =
+                    make_uint2(pack_f16x2(g[0], g[1]), pack_f16x2(g[2], g[3]));
             }
         }
     }
@@ -336,7 +396,8 @@ lc_grad_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
 
 // ===========================================================================
 // lc_out: Z rows of one 256-query block: Z = Q W_c + sum_{key blocks j}
-// mask(Q K_j^T) Gneg_j over the causal 128-key blocks of the chunk. Wave w owns
+// mask(Q K_j^T) Gneg_j over the causal 128-key blocks of the chunk (Gneg_j
+// token-major, its key-contracted B operand read with transpose reads). Wave w owns
 // queries [64w, 64w+64) of the block (two 32-query tiles) and all 128 output
 // features (four 32x32 C tiles per query tile), so every operand read from LDS
 // feeds two MFMAs. K_j and Gneg_j^T tiles (32 KB each) are double-buffered in
@@ -349,7 +410,7 @@ constexpr int QB = 256;                 // queries per lc_out workgroup
 
 struct OutSmem {
     uint16_t k[2][TB * LD];             // K_j [key][feature], swizzled pieces
-    uint16_t g[2][LD * TB];             // Gneg_j^T [feature][key], fp16, swizzled pieces
+    uint16_t g[2][TB * LD];             // Gneg_j [key][feature], fp16, swizzled pieces
 };
 
 
@@ -365,7 +426,7 @@ __device__ __forceinline__ void out_dma(OutSmem& sm, int buf, int kb, int w, int
         char* kdst = reinterpret_cast<char*>(sm.k[buf]) + (8 * w + k) * 1024;
         char* gdst = reinterpret_cast<char*>(sm.g[buf]) + (8 * w + k) * 1024;
         __builtin_amdgcn_global_load_lds(Ku + (size_t)(kb * TB + r) * LD + p * 8, (lds_void*)kdst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(Gu + (size_t)r * N + kb * TB + p * 8, (lds_void*)gdst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(Gu + (size_t)(kb * TB + r) * LD + p * 8, (lds_void*)gdst, 16, 0, 0);
     }
 }
 
@@ -430,6 +491,8 @@ lc_out_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* __r
     }
 
     const int qin = iin * QB + 64 * w;                   // first query of the wave inside the chunk
+    const int q16 = lane >> 4, r16 = lane & 15;          // transpose-read lane coordinates
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
     for (int j = 0; j < nkb; ++j) {
         __syncthreads();                                 // tile j landed; tile j-1 consumed
         if (j + 1 < nkb) out_dma(sm, (j + 1) & 1, kb0 + j + 1, w, lane, N, Ku, Gu);
@@ -465,13 +528,19 @@ lc_out_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* __r
                         f16x8, make_uint4(pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]),
                                           pack_f16x2(x[4], x[5]), pack_f16x2(x[6], x[7])));
                 }
-                const int piece = 4 * kt + 2 * half;
+                const int kbase = 32 * kt + 16 * half;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const int row = 32 * t + l32;
-                    const uint2 lo = *reinterpret_cast<const uint2*>(gt_base + swz(row, piece) + 8 * h);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(gt_base + swz(row, piece + 1) + 8 * h);
-                    const f16x8 gb = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    // B operand: keys kbase + {4h..4h+3, 8+4h..8+4h+3} of feature 32t + l32,
+                    // two transpose reads of the token-major tile
+                    const int grow = kbase + 4 * h + (r16 >> 2);
+                    const int gcol = 32 * t + 16 * (q16 & 1) + 4 * (r16 & 3);
+                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_bf16x4*)(gt_base + swz(grow, gcol >> 3) + (gcol & 7) * 2));
+                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_bf16x4*)(gt_base + swz(grow + 8, gcol >> 3) + (gcol & 7) * 2));
+                    const uint2 ul = __builtin_bit_cast(uint2, lo), uh = __builtin_bit_cast(uint2, hi);
+                    const f16x8 gb = __builtin_bit_cast(f16x8, make_uint4(ul.x, ul.y, uh.x, uh.y));
                     acc[0][t] = mfma_32x32x16_f16(pa[0], gb, acc[0][t]);
                     acc[1][t] = mfma_32x32x16_f16(pa[1], gb, acc[1][t]);
                 }
@@ -523,12 +592,11 @@ hipError_t launch_large_chunk_linear(const LinearArgs& a, hipStream_t stream)
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lc_scan_kernel, dim3(units * 4), dim3(LT), 0, stream, a.N, a.b, a.W0, M, Bm, WT, a.W_end);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int nblk = a.N / TB;
     if (per_token)
-        hipLaunchKernelGGL((lc_grad_kernel<true>), dim3(units * nblk), dim3(LT), 0, stream, a.N, a.b, K, V, a.eta,
+        hipLaunchKernelGGL((lc_grad_kernel<true>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, K, V, a.eta,
                            a.eta_const, WT, GT);
     else
-        hipLaunchKernelGGL((lc_grad_kernel<false>), dim3(units * nblk), dim3(LT), 0, stream, a.N, a.b, K, V, a.eta,
+        hipLaunchKernelGGL((lc_grad_kernel<false>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, K, V, a.eta,
                            a.eta_const, WT, GT);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(lc_out_kernel, dim3(units * C * ((a.b + QB - 1) / QB)), dim3(LT), 0, stream, a.N, a.b, Q,
