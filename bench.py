@@ -1,6 +1,7 @@
 """Benchmark of the TTT-layer forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-b2048] [--copy-calibration]
 
 A step is one forward pass of the layer over one batch of synthetic input (all
 chunks of every (sequence, head) unit), launched through the C ABI. Inputs are
@@ -9,12 +10,15 @@ with LayerNorm+residual, bf16 Q/K/V, B=8 H=12 N=2048 d=64 b=16 with per-token
 step sizes. To keep the 256 MB Infinity Cache from serving repeated reads, the
 steps rotate over four distinct device copies of the inputs and outputs.
 
+With the default workload the line also carries a "b2048" object: the same
+measurement for the large-chunk workload (plain TTT-Linear, bf16, B=1 H=16
+N=32768 d=128 b=2048), whose roofline is the bf16 MFMA peak.
+
 Prints ONE JSON line (stdout). Diagnostics go to stderr.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -27,19 +31,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from weights_ttt_layer_amd import workloads as wlm  # noqa: E402
+from weights_ttt_layer_amd.profile_summary import COPY_BYTES, source_digest  # noqa: E402
 
 DEFAULT_WORKLOAD = "linear_ln_bf16_B8H12N2048_d64_b16"
+LARGE_WORKLOAD = "linear_bf16_B1H16N32768_d128_b2048"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 ROTATE = 4
 METRIC = "TTT layer fwd tokens/sec"
-
-KERNEL_SOURCES = {
-    "plain": ["smallb_linear.hip", "device_common.h"],
-    "ln": ["smallb_linear.hip", "device_common.h"],
-    "mlp": ["smallb_mlp.hip", "device_common.h"],
-    "large": ["large_chunk.hip", "device_common.h"],
-}
 
 
 def log(*a):
@@ -82,14 +81,6 @@ def algorithmic_flops(wl: wlm.Workload) -> int:
     return f * wl.B * wl.H
 
 
-def source_digest(kind_key: str) -> str:
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES[kind_key]:
-        with open(os.path.join(ROOT, "weights_ttt_layer_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(wl: wlm.Workload, kind_key: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when there is none for this workload or the kernel source changed since."""
@@ -108,6 +99,8 @@ def measured_traffic(wl: wlm.Workload, kind_key: str):
 # ---------------------------------------------------------------------------
 
 def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int):
+    """Average time of one launch (ms), from HIP events recorded on the stream the
+    launches go to, over `steps` back-to-back launches after `warmup` untimed ones."""
     import torch
     from weights_ttt_layer_amd import linear_fwd, linear_workspace_bytes, mlp_fwd
 
@@ -151,42 +144,89 @@ def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int):
     ms_total = start.elapsed_time(end)
     z = outs[(steps - 1) % ROTATE][0]
     finite = bool(torch.isfinite(z).all().item())
+    del sets, outs, base
+    torch.cuda.empty_cache()
     return ms_total / steps, finite
+
+
+def copy_calibration(reps: int = 3):
+    """Plain device-to-device copies of COPY_BYTES: the known traffic that scales
+    the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def measure(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int):
+    """tokens/s and the roofline object of one workload."""
+    ms, finite = run_gpu(wl, inp, steps, warmup)
+    if not finite:
+        log(f"[bench] WARNING: non-finite output in {wl.name}")
+    sec = ms / 1e3
+    tokens = wl.B * wl.N
+    large = wl.b >= 256
+    kind_key = "large" if large else wl.kind
+    nbytes = algorithmic_bytes(wl)
+    flops = algorithmic_flops(wl)
+    if large:
+        roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(wl, kind_key)
+    log(f"[bench] {wl.name}: {ms*1e3:.1f} us/step, {tokens/sec:.4g} tokens/s, "
+        f"{nbytes/sec/1e9:.1f} GB/s algorithmic, {flops/sec/1e12:.2f} TFLOP/s algorithmic")
+    return ms, tokens / sec, nbytes, flops, roof
 
 
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle as it stands
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl: wlm.Workload, inp: wlm.Inputs, max_units: int):
+def cpu_baseline(wl: wlm.Workload, inp: wlm.Inputs, max_units: int, min_wall: float = 1.5):
+    """The mini-batch primal fp64 oracle over whole sequences of the same inputs:
+    one untimed run, then repeated runs until `min_wall` seconds have passed (at
+    least three); the best run gives the rate."""
     import oracle
-    threads = len(os.sched_getaffinity(0))
-    threads = min(threads, 16)
-    units = [(bi, hi) for bi in range(wl.B) for hi in range(wl.H)][:max_units]
-    sub_b = sorted({u[0] for u in units})
-    # the sample: the first `max_units` units in (b, h) order, whole sequences
-    q, k, v = inp.f64("q"), inp.f64("k"), inp.f64("v")
-    nb = len(sub_b)
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    nb = max(1, min(wl.B, max_units // wl.H))
     sl = slice(0, nb)
+    q, k, v = inp.f64("q")[sl], inp.f64("k")[sl], inp.f64("v")[sl]
     eta = inp.eta_f64()[sl]
-    t0 = time.perf_counter()
-    if wl.kind == "mlp":
-        oracle.mlp(oracle.MINIBATCH, q[sl], k[sl], v[sl], eta, inp.f64("w1")[sl], inp.f64("w2")[sl],
-                   wl.b, inp.f64("gamma"), inp.f64("beta"), wl.ln_eps, nthreads=threads)
-    else:
-        kind = oracle.LN if wl.kind == "ln" else oracle.PLAIN
-        oracle.linear(oracle.MINIBATCH, kind, q[sl], k[sl], v[sl], eta, inp.f64("w0")[sl], wl.b,
-                      None if inp.gamma is None else inp.f64("gamma"),
-                      None if inp.beta is None else inp.f64("beta"), wl.ln_eps, nthreads=threads)
-    dt = time.perf_counter() - t0
-    token_heads = nb * wl.H * wl.N
+
+    def once():
+        t0 = time.perf_counter()
+        if wl.kind == "mlp":
+            oracle.mlp(oracle.MINIBATCH, q, k, v, eta, inp.f64("w1")[sl], inp.f64("w2")[sl],
+                       wl.b, inp.f64("gamma"), inp.f64("beta"), wl.ln_eps, nthreads=threads)
+        else:
+            kind = oracle.LN if wl.kind == "ln" else oracle.PLAIN
+            oracle.linear(oracle.MINIBATCH, kind, q, k, v, eta, inp.f64("w0")[sl], wl.b,
+                          None if inp.gamma is None else inp.f64("gamma"),
+                          None if inp.beta is None else inp.f64("beta"), wl.ln_eps, nthreads=threads)
+        return time.perf_counter() - t0
+
+    once()
+    times, total = [], 0.0
+    while len(times) < 3 or total < min_wall:
+        times.append(once())
+        total += times[-1]
+    best = min(times)
     return {
-        "value": token_heads / wl.H / dt,
+        "value": nb * wl.N / best,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"mini-batch primal fp64 oracle over {nb} of {wl.B} sequences x {wl.H} heads x "
-                  f"{wl.N} tokens ({dt:.2f} s wall)",
+                  f"{wl.N} tokens, best of {len(times)} runs ({best:.3f} s each at best, "
+                  f"{total:.1f} s wall in all)",
     }
 
 
@@ -197,6 +237,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(wlm.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-b2048", action="store_true",
+                    help="skip the large-chunk measurement that accompanies the default workload")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain device copies of a known size (counter calibration)")
     ap.add_argument("--cpu-units", type=int, default=96,
                     help="cap on (sequence, head) units in the CPU-baseline sample")
     args = ap.parse_args()
@@ -212,24 +256,20 @@ def main():
     inp = wlm.workload_inputs(idx)
     log(f"[bench] workload {wl.name}: generated inputs")
 
-    ms, finite = run_gpu(wl, inp, args.steps, args.warmup)
-    if not finite:
-        log("[bench] WARNING: non-finite output")
-    sec = ms / 1e3
-    tokens = wl.B * wl.N
-    large = wl.b >= 256
-    kind_key = "large" if large else wl.kind
-    nbytes = algorithmic_bytes(wl)
-    flops = algorithmic_flops(wl)
-    if large:
-        roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_BF16_PEAK_TFS,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(wl, kind_key)
-    log(f"[bench] {ms*1e3:.1f} us/step, {tokens/sec:.4g} tokens/s, {nbytes/sec/1e9:.1f} GB/s "
-        f"algorithmic, {flops/sec/1e12:.2f} TFLOP/s algorithmic")
+    ms, value, nbytes, flops, roof = measure(wl, inp, args.steps, args.warmup)
+
+    b2048 = None
+    if wl.name == DEFAULT_WORKLOAD and not args.no_b2048:
+        li = [w.name for w in wlm.WORKLOADS].index(LARGE_WORKLOAD)
+        lwl = wlm.WORKLOADS[li]
+        lms, lval, lbytes, lflops, lroof = measure(lwl, wlm.workload_inputs(li), args.steps, args.warmup)
+        b2048 = {"workload": lwl.name, "value": lval, "unit": "tokens/s", "ms_per_step": lms,
+                 "token_heads_per_s": lval * lwl.H, "algorithmic_bytes": lbytes,
+                 "algorithmic_flops": lflops, "roofline": lroof}
+
+    if args.copy_calibration:
+        copy_calibration()
+        log(f"[bench] calibration copies of {COPY_BYTES} bytes done")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -238,7 +278,7 @@ def main():
 
     rec = {
         "metric": METRIC,
-        "value": tokens / sec,
+        "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -251,11 +291,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "kind": wl.kind, "B": wl.B, "H": wl.H, "N": wl.N,
                    "d": wl.d, "b": wl.b, "qkv_dtype": wl.dtype, "state_dtype": "f32",
-                   "eta": wl.eta, "token_heads_per_s": tokens * wl.H / sec,
+                   "eta": wl.eta, "token_heads_per_s": value * wl.H,
                    "algorithmic_bytes": nbytes, "algorithmic_flops": flops},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if b2048 is not None:
+        rec["b2048"] = b2048
     print(json.dumps(rec), flush=True)
 
 

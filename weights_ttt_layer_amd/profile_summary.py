@@ -1,0 +1,206 @@
+"""Turn rocprofv3 CSV output of ``bench.py`` into the short text and JSON
+summaries kept under ``profiles/``.
+
+    python -m weights_ttt_layer_amd.profile_summary stats   <rocprof dir> <out.txt> --cmd "<command>"
+    python -m weights_ttt_layer_amd.profile_summary traffic <fetch dir> <write dir> <workload> --cmd "<cmd>" --cmd "<cmd>"
+
+``stats`` reads ``*kernel_stats.csv`` (``rocprofv3 --kernel-trace --stats
+--output-format csv``) and writes the per-kernel call count and durations of
+this library's kernels.
+
+``traffic`` reads two counter runs (``rocprofv3 --pmc FETCH_SIZE`` and
+``--pmc WRITE_SIZE`` over ``bench.py --copy-calibration``). FETCH_SIZE and
+WRITE_SIZE are KiB per dispatch of traffic between the L2 and memory. The
+calibration step of the bench copies COPY_BYTES with a plain device-to-device
+copy kernel; the ratio (known bytes / counted bytes) of that copy scales the
+counts of this library's kernels, giving HBM bytes per launch. The record
+carries a digest of the kernel sources so that a later change of the kernels
+makes the bench report the traffic as unknown rather than stale.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "weights_ttt_layer_amd", "csrc")
+
+# plain copy used to calibrate the memory-traffic counters (bench.py --copy-calibration)
+COPY_BYTES = 512 * 1024 * 1024
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+# kernel sources behind each path; their digest tags a traffic record
+KERNEL_SOURCES = {
+    "plain": ["smallb_linear.hip", "smallb_common.h", "device_common.h"],
+    "ln": ["smallb_linear.hip", "smallb_common.h", "device_common.h"],
+    "mlp": ["smallb_mlp.hip", "smallb_common.h", "device_common.h"],
+    "large": ["large_chunk.hip", "device_common.h"],
+}
+
+OUR_KERNELS = ("smallb_linear_kernel", "smallb_mlp_kernel", "lc_gram_kernel", "lc_scan_kernel",
+               "lc_grad_kernel", "lc_out_kernel")
+
+# kernel-name prefixes launched by one call of each path
+PATH_KERNELS = {
+    "plain": ("smallb_linear_kernel<0",),
+    "ln": ("smallb_linear_kernel<1",),
+    "mlp": ("smallb_mlp_kernel",),
+    "large": ("lc_gram_kernel", "lc_scan_kernel", "lc_grad_kernel", "lc_out_kernel"),
+}
+
+
+def source_digest(path_key: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[path_key]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(full: str) -> str:
+    """'void ttt::(anonymous namespace)::lc_out_kernel<true>(int, ...)' -> 'lc_out_kernel<true>'."""
+    s = full.replace("(anonymous namespace)::", "").replace("void ", "").replace("ttt::", "")
+    depth, out = 0, []
+    for ch in s:
+        if ch == "(" and depth == 0:
+            break
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        out.append(ch)
+    return "".join(out).strip()
+
+
+def is_ours(name: str) -> bool:
+    return any(k in name for k in OUR_KERNELS)
+
+
+def find_one(d: str, pattern: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    if not hits:
+        raise SystemExit(f"no {pattern} under {d}")
+    return hits[0]
+
+
+def stats(args):
+    path = find_one(args.dir, "*kernel_stats.csv")
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if is_ours(r["Name"]):
+                rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]),
+                             float(r["MinNs"]), float(r["MaxNs"]), float(r["Percentage"])))
+    lines = [f"# rocprofv3 kernel statistics: {args.title or os.path.basename(args.out)}", "",
+             "Command (from the repository root):", ""]
+    lines += [f"    {c}" for c in args.cmd]
+    lines += ["", "| kernel | calls | average us | min us | max us | % of GPU time |",
+              "|---|---|---|---|---|---|"]
+    for n, c, avg, mn, mx, pct in rows:
+        lines.append(f"| {n} | {c} | {avg/1e3:.1f} | {mn/1e3:.1f} | {mx/1e3:.1f} | {pct:.1f} |")
+    if args.note:
+        lines += ["", args.note]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def load_counter(d: str, counter: str):
+    path = find_one(d, "*counter_collection.csv")
+    per = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            per[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return per
+
+
+def traffic(args):
+    sys.path.insert(0, ROOT)
+    from weights_ttt_layer_amd import workloads as wlm
+    from bench import algorithmic_bytes
+
+    wl = wlm.BY_NAME[args.workload]
+    path_key = "large" if wl.b >= 256 else wl.kind
+    fetch = load_counter(args.fetch_dir, "FETCH_SIZE")
+    write = load_counter(args.write_dir, "WRITE_SIZE")
+    copy_kib = COPY_BYTES / 1024.0
+    # the calibration copies are the copy dispatches that moved about COPY_BYTES
+    cf = [v for v in fetch.get(COPY_KERNEL, []) if 0.5 * copy_kib < v < 2.0 * copy_kib]
+    cw = [v for v in write.get(COPY_KERNEL, []) if 0.5 * copy_kib < v < 2.0 * copy_kib]
+    if not cf or not cw:
+        raise SystemExit("no calibration copy found in the counter runs")
+    f_fac = copy_kib / (sum(cf) / len(cf))
+    w_fac = copy_kib / (sum(cw) / len(cw))
+    kernels = {}
+    total = 0.0
+    for name in sorted(set(fetch) | set(write)):
+        if not name.startswith(PATH_KERNELS[path_key]):
+            continue
+        fk = sum(fetch[name]) / len(fetch[name])
+        wk = sum(write[name]) / len(write[name])
+        hbm = (fk * f_fac + wk * w_fac) * 1024.0
+        kernels[name] = {"fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+                         "hbm_bytes_per_dispatch": hbm, "dispatches": len(fetch[name])}
+        total += hbm
+    if not kernels:
+        raise SystemExit(f"no dispatch of the {path_key} path's kernels in the counter runs")
+    alg = algorithmic_bytes(wl)
+    rec = {
+        "workload": wl.name,
+        "kernels": kernels,
+        "hbm_bytes_per_launch": total,
+        "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": total / alg,
+        "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib_counted": sum(cf) / len(cf),
+                        "write_kib_counted": sum(cw) / len(cw), "fetch_factor": f_fac,
+                        "write_factor": w_fac},
+        "source_digest": source_digest(path_key),
+        "commands": args.cmd,
+    }
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# HBM traffic per launch: {wl.name}", "", "Commands (from the repository root):", ""]
+    lines += [f"    {c}" for c in args.cmd]
+    lines += ["", f"Calibration: a plain device copy of {COPY_BYTES} bytes counted "
+              f"FETCH_SIZE {sum(cf)/len(cf):.0f} KiB and WRITE_SIZE {sum(cw)/len(cw):.0f} KiB "
+              f"(expected {copy_kib:.0f} KiB each): factors {f_fac:.4f} and {w_fac:.4f}.", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB (calibrated) |", "|---|---|---|---|"]
+    for n, k in kernels.items():
+        lines.append(f"| {n} | {k['fetch_kib_per_dispatch']:.0f} | {k['write_kib_per_dispatch']:.0f} | "
+                     f"{k['hbm_bytes_per_dispatch']/1e6:.2f} |")
+    lines += ["", f"Per launch: {total/1e6:.2f} MB measured vs {alg/1e6:.2f} MB algorithmic "
+              f"(ratio {total/alg:.3f}). Source digest {rec['source_digest']}."]
+    with open(os.path.join(ROOT, "profiles", f"traffic_{wl.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("out")
+    s.add_argument("--cmd", action="append", default=[])
+    s.add_argument("--title", default="")
+    s.add_argument("--note", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("workload")
+    t.add_argument("--cmd", action="append", default=[])
+    args = ap.parse_args(argv)
+    stats(args) if args.what == "stats" else traffic(args)
+
+
+if __name__ == "__main__":
+    main()
