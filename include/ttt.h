@@ -102,11 +102,8 @@ typedef enum {
  *
  * Supported (else TTT_ERR_UNSUPPORTED):
  *   small-b path  : kind PLAIN or LN, dtype F32 or BF16, d = 64, 1 <= b <= 16
- *   large-chunk   : kind PLAIN, dtype BF16, d = 128, b >= 256, b % 128 == 0 and
- *                   N % 128 == 0 (needs the workspace). Its causal term
- *                   tril(Q K^T) diag(eta) E is formed with fp16 operands (fp32
- *                   accumulation): |q.k| and |2 eta (k W - v)| must stay below
- *                   6.5e4 (true for L2-normalised keys and moderate eta).
+ *   large-chunk   : kind PLAIN, dtype BF16, d = 128, b >= 256, b % 128 == 0,
+ *                   N % 128 == 0 and N < 2^22 (needs the workspace).
  * ttt_linear_fwd_path() reports which path a combination takes.
  */
 int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b,

@@ -9,24 +9,22 @@
 //     Z_c = Q_c W_c - 2 tril(Q_c K_c^T) diag(eta) E_c.
 // For plain f the chunk update is affine in W:
 //     W_{c+1} = W_c - M_c W_c + B_c,   M_c = K_c^T D K_c,  B_c = K_c^T D V_c,
-// D = diag(2 eta). The path runs four kernels on one stream:
-//   lc_gram : M_c and B_c for every (unit, chunk) at once (no dependence on W);
-//   lc_scan : the 16-step recurrence W_c -> W_{c+1} (one workgroup per
-//             (unit, 32-column block)); writes every W_c^T as two bf16 terms;
-//   lc_grad : Gneg = -D (K W_c - V) per chunk, stored fp16 [token][feature];
-//   lc_out  : Z = Q W_c - tril(Q K^T) diag(...) E in 128x128 blocks: for every
-//             query block, the causal key blocks j <= i of its chunk.
-// Workspace (caller-provided): M, B (fp32), W_c^T terms (bf16), Gneg (fp16).
+// D = diag(2 eta). The path runs three kernels on one stream:
+//   lc_gram  : M_c and B_c for every (unit, chunk) at once (no dependence on W);
+//   lc_scan  : the recurrence W_c -> W_{c+1} (one workgroup per (unit,
+//              32-column block)); writes every W_c^T as two bf16 terms and W_end;
+//   lc_chunk : Z of every (unit, chunk) at once from W_c, fused: the chunk's
+//              residuals, the causal term and the output in one pass over
+//              Q, K, V (sub-blocks of 64 tokens, see below).
+// Workspace (caller-provided): M, B (fp32), W_c^T terms (bf16).
 //
-// Precision: every product involving the fp32 state uses two bf16 terms (16
-// significant bits). The causal term tril(Q K^T) Gneg takes single fp16
-// operands for P = Q K^T and Gneg (11 significant bits, eight times finer than
-// bf16, at the same MFMA rate); this requires |q.k| and |2 eta (k W - v)| to
-// stay below the fp16 range (6.5e4), e.g. L2-normalised keys.
+// Precision: every product involving an fp32 quantity (state, gradient, the
+// causal scores q.k) uses two bf16 terms (16 significant bits); bf16 token
+// streams are exact in one term. All accumulation is fp32.
 //
 // MFMA v_mfma_f32_32x32x16_bf16 throughout. Token-major operands (the token
-// index contracted in K^T K, K^T V) are read from row-major LDS tiles with the
-// gfx950 transpose read ds_read_b64_tr_b16.
+// index contracted in K^T K, K^T V, K^T Gn) are read from row-major LDS tiles
+// with the gfx950 transpose read ds_read_b64_tr_b16.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -35,13 +33,13 @@ namespace {
 
 constexpr int LD = 128;          // head dim of this path
 constexpr int LT = 256;          // threads per workgroup
-constexpr int TB = 128;          // token block of lc_grad / lc_out
+constexpr int TB = 128;          // chunk lengths are multiples of this
 
 // Row of a 32x32 C-layout tile held by lane half h = lane / 32 at slot i.
 __device__ __forceinline__ int crow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
 struct LcLayout {
-    size_t m_off, b_off, wt_off, g_off, total;
+    size_t m_off, b_off, wt_off, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -53,12 +51,9 @@ __host__ __device__ inline LcLayout lc_layout(int units, int N, int b)
     L.m_off = 0;
     L.b_off = align256(L.m_off + (size_t)units * C * LD * LD * 4);
     L.wt_off = align256(L.b_off + (size_t)units * C * LD * LD * 4);
-    L.g_off = align256(L.wt_off + (size_t)units * C * 2 * LD * LD * 2);
-    L.total = align256(L.g_off + (size_t)units * N * LD * 2);
+    L.total = align256(L.wt_off + (size_t)units * C * 2 * LD * LD * 2);
     return L;
 }
-
-__device__ __forceinline__ uint32_t f16_bits_f(float x) { return pack_f16x2(x, 0.f) & 0xFFFFu; }
 
 // ===========================================================================
 // lc_gram: M_c = K^T D K (symmetric: upper 32x32 tiles computed, mirrored on
@@ -70,6 +65,20 @@ typedef __attribute__((address_space(3))) void lds_void;
 // byte offset of piece p (16 B) of row r in a 256-byte-row tile whose pieces
 // are XOR-swizzled (piece p of row r at slot p ^ (r % 16))
 __device__ __forceinline__ int swz(int r, int p) { return r * 256 + ((p ^ (r & 15)) << 4); }
+
+// One 16-byte direct global->LDS load per lane: lane l's bytes land at
+// lds + 16 l. Issued as assembly so that the compiler does not track it: the
+// compiler cannot tell the two LDS buffers apart through the loads' addresses
+// and would otherwise wait for a prefetch before every read of the other
+// buffer. The caller waits for these loads explicitly (vmcnt) before the
+// barrier that publishes the buffer. (M0 written by SALU needs one wait state
+// before an LDS-DMA instruction.)
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 struct GramSmem {
     uint16_t k[2][GR_TOK * LD];         // [token][feature], swizzled pieces
@@ -103,10 +112,8 @@ __device__ __forceinline__ void gram_dma(GramSmem& sm, int buf, int s, int w, in
         const int sl = (4 * w + k) * 64 + lane;
         const int r = sl >> 4, p = (sl & 15) ^ (r & 15);
         const size_t off = (size_t)(s * GR_TOK + r) * LD + p * 8;
-        __builtin_amdgcn_global_load_lds(Ku + off, (lds_void*)(reinterpret_cast<char*>(sm.k[buf]) + (4 * w + k) * 1024),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds(Vu + off, (lds_void*)(reinterpret_cast<char*>(sm.v[buf]) + (4 * w + k) * 1024),
-                                         16, 0, 0);
+        dma16(Ku + off, __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<char*>(sm.k[buf]) + (4 * w + k) * 1024)));
+        dma16(Vu + off, __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<char*>(sm.v[buf]) + (4 * w + k) * 1024)));
     }
 }
 
@@ -143,7 +150,8 @@ lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
     const int C = (N + b - 1) / b;
     const int unit = blockIdx.x / C, c = blockIdx.x % C;
     const int c0 = c * b, nt = min(b, N - c0);
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint16_t* Ku = Kg + ((size_t)unit * N + c0) * LD;
     const uint16_t* Vu = Vg + ((size_t)unit * N + c0) * LD;
     const float* etau = PER_TOKEN ? etag + (size_t)unit * N + c0 : nullptr;
@@ -159,6 +167,7 @@ lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
     gram_dma(sm, 0, 0, w, lane, Ku, Vu);
     for (int s = 0; s < nstage; ++s) {
         const int buf = s & 1;
+        __builtin_amdgcn_s_waitcnt(0x0070);              // this wave's loads of stage s are done
         __syncthreads();                                 // stage s landed; stage s-1 consumed
         if (s + 1 < nstage) gram_dma(sm, buf ^ 1, s + 1, w, lane, Ku, Vu);
         const uint16_t* kt = sm.k[buf];
@@ -304,259 +313,327 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const float* __restri
 }
 
 // ===========================================================================
-// lc_grad: Gneg[t][d] = -D_t (K W_c - V)[t][d] for every token of one chunk.
-// One workgroup per (unit, chunk). W_c^T (two bf16 terms, 64 KB) is staged once
-// in LDS by direct loads and is the A operand (wave w: output features
-// [32w, 32w+32)); the B operand is K^T, i.e. K rows straight from global memory
-// (four 32-token tiles per 128-token block, prefetched a block ahead). The C
-// layout then holds, per lane, one token and four consecutive features, so V is
-// read and Gneg written as 8-byte row segments, with no barrier in the loop.
+// lc_chunk: Z for one (unit, chunk), fused, in sub-blocks of SB = 64 tokens.
+//
+// Inside a chunk every gradient is taken at W_c, so the dual-form output
+//     Z = Q W_c + tril(Q K^T) Gn,     Gn = D (V - K W_c)   (= -D E)
+// splits over sub-blocks i (rows i*SB .. i*SB+SB-1) by associativity:
+//     Z_i = Q_i W'_i + tril(Q_i K_i^T) Gn_i,   W'_i = W_c + sum_{j<i} K_j^T Gn_j.
+// W'_i is the state after the chunk's first i*SB tokens with gradients at W_c
+// (the page's "accumulated weight delta", section 4 of "Test-Time Training:
+// Linear Complexity Beyond Attention", taken at sub-block granularity). The
+// causal product thus only spans SB keys; the rest of the sum is carried by
+// W', which stays in registers as an fp32 MFMA accumulator.
+//
+// Wave w owns output features [32w, 32w+32) of everything (Gn, Z, W').
+// Per sub-block and wave (32x32x16 bf16 MFMA, fp32 accumulation):
+//   Z_m    = Q_m W'                 W' split into two bf16 terms on the fly
+//   G_a    = K_a W_c,  P_am = K_a Q_m^T (m >= a)      one pass over k
+//   Gn_a   = D (V_a - G_a)          two bf16 terms; V read by transpose reads
+//   Z_m   += P_am^T Gn_a            P (masked on the diagonal) as two bf16 terms
+//   W'    += K_a^T Gn_a             K^T by transpose reads
+// The C layout of G and P (lane = column, rows 8(i/4) + 4h + i%4) is used
+// directly as the B / A operand of the next product: the k index runs over
+// those rows in that order, and the other operand is read to match.
+//
+// LDS: W_c^T (two terms, 64 KB) and two buffers of K, Q, V sub-block tiles
+// (48 KB each), filled by direct global->LDS loads. The two buffers are
+// distinct arrays and the loop is unrolled by two, so the compiler can tell a
+// prefetch into one buffer from reads of the other and does not wait for the
+// prefetch before reading. Z of a sub-block is stored after the next barrier,
+// which leaves the stores a whole sub-block to drain before the next wait.
 // ===========================================================================
-struct GradSmem {
-    uint16_t wt[2][LD * LD];             // W_c^T [dout][din], term 0 and 1, swizzled rows
+constexpr int SB = 64;                  // tokens per sub-block
+
+// Rows are 256 bytes = 16 pieces of 16 bytes; piece p of row r is stored at
+// slot p ^ rsw(r). rsw is a bijection of r % 16 whose low three bits differ
+// across 8 consecutive rows and whose bits 1-2 differ across 4 aligned rows,
+// which keeps the row reads (8 or 16 rows, one piece) and the transpose reads
+// (4 rows, two adjacent pieces) free of bank conflicts.
+__device__ __forceinline__ int rsw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+__device__ __forceinline__ int swz2(int r, int p) { return r * 256 + ((p ^ rsw(r)) << 4); }
+
+__shared__ __attribute__((aligned(16))) uint16_t lc_wc[2 * LD * LD];    // W_c^T [term][n][k]
+__shared__ __attribute__((aligned(16))) uint16_t lc_buf0[3 * SB * LD];  // K, Q, V of even sub-blocks
+__shared__ __attribute__((aligned(16))) uint16_t lc_buf1[3 * SB * LD];  // K, Q, V of odd sub-blocks
+
+// Direct loads of 256-byte rows from `src` (row-major, LD bf16 per row) into a
+// swizzled LDS tile: 1 KB (4 rows) per wave instruction, PER_WAVE instructions
+// per wave; w must be wave-uniform.
+template <int PER_WAVE>
+__device__ __forceinline__ void rows_dma(char* dst, const uint16_t* src, int w, int lane)
+{
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) {
+        const int ins = PER_WAVE * w + k;
+        const int sl = ins * 64 + lane;
+        const int r = sl >> 4, p = (sl & 15) ^ rsw(r);
+        dma16(src + (size_t)r * LD + p * 8, __builtin_amdgcn_readfirstlane(lds_addr(dst + ins * 1024)));
+    }
+}
+
+// K, Q, V rows [t, t + SB) of the unit into one buffer (3 x 16 KB).
+__device__ __forceinline__ void sub_dma(uint16_t* buf, const uint16_t* Ku, const uint16_t* Qu, const uint16_t* Vu,
+                                        int t, int w, int lane)
+{
+    char* b = reinterpret_cast<char*>(buf);
+    rows_dma<4>(b, Ku + (size_t)t * LD, w, lane);
+    rows_dma<4>(b + SB * LD * 2, Qu + (size_t)t * LD, w, lane);
+    rows_dma<4>(b + 2 * SB * LD * 2, Vu + (size_t)t * LD, w, lane);
+}
+
+// Row read: piece p of row r (16 bytes).
+__device__ __forceinline__ bf16x8 ld_piece(const char* tile, int r, int p)
+{
+    return *reinterpret_cast<const bf16x8*>(tile + swz2(r, p));
+}
+
+// Transpose read: lane gets rows row0 + 4h + 0..3 of column col0 + lane % 32.
+__device__ __forceinline__ uint2 ld_tr4(const char* tile, int row0, int col0, int lane)
+{
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int row = row0 + 4 * (q >> 1) + (r16 >> 2);
+    const int col = col0 + 16 * (q & 1) + 4 * (r16 & 3);
+    const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(tile + swz2(row, col >> 3) + (col & 7) * 2));
+    return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ bf16x8 cat8(uint2 a, uint2 b)
+{
+    return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// Eight fp32 values (C slots 8s .. 8s+7) as two bf16 operand terms, optionally
+// masked to the causal part of a diagonal tile (key row <= query column).
+__device__ __forceinline__ void pack_p(const f32x16& p, int s, bool diag, int h, int l32, bf16x8 (&out)[2])
+{
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int i = 8 * s + j;
+        x[j] = (!diag || crow(i, h) <= l32) ? p[i] : 0.f;
+    }
+    terms8<2>(x, out);
+}
+
+struct ChunkCtx {
+    const uint16_t *Ku, *Qu, *Vu;
+    const float* etau;                  // per-token eta of the unit, or null
+    float two_eta;                      // 2 eta_const
+    __amdgpu_buffer_rsrc_t zr;          // Z rows of the unit (buffer stores: uniform row offsets)
+    int c0, nsb, w, lane, h, l32;
 };
+
+// Z rows of sub-block i from the C-layout accumulators: lane stores column
+// 32w + l32 of rows crow(e, h); the row offset is split into a uniform part
+// (8 (e / 4) rows) and an immediate (e % 4 rows).
+__device__ __forceinline__ void store_z(const ChunkCtx& x, const f32x16 (&z)[2], int i)
+{
+    const int voff = ((4 * x.h) * LD + 32 * x.w + x.l32) * 4;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int srow = __builtin_amdgcn_readfirstlane(x.c0 + i * SB + 32 * m + 8 * (e >> 2));
+            const float v = z[m][e];     // (a bit cast of the vector element itself would read element 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), x.zr, voff + (e & 3) * LD * 4,
+                                                  srow * LD * 4, 0);
+        }
+}
+
+// Two bf16 terms of Gn = D (V - G) for one 32-token tile (C layout of G:
+// column = feature 32w + l32, rows = tokens 32a + crow(e, h)), per k-step s.
+template <bool PER_TOKEN>
+__device__ __forceinline__ void grad_terms(const ChunkCtx& x, const char* vt, int i, int a, const f32x16& g,
+                                           bf16x8 (&gnb)[2][2])
+{
+    float gn[16];
+#pragma unroll
+    for (int mq = 0; mq < 4; ++mq) {
+        const uint2 vv = ld_tr4(vt, 32 * a + 8 * mq, 32 * x.w, x.lane);
+        const float v4[4] = {__builtin_bit_cast(float, vv.x << 16), __builtin_bit_cast(float, vv.x & 0xFFFF0000u),
+                             __builtin_bit_cast(float, vv.y << 16), __builtin_bit_cast(float, vv.y & 0xFFFF0000u)};
+        float d4[4] = {x.two_eta, x.two_eta, x.two_eta, x.two_eta};
+        if constexpr (PER_TOKEN) {
+            const float4 e4 = *reinterpret_cast<const float4*>(x.etau + x.c0 + i * SB + 32 * a + 8 * mq + 4 * x.h);
+            d4[0] = 2.f * e4.x;
+            d4[1] = 2.f * e4.y;
+            d4[2] = 2.f * e4.z;
+            d4[3] = 2.f * e4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gn[4 * mq + e] = d4[e] * (v4[e] - g[4 * mq + e]);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        float xv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[j] = gn[8 * s + j];
+        terms8<2>(xv, gnb[s]);
+    }
+}
+
+template <bool PER_TOKEN>
+__device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uint16_t* nxt, int i, f32x16 (&accW)[4],
+                                           f32x16 (&zacc)[2])
+{
+    const int w = x.w, lane = x.lane, h = x.h, l32 = x.l32;
+    // this wave's loads into `cur` are done; after the barrier every wave's are,
+    // and no wave still reads `nxt`
+    __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    if (i + 1 < x.nsb) sub_dma(nxt, x.Ku, x.Qu, x.Vu, x.c0 + (i + 1) * SB, w, lane);
+    if (i > 0) store_z(x, zacc, i - 1);
+
+    const char* kt = reinterpret_cast<const char*>(cur);
+    const char* qt = kt + SB * LD * 2;
+    const char* vt = kt + 2 * SB * LD * 2;
+    const char* wc = reinterpret_cast<const char*>(lc_wc);
+
+    // Z_m = Q_m W' ; W' as B operand: k = in-features 32r + crow(8s + j, h)
+    zacc[0] = f32x16{};
+    zacc[1] = f32x16{};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            float xv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xv[j] = accW[r][8 * s + j];
+            bf16x8 wb[2];
+            terms8<2>(xv, wb);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const char* row = qt + (32 * m + l32) * 256;
+                const int p0 = 4 * r + 2 * s;
+                const int sw = rsw(l32);
+                const uint2 lo = *reinterpret_cast<const uint2*>(row + ((p0 ^ sw) << 4) + 8 * h);
+                const uint2 hi = *reinterpret_cast<const uint2*>(row + (((p0 + 1) ^ sw) << 4) + 8 * h);
+                const bf16x8 qa = cat8(lo, hi);
+                zacc[m] = mfma_32x32x16(qa, wb[1], zacc[m]);
+                zacc[m] = mfma_32x32x16(qa, wb[0], zacc[m]);
+            }
+        }
+
+    // G_a = K_a W_c (two terms of W_c) -> Gn_a terms
+    bf16x8 gnb[2][2][2];                                 // [a][s][term]
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        f32x16 g = {};
+#pragma unroll
+        for (int ks = 0; ks < LD / 16; ++ks) {
+            const bf16x8 w0 = ld_piece(wc, 32 * w + l32, 2 * ks + h);
+            const bf16x8 w1 = ld_piece(wc + LD * LD * 2, 32 * w + l32, 2 * ks + h);
+            const bf16x8 ka = ld_piece(kt, 32 * a + l32, 2 * ks + h);
+            g = mfma_32x32x16(ka, w1, g);
+            g = mfma_32x32x16(ka, w0, g);
+        }
+        grad_terms<PER_TOKEN>(x, vt, i, a, g, gnb[a]);
+    }
+
+    // the three causal score tiles P^T_am = K_a Q_m^T (keys x queries), m >= a
+    f32x16 p00 = {}, p01 = {}, p11 = {};
+#pragma unroll
+    for (int ks = 0; ks < LD / 16; ++ks) {
+        const bf16x8 k0 = ld_piece(kt, l32, 2 * ks + h);
+        const bf16x8 k1 = ld_piece(kt, 32 + l32, 2 * ks + h);
+        const bf16x8 q0 = ld_piece(qt, l32, 2 * ks + h);
+        const bf16x8 q1 = ld_piece(qt, 32 + l32, 2 * ks + h);
+        p00 = mfma_32x32x16(k0, q0, p00);
+        p01 = mfma_32x32x16(k0, q1, p01);
+        p11 = mfma_32x32x16(k1, q1, p11);
+    }
+
+    // Z_m += P_am^T Gn_a over the causal pairs (0,0), (0,1), (1,1); two terms of
+    // each, the pairs (lo, lo) dropped
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        bf16x8 pa00[2], pa01[2], pa11[2];
+        pack_p(p00, s, true, h, l32, pa00);
+        pack_p(p01, s, false, h, l32, pa01);
+        pack_p(p11, s, true, h, l32, pa11);
+        zacc[0] = mfma_32x32x16(pa00[1], gnb[0][s][0], zacc[0]);
+        zacc[0] = mfma_32x32x16(pa00[0], gnb[0][s][1], zacc[0]);
+        zacc[0] = mfma_32x32x16(pa00[0], gnb[0][s][0], zacc[0]);
+        zacc[1] = mfma_32x32x16(pa01[1], gnb[0][s][0], zacc[1]);
+        zacc[1] = mfma_32x32x16(pa01[0], gnb[0][s][1], zacc[1]);
+        zacc[1] = mfma_32x32x16(pa01[0], gnb[0][s][0], zacc[1]);
+        zacc[1] = mfma_32x32x16(pa11[1], gnb[1][s][0], zacc[1]);
+        zacc[1] = mfma_32x32x16(pa11[0], gnb[1][s][1], zacc[1]);
+        zacc[1] = mfma_32x32x16(pa11[0], gnb[1][s][0], zacc[1]);
+    }
+
+    // W' += K_a^T Gn_a ; A = K^T rows 32r + l32, k = tokens 32a + crow(8s + j, h)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const bf16x8 ka = cat8(ld_tr4(kt, 32 * a + 16 * s, 32 * r, lane),
+                                       ld_tr4(kt, 32 * a + 16 * s + 8, 32 * r, lane));
+                accW[r] = mfma_32x32x16(ka, gnb[a][s][1], accW[r]);
+                accW[r] = mfma_32x32x16(ka, gnb[a][s][0], accW[r]);
+            }
+}
 
 template <bool PER_TOKEN>
 __global__ void __launch_bounds__(LT)
-lc_grad_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
-               const float* __restrict__ etag, float eta_const, const uint16_t* __restrict__ WT,
-               uint16_t* __restrict__ Gg)
+lc_chunk_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
+                const uint16_t* __restrict__ Vg, const float* __restrict__ etag, float eta_const,
+                const uint16_t* __restrict__ WT, float* __restrict__ Zg)
 {
-    __shared__ GradSmem sm;
     const int C = (N + b - 1) / b;
     const int unit = blockIdx.x / C, c = blockIdx.x % C;
-    const int c0 = c * b, nblk = min(b, N - c0) / TB;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-    const uint16_t* Ku = Kg + (size_t)unit * N * LD;
-    const uint16_t* Vu = Vg + (size_t)unit * N * LD;
-    const uint16_t* wt = WT + ((size_t)unit * C + c) * 2 * LD * LD;
-    uint16_t* Gu = Gg + (size_t)unit * N * LD;
+    ChunkCtx x;
+    x.c0 = c * b;
+    x.nsb = min(b, N - x.c0) / SB;                       // even: chunks hold a multiple of 128 tokens
+    x.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    x.lane = threadIdx.x & 63;
+    x.h = x.lane >> 5;
+    x.l32 = x.lane & 31;
+    x.Ku = Kg + (size_t)unit * N * LD;
+    x.Qu = Qg + (size_t)unit * N * LD;
+    x.Vu = Vg + (size_t)unit * N * LD;
+    x.etau = PER_TOKEN ? etag + (size_t)unit * N : nullptr;
+    x.two_eta = 2.f * eta_const;
+    x.zr = __builtin_amdgcn_make_buffer_rsrc(Zg + (size_t)unit * N * LD, (short)0, N * LD * 4, 0x00020000);
 
-    // W_c^T terms: 4096 16-byte pieces, 16 wave instructions per wave
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int ins = 16 * w + k;
-        const int sl = ins * 64 + lane;
-        const int term = sl >> 11, rem = sl & 2047;
-        const int r = rem >> 4, pc = (rem & 15) ^ (r & 15);
-        __builtin_amdgcn_global_load_lds(wt + (size_t)term * LD * LD + r * LD + pc * 8,
-                                         (lds_void*)(reinterpret_cast<char*>(&sm.wt[0][0]) + ins * 1024), 16, 0, 0);
-    }
-    // K rows of the first block (B operand, lane: token 32tt + l32)
-    bf16x8 kb[4][LD / 16];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int ks = 0; ks < LD / 16; ++ks)
-            kb[tt][ks] = *reinterpret_cast<const bf16x8*>(Ku + (size_t)(c0 + 32 * tt + l32) * LD + 16 * ks + 8 * h);
+    // W_c^T (both terms, 512 rows of 256 B) and the first sub-block
+    rows_dma<16>(reinterpret_cast<char*>(lc_wc), WT + ((size_t)unit * C + c) * 2 * LD * LD, x.w, x.lane);
+    sub_dma(lc_buf0, x.Ku, x.Qu, x.Vu, x.c0, x.w, x.lane);
+    __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
 
-    // A operands (W_c^T rows 32w + l32, two terms) stay in registers for the chunk
-    const char* wtb = reinterpret_cast<const char*>(&sm.wt[0][0]);
-    bf16x8 wa[LD / 16][2];
+    // W' = W_c in fp32 (hi + lo), C layout: rows = in-features 32r + crow(e, h),
+    // column = output feature 32w + l32
+    f32x16 accW[4];
+    {
+        const char* wc = reinterpret_cast<const char*>(lc_wc);
+        const int n = 32 * x.w + x.l32;
 #pragma unroll
-    for (int ks = 0; ks < LD / 16; ++ks) {
-        wa[ks][0] = *reinterpret_cast<const bf16x8*>(wtb + swz(32 * w + l32, 2 * ks + h));
-        wa[ks][1] = *reinterpret_cast<const bf16x8*>(wtb + LD * LD * 2 + swz(32 * w + l32, 2 * ks + h));
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int mq = 0; mq < 4; ++mq) {
+                const int k0 = 32 * r + 8 * mq + 4 * x.h;
+                const int off = swz2(n, k0 >> 3) + (k0 & 7) * 2;
+                const uint2 hi = *reinterpret_cast<const uint2*>(wc + off);
+                const uint2 lo = *reinterpret_cast<const uint2*>(wc + LD * LD * 2 + off);
+                const uint32_t hv[4] = {hi.x << 16, hi.x & 0xFFFF0000u, hi.y << 16, hi.y & 0xFFFF0000u};
+                const uint32_t lv[4] = {lo.x << 16, lo.x & 0xFFFF0000u, lo.y << 16, lo.y & 0xFFFF0000u};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    accW[r][4 * mq + e] = __builtin_bit_cast(float, hv[e]) + __builtin_bit_cast(float, lv[e]);
+            }
     }
 
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int tb0 = c0 + blk * TB;
-        const int tn = (blk + 1 < nblk) ? tb0 + TB : tb0;      // next block (clamped: unconditional loads)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            // G^T tile: rows = features 32w + crow(i,h), column = token tb0 + 32tt + l32
-            f32x16 acc = {};
-#pragma unroll
-            for (int ks = 0; ks < LD / 16; ++ks) {
-                acc = mfma_32x32x16(wa[ks][1], kb[tt][ks], acc);
-                acc = mfma_32x32x16(wa[ks][0], kb[tt][ks], acc);
-            }
-            const int tok = tb0 + 32 * tt + l32;
-            // prefetch this tile's rows of the next block
-#pragma unroll
-            for (int ks = 0; ks < LD / 16; ++ks)
-                kb[tt][ks] = *reinterpret_cast<const bf16x8*>(Ku + (size_t)(tn + 32 * tt + l32) * LD + 16 * ks + 8 * h);
-            const float dt = 2.f * (PER_TOKEN ? etag[(size_t)unit * N + tok] : eta_const);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d0 = 32 * w + 8 * q4 + 4 * h;
-                const uint2 vv = *reinterpret_cast<const uint2*>(Vu + (size_t)tok * LD + d0);
-                const float v4[4] = {__builtin_bit_cast(float, vv.x << 16), __builtin_bit_cast(float, vv.x & 0xFFFF0000u),
-                                     __builtin_bit_cast(float, vv.y << 16), __builtin_bit_cast(float, vv.y & 0xFFFF0000u)};
-                float g[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) g[e] = -dt * (acc[4 * q4 + e] - v4[e]);
-                *reinterpret_cast<uint2*>(Gu + (size_t)tok * LD + d0) =
-                    make_uint2(pack_f16x2(g[0], g[1]), pack_f16x2(g[2], g[3]));
-            }
-        }
+    f32x16 zacc[2] = {f32x16{}, f32x16{}};
+    for (int i = 0; i < x.nsb; i += 2) {
+        chunk_step<PER_TOKEN>(x, lc_buf0, lc_buf1, i, accW, zacc);
+        chunk_step<PER_TOKEN>(x, lc_buf1, lc_buf0, i + 1, accW, zacc);
     }
-}
-
-// ===========================================================================
-// lc_out: Z rows of one 256-query block: Z = Q W_c + sum_{key blocks j}
-// mask(Q K_j^T) Gneg_j over the causal 128-key blocks of the chunk (Gneg_j
-// token-major, its key-contracted B operand read with transpose reads). Wave w owns
-// queries [64w, 64w+64) of the block (two 32-query tiles) and all 128 output
-// features (four 32x32 C tiles per query tile), so every operand read from LDS
-// feeds two MFMAs. K_j and Gneg_j^T tiles (32 KB each) are double-buffered in
-// LDS and filled by direct global->LDS loads (no registers): one 16-byte piece
-// per lane, 1 KB per wave instruction. Rows are 256 B; the 16 pieces of row r
-// are stored XOR-swizzled (piece p at slot p ^ (r % 16)) so that 32 lanes
-// reading the same piece of 32 different rows hit distinct banks.
-// ===========================================================================
-constexpr int QB = 256;                 // queries per lc_out workgroup
-
-struct OutSmem {
-    uint16_t k[2][TB * LD];             // K_j [key][feature], swizzled pieces
-    uint16_t g[2][TB * LD];             // Gneg_j [key][feature], fp16, swizzled pieces
-};
-
-
-// Fill one K tile and one Gneg^T tile (key block kb) with direct LDS loads:
-// wave w writes LDS pieces [(8w + k) * 64, +64) of each tile.
-__device__ __forceinline__ void out_dma(OutSmem& sm, int buf, int kb, int w, int lane, int N,
-                                        const uint16_t* Ku, const uint16_t* Gu)
-{
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int sl = (8 * w + k) * 64 + lane;          // 16-byte slot in the tile
-        const int r = sl >> 4, p = (sl & 15) ^ (r & 15); // row and the piece that lives there
-        char* kdst = reinterpret_cast<char*>(sm.k[buf]) + (8 * w + k) * 1024;
-        char* gdst = reinterpret_cast<char*>(sm.g[buf]) + (8 * w + k) * 1024;
-        __builtin_amdgcn_global_load_lds(Ku + (size_t)(kb * TB + r) * LD + p * 8, (lds_void*)kdst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(Gu + (size_t)(kb * TB + r) * LD + p * 8, (lds_void*)gdst, 16, 0, 0);
-    }
-}
-
-__global__ void __launch_bounds__(LT)
-lc_out_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
-              const uint16_t* __restrict__ WT, const uint16_t* __restrict__ GT, float* __restrict__ Zg)
-{
-    __shared__ OutSmem sm;
-    const int C = (N + b - 1) / b;
-    const int bpc = (b + QB - 1) / QB;                   // query blocks per (full) chunk
-    const int units = gridDim.x / (C * bpc);
-    // heaviest blocks (largest in-chunk index, most key blocks) first
-    const int unit = blockIdx.x % units;
-    const int rank = blockIdx.x / units;
-    const int iin = bpc - 1 - rank / C;                  // query block index inside the chunk
-    const int c = rank % C;
-    const int c0 = c * b;
-    const int q0 = c0 + iin * QB;                        // first query of the block
-    const int cend = min(c0 + b, N);                     // end of the chunk
-    if (q0 >= cend) return;                              // past a short chunk
-    const int nq = min(QB, cend - q0);                   // 128 or 256
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-    const uint16_t* Qu = Qg + (size_t)unit * N * LD;
-    const uint16_t* Ku = Kg + (size_t)unit * N * LD;
-    const uint16_t* Gu = GT + (size_t)unit * LD * N;
-    const uint16_t* wt = WT + ((size_t)unit * C + c) * 2 * LD * LD;
-    const bool active = 64 * w < nq;                     // this wave has queries
-    const int qw = q0 + 64 * w;                          // first query of this wave
-
-    // causal key blocks of the chunk visible to this query block
-    const int kb0 = c0 / TB;
-    const int nkb = (iin * QB + nq) / TB;
-    out_dma(sm, 0, kb0, w, lane, N, Ku, Gu);
-
-    // Q rows as operands: A of Q W_c and B of K_j Q^T share the registers
-    bf16x8 qa[2][LD / 16];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int ks = 0; ks < LD / 16; ++ks) {
-            const int q = active ? qw + 32 * qt + l32 : q0;
-            qa[qt][ks] = *reinterpret_cast<const bf16x8*>(Qu + (size_t)q * LD + 16 * ks + 8 * h);
-        }
-
-    // Z = Q W_c  (B = W_c: row k = input feature, column n -> W_c^T row n, two terms)
-    f32x16 acc[2][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        acc[0][t] = f32x16{};
-        acc[1][t] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < LD / 16; ++ks) {
-            const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(wt + (size_t)(32 * t + l32) * LD + 16 * ks + 8 * h);
-            const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(wt + (size_t)LD * LD + (size_t)(32 * t + l32) * LD +
-                                                               16 * ks + 8 * h);
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                acc[qt][t] = mfma_32x32x16(qa[qt][ks], b1, acc[qt][t]);
-                acc[qt][t] = mfma_32x32x16(qa[qt][ks], b0, acc[qt][t]);
-            }
-        }
-    }
-
-    const int qin = iin * QB + 64 * w;                   // first query of the wave inside the chunk
-    const int q16 = lane >> 4, r16 = lane & 15;          // transpose-read lane coordinates
-    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-    for (int j = 0; j < nkb; ++j) {
-        __syncthreads();                                 // tile j landed; tile j-1 consumed
-        if (j + 1 < nkb) out_dma(sm, (j + 1) & 1, kb0 + j + 1, w, lane, N, Ku, Gu);
-        if (!active || TB * j > qin + 63) continue;      // every key of the block is after every query
-        const char* kt_base = reinterpret_cast<const char*>(sm.k[j & 1]);
-        const char* gt_base = reinterpret_cast<const char*>(sm.g[j & 1]);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const int kmin = TB * j + 32 * kt;           // first key of the tile inside the chunk
-            if (kmin > qin + 63) continue;
-            // P^T = K Q^T for 32 keys x 64 queries
-            f32x16 pt[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-            for (int ks = 0; ks < LD / 16; ++ks) {
-                const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt_base + swz(32 * kt + l32, 2 * ks + h));
-                pt[0] = mfma_32x32x16(ak, qa[0][ks], pt[0]);
-                pt[1] = mfma_32x32x16(ak, qa[1][ks], pt[1]);
-            }
-            const bool need_mask = kmin + 31 > qin;      // some key of the tile is after some query
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                f16x8 pa[2];
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
-                    float x[8];
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) {
-                        const int i = 8 * half + jj;
-                        const bool keep = !need_mask || kmin + crow(i, h) <= qin + 32 * qt + l32;
-                        x[jj] = keep ? pt[qt][i] : 0.f;
-                    }
-                    pa[qt] = __builtin_bit_cast(
-                        f16x8, make_uint4(pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]),
-                                          pack_f16x2(x[4], x[5]), pack_f16x2(x[6], x[7])));
-                }
-                const int kbase = 32 * kt + 16 * half;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    // B operand: keys kbase + {4h..4h+3, 8+4h..8+4h+3} of feature 32t + l32,
-                    // two transpose reads of the token-major tile
-                    const int grow = kbase + 4 * h + (r16 >> 2);
-                    const int gcol = 32 * t + 16 * (q16 & 1) + 4 * (r16 & 3);
-                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_bf16x4*)(gt_base + swz(grow, gcol >> 3) + (gcol & 7) * 2));
-                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_bf16x4*)(gt_base + swz(grow + 8, gcol >> 3) + (gcol & 7) * 2));
-                    const uint2 ul = __builtin_bit_cast(uint2, lo), uh = __builtin_bit_cast(uint2, hi);
-                    const f16x8 gb = __builtin_bit_cast(f16x8, make_uint4(ul.x, ul.y, uh.x, uh.y));
-                    acc[0][t] = mfma_32x32x16_f16(pa[0], gb, acc[0][t]);
-                    acc[1][t] = mfma_32x32x16_f16(pa[1], gb, acc[1][t]);
-                }
-            }
-        }
-    }
-
-    if (!active) return;
-    float* Zu = Zg + (size_t)unit * N * LD;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                Zu[(size_t)(qw + 32 * qt + crow(i, h)) * LD + 32 * t + l32] = acc[qt][t][i];
+    store_z(x, zacc, x.nsb - 1);
 }
 
 }  // namespace
@@ -576,7 +653,6 @@ hipError_t launch_large_chunk_linear(const LinearArgs& a, hipStream_t stream)
     float* M = reinterpret_cast<float*>(ws + L.m_off);
     float* Bm = reinterpret_cast<float*>(ws + L.b_off);
     uint16_t* WT = reinterpret_cast<uint16_t*>(ws + L.wt_off);
-    uint16_t* GT = reinterpret_cast<uint16_t*>(ws + L.g_off);
     const uint16_t* Q = static_cast<const uint16_t*>(a.Q);
     const uint16_t* K = static_cast<const uint16_t*>(a.K);
     const uint16_t* V = static_cast<const uint16_t*>(a.V);
@@ -593,14 +669,11 @@ hipError_t launch_large_chunk_linear(const LinearArgs& a, hipStream_t stream)
     hipLaunchKernelGGL(lc_scan_kernel, dim3(units * 4), dim3(LT), 0, stream, a.N, a.b, a.W0, M, Bm, WT, a.W_end);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (per_token)
-        hipLaunchKernelGGL((lc_grad_kernel<true>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, K, V, a.eta,
-                           a.eta_const, WT, GT);
+        hipLaunchKernelGGL((lc_chunk_kernel<true>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, Q, K, V, a.eta,
+                           a.eta_const, WT, a.Z);
     else
-        hipLaunchKernelGGL((lc_grad_kernel<false>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, K, V, a.eta,
-                           a.eta_const, WT, GT);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(lc_out_kernel, dim3(units * C * ((a.b + QB - 1) / QB)), dim3(LT), 0, stream, a.N, a.b, Q,
-                       K, WT, GT, a.Z);
+        hipLaunchKernelGGL((lc_chunk_kernel<false>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, Q, K, V, a.eta,
+                           a.eta_const, WT, a.Z);
     return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ constexpr int SMALLB_MAX_B = 16;
 constexpr int LARGE_D = 128;
 constexpr int LARGE_MIN_B = 256;
 constexpr int LARGE_B_MULT = 128;
+constexpr int LARGE_MAX_N = 1 << 22;   // Z rows of one unit addressed with 32-bit byte offsets
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -63,7 +64,8 @@ int ttt_linear_fwd_path(int kind, int qkv_dtype, int d, int b) { return linear_p
 size_t ttt_linear_fwd_workspace_bytes(int kind, int qkv_dtype, int B, int H, int N, int d, int b)
 {
     if (B < 1 || H < 1 || N < 1 || d < 1 || b < 1) return 0;
-    if (linear_path(kind, qkv_dtype, d, b) != TTT_PATH_LARGE_CHUNK || N % LARGE_B_MULT != 0) return 0;
+    if (linear_path(kind, qkv_dtype, d, b) != TTT_PATH_LARGE_CHUNK || N % LARGE_B_MULT != 0 || N >= LARGE_MAX_N)
+        return 0;
     return ttt::large_chunk_workspace_bytes(B, H, N, d, b);
 }
 
@@ -128,7 +130,7 @@ int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b, c
     if (path == TTT_PATH_SMALL_B) {
         err = ttt::launch_smallb_linear(a, stream);
     } else {
-        if (N % LARGE_B_MULT != 0) return TTT_ERR_UNSUPPORTED;
+        if (N % LARGE_B_MULT != 0 || N >= LARGE_MAX_N) return TTT_ERR_UNSUPPORTED;
         const size_t need = ttt::large_chunk_workspace_bytes(B, H, N, d, b);
         if (workspace_bytes < need || (need > 0 && !workspace)) return TTT_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned(workspace, 256)) return TTT_ERR_INVALID_ARGUMENT;
