@@ -62,9 +62,14 @@ __host__ __device__ inline LcLayout lc_layout(int units, int N, int b)
 constexpr int GR_TOK = 64;              // tokens per LDS stage
 typedef __attribute__((address_space(3))) void lds_void;
 
-// byte offset of piece p (16 B) of row r in a 256-byte-row tile whose pieces
-// are XOR-swizzled (piece p of row r at slot p ^ (r % 16))
-__device__ __forceinline__ int swz(int r, int p) { return r * 256 + ((p ^ (r & 15)) << 4); }
+// LDS tiles have 256-byte rows = 16 pieces of 16 bytes; piece p of row r is
+// stored at slot p ^ rsw(r). rsw is a bijection of r % 16 whose low three bits
+// differ across 8 consecutive rows and whose bits 1-2 differ across 4 aligned
+// rows, which keeps the row reads (8 or 16 rows, one piece) and the transpose
+// reads (4 rows, two adjacent pieces) free of bank conflicts.
+__device__ __forceinline__ int rsw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+// byte offset of piece p of row r
+__device__ __forceinline__ int swz(int r, int p) { return r * 256 + ((p ^ rsw(r)) << 4); }
 
 // One 16-byte direct global->LDS load per lane: lane l's bytes land at
 // lds + 16 l. Issued as assembly so that the compiler does not track it: the
@@ -110,7 +115,7 @@ __device__ __forceinline__ void gram_dma(GramSmem& sm, int buf, int s, int w, in
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int sl = (4 * w + k) * 64 + lane;
-        const int r = sl >> 4, p = (sl & 15) ^ (r & 15);
+        const int r = sl >> 4, p = (sl & 15) ^ rsw(r);
         const size_t off = (size_t)(s * GR_TOK + r) * LD + p * 8;
         dma16(Ku + off, __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<char*>(sm.k[buf]) + (4 * w + k) * 1024)));
         dma16(Vu + off, __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<char*>(sm.v[buf]) + (4 * w + k) * 1024)));
@@ -337,21 +342,11 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const float* __restri
 // those rows in that order, and the other operand is read to match.
 //
 // LDS: W_c^T (two terms, 64 KB) and two buffers of K, Q, V sub-block tiles
-// (48 KB each), filled by direct global->LDS loads. The two buffers are
-// distinct arrays and the loop is unrolled by two, so the compiler can tell a
-// prefetch into one buffer from reads of the other and does not wait for the
-// prefetch before reading. Z of a sub-block is stored after the next barrier,
-// which leaves the stores a whole sub-block to drain before the next wait.
+// (48 KB each), filled by direct global->LDS loads issued one sub-block
+// ahead. Z of a sub-block is stored before the W' update, which gives the
+// stores that long to drain before the next barrier's wait.
 // ===========================================================================
 constexpr int SB = 64;                  // tokens per sub-block
-
-// Rows are 256 bytes = 16 pieces of 16 bytes; piece p of row r is stored at
-// slot p ^ rsw(r). rsw is a bijection of r % 16 whose low three bits differ
-// across 8 consecutive rows and whose bits 1-2 differ across 4 aligned rows,
-// which keeps the row reads (8 or 16 rows, one piece) and the transpose reads
-// (4 rows, two adjacent pieces) free of bank conflicts.
-__device__ __forceinline__ int rsw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
-__device__ __forceinline__ int swz2(int r, int p) { return r * 256 + ((p ^ rsw(r)) << 4); }
 
 __shared__ __attribute__((aligned(16))) uint16_t lc_wc[2 * LD * LD];    // W_c^T [term][n][k]
 __shared__ __attribute__((aligned(16))) uint16_t lc_buf0[3 * SB * LD];  // K, Q, V of even sub-blocks
@@ -385,7 +380,7 @@ __device__ __forceinline__ void sub_dma(uint16_t* buf, const uint16_t* Ku, const
 // Row read: piece p of row r (16 bytes).
 __device__ __forceinline__ bf16x8 ld_piece(const char* tile, int r, int p)
 {
-    return *reinterpret_cast<const bf16x8*>(tile + swz2(r, p));
+    return *reinterpret_cast<const bf16x8*>(tile + swz(r, p));
 }
 
 // Transpose read: lane gets rows row0 + 4h + 0..3 of column col0 + lane % 32.
@@ -395,7 +390,7 @@ __device__ __forceinline__ uint2 ld_tr4(const char* tile, int row0, int col0, in
     const int q = lane >> 4, r16 = lane & 15;
     const int row = row0 + 4 * (q >> 1) + (r16 >> 2);
     const int col = col0 + 16 * (q & 1) + 4 * (r16 & 3);
-    const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(tile + swz2(row, col >> 3) + (col & 7) * 2));
+    const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(tile + swz(row, col >> 3) + (col & 7) * 2));
     return __builtin_bit_cast(uint2, v);
 }
 
@@ -474,26 +469,100 @@ __device__ __forceinline__ void grad_terms(const ChunkCtx& x, const char* vt, in
     }
 }
 
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_R = 0x020, SG_DS_R = 0x100 };
+#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 template <bool PER_TOKEN>
-__device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uint16_t* nxt, int i, f32x16 (&accW)[4],
-                                           f32x16 (&zacc)[2])
+__device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uint16_t* nxt, int i, f32x16 (&accW)[4])
 {
     const int w = x.w, lane = x.lane, h = x.h, l32 = x.l32;
-    // this wave's loads into `cur` are done; after the barrier every wave's are,
-    // and no wave still reads `nxt`
+    // this wave's loads into `cur` (and its Z stores) are done; after the
+    // barrier every wave's are, and no wave still reads `nxt`
     __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
     if (i + 1 < x.nsb) sub_dma(nxt, x.Ku, x.Qu, x.Vu, x.c0 + (i + 1) * SB, w, lane);
-    if (i > 0) store_z(x, zacc, i - 1);
+    __builtin_amdgcn_sched_barrier(0);
 
     const char* kt = reinterpret_cast<const char*>(cur);
     const char* qt = kt + SB * LD * 2;
     const char* vt = kt + 2 * SB * LD * 2;
     const char* wc = reinterpret_cast<const char*>(lc_wc);
+    const int wrow = 32 * w + l32;
 
-    // Z_m = Q_m W' ; W' as B operand: k = in-features 32r + crow(8s + j, h)
-    zacc[0] = f32x16{};
-    zacc[1] = f32x16{};
+    // ---- G_a = K_a W_c for both token tiles (two terms of W_c), then the
+    // three causal score tiles P^T_am = K_a Q_m^T; operands one k-step ahead
+    f32x16 g0 = {}, g1 = {};
+    {
+        bf16x8 w0 = ld_piece(wc, wrow, h), w1 = ld_piece(wc + LD * LD * 2, wrow, h);
+        bf16x8 k0 = ld_piece(kt, l32, h), k1 = ld_piece(kt, 32 + l32, h);
+#pragma unroll
+        for (int ks = 0; ks < LD / 16; ++ks) {
+            bf16x8 w0n = w0, w1n = w1, k0n = k0, k1n = k1;
+            if (ks + 1 < LD / 16) {
+                w0n = ld_piece(wc, wrow, 2 * ks + 2 + h);
+                w1n = ld_piece(wc + LD * LD * 2, wrow, 2 * ks + 2 + h);
+                k0n = ld_piece(kt, l32, 2 * ks + 2 + h);
+                k1n = ld_piece(kt, 32 + l32, 2 * ks + 2 + h);
+            }
+            g0 = mfma_32x32x16(k0, w1, g0);
+            g1 = mfma_32x32x16(k1, w1, g1);
+            g0 = mfma_32x32x16(k0, w0, g0);
+            g1 = mfma_32x32x16(k1, w0, g1);
+            w0 = w0n; w1 = w1n; k0 = k0n; k1 = k1n;
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < LD / 16; ++ks) {
+        SCHED_GROUP(SG_DS_R, 4);
+        SCHED_GROUP(SG_MFMA, 4);
+    }
+    f32x16 p00 = {}, p01 = {}, p11 = {};
+    {
+        bf16x8 k0 = ld_piece(kt, l32, h), k1 = ld_piece(kt, 32 + l32, h);
+        bf16x8 q0 = ld_piece(qt, l32, h), q1 = ld_piece(qt, 32 + l32, h);
+#pragma unroll
+        for (int ks = 0; ks < LD / 16; ++ks) {
+            bf16x8 k0n = k0, k1n = k1, q0n = q0, q1n = q1;
+            if (ks + 1 < LD / 16) {
+                k0n = ld_piece(kt, l32, 2 * ks + 2 + h);
+                k1n = ld_piece(kt, 32 + l32, 2 * ks + 2 + h);
+                q0n = ld_piece(qt, l32, 2 * ks + 2 + h);
+                q1n = ld_piece(qt, 32 + l32, 2 * ks + 2 + h);
+            }
+            p00 = mfma_32x32x16(k0, q0, p00);
+            p01 = mfma_32x32x16(k0, q1, p01);
+            p11 = mfma_32x32x16(k1, q1, p11);
+            k0 = k0n; k1 = k1n; q0 = q0n; q1 = q1n;
+        }
+    }
+    // Gn_a = D (V_a - G_a) as two bf16 terms (VALU, overlapping the P products)
+    bf16x8 gnb[2][2][2];                                 // [a][s][term]
+    grad_terms<PER_TOKEN>(x, vt, i, 0, g0, gnb[0]);
+    grad_terms<PER_TOKEN>(x, vt, i, 1, g1, gnb[1]);
+#pragma unroll
+    for (int ks = 0; ks < LD / 16; ++ks) {
+        SCHED_GROUP(SG_DS_R, 4);
+        SCHED_GROUP(SG_MFMA, 1);
+        SCHED_GROUP(SG_VALU, 6);
+        SCHED_GROUP(SG_MFMA, 1);
+        SCHED_GROUP(SG_VALU, 6);
+        SCHED_GROUP(SG_MFMA, 1);
+        SCHED_GROUP(SG_VALU, 6);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- Z_m = Q_m W' + P_am^T Gn_a ; W' as B operand: k = in-features
+    // 32r + crow(8s + j, h), split into two bf16 terms on the fly
+    bf16x8 pa00[2][2], pa01[2][2], pa11[2][2];           // [s][term]
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        pack_p(p00, s, true, h, l32, pa00[s]);
+        pack_p(p01, s, false, h, l32, pa01[s]);
+        pack_p(p11, s, true, h, l32, pa11[s]);
+    }
+    f32x16 zacc[2] = {f32x16{}, f32x16{}};
+    const int sw = rsw(l32);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -503,79 +572,64 @@ __device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uin
             for (int j = 0; j < 8; ++j) xv[j] = accW[r][8 * s + j];
             bf16x8 wb[2];
             terms8<2>(xv, wb);
+            const int p0 = 4 * r + 2 * s;
+            bf16x8 qa[2];
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const char* row = qt + (32 * m + l32) * 256;
-                const int p0 = 4 * r + 2 * s;
-                const int sw = rsw(l32);
                 const uint2 lo = *reinterpret_cast<const uint2*>(row + ((p0 ^ sw) << 4) + 8 * h);
                 const uint2 hi = *reinterpret_cast<const uint2*>(row + (((p0 + 1) ^ sw) << 4) + 8 * h);
-                const bf16x8 qa = cat8(lo, hi);
-                zacc[m] = mfma_32x32x16(qa, wb[1], zacc[m]);
-                zacc[m] = mfma_32x32x16(qa, wb[0], zacc[m]);
+                qa[m] = cat8(lo, hi);
             }
+            zacc[0] = mfma_32x32x16(qa[0], wb[1], zacc[0]);
+            zacc[1] = mfma_32x32x16(qa[1], wb[1], zacc[1]);
+            zacc[0] = mfma_32x32x16(qa[0], wb[0], zacc[0]);
+            zacc[1] = mfma_32x32x16(qa[1], wb[0], zacc[1]);
         }
-
-    // G_a = K_a W_c (two terms of W_c) -> Gn_a terms
-    bf16x8 gnb[2][2][2];                                 // [a][s][term]
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-        f32x16 g = {};
-#pragma unroll
-        for (int ks = 0; ks < LD / 16; ++ks) {
-            const bf16x8 w0 = ld_piece(wc, 32 * w + l32, 2 * ks + h);
-            const bf16x8 w1 = ld_piece(wc + LD * LD * 2, 32 * w + l32, 2 * ks + h);
-            const bf16x8 ka = ld_piece(kt, 32 * a + l32, 2 * ks + h);
-            g = mfma_32x32x16(ka, w1, g);
-            g = mfma_32x32x16(ka, w0, g);
-        }
-        grad_terms<PER_TOKEN>(x, vt, i, a, g, gnb[a]);
-    }
-
-    // the three causal score tiles P^T_am = K_a Q_m^T (keys x queries), m >= a
-    f32x16 p00 = {}, p01 = {}, p11 = {};
-#pragma unroll
-    for (int ks = 0; ks < LD / 16; ++ks) {
-        const bf16x8 k0 = ld_piece(kt, l32, 2 * ks + h);
-        const bf16x8 k1 = ld_piece(kt, 32 + l32, 2 * ks + h);
-        const bf16x8 q0 = ld_piece(qt, l32, 2 * ks + h);
-        const bf16x8 q1 = ld_piece(qt, 32 + l32, 2 * ks + h);
-        p00 = mfma_32x32x16(k0, q0, p00);
-        p01 = mfma_32x32x16(k0, q1, p01);
-        p11 = mfma_32x32x16(k1, q1, p11);
-    }
-
-    // Z_m += P_am^T Gn_a over the causal pairs (0,0), (0,1), (1,1); two terms of
-    // each, the pairs (lo, lo) dropped
+    // causal pairs (0,0), (0,1), (1,1); two terms each, the pair (lo, lo) dropped
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        bf16x8 pa00[2], pa01[2], pa11[2];
-        pack_p(p00, s, true, h, l32, pa00);
-        pack_p(p01, s, false, h, l32, pa01);
-        pack_p(p11, s, true, h, l32, pa11);
-        zacc[0] = mfma_32x32x16(pa00[1], gnb[0][s][0], zacc[0]);
-        zacc[0] = mfma_32x32x16(pa00[0], gnb[0][s][1], zacc[0]);
-        zacc[0] = mfma_32x32x16(pa00[0], gnb[0][s][0], zacc[0]);
-        zacc[1] = mfma_32x32x16(pa01[1], gnb[0][s][0], zacc[1]);
-        zacc[1] = mfma_32x32x16(pa01[0], gnb[0][s][1], zacc[1]);
-        zacc[1] = mfma_32x32x16(pa01[0], gnb[0][s][0], zacc[1]);
-        zacc[1] = mfma_32x32x16(pa11[1], gnb[1][s][0], zacc[1]);
-        zacc[1] = mfma_32x32x16(pa11[0], gnb[1][s][1], zacc[1]);
-        zacc[1] = mfma_32x32x16(pa11[0], gnb[1][s][0], zacc[1]);
+        zacc[0] = mfma_32x32x16(pa00[s][1], gnb[0][s][0], zacc[0]);
+        zacc[1] = mfma_32x32x16(pa01[s][1], gnb[0][s][0], zacc[1]);
+        zacc[0] = mfma_32x32x16(pa00[s][0], gnb[0][s][1], zacc[0]);
+        zacc[1] = mfma_32x32x16(pa01[s][0], gnb[0][s][1], zacc[1]);
+        zacc[0] = mfma_32x32x16(pa00[s][0], gnb[0][s][0], zacc[0]);
+        zacc[1] = mfma_32x32x16(pa01[s][0], gnb[0][s][0], zacc[1]);
+        zacc[1] = mfma_32x32x16(pa11[s][1], gnb[1][s][0], zacc[1]);
+        zacc[1] = mfma_32x32x16(pa11[s][0], gnb[1][s][1], zacc[1]);
+        zacc[1] = mfma_32x32x16(pa11[s][0], gnb[1][s][0], zacc[1]);
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        SCHED_GROUP(SG_DS_R, 2);
+        SCHED_GROUP(SG_VALU, 12);
+        SCHED_GROUP(SG_MFMA, 2);
+        SCHED_GROUP(SG_VALU, 12);
+        SCHED_GROUP(SG_MFMA, 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    store_z(x, zacc, i);                                 // drains during the W' update
+    __builtin_amdgcn_sched_barrier(0);
 
-    // W' += K_a^T Gn_a ; A = K^T rows 32r + l32, k = tokens 32a + crow(8s + j, h)
+    // ---- W' += K_a^T Gn_a ; A = K^T rows 32r + l32, k = tokens 32a + crow(8s + j, h)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 ka[4];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const bf16x8 ka = cat8(ld_tr4(kt, 32 * a + 16 * s, 32 * r, lane),
-                                       ld_tr4(kt, 32 * a + 16 * s + 8, 32 * r, lane));
-                accW[r] = mfma_32x32x16(ka, gnb[a][s][1], accW[r]);
-                accW[r] = mfma_32x32x16(ka, gnb[a][s][0], accW[r]);
-            }
+            for (int r = 0; r < 4; ++r)
+                ka[r] = cat8(ld_tr4(kt, 32 * a + 16 * s, 32 * r, lane), ld_tr4(kt, 32 * a + 16 * s + 8, 32 * r, lane));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accW[r] = mfma_32x32x16(ka[r], gnb[a][s][1], accW[r]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accW[r] = mfma_32x32x16(ka[r], gnb[a][s][0], accW[r]);
+        }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        SCHED_GROUP(SG_DS_R, 8);
+        SCHED_GROUP(SG_MFMA, 8);
+    }
 }
 
 template <bool PER_TOKEN>
@@ -617,7 +671,7 @@ lc_chunk_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* _
 #pragma unroll
             for (int mq = 0; mq < 4; ++mq) {
                 const int k0 = 32 * r + 8 * mq + 4 * x.h;
-                const int off = swz2(n, k0 >> 3) + (k0 & 7) * 2;
+                const int off = swz(n, k0 >> 3) + (k0 & 7) * 2;
                 const uint2 hi = *reinterpret_cast<const uint2*>(wc + off);
                 const uint2 lo = *reinterpret_cast<const uint2*>(wc + LD * LD * 2 + off);
                 const uint32_t hv[4] = {hi.x << 16, hi.x & 0xFFFF0000u, hi.y << 16, hi.y & 0xFFFF0000u};
@@ -628,12 +682,10 @@ lc_chunk_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* _
             }
     }
 
-    f32x16 zacc[2] = {f32x16{}, f32x16{}};
     for (int i = 0; i < x.nsb; i += 2) {
-        chunk_step<PER_TOKEN>(x, lc_buf0, lc_buf1, i, accW, zacc);
-        chunk_step<PER_TOKEN>(x, lc_buf1, lc_buf0, i + 1, accW, zacc);
+        chunk_step<PER_TOKEN>(x, lc_buf0, lc_buf1, i, accW);
+        chunk_step<PER_TOKEN>(x, lc_buf1, lc_buf0, i + 1, accW);
     }
-    store_z(x, zacc, x.nsb - 1);
 }
 
 }  // namespace
