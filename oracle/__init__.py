@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ttt_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libttt_oracle.so")
 
-ONLINE, MINIBATCH, DUAL = 0, 1, 2
+ONLINE, MINIBATCH, DUAL, BLOCK_BEFORE, BLOCK_AFTER = 0, 1, 2, 3, 4
 PLAIN, LN = 0, 1
 
 _lib = None

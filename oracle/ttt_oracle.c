@@ -47,6 +47,17 @@
  *                 Z   = f evaluated on  Q W_c - tril(Q K^T) diag(eta) G
  *                 W  <- W_c - K^T diag(eta) G
  *               tril includes the diagonal. The MLP applies this to each layer.
+ *     BLOCK_BEFORE, BLOCK_AFTER
+ *               block-causal large chunks. Page "Test-Time Training Done Right"
+ *               (abstract) argues for large mini-batches and contrasts them with
+ *               the fine-grained block-wise causal dependencies of small ones;
+ *               read plainly, a large chunk takes one step with every gradient
+ *               at its starting weights (as MINIBATCH) and its tokens' outputs
+ *               use one set of weights for the whole chunk, with no causal
+ *               mask inside it: the weights before the chunk's step
+ *               (BLOCK_BEFORE: z_t = f(q_t; theta_c)) or after it (BLOCK_AFTER:
+ *               z_t = f(q_t; theta_{c+1})). The state sequence, and so the final
+ *               state, equals MINIBATCH's.
  *
  * Layouts (row-major, C order): Q,K,V [B,H,N,d]; eta [B,H,N]; W0 [B,H,d,d]
  * (row index = input feature); W1 [B,H,d,hid]; W2 [B,H,hid,d]; gamma, beta
@@ -61,6 +72,8 @@
 #define MODE_ONLINE 0
 #define MODE_MINIBATCH 1
 #define MODE_DUAL 2
+#define MODE_BLOCK_BEFORE 3
+#define MODE_BLOCK_AFTER 4
 #define KIND_PLAIN 0
 #define KIND_LN 1
 
@@ -236,6 +249,18 @@ static void lin_unit(int mode, const lin_model* m, int N, int b, const double* Q
                 lin_f(m, W, Q + (size_t)t * d, Z + (size_t)t * d, scratch);
             }
         }
+    } else if (mode == MODE_BLOCK_BEFORE || mode == MODE_BLOCK_AFTER) {
+        for (int c0 = 0; c0 < N; c0 += b) {
+            int c1 = c0 + b < N ? c0 + b : N;
+            memcpy(Wc, W, dd * sizeof(double));
+            /* one step for the whole chunk, every gradient at theta_c */
+            for (int t = c0; t < c1; ++t) {
+                lin_preact_grad(m, Wc, K + (size_t)t * d, V + (size_t)t * d, g, scratch);
+                rank1_sub(d, d, eta[t], K + (size_t)t * d, g, W);
+            }
+            const double* Wout = mode == MODE_BLOCK_BEFORE ? Wc : W;
+            for (int t = c0; t < c1; ++t) lin_f(m, Wout, Q + (size_t)t * d, Z + (size_t)t * d, scratch);
+        }
     } else { /* MODE_DUAL */
         double* G = malloc((size_t)b * d * sizeof(double));
         double* hq = malloc((size_t)d * sizeof(double));
@@ -285,7 +310,7 @@ int ttt_oracle_linear(int mode, int kind, int B, int H, int N, int d, int b, con
                       const double* gamma, const double* beta, double eps, double* Z, double* Wend,
                       int nthreads)
 {
-    if (mode < 0 || mode > 2 || (kind != KIND_PLAIN && kind != KIND_LN)) return -1;
+    if (mode < 0 || mode > 4 || (kind != KIND_PLAIN && kind != KIND_LN)) return -1;
     if (B < 1 || H < 1 || N < 0 || d < 1 || b < 1) return -1;
     if (kind == KIND_LN && (!gamma || !beta)) return -1;
     int units = B * H;

@@ -371,3 +371,105 @@ def test_units_independent(oracle_mod):
     pb = [2, 0, 1]
     Zp, Wp = oracle_mod.linear(oracle_mod.DUAL, 1, Q[pb], K[pb], V[pb], eta[pb], W0[pb], 3, g, bt)
     assert rel(Zp, Z[pb]) < 1e-15 and rel(Wp, W[pb]) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# P-B: block-causal large chunks (page "Test-Time Training Done Right",
+# abstract): one step per chunk with gradients at the chunk's starting weights
+# (the same state recursion as the mini-batch form) and one set of weights for
+# every output of the chunk, the weights before or after the chunk's step.
+# ---------------------------------------------------------------------------
+BLOCK_SHAPES = [(1, 2, 12, 4, 4), (2, 1, 11, 8, 3), (1, 1, 16, 8, 16), (1, 2, 9, 4, 1)]
+
+
+@pytest.mark.parametrize("B,H,N,d,b", BLOCK_SHAPES)
+@pytest.mark.parametrize("kind", [0, 1])
+def test_block_state_equals_minibatch_state(oracle_mod, B, H, N, d, b, kind):
+    """Both block modes step the state exactly as the mini-batch form does."""
+    rng = np.random.default_rng(500 + N + b + kind)
+    Q, K, V, eta, W0, g, bt = rand_problem(rng, B, H, N, d)
+    _, Wm = oracle_mod.linear(oracle_mod.MINIBATCH, kind, Q, K, V, eta, W0, b, g, bt, 1e-6)
+    for mode in (oracle_mod.BLOCK_BEFORE, oracle_mod.BLOCK_AFTER):
+        _, Wb = oracle_mod.linear(mode, kind, Q, K, V, eta, W0, b, g, bt, 1e-6)
+        assert rel(Wb, Wm) < 1e-12
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_block_after_b1_is_online(oracle_mod, kind):
+    """With one token per chunk, outputs after the step are online GD's outputs
+    (page 1, sections 2 and 3: z_t uses the weights updated with token t)."""
+    rng = np.random.default_rng(41 + kind)
+    Q, K, V, eta, W0, g, bt = rand_problem(rng, 1, 2, 13, 8)
+    Zo, Wo = oracle_mod.linear(oracle_mod.ONLINE, kind, Q, K, V, eta, W0, 1, g, bt, 1e-6)
+    Za, Wa = oracle_mod.linear(oracle_mod.BLOCK_AFTER, kind, Q, K, V, eta, W0, 1, g, bt, 1e-6)
+    assert rel(Za, Zo) < 1e-12 and rel(Wa, Wo) < 1e-12
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("mode_name", ["BLOCK_BEFORE", "BLOCK_AFTER"])
+def test_block_outputs_from_prefix_states(oracle_mod, kind, mode_name):
+    """Chunk c's outputs are f(Q_c; W) with W the state after chunks 0..c-1
+    (before) or 0..c (after): the state of a prefix run of the mini-batch form,
+    evaluated through eta = 0 (which leaves W untouched and gives f(Q; W))."""
+    rng = np.random.default_rng(77 + kind)
+    B, H, N, d, b = 1, 2, 14, 8, 4
+    Q, K, V, eta, W0, g, bt = rand_problem(rng, B, H, N, d)
+    mode = getattr(oracle_mod, mode_name)
+    Zb, _ = oracle_mod.linear(mode, kind, Q, K, V, eta, W0, b, g, bt, 1e-6)
+    for c0 in range(0, N, b):
+        c1 = min(c0 + b, N)
+        upto = c0 if mode_name == "BLOCK_BEFORE" else c1
+        if upto > 0:
+            _, Wp = oracle_mod.linear(oracle_mod.MINIBATCH, kind, Q[:, :, :upto], K[:, :, :upto],
+                                      V[:, :, :upto], eta[:, :, :upto], W0, b, g, bt, 1e-6)
+        else:
+            Wp = W0
+        zero = np.zeros((B, H, c1 - c0))
+        Zf, _ = oracle_mod.linear(oracle_mod.MINIBATCH, kind, Q[:, :, c0:c1], K[:, :, c0:c1],
+                                  V[:, :, c0:c1], zero, Wp, b, g, bt, 1e-6)
+        assert rel(Zb[:, :, c0:c1], Zf) < 1e-12
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_block_after_last_token_matches_dual(oracle_mod, kind):
+    """The last token of a full chunk sees every token of its chunk under the
+    causal mask, so the dual form's output there equals the after-step output."""
+    rng = np.random.default_rng(90 + kind)
+    Q, K, V, eta, W0, g, bt = rand_problem(rng, 2, 1, 15, 8)
+    b = 5
+    Zd, _ = oracle_mod.linear(oracle_mod.DUAL, kind, Q, K, V, eta, W0, b, g, bt, 1e-6)
+    Za, _ = oracle_mod.linear(oracle_mod.BLOCK_AFTER, kind, Q, K, V, eta, W0, b, g, bt, 1e-6)
+    last = [c0 + b - 1 for c0 in range(0, 15, b)]
+    assert rel(Za[:, :, last], Zd[:, :, last]) < 1e-12
+    # and not elsewhere (the mask matters inside the chunk)
+    assert rel(Za[:, :, 0], Zd[:, :, 0]) > 1e-6
+
+
+def test_block_single_chunk_closed_forms(oracle_mod):
+    """Plain f, W0 = 0, one chunk: before -> Z = Q W0 = 0; after -> Z = Q (2 K^T D V)."""
+    rng = np.random.default_rng(12)
+    Q, K, V, eta, W0, g, bt = rand_problem(rng, 1, 1, 10, 6)
+    W0 = np.zeros_like(W0)
+    Zb, _ = oracle_mod.linear(oracle_mod.BLOCK_BEFORE, 0, Q, K, V, eta, W0, 10, g, bt, 1e-6)
+    Za, Wa = oracle_mod.linear(oracle_mod.BLOCK_AFTER, 0, Q, K, V, eta, W0, 10, g, bt, 1e-6)
+    q, k, v, e = Q[0, 0], K[0, 0], V[0, 0], eta[0, 0]
+    Wc = 2.0 * k.T @ (e[:, None] * v)
+    assert np.max(np.abs(Zb)) == 0.0
+    assert rel(Wa[0, 0], Wc) < 1e-12
+    assert rel(Za[0, 0], q @ Wc) < 1e-12
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_online_one_token_steps_compose(oracle_mod, kind):
+    """A single-token decode step is the online rule applied once (page 1,
+    section 2); N such steps, each from the previous state, are online GD over
+    the N tokens."""
+    rng = np.random.default_rng(300 + kind)
+    Q, K, V, eta, W0, g, bt = rand_problem(rng, 2, 2, 6, 8)
+    Zo, Wo = oracle_mod.linear(oracle_mod.ONLINE, kind, Q, K, V, eta, W0, 1, g, bt, 1e-6)
+    W = W0
+    for t in range(6):
+        z, W = oracle_mod.linear(oracle_mod.ONLINE, kind, Q[:, :, t:t + 1], K[:, :, t:t + 1],
+                                 V[:, :, t:t + 1], eta[:, :, t:t + 1], W, 1, g, bt, 1e-6)
+        assert rel(z[:, :, 0], Zo[:, :, t]) < 1e-12
+    assert rel(W, Wo) < 1e-12
