@@ -117,6 +117,65 @@ int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b,
  * small-b path). Returns 0 as well for unsupported or invalid combinations. */
 size_t ttt_linear_fwd_workspace_bytes(int kind, int qkv_dtype, int B, int H, int N, int d, int b);
 
+typedef enum {
+    TTT_APPLY_BEFORE_STEP = 0,  /* chunk outputs use the chunk's starting weights W_c */
+    TTT_APPLY_AFTER_STEP = 1    /* chunk outputs use the weights after its step, W_{c+1} */
+} ttt_block_apply;
+
+/*
+ * ttt_linear_fwd_block -- block-causal large-chunk TTT-Linear forward.
+ *
+ * Page "Test-Time Training Done Right" (abstract) argues for large chunks over
+ * small mini-batches with fine-grained block-wise causal dependencies. Read
+ * plainly: the state takes one step per chunk with every gradient at the
+ * chunk's starting weights (exactly as ttt_linear_fwd, so W_end is the same),
+ * and every output of chunk c uses one set of weights, with no causal mask
+ * inside the chunk:
+ *     apply = TTT_APPLY_BEFORE_STEP:  Z_c = f(Q_c; W_c)
+ *     apply = TTT_APPLY_AFTER_STEP:   Z_c = f(Q_c; W_{c+1})
+ * Arguments, layouts, ownership, aliasing and errors are those of
+ * ttt_linear_fwd; an invalid `apply` is TTT_ERR_INVALID_ARGUMENT.
+ * Supported (else TTT_ERR_UNSUPPORTED): the large-chunk combinations of
+ * ttt_linear_fwd (kind PLAIN, BF16, d = 128, b >= 256, b % 128 == 0,
+ * N % 128 == 0, N < 2^22), with the workspace below.
+ */
+int ttt_linear_fwd_block(int apply, int kind, int qkv_dtype, int B, int H, int N, int d, int b,
+                         const void* Q, const void* K, const void* V,
+                         const float* eta, float eta_const, const float* W0,
+                         const float* ln_gamma, const float* ln_beta, float ln_eps,
+                         float* Z, float* W_end,
+                         void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes of ttt_linear_fwd_block (0 for unsupported or invalid input). */
+size_t ttt_linear_fwd_block_workspace_bytes(int apply, int kind, int qkv_dtype, int B, int H, int N,
+                                            int d, int b);
+
+/*
+ * ttt_linear_decode -- one generated token for each of B*H independent
+ * (sequence, head) streams: the online rule of page "Test-Time Training:
+ * Linear Complexity Beyond Attention" (section "2. The Online Gradient Descent
+ * Update Rule", output as in section "3. Forward Evaluation and Output
+ * Projection"), i.e. a mini-batch of one token:
+ *     g = d ||f(k; W) - v||^2 / d(k W),   W <- W - eta k^T g,   z = f(q; W).
+ *
+ *   kind        TTT_LINEAR_PLAIN or TTT_LINEAR_LN (conventions of ttt_linear_fwd)
+ *   qkv_dtype   dtype of q, k, v
+ *   B, H, d     streams = B*H, head dim
+ *   q, k, v     device [B,H,d] qkv_dtype
+ *   eta         device [B,H] fp32 step size of this token, or NULL (eta_const)
+ *   W           device [B,H,d,d] fp32 state, read and overwritten in place
+ *   ln_gamma, ln_beta, ln_eps   as for ttt_linear_fwd
+ *   z           device [B,H,d] fp32 output
+ * W and z must not overlap each other or any input. Asynchronous on hip_stream;
+ * validation on the host before any HIP call. Supported: d = 64 (else
+ * TTT_ERR_UNSUPPORTED).
+ */
+int ttt_linear_decode(int kind, int qkv_dtype, int B, int H, int d,
+                      const void* q, const void* k, const void* v,
+                      const float* eta, float eta_const, float* W,
+                      const float* ln_gamma, const float* ln_beta, float ln_eps,
+                      float* z, void* hip_stream);
+
 /* Which ttt_path a (kind, dtype, d, b) combination takes; TTT_PATH_NONE if none. */
 int ttt_linear_fwd_path(int kind, int qkv_dtype, int d, int b);
 

@@ -71,3 +71,33 @@ def sample_units(wl: wlm.Workload, count: int, seed: int = 0):
     while len(units) < min(count, wl.B * wl.H):
         units.add((int(rng.integers(wl.B)), int(rng.integers(wl.H))))
     return sorted(units)
+
+
+def gpu_linear_block(inp: wlm.Inputs, apply: str):
+    import torch
+    from weights_ttt_layer_amd import linear_fwd_block
+    t = wlm.to_device(inp)
+    wl = inp.wl
+    z, w = linear_fwd_block(t["q"], t["k"], t["v"], t["w0"], t["eta"], b=wl.b, apply=apply, kind=wl.kind,
+                            eta_const=inp.eta_const, ln_gamma=t["gamma"], ln_beta=t["beta"], ln_eps=wl.ln_eps)
+    torch.cuda.synchronize()
+    return z.cpu().numpy(), w.cpu().numpy()
+
+
+def gpu_decode(inp: wlm.Inputs):
+    """Run the N tokens of `inp` as N successive single-token decode steps from
+    W0. Returns (Z [B,H,N,d], final W)."""
+    import torch
+    from weights_ttt_layer_amd import linear_decode
+    t = wlm.to_device(inp)
+    wl = inp.wl
+    w = t["w0"].clone()
+    zs = []
+    for i in range(wl.N):
+        eta = None if t["eta"] is None else t["eta"][:, :, i].contiguous()
+        z = linear_decode(t["q"][:, :, i].contiguous(), t["k"][:, :, i].contiguous(),
+                          t["v"][:, :, i].contiguous(), w, eta, kind=wl.kind, eta_const=inp.eta_const,
+                          ln_gamma=t["gamma"], ln_beta=t["beta"], ln_eps=wl.ln_eps)
+        zs.append(z)
+    torch.cuda.synchronize()
+    return torch.stack(zs, 2).cpu().numpy(), w.cpu().numpy()

@@ -124,3 +124,46 @@ def test_mlp_rejections(lib):
     assert call(d=32, hid=128) == U
     assert call(hid=128) == U
     assert call(b=32) == U
+
+
+def block_call(lib, apply=0, kind=0, dt=1, B=1, H=16, N=32768, d=128, b=2048, ws=None, wsb=0, Z=6):
+    return lib.ttt_linear_fwd_block(apply, kind, dt, B, H, N, d, b, addr(0), addr(1), addr(2), None, 0.1,
+                                    addr(3), addr(4), addr(5), 1e-6, addr(Z), addr(7),
+                                    None if ws is None else addr(ws), wsb, None)
+
+
+def test_block_rejections(lib):
+    E, U = binding.TTT_ERR_INVALID_ARGUMENT, binding.TTT_ERR_UNSUPPORTED
+    assert block_call(lib, apply=2) == E
+    assert block_call(lib, apply=-1) == E
+    assert block_call(lib, Z=0) == E                              # Z overlaps Q
+    assert block_call(lib, d=64, b=16, N=64) == U                 # small-b combinations have no block path
+    assert block_call(lib, kind=1) == U
+    assert block_call(lib) == binding.TTT_ERR_WORKSPACE_TOO_SMALL
+    Wb = lib.ttt_linear_fwd_block_workspace_bytes
+    assert Wb(0, 0, 1, 1, 16, 32768, 128, 2048) == lib.ttt_linear_fwd_workspace_bytes(0, 1, 1, 16, 32768, 128, 2048)
+    assert Wb(1, 0, 1, 1, 16, 32768, 128, 2048) > 0
+    assert Wb(2, 0, 1, 1, 16, 32768, 128, 2048) == 0
+    assert Wb(0, 0, 1, 1, 16, 32768, 64, 16) == 0
+
+
+def decode_call(lib, kind=1, dt=1, B=64, H=12, d=64, q=0, k=1, v=2, eta=None, W=3, gam=4, bet=5, eps=1e-6,
+                z=6):
+    p = lambda i: None if i is None else (i if isinstance(i, ctypes.c_void_p) else addr(i))
+    return lib.ttt_linear_decode(kind, dt, B, H, d, p(q), p(k), p(v), p(eta), 0.1, p(W), p(gam), p(bet), eps,
+                                 p(z), None)
+
+
+def test_decode_rejections(lib):
+    E, U = binding.TTT_ERR_INVALID_ARGUMENT, binding.TTT_ERR_UNSUPPORTED
+    assert decode_call(lib, kind=4) == E
+    assert decode_call(lib, dt=2) == E
+    assert decode_call(lib, B=0) == E
+    assert decode_call(lib, q=None) == E
+    assert decode_call(lib, W=None) == E
+    assert decode_call(lib, gam=None) == E
+    assert decode_call(lib, eps=-1.0) == E
+    assert decode_call(lib, z=ctypes.c_void_p(A + 4)) == E        # z overlaps q
+    assert decode_call(lib, W=ctypes.c_void_p(A + (1 << 30) + 8)) == E   # W overlaps k
+    assert decode_call(lib, q=ctypes.c_void_p(A + 1)) == E       # misaligned bf16
+    assert decode_call(lib, d=128) == U

@@ -4,11 +4,15 @@
 
 ``linear_fwd`` runs TTT-Linear (plain or LayerNorm+residual inner model) and
 ``mlp_fwd`` runs TTT-MLP, both in the mini-batch dual form, on device tensors.
+``linear_fwd_block`` gives block-causal large-chunk outputs and
+``linear_decode`` takes one online step per (sequence, head) stream.
 Build the library first with ``python -m weights_ttt_layer_amd.build``.
 """
 from .binding import (  # noqa: F401
     TTTError,
+    linear_decode,
     linear_fwd,
+    linear_fwd_block,
     linear_path,
     linear_workspace_bytes,
     load_library,
@@ -16,5 +20,5 @@ from .binding import (  # noqa: F401
     status_string,
 )
 
-__all__ = ["TTTError", "linear_fwd", "linear_path", "linear_workspace_bytes", "load_library",
-           "mlp_fwd", "status_string"]
+__all__ = ["TTTError", "linear_decode", "linear_fwd", "linear_fwd_block", "linear_path",
+           "linear_workspace_bytes", "load_library", "mlp_fwd", "status_string"]

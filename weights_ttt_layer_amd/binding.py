@@ -52,6 +52,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_mlp_fwd.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, fp, f, fp, fp, fp, fp, f, fp, fp, fp,
                                 vp]
     lib.ttt_mlp_fwd.restype = i
+    lib.ttt_linear_fwd_block.argtypes = [i] + lib.ttt_linear_fwd.argtypes
+    lib.ttt_linear_fwd_block.restype = i
+    lib.ttt_linear_fwd_block_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    lib.ttt_linear_fwd_block_workspace_bytes.restype = sz
+    lib.ttt_linear_decode.argtypes = [i, i, i, i, i, vp, vp, vp, fp, f, fp, fp, fp, f, fp, vp]
+    lib.ttt_linear_decode.restype = i
     lib.ttt_status_string.argtypes = [i]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_abi_version.argtypes = []
@@ -103,19 +109,11 @@ def linear_workspace_bytes(kind: str, dtype: torch.dtype, B: int, H: int, N: int
         KINDS[kind], _qkv_dtype(torch.empty(0, dtype=dtype)), B, H, N, d, b))
 
 
-def linear_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w0: torch.Tensor,
-               eta: Optional[torch.Tensor] = None, *, b: int, kind: str = "plain",
-               eta_const: float = 0.0, ln_gamma: Optional[torch.Tensor] = None,
-               ln_beta: Optional[torch.Tensor] = None, ln_eps: float = 1e-6,
-               z: Optional[torch.Tensor] = None, w_end: Optional[torch.Tensor] = None,
-               workspace: Optional[torch.Tensor] = None, stream=None
-               ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """TTT-Linear forward through ``ttt_linear_fwd``. Returns (Z, W_end).
+APPLY = {"before": 0, "after": 1}
 
-    q, k, v: [B,H,N,d] bf16 or fp32; w0: [B,H,d,d] fp32; eta: [B,H,N] fp32 or
-    None (then ``eta_const`` for every token); ln_gamma/ln_beta: [H,d] fp32 for
-    kind "ln". ``w_end`` may be ``w0`` for an in-place state update.
-    """
+
+def _linear_call(entry: str, apply: Optional[int], q, k, v, w0, eta, b, kind, eta_const, ln_gamma,
+                 ln_beta, ln_eps, z, w_end, workspace, stream):
     lib = load_library()
     if kind not in KINDS:
         raise ValueError(f"kind must be one of {sorted(KINDS)}")
@@ -139,16 +137,92 @@ def linear_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w0: torch.Tens
         w_end = torch.empty_like(w0)
     else:
         _check(w_end, "w_end", (B, H, d, d), torch.float32)
-    need = int(lib.ttt_linear_fwd_workspace_bytes(KINDS[kind], dt, B, H, N, d, b))
+    args = (KINDS[kind], dt, B, H, N, d, int(b))
+    if apply is None:
+        need = int(lib.ttt_linear_fwd_workspace_bytes(*args))
+    else:
+        need = int(lib.ttt_linear_fwd_block_workspace_bytes(apply, *args))
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.ttt_linear_fwd(KINDS[kind], dt, B, H, N, d, int(b), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
-                            float(eta_const), _ptr(w0), _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps),
-                            _ptr(z), _ptr(w_end), _ptr(workspace), ws_bytes, _stream_ptr(stream))
+    rest = (_ptr(q), _ptr(k), _ptr(v), _ptr(eta), float(eta_const), _ptr(w0), _ptr(ln_gamma),
+            _ptr(ln_beta), float(ln_eps), _ptr(z), _ptr(w_end), _ptr(workspace), ws_bytes,
+            _stream_ptr(stream))
+    if apply is None:
+        st = lib.ttt_linear_fwd(*args, *rest)
+    else:
+        st = lib.ttt_linear_fwd_block(apply, *args, *rest)
     if st != TTT_OK:
-        raise TTTError(st, "ttt_linear_fwd")
+        raise TTTError(st, entry)
     return z, w_end
+
+
+def linear_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w0: torch.Tensor,
+               eta: Optional[torch.Tensor] = None, *, b: int, kind: str = "plain",
+               eta_const: float = 0.0, ln_gamma: Optional[torch.Tensor] = None,
+               ln_beta: Optional[torch.Tensor] = None, ln_eps: float = 1e-6,
+               z: Optional[torch.Tensor] = None, w_end: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, stream=None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """TTT-Linear forward through ``ttt_linear_fwd``. Returns (Z, W_end).
+
+    q, k, v: [B,H,N,d] bf16 or fp32; w0: [B,H,d,d] fp32; eta: [B,H,N] fp32 or
+    None (then ``eta_const`` for every token); ln_gamma/ln_beta: [H,d] fp32 for
+    kind "ln". ``w_end`` may be ``w0`` for an in-place state update.
+    """
+    return _linear_call("ttt_linear_fwd", None, q, k, v, w0, eta, b, kind, eta_const, ln_gamma,
+                        ln_beta, ln_eps, z, w_end, workspace, stream)
+
+
+def linear_fwd_block(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w0: torch.Tensor,
+                     eta: Optional[torch.Tensor] = None, *, b: int, apply: str = "before",
+                     kind: str = "plain", eta_const: float = 0.0,
+                     ln_gamma: Optional[torch.Tensor] = None, ln_beta: Optional[torch.Tensor] = None,
+                     ln_eps: float = 1e-6, z: Optional[torch.Tensor] = None,
+                     w_end: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block-causal large-chunk forward through ``ttt_linear_fwd_block``: every
+    output of chunk c uses W_c (apply="before") or W_{c+1} (apply="after").
+    Arguments as for ``linear_fwd``. Returns (Z, W_end)."""
+    if apply not in APPLY:
+        raise ValueError(f"apply must be one of {sorted(APPLY)}")
+    return _linear_call("ttt_linear_fwd_block", APPLY[apply], q, k, v, w0, eta, b, kind, eta_const,
+                        ln_gamma, ln_beta, ln_eps, z, w_end, workspace, stream)
+
+
+def linear_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w: torch.Tensor,
+                  eta: Optional[torch.Tensor] = None, *, kind: str = "plain", eta_const: float = 0.0,
+                  ln_gamma: Optional[torch.Tensor] = None, ln_beta: Optional[torch.Tensor] = None,
+                  ln_eps: float = 1e-6, z: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode token per (sequence, head) through ``ttt_linear_decode``.
+
+    q, k, v: [B,H,d]; w: [B,H,d,d] fp32, updated in place; eta: [B,H] fp32 or
+    None. Returns z [B,H,d] fp32."""
+    lib = load_library()
+    if kind not in KINDS:
+        raise ValueError(f"kind must be one of {sorted(KINDS)}")
+    B, H, d = q.shape
+    dt = _qkv_dtype(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, (B, H, d), q.dtype)
+    _check(w, "w", (B, H, d, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H), torch.float32)
+    if kind == "ln":
+        if ln_gamma is None or ln_beta is None:
+            raise ValueError("kind 'ln' needs ln_gamma and ln_beta")
+        _check(ln_gamma, "ln_gamma", (H, d), torch.float32)
+        _check(ln_beta, "ln_beta", (H, d), torch.float32)
+    if z is None:
+        z = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    else:
+        _check(z, "z", (B, H, d), torch.float32)
+    st = lib.ttt_linear_decode(KINDS[kind], dt, B, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                               float(eta_const), _ptr(w), _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps),
+                               _ptr(z), _stream_ptr(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_linear_decode")
+    return z
 
 
 def mlp_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,

@@ -47,9 +47,15 @@ struct MlpArgs {
 // Small-b path: one workgroup per (sequence, head); d = 64, 1 <= b <= 16.
 hipError_t launch_smallb_linear(const LinearArgs& a, hipStream_t stream);
 
-// Large-chunk path (plain f, bf16, d = 128, b % 128 == 0).
+// Large-chunk path (plain f, bf16, d = 128, b % 128 == 0). `outputs` selects the
+// dual-form outputs (causal inside a chunk) or block-causal ones taken with the
+// chunk's starting or ending weights.
+enum { LC_OUT_DUAL = 0, LC_OUT_BEFORE = 1, LC_OUT_AFTER = 2 };
 size_t large_chunk_workspace_bytes(int B, int H, int N, int d, int b);
-hipError_t launch_large_chunk_linear(const LinearArgs& a, hipStream_t stream);
+hipError_t launch_large_chunk_linear(const LinearArgs& a, int outputs, hipStream_t stream);
+
+// Single-token decode step: one wave per (sequence, head), d = 64.
+hipError_t launch_decode_linear(const LinearArgs& a, hipStream_t stream);
 
 // TTT-MLP small-b path: d = 64, hidden = 256, 1 <= b <= 16.
 hipError_t launch_smallb_mlp(const MlpArgs& a, hipStream_t stream);

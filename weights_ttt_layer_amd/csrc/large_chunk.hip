@@ -15,7 +15,9 @@
 //              32-column block)); writes every W_c^T as two bf16 terms and W_end;
 //   lc_chunk : Z of every (unit, chunk) at once from W_c, fused: the chunk's
 //              residuals, the causal term and the output in one pass over
-//              Q, K, V (sub-blocks of 64 tokens, see below).
+//              Q, K, V (sub-blocks of 64 tokens, see below);
+//   lc_apply : instead of lc_chunk for block-causal outputs, Z_c = Q_c W_c or
+//              Q_c W_{c+1} (no causal term inside a chunk).
 // Workspace (caller-provided): M, B (fp32), W_c^T terms (bf16).
 //
 // Precision: every product involving an fp32 quantity (state, gradient, the
@@ -51,15 +53,10 @@ __host__ __device__ inline LcLayout lc_layout(int units, int N, int b)
     L.m_off = 0;
     L.b_off = align256(L.m_off + (size_t)units * C * LD * LD * 4);
     L.wt_off = align256(L.b_off + (size_t)units * C * LD * LD * 4);
-    L.total = align256(L.wt_off + (size_t)units * C * 2 * LD * LD * 2);
+    L.total = align256(L.wt_off + (size_t)units * (C + 1) * 2 * LD * LD * 2);
     return L;
 }
 
-// ===========================================================================
-// lc_gram: M_c = K^T D K (symmetric: upper 32x32 tiles computed, mirrored on
-// store) and B_c = K^T D V for one (unit, chunk) per workgroup.
-// ===========================================================================
-constexpr int GR_TOK = 64;              // tokens per LDS stage
 typedef __attribute__((address_space(3))) void lds_void;
 
 // LDS tiles have 256-byte rows = 16 pieces of 16 bytes; piece p of row r is
@@ -85,9 +82,26 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds)
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
+// ===========================================================================
+// lc_gram: M_c = K^T D K and B_c = K^T D V for one (unit, chunk) per workgroup.
+// Wave w computes row tile w of both (rows 32w..32w+31, all four column tiles),
+// so one A operand (the D-scaled K^T fragment) feeds eight products. K and V
+// stream through LDS in 64-token stages, GR_NST stages in flight.
+//
+// Outputs are written in the register order in which lc_scan consumes them:
+//  * M_c, as two bf16 terms, tile (r, cc) lane by lane: lc_scan's wave w needs
+//    M_c[32w + l32][k] for k = 32r + crow(8s + j, h) (its k order), which by
+//    symmetry is M_c[32r + crow(8s+j, h)][32w + l32], i.e. slot 8s + j of lane
+//    (l32, h) of tile (r, cc = w).  Layout [tile][term][s][lane][8].
+//  * B_c, fp32, tile (r, cc) lane by lane in its C layout: [tile][q][lane][4]
+//    (slots 4q .. 4q+3).
+// ===========================================================================
+constexpr int GR_TOK = 64;              // tokens per LDS stage
+constexpr int GR_NST = 4;               // LDS stages (three in flight while one is read)
+
 struct GramSmem {
-    uint16_t k[2][GR_TOK * LD];         // [token][feature], swizzled pieces
-    uint16_t v[2][GR_TOK * LD];
+    uint16_t k[GR_NST][GR_TOK * LD];    // [token][feature], swizzled pieces
+    uint16_t v[GR_NST][GR_TOK * LD];
 };
 
 // Token-major operand fragment of a [tokens x 128] bf16 LDS tile: lane l gets
@@ -140,43 +154,49 @@ __device__ __forceinline__ void scaled_frag(const bf16x8& f, const float* eta8, 
     }
 }
 
-// The 10 upper tiles of M and the 16 tiles of B, spread over 4 waves.
-__device__ __constant__ const int kGramM[4][3][2] = {
-    {{0, 0}, {0, 1}, {0, 2}}, {{0, 3}, {1, 1}, {1, 2}}, {{1, 3}, {2, 2}, {-1, -1}}, {{2, 3}, {3, 3}, {-1, -1}}};
+// s_waitcnt immediate: at most `vm` vector-memory operations outstanding
+// (lgkmcnt and expcnt not waited for).
+constexpr int vmcnt_imm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <bool PER_TOKEN>
 __global__ void __launch_bounds__(LT)
 lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
-               const float* __restrict__ etag, float eta_const, float* __restrict__ Mout,
+               const float* __restrict__ etag, float eta_const, uint16_t* __restrict__ Mout,
                float* __restrict__ Bout)
 {
     constexpr int TA = PER_TOKEN ? 2 : 1;    // terms of the D-scaled operand
+    constexpr int OPS = 8;                   // direct loads per wave per stage
     __shared__ GramSmem sm;
     const int C = (N + b - 1) / b;
     const int unit = blockIdx.x / C, c = blockIdx.x % C;
     const int c0 = c * b, nt = min(b, N - c0);
-    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint16_t* Ku = Kg + ((size_t)unit * N + c0) * LD;
     const uint16_t* Vu = Vg + ((size_t)unit * N + c0) * LD;
     const float* etau = PER_TOKEN ? etag + (size_t)unit * N + c0 : nullptr;
 
-    // wave w: B row tile w (4 tiles) + up to 3 upper M tiles
-    f32x16 accB[4], accM[3];
+    f32x16 accB[4], accM[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) accB[t] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < 3; ++t) accM[t] = f32x16{};
+    for (int t = 0; t < 4; ++t) {
+        accB[t] = f32x16{};
+        accM[t] = f32x16{};
+    }
 
     const int nstage = nt / GR_TOK;
-    gram_dma(sm, 0, 0, w, lane, Ku, Vu);
+#pragma unroll
+    for (int s = 0; s < GR_NST - 1; ++s)
+        if (s < nstage) gram_dma(sm, s, s, w, lane, Ku, Vu);
     for (int s = 0; s < nstage; ++s) {
-        const int buf = s & 1;
-        __builtin_amdgcn_s_waitcnt(0x0070);              // this wave's loads of stage s are done
-        __syncthreads();                                 // stage s landed; stage s-1 consumed
-        if (s + 1 < nstage) gram_dma(sm, buf ^ 1, s + 1, w, lane, Ku, Vu);
-        const uint16_t* kt = sm.k[buf];
-        const uint16_t* vt = sm.v[buf];
+        // stage s is this wave's oldest outstanding group of loads
+        const int later = min(GR_NST - 2, nstage - 1 - s);
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * OPS));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(OPS));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();                                 // stage s landed everywhere; stage s-1 consumed
+        if (s + GR_NST - 1 < nstage) gram_dma(sm, (s + GR_NST - 1) % GR_NST, s + GR_NST - 1, w, lane, Ku, Vu);
+        const uint16_t* kt = sm.k[s % GR_NST];
+        const uint16_t* vt = sm.v[s % GR_NST];
 #pragma unroll
         for (int ks = 0; ks < GR_TOK / 16; ++ks) {
             const float* er = PER_TOKEN ? etau + s * GR_TOK + 16 * ks + 8 * h : nullptr;
@@ -185,18 +205,11 @@ lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const bf16x8 bv = tok_major_frag(vt, 16 * ks, t, lane);
+                const bf16x8 bk = tok_major_frag(kt, 16 * ks, t, lane);
 #pragma unroll
-                for (int s2 = TA - 1; s2 >= 0; --s2) accB[t] = mfma_32x32x16(aw[s2], bv, accB[t]);
-            }
-#pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                const int r = kGramM[w][t][0], cc = kGramM[w][t][1];
-                if (r >= 0) {
-                    bf16x8 ar[TA];
-                    scaled_frag<PER_TOKEN, TA>(tok_major_frag(kt, 16 * ks, r, lane), er, ar);
-                    const bf16x8 bk = tok_major_frag(kt, 16 * ks, cc, lane);
-#pragma unroll
-                    for (int s2 = TA - 1; s2 >= 0; --s2) accM[t] = mfma_32x32x16(ar[s2], bk, accM[t]);
+                for (int s2 = TA - 1; s2 >= 0; --s2) {
+                    accB[t] = mfma_32x32x16(aw[s2], bv, accB[t]);
+                    accM[t] = mfma_32x32x16(aw[s2], bk, accM[t]);
                 }
             }
         }
@@ -204,53 +217,99 @@ lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
 
     const float scale = PER_TOKEN ? 1.f : 2.f * eta_const;
     const size_t base = ((size_t)unit * C + c) * LD * LD;
-    float* Mo = Mout + base;
+    uint16_t* Mo = Mout + 2 * base;                      // two bf16 terms per element
     float* Bo = Bout + base;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+        const int tile = 4 * w + t;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Bo[(32 * w + crow(i, h)) * LD + 32 * t + l32] = scale * accB[t][i];
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(Bo + ((size_t)(tile * 4 + q) * 64 + lane) * 4) =
+                make_float4(scale * accB[t][4 * q], scale * accB[t][4 * q + 1], scale * accB[t][4 * q + 2],
+                            scale * accB[t][4 * q + 3]);
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
-        const int r = kGramM[w][t][0], cc = kGramM[w][t][1];
-        if (r >= 0) {
+        for (int s2 = 0; s2 < 2; ++s2) {
+            float x[8];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float v = scale * accM[t][i];
-                Mo[(32 * r + crow(i, h)) * LD + 32 * cc + l32] = v;
-                if (r != cc) Mo[(32 * cc + l32) * LD + 32 * r + crow(i, h)] = v;
-            }
+            for (int j = 0; j < 8; ++j) x[j] = scale * accM[t][8 * s2 + j];
+            bf16x8 mt[2];
+            terms8<2>(x, mt);
+#pragma unroll
+            for (int term = 0; term < 2; ++term)
+                *reinterpret_cast<bf16x8*>(Mo + ((size_t)((tile * 2 + term) * 2 + s2) * 64 + lane) * 8) = mt[term];
         }
     }
 }
 
 // ===========================================================================
 // lc_scan: W_{c+1} = W_c - M_c W_c + B_c for one (unit, 32-column block).
-// Wave w holds rows [32w, 32w+32) of the block as one 32x32 C tile.
+// Wave w holds rows [32w, 32w+32) of the block as one 32x32 C tile (acc).
+// The product M_c W_c runs over k in the order 32r + crow(8s + j, h): in that
+// order the B operand (rows of W_c) of k-step (r, s) is exactly what wave r
+// holds in slots 8s .. 8s+7 of the same lane, so every wave publishes its
+// tile's two bf16 terms lane by lane in LDS and reads the others' at its own
+// lane index; the A operand comes ready-split from lc_gram in that order.
+// The operands of step c+2 are requested while step c runs. W_0 .. W_C are all
+// published (W_C, the final state, for outputs taken after the last step).
 // ===========================================================================
-constexpr int SC_STRIDE = LD + 4;   // floats per column of the column-major LDS block
+struct ScanOps {
+    bf16x8 a[4][2][2];                  // M_c A operand [r][s][term]
+    float4 bq[4];                       // B_c entries of this lane's C tile
+};
 
-// Operands of one scan step: this lane's A rows of M_c (row 32w + l32, the
-// 8 k values of each k-step) and its 16 entries of B_c in the C layout.
-__device__ __forceinline__ void scan_load(const float* Mg, const float* Bg, int unit, int C, int c, int w, int l32,
-                                          int h, int colg, float4 (&ma)[LD / 16][2], float (&bv)[16])
+__device__ __forceinline__ void scan_load(const uint16_t* Mg, const float* Bg, int unit, int C, int c, int w,
+                                          int cb, int lane, ScanOps& o)
 {
-    const float* Mc = Mg + ((size_t)unit * C + c) * LD * LD;
-    const float* Bc = Bg + ((size_t)unit * C + c) * LD * LD;
+    const size_t base = ((size_t)unit * C + c) * LD * LD;
+    const uint16_t* Mc = Mg + 2 * base;
+    const float* Bc = Bg + base;
 #pragma unroll
-    for (int ks = 0; ks < LD / 16; ++ks) {
-        ma[ks][0] = *reinterpret_cast<const float4*>(Mc + (size_t)(32 * w + l32) * LD + 16 * ks + 8 * h);
-        ma[ks][1] = *reinterpret_cast<const float4*>(Mc + (size_t)(32 * w + l32) * LD + 16 * ks + 8 * h + 4);
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int term = 0; term < 2; ++term)
+                o.a[r][s][term] = *reinterpret_cast<const bf16x8*>(
+                    Mc + ((size_t)(((4 * r + w) * 2 + term) * 2 + s) * 64 + lane) * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        o.bq[q] = *reinterpret_cast<const float4*>(Bc + ((size_t)((4 * w + cb) * 4 + q) * 64 + lane) * 4);
+}
+
+// Two bf16 terms of this lane's 16 state entries: into `pub` (lane by lane, if
+// given) and into W^T of the workspace (wt: [term][column][row]).
+__device__ __forceinline__ void publish_state(const f32x16& acc, uint16_t* wt, bf16x8 (*pub)[2][64], int w,
+                                              int lane, int h, int colg)
+{
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = acc[8 * s + j];
+        bf16x8 tw[2];
+        terms8<2>(x, tw);
+        if (pub) {
+            pub[0][s][lane] = tw[0];
+            pub[1][s][lane] = tw[1];
+        }
+        // slots 8s .. 8s+3 and 8s+4 .. 8s+7 are rows row0 .. row0+3 and row0+8 .. row0+11
+        const int row0 = 32 * w + 16 * s + 4 * h;
+#pragma unroll
+        for (int term = 0; term < 2; ++term) {
+            const uint4 u = __builtin_bit_cast(uint4, tw[term]);
+            *reinterpret_cast<uint2*>(wt + (size_t)term * LD * LD + (size_t)colg * LD + row0) = make_uint2(u.x, u.y);
+            *reinterpret_cast<uint2*>(wt + (size_t)term * LD * LD + (size_t)colg * LD + row0 + 8) =
+                make_uint2(u.z, u.w);
+        }
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) bv[i] = Bc[(size_t)(32 * w + crow(i, h)) * LD + colg];
 }
 
 __global__ void __launch_bounds__(LT)
-lc_scan_kernel(int N, int b, const float* __restrict__ W0, const float* __restrict__ Mg,
+lc_scan_kernel(int N, int b, const float* __restrict__ W0, const uint16_t* __restrict__ Mg,
                const float* __restrict__ Bg, uint16_t* __restrict__ WT, float* __restrict__ Wend)
 {
-    __shared__ __attribute__((aligned(16))) float wcol[32 * SC_STRIDE];   // [column][row]
+    // [buffer][wave][term][s][lane] bf16x8: W_c rows of every wave, lane by lane
+    __shared__ __attribute__((aligned(16))) bf16x8 wpub[2][4][2][2][64];
     const int C = (N + b - 1) / b;
     const int unit = blockIdx.x >> 2, cb = blockIdx.x & 3;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -261,57 +320,40 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const float* __restri
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = W0u[(32 * w + crow(i, h)) * LD + colg];
 
-    float4 ma[LD / 16][2];
-    float bv[16];
-    scan_load(Mg, Bg, unit, C, 0, w, l32, h, colg, ma, bv);
+    ScanOps o0, o1;
+    scan_load(Mg, Bg, unit, C, 0, w, cb, lane, o0);
+    scan_load(Mg, Bg, unit, C, min(1, C - 1), w, cb, lane, o1);
     for (int c = 0; c < C; ++c) {
-        // publish W_c: column-major block in LDS, W_c^T terms in the workspace
-        uint16_t* wt = WT + ((size_t)unit * C + c) * 2 * LD * LD;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 v = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
-            const int row0 = 32 * w + 8 * q + 4 * h;
-            *reinterpret_cast<float4*>(&wcol[l32 * SC_STRIDE + row0]) = v;
-            uint32_t p01[2], p23[2];   // [term] packed bf16 pairs of rows row0, row0+1 / row0+2, row0+3
-            split_pair<2>(v.x, v.y, p01);
-            split_pair<2>(v.z, v.w, p23);
-            // W_c^T[col][row0..row0+3], term 0 and term 1
-            *reinterpret_cast<uint2*>(wt + (size_t)colg * LD + row0) = make_uint2(p01[0], p23[0]);
-            *reinterpret_cast<uint2*>(wt + (size_t)LD * LD + (size_t)colg * LD + row0) =
-                make_uint2(p01[1], p23[1]);
-        }
-        __syncthreads();
-        // prefetch M_{c+1}, B_{c+1} (clamped: the last step reloads its own)
-        float4 mn[LD / 16][2];
-        float bn[16];
-        scan_load(Mg, Bg, unit, C, min(c + 1, C - 1), w, l32, h, colg, mn, bn);
+        const int buf = c & 1;
+        // publish W_c: two bf16 terms, lane by lane in LDS and as W_c^T in the workspace
+        publish_state(acc, WT + ((size_t)unit * (C + 1) + c) * 2 * LD * LD, wpub[buf][w], w, lane, h, colg);
+        __syncthreads();                                 // one barrier per step: wpub is double-buffered
+        // operands of step c + 2 (clamped: the last steps reload their own)
+        ScanOps o2;
+        scan_load(Mg, Bg, unit, C, min(c + 2, C - 1), w, cb, lane, o2);
         f32x16 t = {};
 #pragma unroll
-        for (int ks = 0; ks < LD / 16; ++ks) {
-            // A = M_c rows 32w + l32, k = 16ks + 8h + 0..7 ; B = W_c rows k, column colg
-            const float4 b0 = *reinterpret_cast<const float4*>(&wcol[l32 * SC_STRIDE + 16 * ks + 8 * h]);
-            const float4 b1 = *reinterpret_cast<const float4*>(&wcol[l32 * SC_STRIDE + 16 * ks + 8 * h + 4]);
-            const float xa[8] = {ma[ks][0].x, ma[ks][0].y, ma[ks][0].z, ma[ks][0].w,
-                                 ma[ks][1].x, ma[ks][1].y, ma[ks][1].z, ma[ks][1].w};
-            const float xb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-            bf16x8 ta[2], tb[2];
-            terms8<2>(xa, ta);
-            terms8<2>(xb, tb);
-            t = mfma_32x32x16(ta[1], tb[0], t);
-            t = mfma_32x32x16(ta[0], tb[1], t);
-            t = mfma_32x32x16(ta[0], tb[0], t);
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const bf16x8 b0 = wpub[buf][r][0][s][lane];
+                const bf16x8 b1 = wpub[buf][r][1][s][lane];
+                t = mfma_32x32x16(o0.a[r][s][1], b0, t);
+                t = mfma_32x32x16(o0.a[r][s][0], b1, t);
+                t = mfma_32x32x16(o0.a[r][s][0], b0, t);
+            }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[4 * q] = (acc[4 * q] - t[4 * q]) + o0.bq[q].x;
+            acc[4 * q + 1] = (acc[4 * q + 1] - t[4 * q + 1]) + o0.bq[q].y;
+            acc[4 * q + 2] = (acc[4 * q + 2] - t[4 * q + 2]) + o0.bq[q].z;
+            acc[4 * q + 3] = (acc[4 * q + 3] - t[4 * q + 3]) + o0.bq[q].w;
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = (acc[i] - t[i]) + bv[i];
-#pragma unroll
-        for (int ks = 0; ks < LD / 16; ++ks) {
-            ma[ks][0] = mn[ks][0];
-            ma[ks][1] = mn[ks][1];
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) bv[i] = bn[i];
-        __syncthreads();   // wcol is rewritten next step
+        o0 = o1;
+        o1 = o2;
     }
+    // the final state, for outputs taken after the last chunk's step
+    publish_state(acc, WT + ((size_t)unit * (C + 1) + C) * 2 * LD * LD, nullptr, w, lane, h, colg);
     float* We = Wend + (size_t)unit * LD * LD;
 #pragma unroll
     for (int i = 0; i < 16; ++i) We[(32 * w + crow(i, h)) * LD + colg] = acc[i];
@@ -655,7 +697,7 @@ lc_chunk_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* _
     x.zr = __builtin_amdgcn_make_buffer_rsrc(Zg + (size_t)unit * N * LD, (short)0, N * LD * 4, 0x00020000);
 
     // W_c^T (both terms, 512 rows of 256 B) and the first sub-block
-    rows_dma<16>(reinterpret_cast<char*>(lc_wc), WT + ((size_t)unit * C + c) * 2 * LD * LD, x.w, x.lane);
+    rows_dma<16>(reinterpret_cast<char*>(lc_wc), WT + ((size_t)unit * (C + 1) + c) * 2 * LD * LD, x.w, x.lane);
     sub_dma(lc_buf0, x.Ku, x.Qu, x.Vu, x.c0, x.w, x.lane);
     __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
@@ -688,6 +730,59 @@ lc_chunk_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* _
     }
 }
 
+// ===========================================================================
+// lc_apply: block-causal outputs, Z_c = Q_c W_c (AFTER = false: the chunk's
+// starting weights) or Q_c W_{c+1} (AFTER = true: the weights after its step),
+// with no causal term inside the chunk. One workgroup per 128 tokens; wave w
+// computes output features [32w, 32w+32) with W^T rows (two bf16 terms) held as
+// B operands in registers and Q rows read straight from global memory.
+// ===========================================================================
+template <bool AFTER>
+__global__ void __launch_bounds__(LT)
+lc_apply_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ WT,
+                float* __restrict__ Zg)
+{
+    const int C = (N + b - 1) / b;
+    const int nblk = N / TB;
+    const int unit = blockIdx.x / nblk, t0 = (blockIdx.x % nblk) * TB;
+    const int c = t0 / b;                                // chunk lengths are multiples of TB
+    const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint16_t* wt = WT + ((size_t)unit * (C + 1) + c + (AFTER ? 1 : 0)) * 2 * LD * LD;
+    const uint16_t* Qu = Qg + (size_t)unit * N * LD;
+    const __amdgpu_buffer_rsrc_t zr =
+        __builtin_amdgcn_make_buffer_rsrc(Zg + (size_t)unit * N * LD, (short)0, N * LD * 4, 0x00020000);
+
+    bf16x8 wb[LD / 16][2];
+#pragma unroll
+    for (int ks = 0; ks < LD / 16; ++ks)
+#pragma unroll
+        for (int term = 0; term < 2; ++term)
+            wb[ks][term] = *reinterpret_cast<const bf16x8*>(wt + (size_t)term * LD * LD +
+                                                            (size_t)(32 * w + l32) * LD + 16 * ks + 8 * h);
+    const int voff = ((4 * h) * LD + 32 * w + l32) * 4;
+#pragma unroll
+    for (int tt = 0; tt < TB / 32; ++tt) {
+        bf16x8 qa[LD / 16];
+#pragma unroll
+        for (int ks = 0; ks < LD / 16; ++ks)
+            qa[ks] = *reinterpret_cast<const bf16x8*>(Qu + (size_t)(t0 + 32 * tt + l32) * LD + 16 * ks + 8 * h);
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < LD / 16; ++ks) {
+            acc = mfma_32x32x16(qa[ks], wb[ks][1], acc);
+            acc = mfma_32x32x16(qa[ks], wb[ks][0], acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int srow = __builtin_amdgcn_readfirstlane(t0 + 32 * tt + 8 * (e >> 2));
+            const float v = acc[e];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), zr, voff + (e & 3) * LD * 4,
+                                                  srow * LD * 4, 0);
+        }
+    }
+}
+
 }  // namespace
 
 size_t large_chunk_workspace_bytes(int B, int H, int N, int d, int b)
@@ -696,13 +791,13 @@ size_t large_chunk_workspace_bytes(int B, int H, int N, int d, int b)
     return lc_layout(B * H, N, b).total;
 }
 
-hipError_t launch_large_chunk_linear(const LinearArgs& a, hipStream_t stream)
+hipError_t launch_large_chunk_linear(const LinearArgs& a, int outputs, hipStream_t stream)
 {
     const int units = a.B * a.H;
     const int C = (a.N + a.b - 1) / a.b;
     const LcLayout L = lc_layout(units, a.N, a.b);
     char* ws = static_cast<char*>(a.workspace);
-    float* M = reinterpret_cast<float*>(ws + L.m_off);
+    uint16_t* M = reinterpret_cast<uint16_t*>(ws + L.m_off);
     float* Bm = reinterpret_cast<float*>(ws + L.b_off);
     uint16_t* WT = reinterpret_cast<uint16_t*>(ws + L.wt_off);
     const uint16_t* Q = static_cast<const uint16_t*>(a.Q);
@@ -720,7 +815,13 @@ hipError_t launch_large_chunk_linear(const LinearArgs& a, hipStream_t stream)
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lc_scan_kernel, dim3(units * 4), dim3(LT), 0, stream, a.N, a.b, a.W0, M, Bm, WT, a.W_end);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (per_token)
+    if (outputs == LC_OUT_BEFORE)
+        hipLaunchKernelGGL((lc_apply_kernel<false>), dim3(units * (a.N / TB)), dim3(LT), 0, stream, a.N, a.b, Q, WT,
+                           a.Z);
+    else if (outputs == LC_OUT_AFTER)
+        hipLaunchKernelGGL((lc_apply_kernel<true>), dim3(units * (a.N / TB)), dim3(LT), 0, stream, a.N, a.b, Q, WT,
+                           a.Z);
+    else if (per_token)
         hipLaunchKernelGGL((lc_chunk_kernel<true>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, Q, K, V, a.eta,
                            a.eta_const, WT, a.Z);
     else

@@ -69,10 +69,16 @@ size_t ttt_linear_fwd_workspace_bytes(int kind, int qkv_dtype, int B, int H, int
     return ttt::large_chunk_workspace_bytes(B, H, N, d, b);
 }
 
-int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b, const void* Q,
-                   const void* K, const void* V, const float* eta, float eta_const, const float* W0,
-                   const float* ln_gamma, const float* ln_beta, float ln_eps, float* Z, float* W_end,
-                   void* workspace, size_t workspace_bytes, void* hip_stream)
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the chunked forward entry points; fills `a` and the
+// path on success. Touches no HIP API.
+int check_linear(int kind, int qkv_dtype, int B, int H, int N, int d, int b, const void* Q, const void* K,
+                 const void* V, const float* eta, float eta_const, const float* W0, const float* ln_gamma,
+                 const float* ln_beta, float ln_eps, float* Z, float* W_end, void* workspace,
+                 size_t workspace_bytes, ttt::LinearArgs& a, int& path)
 {
     if (kind != TTT_LINEAR_PLAIN && kind != TTT_LINEAR_LN) return TTT_ERR_INVALID_ARGUMENT;
     if (qkv_dtype != TTT_DTYPE_F32 && qkv_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARGUMENT;
@@ -100,10 +106,19 @@ int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b, c
         overlaps(W_end, w_bytes, V, qkv_bytes) || (eta && overlaps(W_end, w_bytes, eta, tok * 4)))
         return TTT_ERR_INVALID_ARGUMENT;
 
-    const int path = linear_path(kind, qkv_dtype, d, b);
+    path = linear_path(kind, qkv_dtype, d, b);
     if (path == TTT_PATH_NONE) return TTT_ERR_UNSUPPORTED;
+    if (path == TTT_PATH_LARGE_CHUNK) {
+        if (N % LARGE_B_MULT != 0 || N >= LARGE_MAX_N) return TTT_ERR_UNSUPPORTED;
+        const size_t need = ttt::large_chunk_workspace_bytes(B, H, N, d, b);
+        if (workspace_bytes < need || (need > 0 && !workspace)) return TTT_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned(workspace, 256)) return TTT_ERR_INVALID_ARGUMENT;
+        if (overlaps(workspace, need, Z, z_bytes) || overlaps(workspace, need, W_end, w_bytes) ||
+            overlaps(workspace, need, Q, qkv_bytes) || overlaps(workspace, need, K, qkv_bytes) ||
+            overlaps(workspace, need, V, qkv_bytes) || overlaps(workspace, need, W0, w_bytes))
+            return TTT_ERR_INVALID_ARGUMENT;
+    }
 
-    ttt::LinearArgs a;
     a.kind = kind;
     a.dtype = qkv_dtype;
     a.B = B;
@@ -124,22 +139,100 @@ int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b, c
     a.W_end = W_end;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
-    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    return TTT_OK;
+}
 
-    hipError_t err;
-    if (path == TTT_PATH_SMALL_B) {
-        err = ttt::launch_smallb_linear(a, stream);
-    } else {
-        if (N % LARGE_B_MULT != 0 || N >= LARGE_MAX_N) return TTT_ERR_UNSUPPORTED;
-        const size_t need = ttt::large_chunk_workspace_bytes(B, H, N, d, b);
-        if (workspace_bytes < need || (need > 0 && !workspace)) return TTT_ERR_WORKSPACE_TOO_SMALL;
-        if (!aligned(workspace, 256)) return TTT_ERR_INVALID_ARGUMENT;
-        if (overlaps(workspace, need, Z, z_bytes) || overlaps(workspace, need, W_end, w_bytes) ||
-            overlaps(workspace, need, Q, qkv_bytes) || overlaps(workspace, need, K, qkv_bytes) ||
-            overlaps(workspace, need, V, qkv_bytes) || overlaps(workspace, need, W0, w_bytes))
+}  // namespace
+
+extern "C" {
+
+int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b, const void* Q,
+                   const void* K, const void* V, const float* eta, float eta_const, const float* W0,
+                   const float* ln_gamma, const float* ln_beta, float ln_eps, float* Z, float* W_end,
+                   void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    ttt::LinearArgs a;
+    int path = TTT_PATH_NONE;
+    const int st = check_linear(kind, qkv_dtype, B, H, N, d, b, Q, K, V, eta, eta_const, W0, ln_gamma, ln_beta,
+                                ln_eps, Z, W_end, workspace, workspace_bytes, a, path);
+    if (st != TTT_OK) return st;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    const hipError_t err = path == TTT_PATH_SMALL_B ? ttt::launch_smallb_linear(a, stream)
+                                                    : ttt::launch_large_chunk_linear(a, ttt::LC_OUT_DUAL, stream);
+    return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+size_t ttt_linear_fwd_block_workspace_bytes(int apply, int kind, int qkv_dtype, int B, int H, int N, int d, int b)
+{
+    if (apply != TTT_APPLY_BEFORE_STEP && apply != TTT_APPLY_AFTER_STEP) return 0;
+    return ttt_linear_fwd_workspace_bytes(kind, qkv_dtype, B, H, N, d, b);
+}
+
+int ttt_linear_fwd_block(int apply, int kind, int qkv_dtype, int B, int H, int N, int d, int b, const void* Q,
+                         const void* K, const void* V, const float* eta, float eta_const, const float* W0,
+                         const float* ln_gamma, const float* ln_beta, float ln_eps, float* Z, float* W_end,
+                         void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    if (apply != TTT_APPLY_BEFORE_STEP && apply != TTT_APPLY_AFTER_STEP) return TTT_ERR_INVALID_ARGUMENT;
+    ttt::LinearArgs a;
+    int path = TTT_PATH_NONE;
+    const int st = check_linear(kind, qkv_dtype, B, H, N, d, b, Q, K, V, eta, eta_const, W0, ln_gamma, ln_beta,
+                                ln_eps, Z, W_end, workspace, workspace_bytes, a, path);
+    if (st != TTT_OK) return st;
+    if (path != TTT_PATH_LARGE_CHUNK) return TTT_ERR_UNSUPPORTED;
+    const hipError_t err = ttt::launch_large_chunk_linear(
+        a, apply == TTT_APPLY_BEFORE_STEP ? ttt::LC_OUT_BEFORE : ttt::LC_OUT_AFTER,
+        reinterpret_cast<hipStream_t>(hip_stream));
+    return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+int ttt_linear_decode(int kind, int qkv_dtype, int B, int H, int d, const void* q, const void* k, const void* v,
+                      const float* eta, float eta_const, float* W, const float* ln_gamma, const float* ln_beta,
+                      float ln_eps, float* z, void* hip_stream)
+{
+    if (kind != TTT_LINEAR_PLAIN && kind != TTT_LINEAR_LN) return TTT_ERR_INVALID_ARGUMENT;
+    if (qkv_dtype != TTT_DTYPE_F32 && qkv_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARGUMENT;
+    if (B < 1 || H < 1 || d < 1) return TTT_ERR_INVALID_ARGUMENT;
+    if (!q || !k || !v || !W || !z) return TTT_ERR_INVALID_ARGUMENT;
+    if (kind == TTT_LINEAR_LN && (!ln_gamma || !ln_beta || !(ln_eps >= 0.f))) return TTT_ERR_INVALID_ARGUMENT;
+    const size_t es = elem_size(qkv_dtype);
+    if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(W, 4) || !aligned(z, 4) ||
+        (eta && !aligned(eta, 4)))
+        return TTT_ERR_INVALID_ARGUMENT;
+    const size_t units = (size_t)B * (size_t)H;
+    if (units > (size_t)INT32_MAX) return TTT_ERR_INVALID_ARGUMENT;
+    const size_t vec_bytes = units * (size_t)d * es;
+    const size_t z_bytes = units * (size_t)d * 4;
+    const size_t w_bytes = units * (size_t)d * (size_t)d * 4;
+    const void* ins[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(z, z_bytes, ins[i], vec_bytes) || overlaps(W, w_bytes, ins[i], vec_bytes))
             return TTT_ERR_INVALID_ARGUMENT;
-        err = ttt::launch_large_chunk_linear(a, stream);
-    }
+    if (overlaps(z, z_bytes, W, w_bytes) || (eta && (overlaps(z, z_bytes, eta, units * 4) ||
+                                                     overlaps(W, w_bytes, eta, units * 4))))
+        return TTT_ERR_INVALID_ARGUMENT;
+    if (d != SMALLB_D) return TTT_ERR_UNSUPPORTED;
+
+    ttt::LinearArgs a{};
+    a.kind = kind;
+    a.dtype = qkv_dtype;
+    a.B = B;
+    a.H = H;
+    a.N = 1;
+    a.d = d;
+    a.b = 1;
+    a.Q = q;
+    a.K = k;
+    a.V = v;
+    a.eta = eta;
+    a.eta_const = eta_const;
+    a.W0 = W;
+    a.gamma = ln_gamma;
+    a.beta = ln_beta;
+    a.eps = ln_eps;
+    a.Z = z;
+    a.W_end = W;
+    const hipError_t err = ttt::launch_decode_linear(a, reinterpret_cast<hipStream_t>(hip_stream));
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

@@ -86,7 +86,8 @@ class Workload:
         return Workload(**d)
 
 
-# The five named workloads. Index i uses seed SEED_BASE + i.
+# The named workloads. Index i uses seed SEED_BASE + i. The first five are the
+# forward-pass workloads; the last is the single-token decode step.
 WORKLOADS = [
     Workload("linear_f32_B1H1N256_d64_b16", "plain", "f32", 1, 1, 256, 64, 16, "const", 0.1,
              qkv_std=1.0 / 8.0,
@@ -103,6 +104,9 @@ WORKLOADS = [
              "const", 0.01, l2_rows=True,
              description="large-chunk TTT-Linear, bf16 L2-normalised rows, B=1 H=16 N=32768 "
                          "d=128 b=2048, eta=0.01"),
+    Workload("decode_ln_bf16_B64H12_d64", "ln", "bf16", 64, 12, 1, 64, 1, "sigmoid",
+             description="single-token decode step of TTT-Linear+LN for B*H = 768 streams, bf16 "
+                         "q/k/v, d=64, per-token eta (inputs drawn as the B=8 H=12 workload's)"),
 ]
 
 BY_NAME = {w.name: w for w in WORKLOADS}
