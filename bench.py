@@ -12,7 +12,10 @@ steps rotate over four distinct device copies of the inputs and outputs.
 
 With the default workload the line also carries a "b2048" object: the same
 measurement for the large-chunk workload (plain TTT-Linear, bf16, B=1 H=16
-N=32768 d=128 b=2048), whose roofline is the bf16 MFMA peak.
+N=32768 d=128 b=2048), whose roofline is the bf16 MFMA peak; and "next_rows":
+the block-causal outputs of that workload (chunk outputs with the chunk's
+starting or ending weights) and the single-token decode step of B*H = 768
+TTT-Linear+LN streams (d=64), each against the HBM roofline.
 
 Prints ONE JSON line (stdout). Diagnostics go to stderr.
 """
@@ -35,6 +38,7 @@ from weights_ttt_layer_amd.profile_summary import COPY_BYTES, source_digest  # n
 
 DEFAULT_WORKLOAD = "linear_ln_bf16_B8H12N2048_d64_b16"
 LARGE_WORKLOAD = "linear_bf16_B1H16N32768_d128_b2048"
+DECODE_WORKLOAD = "decode_ln_bf16_B64H12_d64"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 ROTATE = 4
@@ -81,15 +85,16 @@ def algorithmic_flops(wl: wlm.Workload) -> int:
     return f * wl.B * wl.H
 
 
-def measured_traffic(wl: wlm.Workload, kind_key: str):
+def measured_traffic(wl: wlm.Workload, path_key: str, variant: str = "dual"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when there is none for this workload or the kernel source changed since."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    suffix = "" if variant == "dual" else f"_{variant}"
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}{suffix}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_digest") != source_digest(kind_key):
+    if rec.get("source_digest") != source_digest(path_key):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -98,11 +103,15 @@ def measured_traffic(wl: wlm.Workload, kind_key: str):
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int):
+def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int, variant: str = "dual"):
     """Average time of one launch (ms), from HIP events recorded on the stream the
-    launches go to, over `steps` back-to-back launches after `warmup` untimed ones."""
+    launches go to, over `steps` back-to-back launches after `warmup` untimed ones.
+    variant: "dual" (ttt_linear_fwd / ttt_mlp_fwd), "block_before", "block_after"
+    (ttt_linear_fwd_block) or "decode" (ttt_linear_decode, one token per stream,
+    the state updated in place)."""
     import torch
-    from weights_ttt_layer_amd import linear_fwd, linear_workspace_bytes, mlp_fwd
+    from weights_ttt_layer_amd import (linear_decode, linear_fwd, linear_fwd_block, linear_workspace_bytes,
+                                       mlp_fwd)
 
     dev = torch.device("cuda:0")
     base = wlm.to_device(inp, dev)
@@ -111,6 +120,13 @@ def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int):
     B, H, N, d = wl.B, wl.H, wl.N, wl.d
     outs = []
     for s in sets:
+        if variant == "decode":
+            for key in ("q", "k", "v"):
+                s[key] = s[key][:, :, 0].contiguous()
+            if s["eta"] is not None:
+                s["eta"] = s["eta"][:, :, 0].contiguous()
+            outs.append((torch.empty((B, H, d), dtype=torch.float32, device=dev),))
+            continue
         z = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
         if wl.kind == "mlp":
             outs.append((z, torch.empty_like(s["w1"]), torch.empty_like(s["w2"])))
@@ -122,10 +138,17 @@ def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int):
 
     def step(i):
         s, o = sets[i % ROTATE], outs[i % ROTATE]
-        if wl.kind == "mlp":
+        if variant == "decode":
+            linear_decode(s["q"], s["k"], s["v"], s["w0"], s["eta"], kind=wl.kind, eta_const=inp.eta_const,
+                          ln_gamma=s["gamma"], ln_beta=s["beta"], ln_eps=wl.ln_eps, z=o[0], stream=stream)
+        elif wl.kind == "mlp":
             mlp_fwd(s["q"], s["k"], s["v"], s["w1"], s["w2"], s["eta"], b=wl.b,
                     eta_const=inp.eta_const, ln_gamma=s["gamma"], ln_beta=s["beta"],
                     ln_eps=wl.ln_eps, z=o[0], w1_end=o[1], w2_end=o[2], stream=stream)
+        elif variant in ("block_before", "block_after"):
+            linear_fwd_block(s["q"], s["k"], s["v"], s["w0"], s["eta"], b=wl.b, apply=variant[6:],
+                             kind=wl.kind, eta_const=inp.eta_const, ln_gamma=s["gamma"], ln_beta=s["beta"],
+                             ln_eps=wl.ln_eps, z=o[0], w_end=o[1], workspace=o[2], stream=stream)
         else:
             linear_fwd(s["q"], s["k"], s["v"], s["w0"], s["eta"], b=wl.b, kind=wl.kind,
                        eta_const=inp.eta_const, ln_gamma=s["gamma"], ln_beta=s["beta"],
@@ -163,27 +186,46 @@ def copy_calibration(reps: int = 3):
     torch.cuda.empty_cache()
 
 
-def measure(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int):
-    """tokens/s and the roofline object of one workload."""
-    ms, finite = run_gpu(wl, inp, steps, warmup)
+def algorithmic_flops_variant(wl: wlm.Workload, variant: str) -> int:
+    """Block-causal outputs drop the causal term: 6 d^2 per token-head (K W, the
+    state step, Q W). A decode step is the same 6 d^2 for its single token."""
+    if variant in ("block_before", "block_after", "decode"):
+        return 6 * wl.d * wl.d * wl.B * wl.H * wl.N
+    return algorithmic_flops(wl)
+
+
+def measure(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int, variant: str = "dual"):
+    """tokens/s and the roofline object of one workload (and output variant)."""
+    ms, finite = run_gpu(wl, inp, steps, warmup, variant)
     if not finite:
-        log(f"[bench] WARNING: non-finite output in {wl.name}")
+        log(f"[bench] WARNING: non-finite output in {wl.name} {variant}")
     sec = ms / 1e3
     tokens = wl.B * wl.N
-    large = wl.b >= 256
-    kind_key = "large" if large else wl.kind
     nbytes = algorithmic_bytes(wl)
-    flops = algorithmic_flops(wl)
-    if large:
+    flops = algorithmic_flops_variant(wl, variant)
+    path_key = "large" if wl.b >= 256 else wl.kind
+    if variant != "dual":
+        path_key = variant
+    if wl.b >= 256 and variant == "dual":
         roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(wl, kind_key)
-    log(f"[bench] {wl.name}: {ms*1e3:.1f} us/step, {tokens/sec:.4g} tokens/s, "
+    roof["traffic"] = measured_traffic(wl, path_key, variant)
+    log(f"[bench] {wl.name} {variant}: {ms*1e3:.1f} us/step, {tokens/sec:.4g} tokens/s, "
         f"{nbytes/sec/1e9:.1f} GB/s algorithmic, {flops/sec/1e12:.2f} TFLOP/s algorithmic")
     return ms, tokens / sec, nbytes, flops, roof
+
+
+def side_measurement(name: str, steps: int, warmup: int, variant: str):
+    """One object of the JSON line for a workload other than the headline one."""
+    idx = [w.name for w in wlm.WORKLOADS].index(name)
+    wl = wlm.WORKLOADS[idx]
+    ms, val, nbytes, flops, roof = measure(wl, wlm.workload_inputs(idx), steps, warmup, variant)
+    return {"workload": wl.name, "variant": variant, "value": val, "unit": "tokens/s", "ms_per_step": ms,
+            "token_heads_per_s": val * wl.H, "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "roofline": roof}
 
 
 # ---------------------------------------------------------------------------
@@ -236,6 +278,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(wlm.BY_NAME))
+    ap.add_argument("--variant", default=None, choices=["dual", "block_before", "block_after", "decode"],
+                    help="outputs to measure (default: decode for the decode workload, else dual)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-b2048", action="store_true",
                     help="skip the large-chunk measurement that accompanies the default workload")
@@ -256,23 +300,25 @@ def main():
     inp = wlm.workload_inputs(idx)
     log(f"[bench] workload {wl.name}: generated inputs")
 
-    ms, value, nbytes, flops, roof = measure(wl, inp, args.steps, args.warmup)
+    variant = args.variant or ("decode" if wl.name == DECODE_WORKLOAD else "dual")
+    ms, value, nbytes, flops, roof = measure(wl, inp, args.steps, args.warmup, variant)
 
     b2048 = None
-    if wl.name == DEFAULT_WORKLOAD and not args.no_b2048:
-        li = [w.name for w in wlm.WORKLOADS].index(LARGE_WORKLOAD)
-        lwl = wlm.WORKLOADS[li]
-        lms, lval, lbytes, lflops, lroof = measure(lwl, wlm.workload_inputs(li), args.steps, args.warmup)
-        b2048 = {"workload": lwl.name, "value": lval, "unit": "tokens/s", "ms_per_step": lms,
-                 "token_heads_per_s": lval * lwl.H, "algorithmic_bytes": lbytes,
-                 "algorithmic_flops": lflops, "roofline": lroof}
+    next_rows = None
+    if wl.name == DEFAULT_WORKLOAD and variant == "dual" and not args.no_b2048:
+        b2048 = side_measurement(LARGE_WORKLOAD, args.steps, args.warmup, "dual")
+        next_rows = {
+            "block_before": side_measurement(LARGE_WORKLOAD, args.steps, args.warmup, "block_before"),
+            "block_after": side_measurement(LARGE_WORKLOAD, args.steps, args.warmup, "block_after"),
+            "decode": side_measurement(DECODE_WORKLOAD, args.steps, args.warmup, "decode"),
+        }
 
     if args.copy_calibration:
         copy_calibration()
         log(f"[bench] calibration copies of {COPY_BYTES} bytes done")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and variant == "dual":
         cpu = cpu_baseline(wl, inp, args.cpu_units)
         log(f"[bench] cpu baseline: {cpu['value']:.4g} tokens/s on {cpu['cores']} threads")
 
@@ -298,6 +344,8 @@ def main():
     }
     if b2048 is not None:
         rec["b2048"] = b2048
+    if next_rows is not None:
+        rec["next_rows"] = next_rows
     print(json.dumps(rec), flush=True)
 
 

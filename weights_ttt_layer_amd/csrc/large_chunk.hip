@@ -733,19 +733,22 @@ lc_chunk_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* _
 // ===========================================================================
 // lc_apply: block-causal outputs, Z_c = Q_c W_c (AFTER = false: the chunk's
 // starting weights) or Q_c W_{c+1} (AFTER = true: the weights after its step),
-// with no causal term inside the chunk. One workgroup per 128 tokens; wave w
-// computes output features [32w, 32w+32) with W^T rows (two bf16 terms) held as
-// B operands in registers and Q rows read straight from global memory.
+// with no causal term inside the chunk. One workgroup per (unit, chunk), so the
+// weights are read once per chunk; wave w computes output features
+// [32w, 32w+32) with W^T rows (two bf16 terms) held as B operands in
+// registers. Q streams through LDS in 64-token tiles by direct loads, one tile
+// ahead.
 // ===========================================================================
+__shared__ __attribute__((aligned(16))) uint16_t lc_qbuf[2][SB * LD];
+
 template <bool AFTER>
 __global__ void __launch_bounds__(LT)
 lc_apply_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ WT,
                 float* __restrict__ Zg)
 {
     const int C = (N + b - 1) / b;
-    const int nblk = N / TB;
-    const int unit = blockIdx.x / nblk, t0 = (blockIdx.x % nblk) * TB;
-    const int c = t0 / b;                                // chunk lengths are multiples of TB
+    const int unit = blockIdx.x / C, c = blockIdx.x % C;
+    const int c0 = c * b, nsb = min(b, N - c0) / SB;
     const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint16_t* wt = WT + ((size_t)unit * (C + 1) + c + (AFTER ? 1 : 0)) * 2 * LD * LD;
@@ -753,6 +756,7 @@ lc_apply_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* _
     const __amdgpu_buffer_rsrc_t zr =
         __builtin_amdgcn_make_buffer_rsrc(Zg + (size_t)unit * N * LD, (short)0, N * LD * 4, 0x00020000);
 
+    rows_dma<4>(reinterpret_cast<char*>(lc_qbuf[0]), Qu + (size_t)c0 * LD, w, lane);
     bf16x8 wb[LD / 16][2];
 #pragma unroll
     for (int ks = 0; ks < LD / 16; ++ks)
@@ -761,25 +765,32 @@ lc_apply_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* _
             wb[ks][term] = *reinterpret_cast<const bf16x8*>(wt + (size_t)term * LD * LD +
                                                             (size_t)(32 * w + l32) * LD + 16 * ks + 8 * h);
     const int voff = ((4 * h) * LD + 32 * w + l32) * 4;
-#pragma unroll
-    for (int tt = 0; tt < TB / 32; ++tt) {
-        bf16x8 qa[LD / 16];
-#pragma unroll
-        for (int ks = 0; ks < LD / 16; ++ks)
-            qa[ks] = *reinterpret_cast<const bf16x8*>(Qu + (size_t)(t0 + 32 * tt + l32) * LD + 16 * ks + 8 * h);
-        f32x16 acc = {};
+    for (int i = 0; i < nsb; ++i) {
+        __builtin_amdgcn_s_waitcnt(0x0070);              // this wave's loads of tile i (and stores) are done
+        __syncthreads();                                 // tile i landed everywhere; tile i-1 no longer read
+        if (i + 1 < nsb)
+            rows_dma<4>(reinterpret_cast<char*>(lc_qbuf[(i + 1) & 1]), Qu + (size_t)(c0 + (i + 1) * SB) * LD, w,
+                        lane);
+        const char* qt = reinterpret_cast<const char*>(lc_qbuf[i & 1]);
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int ks = 0; ks < LD / 16; ++ks) {
-            acc = mfma_32x32x16(qa[ks], wb[ks][1], acc);
-            acc = mfma_32x32x16(qa[ks], wb[ks][0], acc);
+            const bf16x8 q0 = ld_piece(qt, l32, 2 * ks + h);
+            const bf16x8 q1 = ld_piece(qt, 32 + l32, 2 * ks + h);
+            acc[0] = mfma_32x32x16(q0, wb[ks][1], acc[0]);
+            acc[1] = mfma_32x32x16(q1, wb[ks][1], acc[1]);
+            acc[0] = mfma_32x32x16(q0, wb[ks][0], acc[0]);
+            acc[1] = mfma_32x32x16(q1, wb[ks][0], acc[1]);
         }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int srow = __builtin_amdgcn_readfirstlane(t0 + 32 * tt + 8 * (e >> 2));
-            const float v = acc[e];
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), zr, voff + (e & 3) * LD * 4,
-                                                  srow * LD * 4, 0);
-        }
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int srow = __builtin_amdgcn_readfirstlane(c0 + i * SB + 32 * m + 8 * (e >> 2));
+                const float v = acc[m][e];
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), zr, voff + (e & 3) * LD * 4,
+                                                      srow * LD * 4, 0);
+            }
     }
 }
 
@@ -816,11 +827,9 @@ hipError_t launch_large_chunk_linear(const LinearArgs& a, int outputs, hipStream
     hipLaunchKernelGGL(lc_scan_kernel, dim3(units * 4), dim3(LT), 0, stream, a.N, a.b, a.W0, M, Bm, WT, a.W_end);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (outputs == LC_OUT_BEFORE)
-        hipLaunchKernelGGL((lc_apply_kernel<false>), dim3(units * (a.N / TB)), dim3(LT), 0, stream, a.N, a.b, Q, WT,
-                           a.Z);
+        hipLaunchKernelGGL((lc_apply_kernel<false>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, Q, WT, a.Z);
     else if (outputs == LC_OUT_AFTER)
-        hipLaunchKernelGGL((lc_apply_kernel<true>), dim3(units * (a.N / TB)), dim3(LT), 0, stream, a.N, a.b, Q, WT,
-                           a.Z);
+        hipLaunchKernelGGL((lc_apply_kernel<true>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, Q, WT, a.Z);
     else if (per_token)
         hipLaunchKernelGGL((lc_chunk_kernel<true>), dim3(units * C), dim3(LT), 0, stream, a.N, a.b, Q, K, V, a.eta,
                            a.eta_const, WT, a.Z);

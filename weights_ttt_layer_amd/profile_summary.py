@@ -41,17 +41,23 @@ KERNEL_SOURCES = {
     "ln": ["smallb_linear.hip", "smallb_common.h", "device_common.h"],
     "mlp": ["smallb_mlp.hip", "smallb_common.h", "device_common.h"],
     "large": ["large_chunk.hip", "device_common.h"],
+    "block_before": ["large_chunk.hip", "device_common.h"],
+    "block_after": ["large_chunk.hip", "device_common.h"],
+    "decode": ["decode.hip", "device_common.h"],
 }
 
 OUR_KERNELS = ("smallb_linear_kernel", "smallb_mlp_kernel", "lc_gram_kernel", "lc_scan_kernel",
-               "lc_grad_kernel", "lc_out_kernel")
+               "lc_chunk_kernel", "lc_apply_kernel", "decode_kernel")
 
 # kernel-name prefixes launched by one call of each path
 PATH_KERNELS = {
     "plain": ("smallb_linear_kernel<0",),
     "ln": ("smallb_linear_kernel<1",),
     "mlp": ("smallb_mlp_kernel",),
-    "large": ("lc_gram_kernel", "lc_scan_kernel", "lc_grad_kernel", "lc_out_kernel"),
+    "large": ("lc_gram_kernel", "lc_scan_kernel", "lc_chunk_kernel"),
+    "block_before": ("lc_gram_kernel", "lc_scan_kernel", "lc_apply_kernel<false>"),
+    "block_after": ("lc_gram_kernel", "lc_scan_kernel", "lc_apply_kernel<true>"),
+    "decode": ("decode_kernel",),
 }
 
 
@@ -129,6 +135,9 @@ def traffic(args):
 
     wl = wlm.BY_NAME[args.workload]
     path_key = "large" if wl.b >= 256 else wl.kind
+    if args.variant != "dual":
+        path_key = args.variant
+    suffix = "" if args.variant == "dual" else f"_{args.variant}"
     fetch = load_counter(args.fetch_dir, "FETCH_SIZE")
     write = load_counter(args.write_dir, "WRITE_SIZE")
     copy_kib = COPY_BYTES / 1024.0
@@ -155,6 +164,7 @@ def traffic(args):
     alg = algorithmic_bytes(wl)
     rec = {
         "workload": wl.name,
+        "variant": args.variant,
         "kernels": kernels,
         "hbm_bytes_per_launch": total,
         "algorithmic_bytes_per_launch": alg,
@@ -166,9 +176,9 @@ def traffic(args):
         "commands": args.cmd,
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"traffic_{wl.name}{suffix}.json"), "w") as f:
         json.dump(rec, f, indent=1)
-    lines = [f"# HBM traffic per launch: {wl.name}", "", "Commands (from the repository root):", ""]
+    lines = [f"# HBM traffic per launch: {wl.name} ({args.variant})", "", "Commands (from the repository root):", ""]
     lines += [f"    {c}" for c in args.cmd]
     lines += ["", f"Calibration: a plain device copy of {COPY_BYTES} bytes counted "
               f"FETCH_SIZE {sum(cf)/len(cf):.0f} KiB and WRITE_SIZE {sum(cw)/len(cw):.0f} KiB "
@@ -179,7 +189,7 @@ def traffic(args):
                      f"{k['hbm_bytes_per_dispatch']/1e6:.2f} |")
     lines += ["", f"Per launch: {total/1e6:.2f} MB measured vs {alg/1e6:.2f} MB algorithmic "
               f"(ratio {total/alg:.3f}). Source digest {rec['source_digest']}."]
-    with open(os.path.join(ROOT, "profiles", f"traffic_{wl.name}.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"traffic_{wl.name}{suffix}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -197,6 +207,7 @@ def main(argv=None):
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
     t.add_argument("workload")
+    t.add_argument("--variant", default="dual", choices=sorted(KERNEL_SOURCES.keys() - {"plain", "ln", "mlp", "large"}) + ["dual"])
     t.add_argument("--cmd", action="append", default=[])
     args = ap.parse_args(argv)
     stats(args) if args.what == "stats" else traffic(args)
