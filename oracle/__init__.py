@@ -185,3 +185,57 @@ def gelu(a: float) -> float:
 
 def gelu_prime(a: float) -> float:
     return _load().ttt_oracle_gelu_prime(float(a))
+
+
+def layer_norm(x, gamma, beta, eps):
+    """LayerNorm over the last axis: biased variance, eps inside the square root."""
+    x = _f64(x)
+    mu = x.mean(axis=-1, keepdims=True)
+    xc = x - mu
+    var = (xc * xc).mean(axis=-1, keepdims=True)
+    return xc / np.sqrt(var + eps) * _f64(gamma) + _f64(beta)
+
+
+def layer(kind, x, Wq, Wk, Wv, Wo, eta, W0, b, H, gamma=None, beta=None, gamma_o=None,
+          beta_o=None, eps=1e-6, mode=DUAL, nthreads=None):
+    """The whole TTT layer around the inner model (TTT-Linear, kind PLAIN or LN).
+
+    Page "Test-Time Training: Linear Complexity Beyond Attention":
+      * section "1. The Self-Supervised Inner-Loop Task": each token x_t (a model
+        vector of width D) is projected to query, key and value, q_t = W_Q x_t,
+        k_t = W_K x_t, v_t = W_V x_t. The projections are [H*d, D] matrices
+        (output index first); the H*d outputs are H heads of width d, head h
+        taking outputs h*d .. h*d + d - 1.
+      * the same page's layer code normalises each key to unit L2 length
+        before the inner loop (a zero key stays zero).
+      * the inner model runs per (sequence, head) exactly as ``linear``.
+      * section "3. Forward Evaluation and Output Projection": the output is
+        y_t = W_O (LayerNorm(z_t) + q_t), the LayerNorm taken per head over the
+        head's d entries with a per-head affine (gamma_o, beta_o of shape
+        [H, d]); W_O is [D, H*d].
+
+    ``x`` is [B, N, D]. Returns (y [B,N,D], W_end [B,H,d,d], parts) in fp64 where
+    ``parts`` holds the intermediate Q, K (normalised), V and Z, each [B,H,N,d].
+    """
+    x = _f64(x)
+    Bn, N, D = x.shape
+    Wq, Wk, Wv, Wo = _f64(Wq), _f64(Wk), _f64(Wv), _f64(Wo)
+    HD = Wq.shape[0]
+    assert HD % H == 0 and Wq.shape == (HD, D) and Wk.shape == (HD, D) and Wv.shape == (HD, D)
+    assert Wo.shape == (D, HD)
+    d = HD // H
+
+    def heads(P):                 # [B, N, H*d] -> [B, H, N, d]
+        return np.ascontiguousarray(P.reshape(Bn, N, H, d).transpose(0, 2, 1, 3))
+
+    Q = heads(x @ Wq.T)
+    K = heads(x @ Wk.T)
+    V = heads(x @ Wv.T)
+    nrm = np.sqrt(np.sum(K * K, axis=-1, keepdims=True))
+    K = K / np.where(nrm > 0, nrm, 1.0)
+    Z, We = linear(mode, kind, Q, K, V, eta, W0, b, gamma, beta, eps, nthreads)
+    go = _f64(gamma_o).reshape(H, 1, d)
+    bo = _f64(beta_o).reshape(H, 1, d)
+    A = layer_norm(Z, go, bo, eps) + Q                   # [B, H, N, d]
+    y = A.transpose(0, 2, 1, 3).reshape(Bn, N, HD) @ Wo.T
+    return y, We, dict(Q=Q, K=K, V=V, Z=Z)
