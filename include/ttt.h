@@ -203,6 +203,56 @@ int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b,
                 const float* ln_gamma, const float* ln_beta, float ln_eps,
                 float* Z, float* W1_end, float* W2_end, void* hip_stream);
 
+/*
+ * ttt_layer_fwd -- the whole TTT layer around TTT-Linear: projections, key
+ * normalisation, the inner model, and the output stage. Page "Test-Time
+ * Training: Linear Complexity Beyond Attention": section "1. The
+ * Self-Supervised Inner-Loop Task" (q, k, v are linear projections of the
+ * token), the page's layer code (keys scaled to unit L2 length before the
+ * inner loop), section "3. Forward Evaluation and Output Projection"
+ * (y = W_O (LayerNorm(z) + q)). Per token x_t (width D) and head h:
+ *     q = W_Q x,  k = W_K x / ||W_K x||,  v = W_V x   (head h: outputs h*d .. h*d+d-1;
+ *                                                     a zero key stays zero)
+ *     z = the inner model of ttt_linear_fwd (kind, chunks of b, eta, W0)
+ *     y = W_O (LayerNorm(z) * out_gamma + out_beta + q)   (LayerNorm per head)
+ *
+ *   kind            TTT_LINEAR_PLAIN or TTT_LINEAR_LN (the inner model)
+ *   B, N, D         sequences, tokens per sequence, model width
+ *   H, d            heads and head width (H*d projection outputs)
+ *   b               chunk length of the inner model
+ *   x               device [B, N, D] bf16 tokens
+ *   Wq, Wk, Wv      device [H*d, D] bf16 (output-major: row o holds the
+ *                   weights of projection output o, as q = W_Q x reads)
+ *   Wo              device [D, H*d] bf16 (row n: weights of model output n)
+ *   eta, eta_const  step sizes as for ttt_linear_fwd ([B, H, N] or NULL)
+ *   W0, W_end       device [B, H, d, d] fp32 inner state in / out (may be equal)
+ *   ln_gamma, ln_beta   [H, d] fp32 inner LayerNorm (kind LN only, else unused)
+ *   out_gamma, out_beta [H, d] fp32 output LayerNorm affine, 16-byte aligned
+ *   ln_eps          epsilon of both LayerNorms (biased variance, inside the root)
+ *   y               device [B, N, D] fp32 output
+ *   workspace       device, 256-byte aligned, at least
+ *                   ttt_layer_fwd_workspace_bytes(B, N, H, d) bytes = 5 S,
+ *                   S = B*H*N*d*4 rounded up to a multiple of 256. On return it
+ *                   holds the fp32 [B, H, N, d] arrays Q, K (normalised), V and Z
+ *                   at offsets 0, S, 2S, 3S; the last S bytes are scratch.
+ * x and the four weights must be 16-byte aligned. y, W_end and the workspace
+ * must not overlap any input or each other (W_end may equal W0). Products run
+ * on bf16 matrix cores with fp32 accumulation; the LayerNorm output enters W_O's
+ * product as two bf16 terms (16 significant bits). Asynchronous on hip_stream;
+ * validation on the host before any HIP call.
+ * Supported: d = 64, 1 <= b <= 16, D a multiple of 64 (else TTT_ERR_UNSUPPORTED).
+ */
+int ttt_layer_fwd(int kind, int B, int N, int D, int H, int d, int b,
+                  const void* x, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                  const float* eta, float eta_const, const float* W0,
+                  const float* ln_gamma, const float* ln_beta,
+                  const float* out_gamma, const float* out_beta, float ln_eps,
+                  float* y, float* W_end, void* workspace, size_t workspace_bytes,
+                  void* hip_stream);
+
+/* Workspace bytes of ttt_layer_fwd (0 for invalid sizes). */
+size_t ttt_layer_fwd_workspace_bytes(int B, int N, int H, int d);
+
 /* Static, NUL-terminated description of a ttt_status value. */
 const char* ttt_status_string(int status);
 

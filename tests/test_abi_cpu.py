@@ -167,3 +167,40 @@ def test_decode_rejections(lib):
     assert decode_call(lib, W=ctypes.c_void_p(A + (1 << 30) + 8)) == E   # W overlaps k
     assert decode_call(lib, q=ctypes.c_void_p(A + 1)) == E       # misaligned bf16
     assert decode_call(lib, d=128) == U
+
+
+def layer_call(lib, kind=1, B=8, N=2048, D=768, H=12, d=64, b=16, x=0, wq=1, wk=2, wv=3, wo=4, eta=None,
+               W0=5, gam=6, bet=7, og=8, ob=9, eps=1e-6, y=10, We=11, ws=12, ws_bytes=0):
+    """Every call here fails validation (the default workspace size is 0)."""
+    p = lambda i: None if i is None else (i if isinstance(i, ctypes.c_void_p) else addr(i))
+    return lib.ttt_layer_fwd(kind, B, N, D, H, d, b, p(x), p(wq), p(wk), p(wv), p(wo), p(eta), 0.1, p(W0),
+                             p(gam), p(bet), p(og), p(ob), eps, p(y), p(We), p(ws), ws_bytes, None)
+
+
+def test_layer_rejections(lib):
+    E, U = binding.TTT_ERR_INVALID_ARGUMENT, binding.TTT_ERR_UNSUPPORTED
+    need = lib.ttt_layer_fwd_workspace_bytes(8, 2048, 12, 64)
+    assert need == 5 * 8 * 12 * 2048 * 64 * 4
+    assert lib.ttt_layer_fwd_workspace_bytes(8, 2048, 12, 128) == 0
+    assert lib.ttt_layer_fwd_workspace_bytes(0, 2048, 12, 64) == 0
+    assert layer_call(lib, kind=2) == E
+    assert layer_call(lib, B=0) == E
+    assert layer_call(lib, N=0) == E
+    assert layer_call(lib, x=None) == E
+    assert layer_call(lib, wo=None) == E
+    assert layer_call(lib, og=None) == E
+    assert layer_call(lib, ws=None) == E
+    assert layer_call(lib, eps=-1.0) == E
+    assert layer_call(lib, x=ctypes.c_void_p(A + 8)) == E            # x not 16-byte aligned
+    assert layer_call(lib, ob=ctypes.c_void_p(A + 9 * (1 << 30) + 4)) == E     # out_beta not 16-byte aligned
+    assert layer_call(lib, ws=ctypes.c_void_p(A + 12 * (1 << 30) + 16)) == E   # workspace not 256-byte aligned
+    assert layer_call(lib, d=128) == U
+    assert layer_call(lib, b=17) == U
+    assert layer_call(lib, D=96) == U
+    assert layer_call(lib) == binding.TTT_ERR_WORKSPACE_TOO_SMALL
+    big = need
+    assert layer_call(lib, y=ctypes.c_void_p(A + 64), ws_bytes=big) == E               # y overlaps x
+    assert layer_call(lib, ws=addr(4), ws_bytes=big) == E             # workspace overlaps W_O
+    assert layer_call(lib, We=ctypes.c_void_p(A + 5 * (1 << 30) + 256), ws_bytes=big) == E       # W_end partly over W0
+    assert layer_call(lib, y=ctypes.c_void_p(A + 12 * (1 << 30) + 1024), ws_bytes=big) == E      # y inside workspace
+    assert layer_call(lib, kind=1, gam=None, ws_bytes=big) == E                        # LN needs the affine

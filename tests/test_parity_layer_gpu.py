@@ -1,0 +1,111 @@
+"""GPU parity of the whole layer (ttt_layer_fwd: projections, key normalisation,
+inner TTT-Linear, output LayerNorm + residual + W_O) with the fp64 oracle, on
+identical seeded inputs (bf16 x and projection weights, fp32 state).
+
+Tolerances (max|gpu - ref| / max|ref| per tensor):
+  * Q, K, V: 1e-5 -- exact bf16 products summed in fp32.
+  * Z, W_end: 1e-5 -- the fp32-stream inner path's bar.
+  * y: 2e-5 -- LayerNorm(z) + q enters W_O's product as two bf16 terms, a
+    relative representation error of at most 2^-16 per entry; summed over
+    H*d products with independent signs it stays near 1e-5 of max|y|.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from weights_ttt_layer_amd import workloads as wlm
+
+from gpu_helpers import rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_PARTS = 1e-5
+TOL_Y = 2e-5
+
+
+def oracle_layer(inp: wlm.LayerInputs, seqs=None):
+    wl = inp.wl
+    sl = slice(None) if seqs is None else seqs
+    kind = oracle.LN if wl.kind == "ln" else oracle.PLAIN
+    return oracle.layer(kind, inp.f64("x")[sl], inp.f64("wq"), inp.f64("wk"), inp.f64("wv"),
+                        inp.f64("wo"), inp.f64("eta")[sl], inp.f64("w0")[sl], wl.b, wl.H,
+                        inp.f64("gamma"), inp.f64("beta"), inp.f64("gamma_o"), inp.f64("beta_o"),
+                        wl.ln_eps)
+
+
+def gpu_layer(inp: wlm.LayerInputs, in_place=False, eta_none=False):
+    import torch
+    from weights_ttt_layer_amd import layer_fwd, layer_parts
+    wl = inp.wl
+    t = wlm.layer_to_device(inp)
+    y, we, ws = layer_fwd(t["x"], t["wq"], t["wk"], t["wv"], t["wo"], t["w0"], t["gamma_o"],
+                          t["beta_o"], None if eta_none else t["eta"], H=wl.H, b=wl.b, kind=wl.kind,
+                          eta_const=0.0, ln_gamma=t["gamma"], ln_beta=t["beta"], ln_eps=wl.ln_eps,
+                          w_end=t["w0"] if in_place else None)
+    torch.cuda.synchronize()
+    parts = {k: v.cpu().numpy() for k, v in layer_parts(ws, wl.B, wl.N, wl.H, wl.d).items()}
+    return y.cpu().numpy(), we.cpu().numpy(), parts
+
+
+def check(inp, y, we, parts, ref, seqs=slice(None)):
+    yr, wr, pr = ref
+    errs = {name: rel_err(parts[name][seqs], pr[name]) for name in "QKVZ"}
+    errs["W_end"] = rel_err(we[seqs], wr)
+    errs["y"] = rel_err(y[seqs], yr)
+    say("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= (TOL_Y if k == "y" else TOL_PARTS), k
+
+
+def case(kind, B, N, D, H, b, seed=3):
+    wl = wlm.LayerWorkload(f"layer_{kind}_B{B}N{N}_D{D}_H{H}_b{b}", kind, B, N, D, H, 64, b)
+    return wlm.generate_layer(wl, seed)
+
+
+@pytest.mark.parametrize("kind,B,N,D,H,b", [
+    ("ln", 2, 200, 128, 2, 16),      # ragged token tile (200 = 128 + 72) and chunk tail (200 % 16 = 8)
+    ("plain", 1, 64, 192, 3, 16),    # odd H: the last projection tile is half full; D not a multiple of 256
+    ("ln", 3, 37, 64, 1, 5),         # one head, D = 64, short ragged sequences
+    ("plain", 1, 300, 512, 8, 1),    # b = 1 (online steps)
+    ("ln", 2, 256, 768, 12, 16),     # the model width of the named workload
+])
+def test_layer_shapes(kind, B, N, D, H, b):
+    inp = case(kind, B, N, D, H, b)
+    say(f"case {inp.wl.name}")
+    y, we, parts = gpu_layer(inp)
+    check(inp, y, we, parts, oracle_layer(inp))
+
+
+def test_layer_in_place_state_and_constant_eta():
+    """W_end == W0 updates the state in place; eta = NULL uses eta_const (0 here:
+    the state must come back unchanged and z = f(q; W0))."""
+    inp = case("ln", 1, 96, 128, 2, 16, seed=4)
+    y, we, parts = gpu_layer(inp, in_place=True, eta_none=True)
+    ref = oracle.layer(oracle.LN, inp.f64("x"), inp.f64("wq"), inp.f64("wk"), inp.f64("wv"),
+                       inp.f64("wo"), 0.0, inp.f64("w0"), 16, 2, inp.f64("gamma"), inp.f64("beta"),
+                       inp.f64("gamma_o"), inp.f64("beta_o"), 1e-6)
+    check(inp, y, we, parts, ref)
+    assert rel_err(we, inp.w0.astype(np.float64)) <= 1e-7
+
+
+def test_layer_zero_input_token():
+    """A token whose x is zero has a zero key (no NaN from the normalisation)."""
+    inp = case("plain", 1, 48, 128, 2, 16, seed=6)
+    inp.x[0, 7, :] = 0
+    y, we, parts = gpu_layer(inp)
+    assert np.all(np.isfinite(y))
+    assert np.all(parts["K"][0, :, 7, :] == 0)
+    check(inp, y, we, parts, oracle_layer(inp))
+
+
+def test_layer_named_workload_sampled():
+    """The named workload at full size, in the launch configuration the
+    benchmark times; two of its eight sequences are checked in full against
+    the oracle (sequences are independent)."""
+    inp = wlm.layer_workload_inputs(0)
+    say(f"case {inp.wl.name}")
+    y, we, parts = gpu_layer(inp)
+    for s in (0, inp.wl.B - 1):
+        seqs = slice(s, s + 1)
+        say(f"  sequence {s}")
+        check(inp, y, we, parts, oracle_layer(inp, seqs), seqs)

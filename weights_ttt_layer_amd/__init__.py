@@ -6,10 +6,15 @@
 ``mlp_fwd`` runs TTT-MLP, both in the mini-batch dual form, on device tensors.
 ``linear_fwd_block`` gives block-causal large-chunk outputs and
 ``linear_decode`` takes one online step per (sequence, head) stream.
+``layer_fwd`` runs the whole layer: projections, key normalisation, the inner
+TTT-Linear model, output LayerNorm + residual and the output projection.
 Build the library first with ``python -m weights_ttt_layer_amd.build``.
 """
 from .binding import (  # noqa: F401
     TTTError,
+    layer_fwd,
+    layer_parts,
+    layer_workspace_bytes,
     linear_decode,
     linear_fwd,
     linear_fwd_block,
@@ -20,5 +25,5 @@ from .binding import (  # noqa: F401
     status_string,
 )
 
-__all__ = ["TTTError", "linear_decode", "linear_fwd", "linear_fwd_block", "linear_path",
+__all__ = ["TTTError", "layer_fwd", "layer_parts", "layer_workspace_bytes", "linear_decode", "linear_fwd", "linear_fwd_block", "linear_path",
            "linear_workspace_bytes", "load_library", "mlp_fwd", "status_string"]

@@ -58,6 +58,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_linear_fwd_block_workspace_bytes.restype = sz
     lib.ttt_linear_decode.argtypes = [i, i, i, i, i, vp, vp, vp, fp, f, fp, fp, fp, f, fp, vp]
     lib.ttt_linear_decode.restype = i
+    lib.ttt_layer_fwd.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, vp, fp, f, fp, fp, fp, fp, fp, f,
+                                  fp, fp, vp, sz, vp]
+    lib.ttt_layer_fwd.restype = i
+    lib.ttt_layer_fwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.ttt_layer_fwd_workspace_bytes.restype = sz
     lib.ttt_status_string.argtypes = [i]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_abi_version.argtypes = []
@@ -253,3 +258,74 @@ def mlp_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tensor,
     if st != TTT_OK:
         raise TTTError(st, "ttt_mlp_fwd")
     return z, w1_end, w2_end
+
+
+def layer_workspace_bytes(B: int, N: int, H: int, d: int) -> int:
+    return int(load_library().ttt_layer_fwd_workspace_bytes(B, N, H, d))
+
+
+def layer_fwd(x: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor,
+              wo: torch.Tensor, w0: torch.Tensor, out_gamma: torch.Tensor, out_beta: torch.Tensor,
+              eta: Optional[torch.Tensor] = None, *, H: int, b: int, kind: str = "plain",
+              eta_const: float = 0.0, ln_gamma: Optional[torch.Tensor] = None,
+              ln_beta: Optional[torch.Tensor] = None, ln_eps: float = 1e-6,
+              y: Optional[torch.Tensor] = None, w_end: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, stream=None
+              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """The whole layer through ``ttt_layer_fwd``. Returns (y, W_end, workspace).
+
+    x: [B,N,D] bf16; wq, wk, wv: [H*d, D] bf16; wo: [D, H*d] bf16; w0: [B,H,d,d]
+    fp32; out_gamma/out_beta (and ln_gamma/ln_beta for kind "ln"): [H,d] fp32;
+    eta: [B,H,N] fp32 or None. The returned workspace holds the fp32 Q, K, V, Z
+    arrays ([B,H,N,d] each, see ``layer_parts``)."""
+    lib = load_library()
+    if kind not in KINDS:
+        raise ValueError(f"kind must be one of {sorted(KINDS)}")
+    B, N, D = x.shape
+    HD = wq.shape[0]
+    if HD % H != 0:
+        raise ValueError(f"projection width {HD} is not a multiple of H={H}")
+    d = HD // H
+    _check(x, "x", (B, N, D), torch.bfloat16)
+    for t, nm in ((wq, "wq"), (wk, "wk"), (wv, "wv")):
+        _check(t, nm, (HD, D), torch.bfloat16)
+    _check(wo, "wo", (D, HD), torch.bfloat16)
+    _check(w0, "w0", (B, H, d, d), torch.float32)
+    _check(out_gamma, "out_gamma", (H, d), torch.float32)
+    _check(out_beta, "out_beta", (H, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H, N), torch.float32)
+    if kind == "ln":
+        if ln_gamma is None or ln_beta is None:
+            raise ValueError("kind 'ln' needs ln_gamma and ln_beta")
+        _check(ln_gamma, "ln_gamma", (H, d), torch.float32)
+        _check(ln_beta, "ln_beta", (H, d), torch.float32)
+    if y is None:
+        y = torch.empty((B, N, D), dtype=torch.float32, device=x.device)
+    else:
+        _check(y, "y", (B, N, D), torch.float32)
+    if w_end is None:
+        w_end = torch.empty_like(w0)
+    else:
+        _check(w_end, "w_end", (B, H, d, d), torch.float32)
+    need = int(lib.ttt_layer_fwd_workspace_bytes(B, N, H, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.ttt_layer_fwd(KINDS[kind], B, N, D, H, d, int(b), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv),
+                           _ptr(wo), _ptr(eta), float(eta_const), _ptr(w0), _ptr(ln_gamma),
+                           _ptr(ln_beta), _ptr(out_gamma), _ptr(out_beta), float(ln_eps), _ptr(y),
+                           _ptr(w_end), _ptr(workspace), ws_bytes, _stream_ptr(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_layer_fwd")
+    return y, w_end, workspace
+
+
+def layer_parts(workspace: torch.Tensor, B: int, N: int, H: int, d: int) -> dict:
+    """Views of the Q, K, V, Z arrays a ``layer_fwd`` call left in its workspace."""
+    region = int(load_library().ttt_layer_fwd_workspace_bytes(B, N, H, d)) // 5
+    n = B * H * N * d
+    out = {}
+    for i, name in enumerate("QKVZ"):
+        out[name] = workspace[i * region:i * region + 4 * n].view(torch.float32).view(B, H, N, d)
+    return out

@@ -60,4 +60,25 @@ hipError_t launch_decode_linear(const LinearArgs& a, hipStream_t stream);
 // TTT-MLP small-b path: d = 64, hidden = 256, 1 <= b <= 16.
 hipError_t launch_smallb_mlp(const MlpArgs& a, hipStream_t stream);
 
+// Whole-layer stages around the inner model (head width 64, D % 64 == 0).
+struct LayerArgs {
+    int B, N, D, H;
+    const void* x;     // [B, N, D] bf16
+    const void* Wq;    // [H*64, D] bf16
+    const void* Wk;
+    const void* Wv;
+    const void* Wo;    // [D, H*64] bf16
+    const float* out_gamma;
+    const float* out_beta;
+    float eps;
+    float* y;          // [B, N, D] fp32
+};
+// Bytes of one fp32 [B, H, N, 64] workspace array, rounded up to 256.
+size_t layer_workspace_region_bytes(int B, int N, int H);
+// Q, K (unit rows), V as fp32 [B, H, N, 64].
+hipError_t launch_layer_qkv(const LayerArgs& a, float* Q, float* K, float* V, hipStream_t stream);
+// y = W_O (LayerNorm(Z) * out_gamma + out_beta + Q), per head; `aext` is one
+// workspace region that receives the two-term operand.
+hipError_t launch_layer_out(const LayerArgs& a, const float* Z, const float* Q, void* aext, hipStream_t stream);
+
 }  // namespace ttt

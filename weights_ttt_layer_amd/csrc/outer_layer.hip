@@ -1,0 +1,346 @@
+// outer_layer.hip -- the projections and the output stage that turn the inner
+// TTT-Linear model into a whole layer (page "Test-Time Training: Linear
+// Complexity Beyond Attention", sections "1. The Self-Supervised Inner-Loop
+// Task" and "3. Forward Evaluation and Output Projection"):
+//
+//     q_t = W_Q x_t,  k_t = W_K x_t / ||W_K x_t||,  v_t = W_V x_t   (per head)
+//     z_t = inner model (the chunked dual form, ttt_linear_fwd's small-b path)
+//     y_t = W_O (LayerNorm(z_t) + q_t)        (LayerNorm per head, own affine)
+//
+// Three kernels:
+//  * layer_gemm_kernel<.., EPI_QKV>: [Q | K | V] = x [W_Q; W_K; W_V]^T on bf16
+//    MFMA with fp32 accumulation. Each wave owns 64 tokens x 64 outputs = one
+//    head of one projection, so the key normalisation is a reduction inside
+//    the wave; Q, K, V leave in fp32, head-major [B, H, N, 64], the layout the
+//    inner kernel reads.
+//  * layer_outprep_kernel: A = LayerNorm(z) * gamma_o + beta_o + q per (token,
+//    head) row, written token-major as two bf16 terms (16 significant bits).
+//  * layer_gemm_kernel<.., EPI_ROWS>: y = [A_hi | A_lo] [W_O | W_O]^T, i.e. the
+//    two terms reduced against the same W_O rows; y leaves in fp32.
+// Both GEMMs take the weight output-major ([out][in], in-features contiguous),
+// so both MFMA operands are 16-byte rows of LDS tiles. The logical tile order
+// keeps all output tiles of a token block on one XCD so the re-read token rows
+// hit that XCD's L2.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace ttt {
+namespace {
+
+constexpr int HDIM = 64;     // head width
+constexpr int GT = 256;      // threads per workgroup (four waves)
+
+// Row of a 32x32 C-layout tile held by lane half h = lane / 32 at slot i.
+__device__ __forceinline__ int crow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+// Direct global -> LDS load of 16 bytes per lane to lds + 16 * lane (see
+// large_chunk.hip for why this is assembly and why callers wait explicitly).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// Logical tile of workgroup x. Workgroups are dealt to the eight XCDs round
+// robin; this gives XCD c a contiguous range of logical tiles.
+__device__ __forceinline__ int xcd_tile(int x, int total)
+{
+    const int per = total >> 3, rem = total & 7, c = x & 7, k = x >> 3;
+    return c < rem ? c * (per + 1) + k : rem * (per + 1) + (c - rem) * per + k;
+}
+
+// ===========================================================================
+// The GEMM core shared by both sides:
+//     C[m][n] = sum_{k < K} A[m][k] * Bw[n][k mod KW]
+// with A (bf16, row stride lda) indexed by token m = (sequence bi, token t) and
+// Bw (bf16, output-major, row stride ldb). The wrap KW lets the output stage
+// feed the two bf16 terms of its operand as one K = 2 * H*64 reduction
+// against the same W_O rows. A workgroup computes TM tokens of one sequence x
+// TN outputs with (TM/64) * (TN/64) waves, each owning a 64 x 64 block.
+// Operand tiles stream global -> LDS with direct loads, 32-deep stages, NS
+// stages resident (NS - 1 in flight while one is read).
+// ===========================================================================
+constexpr int GK = 32;       // reduction depth of one LDS stage
+
+// Tiles hold rows of 32 bf16 (64 bytes = 4 pieces); piece p of row r sits at
+// slot p ^ ((r >> 2) & 3), so 16 consecutive rows read at one piece start on
+// 16 different 4-bank groups.
+__device__ __forceinline__ int psw(int r, int p) { return r * 64 + ((p ^ ((r >> 2) & 3)) << 4); }
+
+constexpr int vmcnt_imm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+enum { EPI_QKV = 0, EPI_ROWS = 1 };
+
+struct GemmArgs {
+    int N, H;                    // tokens per sequence, heads
+    int K, KW;                   // reduction length, wrap of the weight's k index
+    int n_out;                   // valid outputs (rows of the stacked weight)
+    int lda, ldb;
+    int tiles_t, tiles_n, total;
+    const uint16_t* A;
+    const uint16_t* W0;          // weight rows [0, rows_per_w), then W1, W2 (EPI_QKV)
+    const uint16_t* W1;
+    const uint16_t* W2;
+    int rows_per_w;
+    float* out0;                 // EPI_QKV: Q, K, V; EPI_ROWS: y [tokens][n_out]
+    float* out1;
+    float* out2;
+};
+
+template <int TM, int TN, int NS, int EPI>
+__global__ void __launch_bounds__(TM * TN / 64)
+layer_gemm_kernel(GemmArgs g)
+{
+    constexpr int WR = TM / 64, WC = TN / 64, NW = WR * WC;
+    constexpr int AI = TM / 16, BI = TN / 16;            // DMA instructions per stage (1 KB each)
+    constexpr int PER = (AI + BI) / NW;                  // ... per wave
+    static_assert((AI + BI) % NW == 0, "DMA instructions must split evenly over the waves");
+    constexpr int SA = TM * GK * 2, SB = TN * GK * 2;    // stage bytes
+    __shared__ __attribute__((aligned(16))) char smem[NS * (SA + SB)];
+
+    const int L = xcd_tile(blockIdx.x, g.total);
+    const int nt = L % g.tiles_n, rt = L / g.tiles_n;
+    const int bi = rt / g.tiles_t, t0 = (rt % g.tiles_t) * TM, n0 = nt * TN;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int wr = w / WC, wc = w % WC;
+
+    // DMA instruction j of this wave covers 16 tile rows; rows past the
+    // sequence or past the last output are clamped to a valid row (their
+    // results are never stored).
+    const uint16_t* src[PER];
+    uint32_t dst[PER];
+    bool isb[PER];
+    const uint32_t base = lds_addr(smem);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int ins = w + NW * j;
+        const bool b = ins >= AI;
+        const int r = (b ? ins - AI : ins) * 16 + (lane >> 2);
+        const int p = (lane & 3) ^ ((r >> 2) & 3);
+        if (!b) {
+            const int t = min(t0 + r, g.N - 1);
+            src[j] = g.A + ((size_t)bi * g.N + t) * g.lda + p * 8;
+            dst[j] = base + ins * 1024;
+        } else {
+            int n = min(n0 + r, g.n_out - 1);
+            const uint16_t* Wt = g.W0;
+            if (EPI == EPI_QKV) {
+                const int which = n / g.rows_per_w;
+                Wt = which == 0 ? g.W0 : (which == 1 ? g.W1 : g.W2);
+                n -= which * g.rows_per_w;
+            }
+            src[j] = Wt + (size_t)n * g.ldb + p * 8;
+            dst[j] = base + NS * SA + (ins - AI) * 1024;
+        }
+        isb[j] = b;
+    }
+    auto issue = [&](int kb, int buf) {
+        const int ka = kb * GK;
+        int kw = ka;
+        if (kw >= g.KW) kw -= g.KW;
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            dma16(src[j] + (isb[j] ? kw : ka),
+                  __builtin_amdgcn_readfirstlane(dst[j] + buf * (isb[j] ? SB : SA)));
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][c][i] = 0.f;
+
+    const int KB = g.K / GK;
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < KB) issue(s, s);
+    for (int kb = 0; kb < KB; ++kb) {
+        // stage kb has landed once at most the later stages' loads are pending
+        const int later = min(KB - 1, kb + NS - 2) - kb;
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        if (kb + NS - 1 < KB) issue(kb + NS - 1, (kb + NS - 1) % NS);
+        const char* A = smem + (kb % NS) * SA;
+        const char* Bt = smem + NS * SA + (kb % NS) * SB;
+#pragma unroll
+        for (int ks = 0; ks < GK / 16; ++ks) {
+            const int p = 2 * ks + h;
+            bf16x8 av[2], bv[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+                av[a] = *reinterpret_cast<const bf16x8*>(A + psw(64 * wr + 32 * a + l32, p));
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                bv[c] = *reinterpret_cast<const bf16x8*>(Bt + psw(64 * wc + 32 * c + l32, p));
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) acc[a][c] = mfma_32x32x16(av[a], bv[c], acc[a][c]);
+        }
+    }
+
+    const int nw = n0 + 64 * wc;                 // this wave's first output
+    if (nw >= g.n_out) return;
+    if (EPI == EPI_QKV) {
+        // The wave's 64 outputs are one head of one projection.
+        const int which = nw / g.rows_per_w, head = (nw - which * g.rows_per_w) / HDIM;
+        float* out = which == 0 ? g.out0 : (which == 1 ? g.out1 : g.out2);
+        float scale[2][16];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) scale[a][i] = 1.f;
+        if (which == 1) {
+            // k / ||k||: the row's 64 entries sit in the 32 lanes of this half
+            // (two column tiles per lane).
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float s = acc[a][0][i] * acc[a][0][i] + acc[a][1][i] * acc[a][1][i];
+                    s = row16_sum(s);
+                    s += __shfl_xor(s, 16, 64);
+                    scale[a][i] = s > 0.f ? 1.f / sqrtf(s) : 0.f;
+                }
+        }
+        float* ob = out + ((size_t)bi * g.H + head) * (size_t)g.N * HDIM;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int t = t0 + 64 * wr + 32 * a + crow(i, h);
+                if (t < g.N) {
+                    float* row = ob + (size_t)t * HDIM + l32;
+                    row[0] = acc[a][0][i] * scale[a][i];
+                    row[32] = acc[a][1][i] * scale[a][i];
+                }
+            }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int n = nw + 32 * c + l32;
+            if (n >= g.n_out) continue;
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = t0 + 64 * wr + 32 * a + crow(i, h);
+                    if (t < g.N) g.out0[((size_t)bi * g.N + t) * g.n_out + n] = acc[a][c][i];
+                }
+        }
+    }
+}
+
+// ===========================================================================
+// Output operand: A = LayerNorm(z) * gamma_o + beta_o + q for every (token,
+// head) row, written token-major as two bf16 terms, Aext[token][0 .. H*64) =
+// hi and Aext[token][H*64 .. 2*H*64) = lo. Sixteen lanes (one DPP row) own a
+// row, four entries each, so the reads of z and q and the writes are
+// contiguous 256- and 128-byte runs and the statistics are DPP row sums.
+// ===========================================================================
+constexpr int PT = 256;
+
+__global__ void __launch_bounds__(PT)
+layer_outprep_kernel(int N, int H, int rows, const float* __restrict__ Z, const float* __restrict__ Qf,
+                     const float* __restrict__ gamma_o, const float* __restrict__ beta_o, float eps,
+                     uint32_t* __restrict__ Aext)
+{
+    const int gid = blockIdx.x * PT + threadIdx.x;
+    const int row = gid >> 4, e = (gid & 15) * 4;     // row = (b*H + h)*N + t of the head-major arrays
+    if (row >= rows) return;                          // whole DPP rows leave together
+    const float4 z = *reinterpret_cast<const float4*>(Z + (size_t)row * HDIM + e);
+    const float4 q = *reinterpret_cast<const float4*>(Qf + (size_t)row * HDIM + e);
+    const int t = row % N, bh = row / N, hh = bh % H, bi = bh / H;
+    const float mu = row16_sum(z.x + z.y + z.z + z.w) * (1.f / HDIM);
+    const float c0 = z.x - mu, c1 = z.y - mu, c2 = z.z - mu, c3 = z.w - mu;
+    const float var = row16_sum(c0 * c0 + c1 * c1 + c2 * c2 + c3 * c3) * (1.f / HDIM);
+    const float rs = 1.f / sqrtf(var + eps);
+    const float4 gm = *reinterpret_cast<const float4*>(gamma_o + hh * HDIM + e);
+    const float4 bt = *reinterpret_cast<const float4*>(beta_o + hh * HDIM + e);
+    const float a0 = fmaf(c0 * rs, gm.x, bt.x) + q.x;
+    const float a1 = fmaf(c1 * rs, gm.y, bt.y) + q.y;
+    const float a2 = fmaf(c2 * rs, gm.z, bt.z) + q.z;
+    const float a3 = fmaf(c3 * rs, gm.w, bt.w) + q.w;
+    uint32_t p01[2], p23[2];
+    split_pair<2>(a0, a1, p01);
+    split_pair<2>(a2, a3, p23);
+    const size_t HD = (size_t)H * HDIM;
+    uint32_t* dst = Aext + (((size_t)bi * N + t) * 2 * HD + (size_t)hh * HDIM + e) / 2;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(p01[0], p23[0]);
+    *reinterpret_cast<uint2*>(dst + HD / 2) = make_uint2(p01[1], p23[1]);
+}
+
+// Tile shapes of the two GEMMs
+constexpr int P_TM = 256, P_TN = 128, P_NS = 3;      // projections
+constexpr int O_TM = 256, O_TN = 128, O_NS = 3;      // output projection
+
+}  // namespace
+
+size_t layer_workspace_region_bytes(int B, int N, int H)
+{
+    const size_t s = (size_t)B * H * N * HDIM * 4;
+    return (s + 255) & ~(size_t)255;
+}
+
+hipError_t launch_layer_qkv(const LayerArgs& a, float* Qo, float* Ko, float* Vo, hipStream_t stream)
+{
+    GemmArgs g{};
+    g.N = a.N;
+    g.H = a.H;
+    g.K = a.D;
+    g.KW = a.D;
+    g.rows_per_w = a.H * HDIM;
+    g.n_out = 3 * g.rows_per_w;
+    g.lda = a.D;
+    g.ldb = a.D;
+    g.tiles_t = (a.N + P_TM - 1) / P_TM;
+    g.tiles_n = (g.n_out + P_TN - 1) / P_TN;
+    g.total = a.B * g.tiles_t * g.tiles_n;
+    g.A = static_cast<const uint16_t*>(a.x);
+    g.W0 = static_cast<const uint16_t*>(a.Wq);
+    g.W1 = static_cast<const uint16_t*>(a.Wk);
+    g.W2 = static_cast<const uint16_t*>(a.Wv);
+    g.out0 = Qo;
+    g.out1 = Ko;
+    g.out2 = Vo;
+    hipLaunchKernelGGL((layer_gemm_kernel<P_TM, P_TN, P_NS, EPI_QKV>), dim3(g.total), dim3(P_TM * P_TN / 64), 0,
+                       stream, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_out(const LayerArgs& a, const float* Z, const float* Qf, void* aext, hipStream_t stream)
+{
+    const int HD = a.H * HDIM;
+    const int rows = a.B * a.H * a.N;
+    const size_t threads = (size_t)rows * 16;
+    hipLaunchKernelGGL(layer_outprep_kernel, dim3((unsigned)((threads + PT - 1) / PT)), dim3(PT), 0, stream, a.N,
+                       a.H, rows, Z, Qf, a.out_gamma, a.out_beta, a.eps, static_cast<uint32_t*>(aext));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    GemmArgs g{};
+    g.N = a.N;
+    g.H = a.H;
+    g.K = 2 * HD;
+    g.KW = HD;
+    g.rows_per_w = a.D;
+    g.n_out = a.D;
+    g.lda = 2 * HD;
+    g.ldb = HD;
+    g.tiles_t = (a.N + O_TM - 1) / O_TM;
+    g.tiles_n = (a.D + O_TN - 1) / O_TN;
+    g.total = a.B * g.tiles_t * g.tiles_n;
+    g.A = static_cast<const uint16_t*>(aext);
+    g.W0 = static_cast<const uint16_t*>(a.Wo);
+    g.out0 = a.y;
+    hipLaunchKernelGGL((layer_gemm_kernel<O_TM, O_TN, O_NS, EPI_ROWS>), dim3(g.total), dim3(O_TM * O_TN / 64), 0,
+                       stream, g);
+    return hipGetLastError();
+}
+
+}  // namespace ttt

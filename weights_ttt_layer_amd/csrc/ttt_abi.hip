@@ -302,4 +302,85 @@ int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b, co
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
+size_t ttt_layer_fwd_workspace_bytes(int B, int N, int H, int d)
+{
+    if (B < 1 || N < 1 || H < 1 || d != SMALLB_D) return 0;
+    if ((size_t)B * (size_t)H > (size_t)INT32_MAX) return 0;
+    return 5 * ttt::layer_workspace_region_bytes(B, N, H);
+}
+
+int ttt_layer_fwd(int kind, int B, int N, int D, int H, int d, int b, const void* x, const void* Wq,
+                  const void* Wk, const void* Wv, const void* Wo, const float* eta, float eta_const,
+                  const float* W0, const float* ln_gamma, const float* ln_beta, const float* out_gamma,
+                  const float* out_beta, float ln_eps, float* y, float* W_end, void* workspace,
+                  size_t workspace_bytes, void* hip_stream)
+{
+    if (kind != TTT_LINEAR_PLAIN && kind != TTT_LINEAR_LN) return TTT_ERR_INVALID_ARGUMENT;
+    if (B < 1 || N < 1 || D < 1 || H < 1 || d < 1 || b < 1) return TTT_ERR_INVALID_ARGUMENT;
+    if (!x || !Wq || !Wk || !Wv || !Wo || !W0 || !out_gamma || !out_beta || !y || !W_end || !workspace)
+        return TTT_ERR_INVALID_ARGUMENT;
+    if (!(ln_eps >= 0.f)) return TTT_ERR_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || !aligned(Wq, 16) || !aligned(Wk, 16) || !aligned(Wv, 16) || !aligned(Wo, 16) ||
+        !aligned(out_gamma, 16) || !aligned(out_beta, 16) || !aligned(y, 4) || !aligned(workspace, 256))
+        return TTT_ERR_INVALID_ARGUMENT;
+    if ((size_t)B * (size_t)H > (size_t)INT32_MAX || (size_t)B * (size_t)N > (size_t)INT32_MAX)
+        return TTT_ERR_INVALID_ARGUMENT;
+    if (d != SMALLB_D || b > SMALLB_MAX_B || D % 64 != 0 || (size_t)H * d * 3 > (size_t)INT32_MAX)
+        return TTT_ERR_UNSUPPORTED;
+    const size_t region = ttt::layer_workspace_region_bytes(B, N, H);
+    if (workspace_bytes < 5 * region) return TTT_ERR_WORKSPACE_TOO_SMALL;
+
+    const size_t HD = (size_t)H * d;
+    const size_t x_bytes = (size_t)B * N * D * 2, y_bytes = (size_t)B * N * D * 4;
+    const size_t wp_bytes = HD * (size_t)D * 2, w_bytes = (size_t)B * H * d * d * 4;
+    const size_t hv_bytes = HD * 4, eta_bytes = (size_t)B * H * N * 4;
+    const void* ins[8] = {x, Wq, Wk, Wv, Wo, W0, out_gamma, out_beta};
+    const size_t in_bytes[8] = {x_bytes, wp_bytes, wp_bytes, wp_bytes, wp_bytes, w_bytes, hv_bytes, hv_bytes};
+    for (int i = 0; i < 8; ++i) {
+        if (overlaps(y, y_bytes, ins[i], in_bytes[i]) || overlaps(workspace, 5 * region, ins[i], in_bytes[i]))
+            return TTT_ERR_INVALID_ARGUMENT;
+        if (i != 5 && overlaps(W_end, w_bytes, ins[i], in_bytes[i])) return TTT_ERR_INVALID_ARGUMENT;
+    }
+    if (W_end != W0 && overlaps(W_end, w_bytes, W0, w_bytes)) return TTT_ERR_INVALID_ARGUMENT;
+    if (overlaps(y, y_bytes, W_end, w_bytes) || overlaps(y, y_bytes, workspace, 5 * region) ||
+        overlaps(W_end, w_bytes, workspace, 5 * region))
+        return TTT_ERR_INVALID_ARGUMENT;
+    if (eta && (overlaps(y, y_bytes, eta, eta_bytes) || overlaps(W_end, w_bytes, eta, eta_bytes) ||
+                overlaps(workspace, 5 * region, eta, eta_bytes)))
+        return TTT_ERR_INVALID_ARGUMENT;
+
+    char* ws = static_cast<char*>(workspace);
+    float* Qf = reinterpret_cast<float*>(ws);
+    float* Kf = reinterpret_cast<float*>(ws + region);
+    float* Vf = reinterpret_cast<float*>(ws + 2 * region);
+    float* Zf = reinterpret_cast<float*>(ws + 3 * region);
+    void* Aext = ws + 4 * region;
+    ttt::LinearArgs inner;
+    int path = TTT_PATH_NONE;
+    const int st = check_linear(kind, TTT_DTYPE_F32, B, H, N, d, b, Qf, Kf, Vf, eta, eta_const, W0, ln_gamma,
+                                ln_beta, ln_eps, Zf, W_end, nullptr, 0, inner, path);
+    if (st != TTT_OK) return st;
+    if (path != TTT_PATH_SMALL_B) return TTT_ERR_UNSUPPORTED;
+
+    ttt::LayerArgs a;
+    a.B = B;
+    a.N = N;
+    a.D = D;
+    a.H = H;
+    a.x = x;
+    a.Wq = Wq;
+    a.Wk = Wk;
+    a.Wv = Wv;
+    a.Wo = Wo;
+    a.out_gamma = out_gamma;
+    a.out_beta = out_beta;
+    a.eps = ln_eps;
+    a.y = y;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    hipError_t err = ttt::launch_layer_qkv(a, Qf, Kf, Vf, stream);
+    if (err == hipSuccess) err = ttt::launch_smallb_linear(inner, stream);
+    if (err == hipSuccess) err = ttt::launch_layer_out(a, Zf, Qf, Aext, stream);
+    return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
 }  // extern "C"

@@ -17,6 +17,13 @@ Recipe (the same for every workload):
     independent draw per (batch, head, token), stored fp32 [B,H,N].
   * The large-chunk workload L2-normalises every Q/K/V row in fp64 before
     rounding.
+
+Whole-layer workloads (``LAYER_WORKLOADS``, seed ``20261303 + index``) draw, in
+this order: x ~ N(0,1) [B,N,D]; W_Q, W_K, W_V ~ N(0, 1/D) [H*d, D];
+W_O ~ N(0, 1/(H*d)) [D, H*d] (all rounded to bf16); W0 ~ N(0, 1/d) fp32;
+u ~ N(0,1) [B,H,N] with eta = sigmoid(u) / d; then for the LN inner model its
+gamma, beta; then the output LayerNorm's gamma_o, beta_o (same laws as gamma,
+beta).
 """
 from __future__ import annotations
 
@@ -199,6 +206,94 @@ def generate(wl: Workload, seed: int) -> Inputs:
 def workload_inputs(index: int) -> Inputs:
     """Inputs of the index-th named workload with its documented seed."""
     return generate(WORKLOADS[index], SEED_BASE + index)
+
+
+@dataclass(frozen=True)
+class LayerWorkload:
+    name: str
+    kind: str            # inner model: "plain" | "ln"
+    B: int
+    N: int
+    D: int
+    H: int
+    d: int
+    b: int
+    ln_eps: float = 1e-6
+    description: str = ""
+
+
+LAYER_SEED_BASE = 20261303
+
+LAYER_WORKLOADS = [
+    LayerWorkload("layer_ln_B8N2048_D768_H12_d64_b16", "ln", 8, 2048, 768, 12, 64, 16,
+                  description="whole TTT layer around TTT-Linear+LN: bf16 x and projections, "
+                              "B=8 N=2048 D=768 H=12 d=64 b=16, per-token eta"),
+]
+
+
+@dataclass
+class LayerInputs:
+    """Rounded whole-layer inputs; bf16 arrays hold bit patterns (uint16)."""
+    wl: LayerWorkload
+    x: np.ndarray
+    wq: np.ndarray
+    wk: np.ndarray
+    wv: np.ndarray
+    wo: np.ndarray
+    w0: np.ndarray
+    eta: np.ndarray
+    gamma: Optional[np.ndarray]
+    beta: Optional[np.ndarray]
+    gamma_o: np.ndarray
+    beta_o: np.ndarray
+
+    def f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        if name in ("x", "wq", "wk", "wv", "wo"):
+            return storage_to_f64(a, "bf16")
+        return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def generate_layer(wl: LayerWorkload, seed: int) -> LayerInputs:
+    """Draw the inputs of a whole-layer workload from ``PCG64(seed)`` in the documented order."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, N, D, H, d = wl.B, wl.N, wl.D, wl.H, wl.d
+    HD = H * d
+    bf = lambda a: _round_store(a, "bf16")
+    x = bf(rng.standard_normal((B, N, D)))
+    wq = bf(rng.standard_normal((HD, D)) / np.sqrt(D))
+    wk = bf(rng.standard_normal((HD, D)) / np.sqrt(D))
+    wv = bf(rng.standard_normal((HD, D)) / np.sqrt(D))
+    wo = bf(rng.standard_normal((D, HD)) / np.sqrt(HD))
+    w0 = (rng.standard_normal((B, H, d, d)) / np.sqrt(d)).astype(np.float32)
+    u = rng.standard_normal((B, H, N))
+    eta = (1.0 / (1.0 + np.exp(-u)) / d).astype(np.float32)
+    gamma = beta = None
+    if wl.kind == "ln":
+        gamma = (1.0 + 0.02 * rng.standard_normal((H, d))).astype(np.float32)
+        beta = (0.02 * rng.standard_normal((H, d))).astype(np.float32)
+    gamma_o = (1.0 + 0.02 * rng.standard_normal((H, d))).astype(np.float32)
+    beta_o = (0.02 * rng.standard_normal((H, d))).astype(np.float32)
+    return LayerInputs(wl, x, wq, wk, wv, wo, w0, eta, gamma, beta, gamma_o, beta_o)
+
+
+def layer_workload_inputs(index: int) -> LayerInputs:
+    return generate_layer(LAYER_WORKLOADS[index], LAYER_SEED_BASE + index)
+
+
+def layer_to_device(inp: LayerInputs, device="cuda"):
+    """Device tensors of a whole-layer problem (bf16 arrays keep their bit patterns)."""
+    import torch
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+    def f32(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    return dict(x=bf16(inp.x), wq=bf16(inp.wq), wk=bf16(inp.wk), wv=bf16(inp.wv), wo=bf16(inp.wo),
+                w0=f32(inp.w0), eta=f32(inp.eta), gamma=f32(inp.gamma), beta=f32(inp.beta),
+                gamma_o=f32(inp.gamma_o), beta_o=f32(inp.beta_o))
 
 
 def to_device(inp: Inputs, device="cuda"):
