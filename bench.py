@@ -15,7 +15,10 @@ measurement for the large-chunk workload (plain TTT-Linear, bf16, B=1 H=16
 N=32768 d=128 b=2048), whose roofline is the bf16 MFMA peak; and "next_rows":
 the block-causal outputs of that workload (chunk outputs with the chunk's
 starting or ending weights) and the single-token decode step of B*H = 768
-TTT-Linear+LN streams (d=64), each against the HBM roofline.
+TTT-Linear+LN streams (d=64), each against the HBM roofline, and the whole
+layer (projections, key normalisation, inner TTT-Linear+LN, output LayerNorm +
+residual + output projection; B=8 N=2048 D=768 H=12 d=64 b=16) against the
+bf16 MFMA roofline of its GEMM work.
 
 Prints ONE JSON line (stdout). Diagnostics go to stderr.
 """
@@ -228,6 +231,73 @@ def side_measurement(name: str, steps: int, warmup: int, variant: str):
             "roofline": roof}
 
 
+def layer_algorithmic(wl: wlm.LayerWorkload):
+    """Compulsory HBM bytes of one whole-layer call (read x, the four projection
+    weights, eta, the state and the LayerNorm parameters; write y and the state)
+    and its FLOPs (the three input projections, the inner model, the output
+    projection; the output projection counted once although it runs on two bf16
+    terms)."""
+    HD = wl.H * wl.d
+    tok = wl.B * wl.N
+    nbytes = tok * wl.D * 2 + 4 * HD * wl.D * 2 + wl.B * wl.H * wl.N * 4 + tok * wl.D * 4
+    nbytes += 2 * wl.B * wl.H * wl.d * wl.d * 4 + (4 if wl.kind == "ln" else 2) * HD * 4
+    inner = wlm.Workload("inner", wl.kind, "f32", wl.B, wl.H, wl.N, wl.d, wl.b, "sigmoid")
+    flops = 2 * tok * wl.D * 3 * HD + algorithmic_flops(inner) + 2 * tok * HD * wl.D
+    return nbytes, flops
+
+
+def layer_measurement(steps: int, warmup: int):
+    """Whole-layer calls (ttt_layer_fwd) on the named layer workload. Per-call
+    inputs (x, eta, the state) and outputs rotate over ROTATE device copies; the
+    projection weights are shared, as they are across the calls of a model."""
+    import torch
+    from weights_ttt_layer_amd import layer_fwd, layer_workspace_bytes
+
+    inp = wlm.layer_workload_inputs(0)
+    wl = inp.wl
+    dev = torch.device("cuda:0")
+    base = wlm.layer_to_device(inp, dev)
+    sets = [base] + [dict(base, x=base["x"].clone(), eta=base["eta"].clone(), w0=base["w0"].clone())
+                     for _ in range(ROTATE - 1)]
+    need = layer_workspace_bytes(wl.B, wl.N, wl.H, wl.d)
+    outs = [(torch.empty((wl.B, wl.N, wl.D), dtype=torch.float32, device=dev), torch.empty_like(base["w0"]),
+             torch.empty(need, dtype=torch.uint8, device=dev)) for _ in range(ROTATE)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s, o = sets[i % ROTATE], outs[i % ROTATE]
+        layer_fwd(s["x"], s["wq"], s["wk"], s["wv"], s["wo"], s["w0"], s["gamma_o"], s["beta_o"], s["eta"],
+                  H=wl.H, b=wl.b, kind=wl.kind, ln_gamma=s["gamma"], ln_beta=s["beta"], ln_eps=wl.ln_eps,
+                  y=o[0], w_end=o[1], workspace=o[2], stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    finite = bool(torch.isfinite(outs[(steps - 1) % ROTATE][0]).all().item())
+    if not finite:
+        log(f"[bench] WARNING: non-finite output in {wl.name}")
+    del sets, outs, base
+    torch.cuda.empty_cache()
+    sec = ms / 1e3
+    nbytes, flops = layer_algorithmic(wl)
+    tokens = wl.B * wl.N
+    roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(wl, "layer", "layer")
+    log(f"[bench] {wl.name}: {ms*1e3:.1f} us/step, {tokens/sec:.4g} tokens/s, "
+        f"{flops/sec/1e12:.2f} TFLOP/s algorithmic")
+    return {"workload": wl.name, "variant": "layer", "value": tokens / sec, "unit": "tokens/s",
+            "ms_per_step": ms, "algorithmic_bytes": nbytes, "algorithmic_flops": flops, "roofline": roof}
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle as it stands
 # ---------------------------------------------------------------------------
@@ -311,6 +381,7 @@ def main():
             "block_before": side_measurement(LARGE_WORKLOAD, args.steps, args.warmup, "block_before"),
             "block_after": side_measurement(LARGE_WORKLOAD, args.steps, args.warmup, "block_after"),
             "decode": side_measurement(DECODE_WORKLOAD, args.steps, args.warmup, "decode"),
+            "layer": layer_measurement(args.steps, args.warmup),
         }
 
     if args.copy_calibration:

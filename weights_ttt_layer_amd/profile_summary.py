@@ -44,20 +44,23 @@ KERNEL_SOURCES = {
     "block_before": ["large_chunk.hip", "device_common.h"],
     "block_after": ["large_chunk.hip", "device_common.h"],
     "decode": ["decode.hip", "device_common.h"],
+    "layer": ["outer_layer.hip", "smallb_linear.hip", "smallb_common.h", "device_common.h"],
 }
 
 OUR_KERNELS = ("smallb_linear_kernel", "smallb_mlp_kernel", "lc_gram_kernel", "lc_scan_kernel",
-               "lc_chunk_kernel", "lc_apply_kernel", "decode_kernel")
+               "lc_chunk_kernel", "lc_apply_kernel", "decode_kernel", "layer_gemm_kernel",
+               "layer_outprep_kernel")
 
 # kernel-name prefixes launched by one call of each path
 PATH_KERNELS = {
     "plain": ("smallb_linear_kernel<0",),
-    "ln": ("smallb_linear_kernel<1",),
+    "ln": ("smallb_linear_kernel<1, unsigned short>",),
     "mlp": ("smallb_mlp_kernel",),
     "large": ("lc_gram_kernel", "lc_scan_kernel", "lc_chunk_kernel"),
     "block_before": ("lc_gram_kernel", "lc_scan_kernel", "lc_apply_kernel<false>"),
     "block_after": ("lc_gram_kernel", "lc_scan_kernel", "lc_apply_kernel<true>"),
     "decode": ("decode_kernel",),
+    "layer": ("layer_gemm_kernel", "layer_outprep_kernel", "smallb_linear_kernel<1, float>"),
 }
 
 
@@ -131,10 +134,17 @@ def load_counter(d: str, counter: str):
 def traffic(args):
     sys.path.insert(0, ROOT)
     from weights_ttt_layer_amd import workloads as wlm
-    from bench import algorithmic_bytes
+    from bench import algorithmic_bytes, layer_algorithmic
 
-    wl = wlm.BY_NAME[args.workload]
-    path_key = "large" if wl.b >= 256 else wl.kind
+    layers = {w.name: w for w in wlm.LAYER_WORKLOADS}
+    if args.workload in layers:
+        wl = layers[args.workload]
+        path_key = "layer"
+        alg = layer_algorithmic(wl)[0]
+    else:
+        wl = wlm.BY_NAME[args.workload]
+        path_key = "large" if wl.b >= 256 else wl.kind
+        alg = algorithmic_bytes(wl)
     if args.variant != "dual":
         path_key = args.variant
     suffix = "" if args.variant == "dual" else f"_{args.variant}"
@@ -161,7 +171,6 @@ def traffic(args):
         total += hbm
     if not kernels:
         raise SystemExit(f"no dispatch of the {path_key} path's kernels in the counter runs")
-    alg = algorithmic_bytes(wl)
     rec = {
         "workload": wl.name,
         "variant": args.variant,
