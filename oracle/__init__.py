@@ -60,6 +60,9 @@ def _load():
     lib.ttt_oracle_mlp_loss.restype = d
     lib.ttt_oracle_mlp_grad.argtypes = [i, i, P, P, P, P, P, P, d, P, P]
     lib.ttt_oracle_mlp_grad.restype = None
+    lib.ttt_oracle_linear_bwd.argtypes = [i, i, i, i, i, i, P, P, P, P, P, P, P, d, P, P, P, P, P, P, P,
+                                          P, P, i]
+    lib.ttt_oracle_linear_bwd.restype = i
     lib.ttt_oracle_gelu.argtypes = [d]
     lib.ttt_oracle_gelu.restype = d
     lib.ttt_oracle_gelu_prime.argtypes = [d]
@@ -112,6 +115,32 @@ def linear(mode, kind, Q, K, V, eta, W0, b, gamma=None, beta=None, eps=1e-6, nth
     if rc != 0:
         raise ValueError("ttt_oracle_linear rejected its arguments")
     return Z, We
+
+
+def linear_bwd(kind, Q, K, V, eta, W0, b, dZ, dW_end=None, gamma=None, beta=None, eps=1e-6,
+               nthreads=None):
+    """Gradients of TTT-Linear (kind PLAIN or LN, the mini-batch dual form) with
+    respect to all inputs, given dZ [B,H,N,d] and dW_end [B,H,d,d] (None = 0).
+    Returns dict(dQ, dK, dV, deta [B,H,N], dW0, dgamma, dbeta [H,d] or None)."""
+    lib = _load()
+    Q, K, V, W0, dZ = _f64(Q), _f64(K), _f64(V), _f64(W0), _f64(dZ)
+    B, H, N, d = Q.shape
+    e = _eta_array(eta, B, H, N)
+    g = _f64(gamma).reshape(H, d) if kind == LN else None
+    bt = _f64(beta).reshape(H, d) if kind == LN else None
+    dWe = None if dW_end is None else _f64(dW_end)
+    out = {k: np.zeros((B, H, N, d)) for k in ("dQ", "dK", "dV")}
+    out["deta"] = np.zeros((B, H, N))
+    out["dW0"] = np.zeros((B, H, d, d))
+    out["dgamma"] = np.zeros((H, d)) if kind == LN else None
+    out["dbeta"] = np.zeros((H, d)) if kind == LN else None
+    rc = lib.ttt_oracle_linear_bwd(kind, B, H, N, d, int(b), _ptr(Q), _ptr(K), _ptr(V), _ptr(e), _ptr(W0),
+                                   _ptr(g), _ptr(bt), float(eps), _ptr(dZ), _ptr(dWe), _ptr(out["dQ"]),
+                                   _ptr(out["dK"]), _ptr(out["dV"]), _ptr(out["deta"]), _ptr(out["dW0"]),
+                                   _ptr(out["dgamma"]), _ptr(out["dbeta"]), nthreads or _default_threads())
+    if rc != 0:
+        raise ValueError("ttt_oracle_linear_bwd rejected its arguments")
+    return out
 
 
 def mlp(mode, Q, K, V, eta, W1, W2, b, gamma, beta, eps=1e-6, nthreads=None):

@@ -1,5 +1,6 @@
 /*
- * ttt_oracle.c -- slow, plain fp64 CPU oracle for the TTT-layer forward pass.
+ * ttt_oracle.c -- slow, plain fp64 CPU oracle for the TTT-layer forward pass and
+ * the backward of TTT-Linear.
  *
  * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call
  * this file. Only the tests, the smoke check and the benchmark's CPU-baseline leg
@@ -549,3 +550,284 @@ void ttt_oracle_mlp_grad(int d, int hid, const double* W1, const double* W2, con
 /* Scalar helpers exposed so tests can pin them against closed forms. */
 double ttt_oracle_gelu(double a) { return gelu(a); }
 double ttt_oracle_gelu_prime(double a) { return gelu_prime(a); }
+
+/* ------------------------------------------------------------------------ */
+/* Backward of TTT-Linear (PLAIN or LN) through the mini-batch dual form     */
+/* ------------------------------------------------------------------------ */
+/*
+ * Reverse-mode differentiation of the DUAL computation above (its result is
+ * MINIBATCH's), for outer-loop training: page 1 section "1. The
+ * Self-Supervised Inner-Loop Task" has the projections and layer norms trained
+ * by ordinary backpropagation through the inner loop. Given the gradients of a
+ * scalar objective with respect to the outputs, dZ [B,H,N,d] and dW_end
+ * [B,H,d,d], it returns the gradients with respect to every input: dQ, dK, dV
+ * [B,H,N,d], deta [B,H,N], dW0 [B,H,d,d] and, for LN, dgamma and dbeta [H,d]
+ * summed over the batch. The chunk-start weights W_c are recomputed by a
+ * forward pass and kept; the chunks are then visited in reverse with the
+ * weight gradient carried from chunk c+1 to chunk c. Per chunk, in the
+ * notation of the forward (row vectors, a_ts = q_t . k_s, s <= t):
+ *   h_s = k_s W_c,  g_s = d l_s / d h_s,
+ *   hq_t = q_t W_c - sum_{s<=t} a_ts eta_s g_s,  z_t = hq_t or q_t + LN(hq_t),
+ *   W_{c+1} = W_c - sum_s eta_s k_s^T g_s.
+ */
+
+/* Backward of g = d l / d h (lin_preact_grad) given dg. Adds k^T dh to dW and the
+ * contributions to dk, dv, dgamma, dbeta. scratch needs 8*d doubles. */
+static void lin_preact_grad_bwd(const lin_model* m, const double* W, const double* k, const double* v,
+                                const double* dg, double* dW, double* dk, double* dv, double* dgam,
+                                double* dbet, double* scratch)
+{
+    int d = m->d;
+    double* h = scratch;
+    double* dh = scratch + d;
+    vec_mat(d, d, k, W, h);
+    if (m->kind == KIND_PLAIN) {
+        /* g = 2 (h - v) */
+        for (int j = 0; j < d; ++j) {
+            dh[j] = 2.0 * dg[j];
+            dv[j] -= 2.0 * dg[j];
+        }
+    } else {
+        /* g = r (gx - m1 - xhat m2), gx = gamma dy, dy = 2 (k + gamma xhat + beta - v),
+         * xhat = c r, c = h - mu, r = (var + eps)^(-1/2), var = mean(c^2),
+         * m1 = mean(gx), m2 = mean(gx xhat). */
+        const double* gam = m->gamma;
+        const double* bet = m->beta;
+        double* c = scratch + 2 * d;
+        double* xh = scratch + 3 * d;
+        double* dy = scratch + 4 * d;
+        double* gx = scratch + 5 * d;
+        double* dxh = scratch + 6 * d;
+        double* dgx = scratch + 7 * d;
+        double mu = 0.0;
+        for (int j = 0; j < d; ++j) mu += h[j];
+        mu /= d;
+        double var = 0.0;
+        for (int j = 0; j < d; ++j) {
+            c[j] = h[j] - mu;
+            var += c[j] * c[j];
+        }
+        var /= d;
+        double r = 1.0 / sqrt(var + m->eps);
+        double m1 = 0.0, m2 = 0.0;
+        for (int j = 0; j < d; ++j) {
+            xh[j] = c[j] * r;
+            dy[j] = 2.0 * (k[j] + gam[j] * xh[j] + bet[j] - v[j]);
+            gx[j] = gam[j] * dy[j];
+            m1 += gx[j];
+            m2 += gx[j] * xh[j];
+        }
+        m1 /= d;
+        m2 /= d;
+        /* through g = r (gx - m1 - xhat m2) */
+        double dr = 0.0, s1 = 0.0, s2 = 0.0;
+        for (int j = 0; j < d; ++j) {
+            dr += dg[j] * (gx[j] - m1 - xh[j] * m2);
+            s1 += dg[j];
+            s2 += dg[j] * xh[j];
+        }
+        double dm1 = -r * s1, dm2 = -r * s2;
+        for (int j = 0; j < d; ++j) {
+            dgx[j] = r * dg[j] + dm1 / d + dm2 * xh[j] / d;
+            dxh[j] = -r * dg[j] * m2 + dm2 * gx[j] / d;
+        }
+        /* through gx = gamma dy and dy = 2 (k + gamma xhat + beta - v) */
+        for (int j = 0; j < d; ++j) {
+            dgam[j] += dgx[j] * dy[j];
+            double ddy = dgx[j] * gam[j];
+            dk[j] += 2.0 * ddy;
+            dgam[j] += 2.0 * ddy * xh[j];
+            dxh[j] += 2.0 * ddy * gam[j];
+            dbet[j] += 2.0 * ddy;
+            dv[j] -= 2.0 * ddy;
+        }
+        /* through xhat = c r, r = (var + eps)^(-1/2), var = mean(c^2), c = h - mu */
+        for (int j = 0; j < d; ++j) dr += dxh[j] * c[j];
+        double dvar = -0.5 * dr * r * r * r;
+        double mean_dc = 0.0;
+        for (int j = 0; j < d; ++j) {
+            dh[j] = dxh[j] * r + dvar * 2.0 * c[j] / d;   /* dc for now */
+            mean_dc += dh[j];
+        }
+        mean_dc /= d;
+        for (int j = 0; j < d; ++j) dh[j] -= mean_dc;
+    }
+    /* h = k W */
+    for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < d; ++j) {
+            acc += dh[j] * W[(size_t)i * d + j];
+            dW[(size_t)i * d + j] += k[i] * dh[j];
+        }
+        dk[i] += acc;
+    }
+}
+
+/* One (sequence, head) unit. dgam, dbet are per-unit partial sums. */
+static void lin_unit_bwd(const lin_model* m, int N, int b, const double* Q, const double* K, const double* V,
+                         const double* eta, const double* W0, const double* dZ, const double* dWend,
+                         double* dQ, double* dK, double* dV, double* deta, double* dW0, double* dgam,
+                         double* dbet)
+{
+    int d = m->d;
+    size_t dd = (size_t)d * d;
+    int C = (N + b - 1) / b;
+    double* Ws = malloc((size_t)(C > 0 ? C : 1) * dd * sizeof(double));  /* W_c of every chunk */
+    double* W = malloc(dd * sizeof(double));
+    double* dW = malloc(dd * sizeof(double));
+    double* G = malloc((size_t)b * d * sizeof(double));
+    double* dG = malloc((size_t)b * d * sizeof(double));
+    double* hq = malloc((size_t)d * sizeof(double));
+    double* dhq = malloc((size_t)d * sizeof(double));
+    double* xh = malloc((size_t)d * sizeof(double));
+    double* y = malloc((size_t)d * sizeof(double));
+    double* kd = malloc((size_t)d * sizeof(double));
+    double* scratch = malloc(8 * (size_t)d * sizeof(double));
+
+    /* forward: the chunk-start weights */
+    memcpy(W, W0, dd * sizeof(double));
+    for (int c = 0; c < C; ++c) {
+        int c0 = c * b, n = (c0 + b < N ? c0 + b : N) - c0;
+        memcpy(Ws + (size_t)c * dd, W, dd * sizeof(double));
+        for (int s = 0; s < n; ++s)
+            lin_preact_grad(m, Ws + (size_t)c * dd, K + (size_t)(c0 + s) * d, V + (size_t)(c0 + s) * d,
+                            G + (size_t)s * d, scratch);
+        for (int s = 0; s < n; ++s)
+            rank1_sub(d, d, eta[c0 + s], K + (size_t)(c0 + s) * d, G + (size_t)s * d, W);
+    }
+
+    memset(dQ, 0, (size_t)N * d * sizeof(double));
+    memset(dK, 0, (size_t)N * d * sizeof(double));
+    memset(dV, 0, (size_t)N * d * sizeof(double));
+    memset(deta, 0, (size_t)N * sizeof(double));
+    if (dWend) memcpy(dW, dWend, dd * sizeof(double));
+    else memset(dW, 0, dd * sizeof(double));
+
+    for (int c = C - 1; c >= 0; --c) {
+        int c0 = c * b, n = (c0 + b < N ? c0 + b : N) - c0;
+        const double* Wc = Ws + (size_t)c * dd;
+        const double* Qc = Q + (size_t)c0 * d;
+        const double* Kc = K + (size_t)c0 * d;
+        const double* Vc = V + (size_t)c0 * d;
+        const double* et = eta + c0;
+        double* dQc = dQ + (size_t)c0 * d;
+        double* dKc = dK + (size_t)c0 * d;
+        double* dVc = dV + (size_t)c0 * d;
+        double* dec = deta + c0;
+        for (int s = 0; s < n; ++s)
+            lin_preact_grad(m, Wc, Kc + (size_t)s * d, Vc + (size_t)s * d, G + (size_t)s * d, scratch);
+        memset(dG, 0, (size_t)n * d * sizeof(double));
+
+        /* W_{c+1} = W_c - sum_s eta_s k_s^T g_s, with dW holding d/dW_{c+1} */
+        for (int s = 0; s < n; ++s) {
+            const double* ks = Kc + (size_t)s * d;
+            const double* gs = G + (size_t)s * d;
+            vec_mat(d, d, ks, dW, kd);                       /* k_s dW */
+            double kdg = dot(d, kd, gs);                      /* k_s dW g_s^T */
+            for (int j = 0; j < d; ++j) dG[(size_t)s * d + j] -= et[s] * kd[j];
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < d; ++j) acc += gs[j] * dW[(size_t)i * d + j];
+                dKc[(size_t)s * d + i] -= et[s] * acc;       /* g_s dW^T */
+            }
+            dec[s] -= kdg;
+        }
+        /* dW now accumulates d/dW_c: the direct path through W_{c+1} is dW itself */
+
+        for (int t = 0; t < n; ++t) {
+            const double* qt = Qc + (size_t)t * d;
+            const double* dzt = dZ + (size_t)(c0 + t) * d;
+            /* recompute hq_t */
+            vec_mat(d, d, qt, Wc, hq);
+            for (int s = 0; s <= t; ++s) {
+                double a = dot(d, qt, Kc + (size_t)s * d) * et[s];
+                for (int j = 0; j < d; ++j) hq[j] -= a * G[(size_t)s * d + j];
+            }
+            /* output stage */
+            if (m->kind == KIND_PLAIN) {
+                memcpy(dhq, dzt, (size_t)d * sizeof(double));
+            } else {
+                double r = ln_forward(d, hq, m->gamma, m->beta, m->eps, xh, y);
+                ln_backward(d, xh, r, m->gamma, dzt, dhq);
+                for (int j = 0; j < d; ++j) {
+                    dQc[(size_t)t * d + j] += dzt[j];
+                    dgam[j] += dzt[j] * xh[j];
+                    dbet[j] += dzt[j];
+                }
+            }
+            /* hq_t = q_t W_c - sum_{s<=t} (q_t . k_s) eta_s g_s */
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < d; ++j) {
+                    acc += dhq[j] * Wc[(size_t)i * d + j];
+                    dW[(size_t)i * d + j] += qt[i] * dhq[j];
+                }
+                dQc[(size_t)t * d + i] += acc;
+            }
+            for (int s = 0; s <= t; ++s) {
+                const double* ks = Kc + (size_t)s * d;
+                const double* gs = G + (size_t)s * d;
+                double a = dot(d, qt, ks);
+                double dcoef = -dot(d, dhq, gs);              /* d/d(a eta_s) */
+                for (int j = 0; j < d; ++j) dG[(size_t)s * d + j] -= a * et[s] * dhq[j];
+                dec[s] += dcoef * a;
+                double da = dcoef * et[s];
+                for (int j = 0; j < d; ++j) {
+                    dQc[(size_t)t * d + j] += da * ks[j];
+                    dKc[(size_t)s * d + j] += da * qt[j];
+                }
+            }
+        }
+        /* g_s = d l_s / d h_s at W_c */
+        for (int s = 0; s < n; ++s)
+            lin_preact_grad_bwd(m, Wc, Kc + (size_t)s * d, Vc + (size_t)s * d, dG + (size_t)s * d, dW,
+                                dKc + (size_t)s * d, dVc + (size_t)s * d, dgam, dbet, scratch);
+    }
+    memcpy(dW0, dW, dd * sizeof(double));
+    free(Ws); free(W); free(dW); free(G); free(dG); free(hq); free(dhq);
+    free(xh); free(y); free(kd); free(scratch);
+}
+
+/* Returns 0 on success, -1 on a bad argument. dZ and dWend may be NULL (zero).
+ * dgamma, dbeta ([H,d], summed over the batch) may be NULL for kind PLAIN. */
+int ttt_oracle_linear_bwd(int kind, int B, int H, int N, int d, int b, const double* Q, const double* K,
+                          const double* V, const double* eta, const double* W0, const double* gamma,
+                          const double* beta, double eps, const double* dZ, const double* dWend,
+                          double* dQ, double* dK, double* dV, double* deta, double* dW0, double* dgamma,
+                          double* dbeta, int nthreads)
+{
+    if ((kind != KIND_PLAIN && kind != KIND_LN) || B < 1 || H < 1 || N < 1 || d < 1 || b < 1) return -1;
+    if (kind == KIND_LN && (!gamma || !beta || !dgamma || !dbeta)) return -1;
+    int units = B * H;
+    double* zero = NULL;
+    if (!dZ) {
+        zero = calloc((size_t)units * N * d, sizeof(double));
+        dZ = zero;
+    }
+    double* pg = calloc((size_t)units * d, sizeof(double));
+    double* pb = calloc((size_t)units * d, sizeof(double));
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int u = 0; u < units; ++u) {
+        int h = u % H;
+        lin_model m = {kind, d, kind == KIND_LN ? gamma + (size_t)h * d : NULL,
+                       kind == KIND_LN ? beta + (size_t)h * d : NULL, eps};
+        size_t so = (size_t)u * N * d, wo = (size_t)u * d * d;
+        lin_unit_bwd(&m, N, b, Q + so, K + so, V + so, eta + (size_t)u * N, W0 + wo, dZ + so,
+                     dWend ? dWend + wo : NULL, dQ + so, dK + so, dV + so, deta + (size_t)u * N, dW0 + wo,
+                     pg + (size_t)u * d, pb + (size_t)u * d);
+    }
+    if (kind == KIND_LN) {
+        memset(dgamma, 0, (size_t)H * d * sizeof(double));
+        memset(dbeta, 0, (size_t)H * d * sizeof(double));
+        for (int u = 0; u < units; ++u)
+            for (int j = 0; j < d; ++j) {
+                dgamma[(size_t)(u % H) * d + j] += pg[(size_t)u * d + j];
+                dbeta[(size_t)(u % H) * d + j] += pb[(size_t)u * d + j];
+            }
+    }
+    free(pg);
+    free(pb);
+    free(zero);
+    return 0;
+}
