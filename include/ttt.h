@@ -176,6 +176,50 @@ int ttt_linear_decode(int kind, int qkv_dtype, int B, int H, int d,
                       const float* ln_gamma, const float* ln_beta, float ln_eps,
                       float* z, void* hip_stream);
 
+/*
+ * ttt_linear_bwd -- backward of ttt_linear_fwd (small-b combinations): the
+ * gradients of a scalar objective with respect to every input, given its
+ * gradients with respect to the outputs. Page "Test-Time Training: Linear
+ * Complexity Beyond Attention" (section "1. The Self-Supervised Inner-Loop
+ * Task") trains the outer parameters by backpropagation through the inner
+ * loop; this differentiates the chunked computation of section "4. Mini-Batch
+ * Parallelism (Dual Formulation)" exactly (every gradient at the chunk-start
+ * weights, outputs with the updated weights), including the LayerNorm
+ * statistics inside the inner loss and the output.
+ *
+ *   kind, qkv_dtype, B, H, N, d, b, Q, K, V, eta, eta_const, W0, ln_gamma,
+ *   ln_beta, ln_eps      the forward call's arguments (read only)
+ *   dZ          device [B,H,N,d] fp32, d objective / d Z
+ *   dW_end      device [B,H,d,d] fp32, d objective / d W_end, or NULL (zero)
+ *   dQ, dK, dV  device [B,H,N,d] fp32 outputs
+ *   deta        device [B,H,N] fp32 output: d objective / d eta_t for every
+ *               token (also when eta == NULL: then their sum is the gradient
+ *               with respect to eta_const)
+ *   dW0         device [B,H,d,d] fp32 output
+ *   dgamma, dbeta   device [H,d] fp32 outputs, summed over the batch (kind LN;
+ *               ignored, may be NULL, for PLAIN)
+ *   workspace   device, 256-byte aligned, ttt_linear_bwd_workspace_bytes(...)
+ *               bytes: the chunk-start states (B*H*ceil(N/b)*d*d*4 bytes) and
+ *               per-unit partial sums
+ * All products run on fp32 matrix cores (exact fp32 products, fp32 sums).
+ * Outputs must not overlap each other, any input or the workspace. Pointers of
+ * token rows, states, dZ, dW_end, the gradient outputs and ln_gamma/ln_beta
+ * must be 16-byte aligned. Asynchronous on hip_stream; validation on the host
+ * before any HIP call. Supported: d = 64, 1 <= b <= 16 (else
+ * TTT_ERR_UNSUPPORTED).
+ */
+int ttt_linear_bwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b,
+                   const void* Q, const void* K, const void* V,
+                   const float* eta, float eta_const, const float* W0,
+                   const float* ln_gamma, const float* ln_beta, float ln_eps,
+                   const float* dZ, const float* dW_end,
+                   float* dQ, float* dK, float* dV, float* deta, float* dW0,
+                   float* dgamma, float* dbeta,
+                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes of ttt_linear_bwd (0 for unsupported or invalid input). */
+size_t ttt_linear_bwd_workspace_bytes(int kind, int qkv_dtype, int B, int H, int N, int d, int b);
+
 /* Which ttt_path a (kind, dtype, d, b) combination takes; TTT_PATH_NONE if none. */
 int ttt_linear_fwd_path(int kind, int qkv_dtype, int d, int b);
 

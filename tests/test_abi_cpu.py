@@ -204,3 +204,37 @@ def test_layer_rejections(lib):
     assert layer_call(lib, We=ctypes.c_void_p(A + 5 * (1 << 30) + 256), ws_bytes=big) == E       # W_end partly over W0
     assert layer_call(lib, y=ctypes.c_void_p(A + 12 * (1 << 30) + 1024), ws_bytes=big) == E      # y inside workspace
     assert layer_call(lib, kind=1, gam=None, ws_bytes=big) == E                        # LN needs the affine
+
+
+def bwd_call(lib, kind=1, dt=1, B=8, H=12, N=2048, d=64, b=16, q=0, k=1, v=2, eta=None, W0=3, gam=4, bet=5,
+             eps=1e-6, dz=6, dwe=None, dq=7, dk=8, dv=9, de=10, dw0=11, dg=12, db=13, ws=14, ws_bytes=0):
+    """Every call here fails validation (the default workspace size is 0)."""
+    p = lambda i: None if i is None else (i if isinstance(i, ctypes.c_void_p) else addr(i))
+    return lib.ttt_linear_bwd(kind, dt, B, H, N, d, b, p(q), p(k), p(v), p(eta), 0.1, p(W0), p(gam), p(bet), eps,
+                              p(dz), p(dwe), p(dq), p(dk), p(dv), p(de), p(dw0), p(dg), p(db), p(ws), ws_bytes,
+                              None)
+
+
+def test_bwd_rejections(lib):
+    E, U = binding.TTT_ERR_INVALID_ARGUMENT, binding.TTT_ERR_UNSUPPORTED
+    need = lib.ttt_linear_bwd_workspace_bytes(1, 1, 8, 12, 2048, 64, 16)
+    assert need == 96 * 128 * 64 * 64 * 4 + 96 * 2 * 64 * 4
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 8, 12, 2048, 128, 16) == 0
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 8, 12, 2048, 64, 17) == 0
+    assert lib.ttt_linear_bwd_workspace_bytes(2, 1, 8, 12, 2048, 64, 16) == 0
+    assert bwd_call(lib, kind=2) == E
+    assert bwd_call(lib, dt=3) == E
+    assert bwd_call(lib, N=0) == E
+    assert bwd_call(lib, dz=None) == E
+    assert bwd_call(lib, de=None) == E
+    assert bwd_call(lib, dg=None) == E                                  # LN needs dgamma
+    assert bwd_call(lib, eps=-1.0) == E
+    assert bwd_call(lib, q=ctypes.c_void_p(A + 8)) == E                 # 16-byte alignment
+    assert bwd_call(lib, ws=ctypes.c_void_p(A + 14 * (1 << 30) + 64)) == E
+    assert bwd_call(lib, d=128) == U
+    assert bwd_call(lib, b=17) == U
+    assert bwd_call(lib) == binding.TTT_ERR_WORKSPACE_TOO_SMALL
+    assert bwd_call(lib, dq=ctypes.c_void_p(A + 1024), ws_bytes=need) == E        # dQ overlaps Q
+    assert bwd_call(lib, dk=addr(7), ws_bytes=need) == E                          # dK equals dQ
+    assert bwd_call(lib, ws=addr(11), ws_bytes=need) == E                         # workspace over dW0
+    assert bwd_call(lib, dwe=ctypes.c_void_p(A + 11 * (1 << 30) + 512), ws_bytes=need) == E   # dW0 over dW_end

@@ -8,6 +8,7 @@
 ``linear_decode`` takes one online step per (sequence, head) stream.
 ``layer_fwd`` runs the whole layer: projections, key normalisation, the inner
 TTT-Linear model, output LayerNorm + residual and the output projection.
+``linear_bwd`` is the backward of ``linear_fwd`` (small-b combinations).
 Build the library first with ``python -m weights_ttt_layer_amd.build``.
 """
 from .binding import (  # noqa: F401
@@ -15,6 +16,7 @@ from .binding import (  # noqa: F401
     layer_fwd,
     layer_parts,
     layer_workspace_bytes,
+    linear_bwd,
     linear_decode,
     linear_fwd,
     linear_fwd_block,
@@ -25,5 +27,6 @@ from .binding import (  # noqa: F401
     status_string,
 )
 
-__all__ = ["TTTError", "layer_fwd", "layer_parts", "layer_workspace_bytes", "linear_decode", "linear_fwd", "linear_fwd_block", "linear_path",
+__all__ = ["TTTError", "layer_fwd", "layer_parts", "layer_workspace_bytes", "linear_bwd",
+           "linear_decode", "linear_fwd", "linear_fwd_block", "linear_path",
            "linear_workspace_bytes", "load_library", "mlp_fwd", "status_string"]

@@ -58,6 +58,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_linear_fwd_block_workspace_bytes.restype = sz
     lib.ttt_linear_decode.argtypes = [i, i, i, i, i, vp, vp, vp, fp, f, fp, fp, fp, f, fp, vp]
     lib.ttt_linear_decode.restype = i
+    lib.ttt_linear_bwd.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, fp, f, fp, fp, fp, f, fp, fp, fp, fp, fp,
+                                   fp, fp, fp, fp, vp, sz, vp]
+    lib.ttt_linear_bwd.restype = i
+    lib.ttt_linear_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.ttt_linear_bwd_workspace_bytes.restype = sz
     lib.ttt_layer_fwd.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, vp, fp, f, fp, fp, fp, fp, fp, f,
                                   fp, fp, vp, sz, vp]
     lib.ttt_layer_fwd.restype = i
@@ -328,4 +333,50 @@ def layer_parts(workspace: torch.Tensor, B: int, N: int, H: int, d: int) -> dict
     out = {}
     for i, name in enumerate("QKVZ"):
         out[name] = workspace[i * region:i * region + 4 * n].view(torch.float32).view(B, H, N, d)
+    return out
+
+
+def linear_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w0: torch.Tensor, dz: torch.Tensor,
+               eta: Optional[torch.Tensor] = None, *, b: int, kind: str = "plain", eta_const: float = 0.0,
+               dw_end: Optional[torch.Tensor] = None, ln_gamma: Optional[torch.Tensor] = None,
+               ln_beta: Optional[torch.Tensor] = None, ln_eps: float = 1e-6,
+               workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Backward of ``linear_fwd`` through ``ttt_linear_bwd``. Returns a dict of
+    dQ, dK, dV ([B,H,N,d]), deta ([B,H,N]), dW0 ([B,H,d,d]) and, for kind "ln",
+    dgamma, dbeta ([H,d]); all fp32."""
+    lib = load_library()
+    if kind not in KINDS:
+        raise ValueError(f"kind must be one of {sorted(KINDS)}")
+    B, H, N, d = q.shape
+    dt = _qkv_dtype(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, (B, H, N, d), q.dtype)
+    _check(w0, "w0", (B, H, d, d), torch.float32)
+    _check(dz, "dz", (B, H, N, d), torch.float32)
+    if dw_end is not None:
+        _check(dw_end, "dw_end", (B, H, d, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H, N), torch.float32)
+    if kind == "ln":
+        if ln_gamma is None or ln_beta is None:
+            raise ValueError("kind 'ln' needs ln_gamma and ln_beta")
+        _check(ln_gamma, "ln_gamma", (H, d), torch.float32)
+        _check(ln_beta, "ln_beta", (H, d), torch.float32)
+    dev = q.device
+    out = {name: torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for name in ("dQ", "dK", "dV")}
+    out["deta"] = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    out["dW0"] = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    out["dgamma"] = torch.empty((H, d), dtype=torch.float32, device=dev) if kind == "ln" else None
+    out["dbeta"] = torch.empty((H, d), dtype=torch.float32, device=dev) if kind == "ln" else None
+    need = int(lib.ttt_linear_bwd_workspace_bytes(KINDS[kind], dt, B, H, N, d, int(b)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.ttt_linear_bwd(KINDS[kind], dt, B, H, N, d, int(b), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                            float(eta_const), _ptr(w0), _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps), _ptr(dz),
+                            _ptr(dw_end), _ptr(out["dQ"]), _ptr(out["dK"]), _ptr(out["dV"]), _ptr(out["deta"]),
+                            _ptr(out["dW0"]), _ptr(out["dgamma"]), _ptr(out["dbeta"]), _ptr(workspace), ws_bytes,
+                            _stream_ptr(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_linear_bwd")
     return out

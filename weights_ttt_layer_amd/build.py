@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libttt.so")
 SOURCES = ["ttt_abi.hip", "smallb_linear.hip", "smallb_mlp.hip", "large_chunk.hip", "decode.hip",
-           "outer_layer.hip"]
+           "outer_layer.hip", "backward.hip"]
 ARCH = "gfx950"
 
 

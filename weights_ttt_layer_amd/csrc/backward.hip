@@ -1,0 +1,550 @@
+// backward.hip -- backward of TTT-Linear (plain and LayerNorm + residual inner
+// model) through the mini-batch dual form, d = 64, 1 <= b <= 16: the gradients
+// of a scalar objective with respect to Q, K, V, eta, W0 (and gamma, beta)
+// given its gradients dZ and dW_end. Page "Test-Time Training: Linear
+// Complexity Beyond Attention" (section "1. The Self-Supervised Inner-Loop
+// Task") trains the outer parameters by backpropagation through the inner
+// loop; this is that backpropagation for the chunked form of section "4.
+// Mini-Batch Parallelism (Dual Formulation)". Per chunk (rows t, s; s <= t):
+//     h_s = k_s W_c,  g_s = d l_s / d h_s,  a_ts = q_t . k_s
+//     hq_t = q_t W_c - sum_{s<=t} a_ts eta_s g_s,   z_t = hq_t  or  q_t + LN(hq_t)
+//     W_{c+1} = W_c - sum_s eta_s k_s^T g_s
+//
+// One workgroup (four waves) per (sequence, head) unit, two passes:
+//  1. the chunk-start states W_c are recomputed and written to the workspace;
+//  2. the chunks are visited in reverse. dW (the gradient with respect to the
+//     state at the current chunk boundary) stays in LDS; each chunk first uses
+//     it as d/dW_{c+1}, then adds the chunk's own terms to make it d/dW_c.
+// Every matrix product runs on the fp32 matrix cores (v_mfma_f32_16x16x4f32,
+// exact fp32 products) over operands staged in LDS; each wave owns one
+// 16-column tile of a 16 x 64 result (or one 16-row band of a 64 x 64 one).
+// The row-wise steps (LayerNorm statistics and their derivatives) give every
+// token row to one DPP row of 16 lanes, four entries per lane.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace ttt {
+namespace {
+
+constexpr int BD = 64;       // head dim
+constexpr int BR = 16;       // rows of a chunk tile (b <= 16)
+constexpr int BT = 256;      // threads per workgroup
+constexpr int LS = 68;       // LDS row stride (floats) of 64-wide tiles
+constexpr int SS = 20;       // LDS row stride of 16-wide tiles
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// sum_k A(i, k) B(k, j) for a 16 x 16 tile, k < KD (a multiple of 16), as four
+// independent accumulation chains. Lane l supplies A(l % 16, k) and B(k, l % 16)
+// with k = 4 u + l / 16 of each group of 16; the result is in the C layout
+// (lane l: rows 4 (l / 16) + r, column l % 16).
+template <int KD, class FA, class FB>
+__device__ __forceinline__ f32x4 tile_mm(FA a, FB b, int lane)
+{
+    const int i = lane & 15, kq = lane >> 4;
+    f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, p2 = p0, p3 = p0;
+#pragma unroll
+    for (int k0 = 0; k0 < KD; k0 += 16) {
+        p0 = mfma4(a(i, k0 + kq), b(k0 + kq, i), p0);
+        p1 = mfma4(a(i, k0 + 4 + kq), b(k0 + 4 + kq, i), p1);
+        p2 = mfma4(a(i, k0 + 8 + kq), b(k0 + 8 + kq, i), p2);
+        p3 = mfma4(a(i, k0 + 12 + kq), b(k0 + 12 + kq, i), p3);
+    }
+    return (p0 + p1) + (p2 + p3);
+}
+
+// C-layout tile <-> LDS (row-major, `stride` floats per row), rows r0.., cols c0..
+__device__ __forceinline__ f32x4 ld_tile(const float* m, int stride, int r0, int c0, int lane)
+{
+    const int j = c0 + (lane & 15), i0 = r0 + 4 * (lane >> 4);
+    f32x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = m[(i0 + r) * stride + j];
+    return v;
+}
+
+__device__ __forceinline__ void st_tile(float* m, int stride, int r0, int c0, const f32x4& v, int lane)
+{
+    const int j = c0 + (lane & 15), i0 = r0 + 4 * (lane >> 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[(i0 + r) * stride + j] = v[r];
+}
+
+struct alignas(16) BwdSmem {
+    float W[BD][LS];     // W_c (pass 2) / the running state (pass 1)
+    float dW[BD][LS];    // gradient with respect to the state at the chunk boundary
+    float K[BR][LS], Q[BR][LS], V[BR][LS], dZ[BR][LS];
+    float H[BR][LS];     // K W_c
+    float HQ[BR][LS];    // Q W_c - A G
+    float KD[BR][LS];    // K dW_{c+1}
+    float GD[BR][LS];    // G dW_{c+1}^T
+    float G[BR][LS];     // g_s (pass 1: eta_s g_s)
+    float dG[BR][LS];
+    float dHq[BR][LS];
+    float dQ[BR][LS], dK[BR][LS], dV[BR][LS];
+    float dh[BR][LS];
+    float S[BR][SS];     // a_ts = q_t . k_s
+    float P[BR][SS];     // dhq_t . g_s
+    float DA[BR][SS];    // d a_ts (causal part)
+    float C2[BR][SS];    // d eta_s contributions of the causal term, per t
+    float eta[BR];
+    float deta[BR];
+    float red[2][BR][BD];
+};
+
+template <typename S>
+__device__ __forceinline__ float4 load4(const S* p);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p)
+{
+    return *reinterpret_cast<const float4*>(p);
+}
+template <>
+__device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* p)
+{
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xFFFF0000u),
+                       __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xFFFF0000u));
+}
+
+__device__ __forceinline__ void put4(float* row, int j0, float4 v)
+{
+    *reinterpret_cast<float4*>(row + j0) = v;
+}
+__device__ __forceinline__ float4 get4(const float* row, int j0) { return *reinterpret_cast<const float4*>(row + j0); }
+
+// Row-wise LayerNorm pieces: the 64 entries of a row sit in one DPP row of 16
+// lanes, four per lane.
+struct LnRow {
+    float c[4], xh[4], r;
+};
+
+__device__ __forceinline__ LnRow ln_stats(const float (&h)[4], float eps)
+{
+    LnRow s;
+    const float mu = row16_sum(h[0] + h[1] + h[2] + h[3]) * (1.f / BD);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s.c[e] = h[e] - mu;
+    const float var = row16_sum(s.c[0] * s.c[0] + s.c[1] * s.c[1] + s.c[2] * s.c[2] + s.c[3] * s.c[3]) * (1.f / BD);
+    s.r = 1.f / sqrtf(var + eps);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s.xh[e] = s.c[e] * s.r;
+    return s;
+}
+
+// dh = r (gx - mean(gx) - xhat mean(gx xhat)), gx = gamma dy
+__device__ __forceinline__ void ln_bwd(const LnRow& s, const float (&gam)[4], const float (&dy)[4], float (&dh)[4])
+{
+    float gx[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gx[e] = gam[e] * dy[e];
+    const float m1 = row16_sum(gx[0] + gx[1] + gx[2] + gx[3]) * (1.f / BD);
+    const float m2 = row16_sum(gx[0] * s.xh[0] + gx[1] * s.xh[1] + gx[2] * s.xh[2] + gx[3] * s.xh[3]) * (1.f / BD);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dh[e] = s.r * (gx[e] - m1 - s.xh[e] * m2);
+}
+
+__device__ __forceinline__ void to4(float4 v, float (&a)[4]) { a[0] = v.x, a[1] = v.y, a[2] = v.z, a[3] = v.w; }
+__device__ __forceinline__ float4 of4(const float (&a)[4]) { return make_float4(a[0], a[1], a[2], a[3]); }
+
+// g = d ||f(k; W) - v||^2 / dh at h = k W (row r of sm.H), for KIND 0 (plain) or 1 (LN).
+template <int KIND>
+__device__ __forceinline__ void preact_grad(const float (&h)[4], const float (&k)[4], const float (&v)[4],
+                                            const float (&gam)[4], const float (&bet)[4], float eps,
+                                            float (&g)[4])
+{
+    if constexpr (KIND == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g[e] = 2.f * (h[e] - v[e]);
+    } else {
+        const LnRow s = ln_stats(h, eps);
+        float dy[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dy[e] = 2.f * (k[e] + gam[e] * s.xh[e] + bet[e] - v[e]);
+        ln_bwd(s, gam, dy, g);
+    }
+}
+
+template <int KIND, typename S>
+__global__ void __launch_bounds__(BT)
+bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __restrict__ Kg,
+                  const S* __restrict__ Vg, const float* __restrict__ etag, float eta_const,
+                  const float* __restrict__ W0, const float* __restrict__ gamma, const float* __restrict__ beta,
+                  float eps, const float* __restrict__ dZg, const float* __restrict__ dWend,
+                  float* __restrict__ dQg, float* __restrict__ dKg, float* __restrict__ dVg,
+                  float* __restrict__ detag, float* __restrict__ dW0g, float* __restrict__ ckpt,
+                  float* __restrict__ gbpart)
+{
+    __shared__ BwdSmem sm;
+    const int unit = blockIdx.x, head = unit % H;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = tid >> 4, j0 = (tid & 15) * 4;          // row-phase layout
+    const int C = (N + b - 1) / b;
+    const size_t tok0 = (size_t)unit * N;
+    float* ck = ckpt + (size_t)unit * C * BD * BD;
+
+    float gam[4] = {0.f, 0.f, 0.f, 0.f}, bet[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KIND == 1) {
+        to4(get4(gamma + head * BD, j0), gam);
+        to4(get4(beta + head * BD, j0), bet);
+    }
+    float pg[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};   // dgamma, dbeta partials
+
+    // rows [t0, t0 + n) of a token stream into an LDS tile (zero past n)
+    auto load_rows = [&](float (*dst)[LS], const S* src, int t0, int n) {
+        const float4 v = r < n ? load4(src + (tok0 + t0 + r) * BD + j0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        put4(dst[r], j0, v);
+    };
+    auto load_eta = [&](int t0, int n) {
+        if (tid < BR) sm.eta[tid] = tid < n ? (etag ? etag[tok0 + t0 + tid] : eta_const) : 0.f;
+    };
+
+    // ---------------- pass 1: chunk-start states ----------------
+    for (int i = tid; i < BD * BD / 4; i += BT) {
+        const int row = i >> 4, col = (i & 15) * 4;
+        put4(sm.W[row], col, get4(W0 + (size_t)unit * BD * BD + row * BD, col));
+    }
+    for (int c = 0; c < C; ++c) {
+        const int t0 = c * b, n = min(b, N - t0);
+        load_rows(sm.K, Kg, t0, n);
+        load_rows(sm.V, Vg, t0, n);
+        load_eta(t0, n);
+        __syncthreads();
+        for (int i = tid; i < BD * BD / 4; i += BT) {
+            const int row = i >> 4, col = (i & 15) * 4;
+            *reinterpret_cast<float4*>(ck + (size_t)c * BD * BD + row * BD + col) = get4(sm.W[row], col);
+        }
+        // H = K W
+        {
+            const f32x4 t = tile_mm<BD>([&](int i, int k) { return sm.K[i][k]; },
+                                        [&](int k, int j) { return sm.W[k][16 * w + j]; }, lane);
+            st_tile(&sm.H[0][0], LS, 0, 16 * w, t, lane);
+        }
+        __syncthreads();
+        {
+            float h[4], k[4], v[4], g[4];
+            to4(get4(sm.H[r], j0), h);
+            to4(get4(sm.K[r], j0), k);
+            to4(get4(sm.V[r], j0), v);
+            preact_grad<KIND>(h, k, v, gam, bet, eps, g);
+            const float e = sm.eta[r];
+            put4(sm.G[r], j0, r < n ? make_float4(e * g[0], e * g[1], e * g[2], e * g[3])
+                                    : make_float4(0.f, 0.f, 0.f, 0.f));
+        }
+        __syncthreads();
+        // W -= K^T (eta G): wave w updates rows 16w .. 16w + 15
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            f32x4 acc = ld_tile(&sm.W[0][0], LS, 16 * w, 16 * tj, lane);
+            acc -= tile_mm<BR>([&](int i, int k) { return sm.K[k][16 * w + i]; },
+                               [&](int k, int j) { return sm.G[k][16 * tj + j]; }, lane);
+            st_tile(&sm.W[0][0], LS, 16 * w, 16 * tj, acc, lane);
+        }
+        __syncthreads();
+    }
+    // the checkpoints are read back by other waves of this workgroup
+    __threadfence();
+    __syncthreads();
+
+    // ---------------- pass 2: reverse sweep ----------------
+    for (int i = tid; i < BD * BD / 4; i += BT) {
+        const int row = i >> 4, col = (i & 15) * 4;
+        put4(sm.dW[row], col, dWend ? get4(dWend + (size_t)unit * BD * BD + row * BD, col)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f));
+    }
+    for (int c = C - 1; c >= 0; --c) {
+        const int t0 = c * b, n = min(b, N - t0);
+        // A: operands of the chunk
+        load_rows(sm.K, Kg, t0, n);
+        load_rows(sm.Q, Qg, t0, n);
+        load_rows(sm.V, Vg, t0, n);
+        put4(sm.dZ[r], j0, r < n ? get4(dZg + (tok0 + t0 + r) * BD, j0) : make_float4(0.f, 0.f, 0.f, 0.f));
+        load_eta(t0, n);
+        for (int i = tid; i < BD * BD / 4; i += BT) {
+            const int row = i >> 4, col = (i & 15) * 4;
+            put4(sm.W[row], col, get4(ck + (size_t)c * BD * BD + row * BD, col));
+        }
+        __syncthreads();
+        // B: H = K W_c, HQ = Q W_c, KD = K dW_{c+1}, S = Q K^T
+        {
+            const int cw = 16 * w;
+            st_tile(&sm.H[0][0], LS, 0, cw,
+                    tile_mm<BD>([&](int i, int k) { return sm.K[i][k]; }, [&](int k, int j) { return sm.W[k][cw + j]; },
+                                lane), lane);
+            st_tile(&sm.HQ[0][0], LS, 0, cw,
+                    tile_mm<BD>([&](int i, int k) { return sm.Q[i][k]; }, [&](int k, int j) { return sm.W[k][cw + j]; },
+                                lane), lane);
+            st_tile(&sm.KD[0][0], LS, 0, cw,
+                    tile_mm<BD>([&](int i, int k) { return sm.K[i][k]; }, [&](int k, int j) { return sm.dW[k][cw + j]; },
+                                lane), lane);
+            if (w == 0)
+                st_tile(&sm.S[0][0], SS, 0, 0,
+                        tile_mm<BD>([&](int i, int k) { return sm.Q[i][k]; }, [&](int k, int j) { return sm.K[j][k]; },
+                                    lane), lane);
+        }
+        __syncthreads();
+        // C: g_s at W_c
+        {
+            float h[4], k[4], v[4], g[4];
+            to4(get4(sm.H[r], j0), h);
+            to4(get4(sm.K[r], j0), k);
+            to4(get4(sm.V[r], j0), v);
+            preact_grad<KIND>(h, k, v, gam, bet, eps, g);
+            put4(sm.G[r], j0, r < n ? of4(g) : make_float4(0.f, 0.f, 0.f, 0.f));
+        }
+        __syncthreads();
+        // D: HQ -= A G (A_ts = a_ts eta_s, s <= t), GD = G dW_{c+1}^T
+        {
+            const int cw = 16 * w;
+            f32x4 acc = ld_tile(&sm.HQ[0][0], LS, 0, cw, lane);
+            acc -= tile_mm<BR>([&](int i, int k) { return k <= i ? sm.S[i][k] * sm.eta[k] : 0.f; },
+                               [&](int k, int j) { return sm.G[k][cw + j]; }, lane);
+            st_tile(&sm.HQ[0][0], LS, 0, cw, acc, lane);
+            st_tile(&sm.GD[0][0], LS, 0, cw,
+                    tile_mm<BD>([&](int i, int k) { return sm.G[i][k]; }, [&](int k, int j) { return sm.dW[cw + j][k]; },
+                                lane), lane);
+        }
+        __syncthreads();
+        // E: output stage, and the terms of W_{c+1} = W_c - sum_s eta_s k_s^T g_s
+        {
+            float dz[4], dhq[4], dq[4] = {0.f, 0.f, 0.f, 0.f};
+            to4(get4(sm.dZ[r], j0), dz);
+            if constexpr (KIND == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dhq[e] = dz[e];
+            } else {
+                float hq[4];
+                to4(get4(sm.HQ[r], j0), hq);
+                const LnRow s = ln_stats(hq, eps);
+                ln_bwd(s, gam, dz, dhq);
+                if (r < n) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dq[e] = dz[e];
+                        pg[e] += dz[e] * s.xh[e];
+                        pb[e] += dz[e];
+                    }
+                }
+            }
+            float kd[4], gd[4], g[4];
+            to4(get4(sm.KD[r], j0), kd);
+            to4(get4(sm.GD[r], j0), gd);
+            to4(get4(sm.G[r], j0), g);
+            const float e = sm.eta[r];
+            const float kdg = row16_sum(kd[0] * g[0] + kd[1] * g[1] + kd[2] * g[2] + kd[3] * g[3]);
+            const bool live = r < n;
+            put4(sm.dHq[r], j0, live ? of4(dhq) : make_float4(0.f, 0.f, 0.f, 0.f));
+            put4(sm.dQ[r], j0, of4(dq));
+            put4(sm.dG[r], j0, live ? make_float4(-e * kd[0], -e * kd[1], -e * kd[2], -e * kd[3])
+                                    : make_float4(0.f, 0.f, 0.f, 0.f));
+            put4(sm.dK[r], j0, live ? make_float4(-e * gd[0], -e * gd[1], -e * gd[2], -e * gd[3])
+                                    : make_float4(0.f, 0.f, 0.f, 0.f));
+            if ((tid & 15) == 0) sm.deta[r] = live ? -kdg : 0.f;
+        }
+        __syncthreads();
+        // F: dQ += dHq W_c^T, dG -= A^T dHq, P = dHq G^T
+        {
+            const int cw = 16 * w;
+            f32x4 acc = ld_tile(&sm.dQ[0][0], LS, 0, cw, lane);
+            acc += tile_mm<BD>([&](int i, int k) { return sm.dHq[i][k]; }, [&](int k, int j) { return sm.W[cw + j][k]; },
+                               lane);
+            st_tile(&sm.dQ[0][0], LS, 0, cw, acc, lane);
+            f32x4 ag = ld_tile(&sm.dG[0][0], LS, 0, cw, lane);
+            ag -= tile_mm<BR>([&](int i, int k) { return i <= k ? sm.S[k][i] * sm.eta[i] : 0.f; },
+                              [&](int k, int j) { return sm.dHq[k][cw + j]; }, lane);
+            st_tile(&sm.dG[0][0], LS, 0, cw, ag, lane);
+            if (w == 0)
+                st_tile(&sm.P[0][0], SS, 0, 0,
+                        tile_mm<BD>([&](int i, int k) { return sm.dHq[i][k]; }, [&](int k, int j) { return sm.G[j][k]; },
+                                    lane), lane);
+        }
+        __syncthreads();
+        // G: causal-term derivatives, d(a_ts eta_s) = -dhq_t . g_s
+        {
+            const int t = tid >> 4, s = tid & 15;
+            const bool on = s <= t && t < n;
+            const float dcoef = on ? -sm.P[t][s] : 0.f;
+            sm.DA[t][s] = dcoef * sm.eta[s];
+            sm.C2[t][s] = dcoef * sm.S[t][s];
+        }
+        __syncthreads();
+        // H: dQ += DA K, dK += DA^T Q; d eta_s += sum_t C2[t][s]
+        {
+            const int cw = 16 * w;
+            f32x4 acc = ld_tile(&sm.dQ[0][0], LS, 0, cw, lane);
+            acc += tile_mm<BR>([&](int i, int k) { return sm.DA[i][k]; }, [&](int k, int j) { return sm.K[k][cw + j]; },
+                               lane);
+            st_tile(&sm.dQ[0][0], LS, 0, cw, acc, lane);
+            f32x4 ak = ld_tile(&sm.dK[0][0], LS, 0, cw, lane);
+            ak += tile_mm<BR>([&](int i, int k) { return sm.DA[k][i]; }, [&](int k, int j) { return sm.Q[k][cw + j]; },
+                              lane);
+            st_tile(&sm.dK[0][0], LS, 0, cw, ak, lane);
+            if (tid < BR) {
+                float a = 0.f;
+#pragma unroll
+                for (int t = 0; t < BR; ++t) a += sm.C2[t][tid];
+                sm.deta[tid] += a;
+            }
+        }
+        __syncthreads();
+        // I: backward of g = d l / d h: dh, and the direct terms of dK, dV, dgamma, dbeta
+        {
+            float dg[4], dh[4], dv[4], dkd[4] = {0.f, 0.f, 0.f, 0.f};
+            to4(get4(sm.dG[r], j0), dg);
+            if constexpr (KIND == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dh[e] = 2.f * dg[e];
+                    dv[e] = -2.f * dg[e];
+                }
+            } else {
+                float h[4], k[4], v[4];
+                to4(get4(sm.H[r], j0), h);
+                to4(get4(sm.K[r], j0), k);
+                to4(get4(sm.V[r], j0), v);
+                const LnRow s = ln_stats(h, eps);
+                float dy[4], gx[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dy[e] = 2.f * (k[e] + gam[e] * s.xh[e] + bet[e] - v[e]);
+                    gx[e] = gam[e] * dy[e];
+                }
+                const float m1 = row16_sum(gx[0] + gx[1] + gx[2] + gx[3]) * (1.f / BD);
+                const float m2 =
+                    row16_sum(gx[0] * s.xh[0] + gx[1] * s.xh[1] + gx[2] * s.xh[2] + gx[3] * s.xh[3]) * (1.f / BD);
+                // through g = r (gx - m1 - xhat m2)
+                float dr = row16_sum(dg[0] * (gx[0] - m1 - s.xh[0] * m2) + dg[1] * (gx[1] - m1 - s.xh[1] * m2) +
+                                     dg[2] * (gx[2] - m1 - s.xh[2] * m2) + dg[3] * (gx[3] - m1 - s.xh[3] * m2));
+                const float s1 = row16_sum(dg[0] + dg[1] + dg[2] + dg[3]);
+                const float s2 = row16_sum(dg[0] * s.xh[0] + dg[1] * s.xh[1] + dg[2] * s.xh[2] + dg[3] * s.xh[3]);
+                const float dm1 = -s.r * s1, dm2 = -s.r * s2;
+                float dxh[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float dgx = s.r * dg[e] + dm1 * (1.f / BD) + dm2 * s.xh[e] * (1.f / BD);
+                    dxh[e] = -s.r * dg[e] * m2 + dm2 * gx[e] * (1.f / BD);
+                    // through gx = gamma dy and dy = 2 (k + gamma xhat + beta - v)
+                    const float ddy = dgx * gam[e];
+                    if (r < n) {
+                        pg[e] += dgx * dy[e] + 2.f * ddy * s.xh[e];
+                        pb[e] += 2.f * ddy;
+                    }
+                    dkd[e] = 2.f * ddy;
+                    dxh[e] += 2.f * ddy * gam[e];
+                    dv[e] = -2.f * ddy;
+                }
+                // through xhat = c r, r = (var + eps)^(-1/2), var = mean(c^2), c = h - mu
+                dr += row16_sum(dxh[0] * s.c[0] + dxh[1] * s.c[1] + dxh[2] * s.c[2] + dxh[3] * s.c[3]);
+                const float dvar = -0.5f * dr * s.r * s.r * s.r;
+                float dc[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dc[e] = dxh[e] * s.r + dvar * 2.f * s.c[e] * (1.f / BD);
+                const float mdc = row16_sum(dc[0] + dc[1] + dc[2] + dc[3]) * (1.f / BD);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dh[e] = dc[e] - mdc;
+            }
+            const bool live = r < n;
+            float dk[4];
+            to4(get4(sm.dK[r], j0), dk);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dk[e] += dkd[e];
+            put4(sm.dK[r], j0, of4(dk));
+            put4(sm.dV[r], j0, live ? of4(dv) : make_float4(0.f, 0.f, 0.f, 0.f));
+            put4(sm.dh[r], j0, live ? of4(dh) : make_float4(0.f, 0.f, 0.f, 0.f));
+        }
+        __syncthreads();
+        // J: dK += dh W_c^T;  dW += Q^T dHq + K^T dh  (wave w: rows 16w .. 16w + 15)
+        {
+            const int cw = 16 * w;
+            f32x4 ak = ld_tile(&sm.dK[0][0], LS, 0, cw, lane);
+            ak += tile_mm<BD>([&](int i, int k) { return sm.dh[i][k]; }, [&](int k, int j) { return sm.W[cw + j][k]; },
+                              lane);
+            st_tile(&sm.dK[0][0], LS, 0, cw, ak, lane);
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
+                f32x4 acc = ld_tile(&sm.dW[0][0], LS, cw, 16 * tj, lane);
+                acc += tile_mm<2 * BR>(
+                    [&](int i, int k) { return k < BR ? sm.Q[k][cw + i] : sm.K[k - BR][cw + i]; },
+                    [&](int k, int j) { return k < BR ? sm.dHq[k][16 * tj + j] : sm.dh[k - BR][16 * tj + j]; }, lane);
+                st_tile(&sm.dW[0][0], LS, cw, 16 * tj, acc, lane);
+            }
+        }
+        __syncthreads();
+        // K: the chunk's gradients to HBM
+        if (r < n) {
+            const size_t o = (tok0 + t0 + r) * BD + j0;
+            *reinterpret_cast<float4*>(dQg + o) = get4(sm.dQ[r], j0);
+            *reinterpret_cast<float4*>(dKg + o) = get4(sm.dK[r], j0);
+            *reinterpret_cast<float4*>(dVg + o) = get4(sm.dV[r], j0);
+        }
+        if (tid < n) detag[tok0 + t0 + tid] = sm.deta[tid];
+        // the next chunk's loads touch none of the buffers read here
+    }
+    __syncthreads();
+    for (int i = tid; i < BD * BD / 4; i += BT) {
+        const int row = i >> 4, col = (i & 15) * 4;
+        *reinterpret_cast<float4*>(dW0g + (size_t)unit * BD * BD + row * BD + col) = get4(sm.dW[row], col);
+    }
+    if constexpr (KIND == 1) {
+        // per-unit dgamma, dbeta: sum the 16 row partials of each column
+        put4(sm.red[0][r], j0, of4(pg));
+        put4(sm.red[1][r], j0, of4(pb));
+        __syncthreads();
+        if (tid < 2 * BD) {
+            const int which = tid >> 6, col = tid & 63;
+            float a = 0.f;
+#pragma unroll
+            for (int t = 0; t < BR; ++t) a += sm.red[which][t][col];
+            gbpart[((size_t)unit * 2 + which) * BD + col] = a;
+        }
+    }
+}
+
+// dgamma[h] = sum over sequences of the per-unit partials (fixed order)
+__global__ void __launch_bounds__(2 * BD)
+bwd_gamma_beta_kernel(int B, int H, const float* __restrict__ gbpart, float* __restrict__ dgamma,
+                      float* __restrict__ dbeta)
+{
+    const int h = blockIdx.x, which = threadIdx.x >> 6, col = threadIdx.x & 63;
+    float a = 0.f;
+    for (int bi = 0; bi < B; ++bi) a += gbpart[(((size_t)bi * H + h) * 2 + which) * BD + col];
+    (which == 0 ? dgamma : dbeta)[h * BD + col] = a;
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int H, int N, int b)
+{
+    const size_t units = (size_t)B * H, C = (size_t)((N + b - 1) / b);
+    const size_t ck = (units * C * BD * BD * 4 + 255) & ~(size_t)255;
+    return ck + units * 2 * BD * 4;
+}
+
+hipError_t launch_bwd_linear(const BwdArgs& a, hipStream_t stream)
+{
+    const int units = a.f.B * a.f.H;
+    const size_t units_z = (size_t)units, C = (size_t)((a.f.N + a.f.b - 1) / a.f.b);
+    float* ckpt = static_cast<float*>(a.f.workspace);
+    float* gbpart = reinterpret_cast<float*>(static_cast<char*>(a.f.workspace) +
+                                             ((units_z * C * BD * BD * 4 + 255) & ~(size_t)255));
+#define TTT_BWD_LAUNCH(KIND, S)                                                                                 \
+    hipLaunchKernelGGL((bwd_linear_kernel<KIND, S>), dim3(units), dim3(BT), 0, stream, a.f.H, a.f.N, a.f.b,     \
+                       static_cast<const S*>(a.f.Q), static_cast<const S*>(a.f.K), static_cast<const S*>(a.f.V), \
+                       a.f.eta, a.f.eta_const, a.f.W0, a.f.gamma, a.f.beta, a.f.eps, a.dZ, a.dW_end, a.dQ, a.dK, \
+                       a.dV, a.deta, a.dW0, ckpt, gbpart)
+    if (a.f.kind == 0 && a.f.dtype == 0) TTT_BWD_LAUNCH(0, float);
+    else if (a.f.kind == 0) TTT_BWD_LAUNCH(0, uint16_t);
+    else if (a.f.dtype == 0) TTT_BWD_LAUNCH(1, float);
+    else TTT_BWD_LAUNCH(1, uint16_t);
+#undef TTT_BWD_LAUNCH
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || a.f.kind == 0) return err;
+    hipLaunchKernelGGL(bwd_gamma_beta_kernel, dim3(a.f.H), dim3(2 * BD), 0, stream, a.f.B, a.f.H, gbpart, a.dgamma,
+                       a.dbeta);
+    return hipGetLastError();
+}
+
+}  // namespace ttt

@@ -60,6 +60,23 @@ hipError_t launch_decode_linear(const LinearArgs& a, hipStream_t stream);
 // TTT-MLP small-b path: d = 64, hidden = 256, 1 <= b <= 16.
 hipError_t launch_smallb_mlp(const MlpArgs& a, hipStream_t stream);
 
+// Backward of TTT-Linear (plain / LN), d = 64, 1 <= b <= 16. `f` carries the
+// forward's inputs and the workspace (chunk-start states and per-unit partials).
+struct BwdArgs {
+    LinearArgs f;
+    const float* dZ;
+    const float* dW_end;   // or nullptr (zero)
+    float* dQ;
+    float* dK;
+    float* dV;
+    float* deta;
+    float* dW0;
+    float* dgamma;
+    float* dbeta;
+};
+size_t bwd_workspace_bytes(int B, int H, int N, int b);
+hipError_t launch_bwd_linear(const BwdArgs& a, hipStream_t stream);
+
 // Whole-layer stages around the inner model (head width 64, D % 64 == 0).
 struct LayerArgs {
     int B, N, D, H;

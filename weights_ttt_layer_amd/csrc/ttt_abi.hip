@@ -383,4 +383,88 @@ int ttt_layer_fwd(int kind, int B, int N, int D, int H, int d, int b, const void
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
+size_t ttt_linear_bwd_workspace_bytes(int kind, int qkv_dtype, int B, int H, int N, int d, int b)
+{
+    if (kind != TTT_LINEAR_PLAIN && kind != TTT_LINEAR_LN) return 0;
+    if (qkv_dtype != TTT_DTYPE_F32 && qkv_dtype != TTT_DTYPE_BF16) return 0;
+    if (B < 1 || H < 1 || N < 1 || d != SMALLB_D || b < 1 || b > SMALLB_MAX_B) return 0;
+    if ((size_t)B * (size_t)H > (size_t)INT32_MAX) return 0;
+    return ttt::bwd_workspace_bytes(B, H, N, b);
+}
+
+int ttt_linear_bwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b, const void* Q, const void* K,
+                   const void* V, const float* eta, float eta_const, const float* W0, const float* ln_gamma,
+                   const float* ln_beta, float ln_eps, const float* dZ, const float* dW_end, float* dQ, float* dK,
+                   float* dV, float* deta, float* dW0, float* dgamma, float* dbeta, void* workspace,
+                   size_t workspace_bytes, void* hip_stream)
+{
+    if (kind != TTT_LINEAR_PLAIN && kind != TTT_LINEAR_LN) return TTT_ERR_INVALID_ARGUMENT;
+    if (qkv_dtype != TTT_DTYPE_F32 && qkv_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARGUMENT;
+    if (B < 1 || H < 1 || N < 1 || d < 1 || b < 1) return TTT_ERR_INVALID_ARGUMENT;
+    if (!Q || !K || !V || !W0 || !dZ || !dQ || !dK || !dV || !deta || !dW0 || !workspace)
+        return TTT_ERR_INVALID_ARGUMENT;
+    const bool ln = kind == TTT_LINEAR_LN;
+    if (ln && (!ln_gamma || !ln_beta || !dgamma || !dbeta || !(ln_eps >= 0.f))) return TTT_ERR_INVALID_ARGUMENT;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(W0, 16) || !aligned(dZ, 16) ||
+        (dW_end && !aligned(dW_end, 16)) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) ||
+        !aligned(deta, 4) || !aligned(dW0, 16) || (eta && !aligned(eta, 4)) || !aligned(workspace, 256))
+        return TTT_ERR_INVALID_ARGUMENT;
+    if (ln && (!aligned(ln_gamma, 16) || !aligned(ln_beta, 16) || !aligned(dgamma, 4) || !aligned(dbeta, 4)))
+        return TTT_ERR_INVALID_ARGUMENT;
+    const size_t units = (size_t)B * (size_t)H;
+    const size_t tok = units * (size_t)N;
+    if (units > (size_t)INT32_MAX || tok / units != (size_t)N) return TTT_ERR_INVALID_ARGUMENT;
+    if (d != SMALLB_D || b > SMALLB_MAX_B) return TTT_ERR_UNSUPPORTED;
+    const size_t need = ttt::bwd_workspace_bytes(B, H, N, b);
+    if (workspace_bytes < need) return TTT_ERR_WORKSPACE_TOO_SMALL;
+
+    const size_t qkv_bytes = tok * (size_t)d * elem_size(qkv_dtype), f_bytes = tok * (size_t)d * 4;
+    const size_t w_bytes = units * (size_t)d * (size_t)d * 4, e_bytes = tok * 4, hv_bytes = (size_t)H * d * 4;
+    // outputs: disjoint from each other, from every input and from the workspace
+    const void* outs[7] = {dQ, dK, dV, deta, dW0, ln ? dgamma : nullptr, ln ? dbeta : nullptr};
+    const size_t out_bytes[7] = {f_bytes, f_bytes, f_bytes, e_bytes, w_bytes, hv_bytes, hv_bytes};
+    const void* ins[10] = {Q, K, V, eta, W0, ln ? ln_gamma : nullptr, ln ? ln_beta : nullptr, dZ, dW_end, workspace};
+    const size_t in_bytes[10] = {qkv_bytes, qkv_bytes, qkv_bytes, e_bytes, w_bytes, hv_bytes, hv_bytes, f_bytes,
+                                 w_bytes, need};
+    for (int i = 0; i < 7; ++i) {
+        for (int j = 0; j < 10; ++j)
+            if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return TTT_ERR_INVALID_ARGUMENT;
+        for (int j = i + 1; j < 7; ++j)
+            if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return TTT_ERR_INVALID_ARGUMENT;
+    }
+    for (int j = 0; j < 9; ++j)
+        if (overlaps(workspace, need, ins[j], in_bytes[j])) return TTT_ERR_INVALID_ARGUMENT;
+
+    ttt::BwdArgs a{};
+    a.f.kind = kind;
+    a.f.dtype = qkv_dtype;
+    a.f.B = B;
+    a.f.H = H;
+    a.f.N = N;
+    a.f.d = d;
+    a.f.b = b;
+    a.f.Q = Q;
+    a.f.K = K;
+    a.f.V = V;
+    a.f.eta = eta;
+    a.f.eta_const = eta_const;
+    a.f.W0 = W0;
+    a.f.gamma = ln_gamma;
+    a.f.beta = ln_beta;
+    a.f.eps = ln_eps;
+    a.f.workspace = workspace;
+    a.f.workspace_bytes = workspace_bytes;
+    a.dZ = dZ;
+    a.dW_end = dW_end;
+    a.dQ = dQ;
+    a.dK = dK;
+    a.dV = dV;
+    a.deta = deta;
+    a.dW0 = dW0;
+    a.dgamma = dgamma;
+    a.dbeta = dbeta;
+    const hipError_t err = ttt::launch_bwd_linear(a, reinterpret_cast<hipStream_t>(hip_stream));
+    return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
 }  // extern "C"

@@ -203,6 +203,16 @@ def generate(wl: Workload, seed: int) -> Inputs:
     return Inputs(wl, q, k, v, eta, wl.eta_const, w0, w1, w2, gamma, beta)
 
 
+def upstream_grads(wl: Workload, seed: int):
+    """Gradients of a scalar objective with respect to the forward's outputs, for
+    backward tests: dZ ~ N(0,1) [B,H,N,d] and dW_end ~ N(0,1) [B,H,d,d], fp32,
+    drawn from PCG64(seed) in that order."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dz = rng.standard_normal((wl.B, wl.H, wl.N, wl.d)).astype(np.float32)
+    dw = rng.standard_normal((wl.B, wl.H, wl.d, wl.d)).astype(np.float32)
+    return dz, dw
+
+
 def workload_inputs(index: int) -> Inputs:
     """Inputs of the index-th named workload with its documented seed."""
     return generate(WORKLOADS[index], SEED_BASE + index)
