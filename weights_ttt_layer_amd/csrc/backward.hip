@@ -38,9 +38,11 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
 }
 
 // sum_k A(i, k) B(k, j) for a 16 x 16 tile, k < KD (a multiple of 16), as four
-// independent accumulation chains. Lane l supplies A(l % 16, k) and B(k, l % 16)
-// with k = 4 u + l / 16 of each group of 16; the result is in the C layout
-// (lane l: rows 4 (l / 16) + r, column l % 16).
+// independent accumulation chains. The accessors return four consecutive k:
+// a(i, k) = A(i, k .. k+3), b(k, j) = B(k .. k+3, j). Lane l supplies row / column
+// l % 16 at k = k0 + 4 (l / 16) + u to product u, so an operand stored with k
+// contiguous is one 16-byte read. The result is in the C layout (lane l: rows
+// 4 (l / 16) + r, column l % 16).
 template <int KD, class FA, class FB>
 __device__ __forceinline__ f32x4 tile_mm(FA a, FB b, int lane)
 {
@@ -48,12 +50,25 @@ __device__ __forceinline__ f32x4 tile_mm(FA a, FB b, int lane)
     f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, p2 = p0, p3 = p0;
 #pragma unroll
     for (int k0 = 0; k0 < KD; k0 += 16) {
-        p0 = mfma4(a(i, k0 + kq), b(k0 + kq, i), p0);
-        p1 = mfma4(a(i, k0 + 4 + kq), b(k0 + 4 + kq, i), p1);
-        p2 = mfma4(a(i, k0 + 8 + kq), b(k0 + 8 + kq, i), p2);
-        p3 = mfma4(a(i, k0 + 12 + kq), b(k0 + 12 + kq, i), p3);
+        const float4 av = a(i, k0 + 4 * kq), bv = b(k0 + 4 * kq, i);
+        p0 = mfma4(av.x, bv.x, p0);
+        p1 = mfma4(av.y, bv.y, p1);
+        p2 = mfma4(av.z, bv.z, p2);
+        p3 = mfma4(av.w, bv.w, p3);
     }
     return (p0 + p1) + (p2 + p3);
+}
+
+// Operand accessors: rows of a row-major tile (k contiguous), or a column of
+// one (k strided).
+#define ROW4(M, i, k) (*reinterpret_cast<const float4*>(&(M)[i][k]))
+#define COL4(M, k, j) make_float4((M)[k][j], (M)[(k) + 1][j], (M)[(k) + 2][j], (M)[(k) + 3][j])
+
+// C-layout tile stored transposed (row-major m^T)
+__device__ __forceinline__ void st_tile_t(float* m, int stride, int r0, int c0, const f32x4& v, int lane)
+{
+    const int j = c0 + (lane & 15), i0 = r0 + 4 * (lane >> 4);
+    *reinterpret_cast<float4*>(&m[j * stride + i0]) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
 // C-layout tile <-> LDS (row-major, `stride` floats per row), rows r0.., cols c0..
@@ -75,7 +90,9 @@ __device__ __forceinline__ void st_tile(float* m, int stride, int r0, int c0, co
 
 struct alignas(16) BwdSmem {
     float W[BD][LS];     // W_c (pass 2) / the running state (pass 1)
+    float WT[BD][LS];    // its transpose
     float dW[BD][LS];    // gradient with respect to the state at the chunk boundary
+    float dWT[BD][LS];   // its transpose
     float K[BR][LS], Q[BR][LS], V[BR][LS], dZ[BR][LS];
     float H[BR][LS];     // K W_c
     float HQ[BR][LS];    // Q W_c - A G
@@ -90,8 +107,8 @@ struct alignas(16) BwdSmem {
     float P[BR][SS];     // dhq_t . g_s
     float DA[BR][SS];    // d a_ts (causal part)
     float C2[BR][SS];    // d eta_s contributions of the causal term, per t
-    float eta[BR];
-    float deta[BR];
+    alignas(16) float eta[BR];
+    alignas(16) float deta[BR];
     float red[2][BR][BD];
 };
 
@@ -193,25 +210,55 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
     }
     float pg[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};   // dgamma, dbeta partials
 
-    // rows [t0, t0 + n) of a token stream into an LDS tile (zero past n)
-    auto load_rows = [&](float (*dst)[LS], const S* src, int t0, int n) {
-        const float4 v = r < n ? load4(src + (tok0 + t0 + r) * BD + j0) : make_float4(0.f, 0.f, 0.f, 0.f);
-        put4(dst[r], j0, v);
+    // this thread's four entries of row r of a token stream (zero past n)
+    auto fetch_row = [&](const S* src, int t0, int n) {
+        return r < n ? load4(src + (tok0 + t0 + r) * BD + j0) : make_float4(0.f, 0.f, 0.f, 0.f);
     };
-    auto load_eta = [&](int t0, int n) {
-        if (tid < BR) sm.eta[tid] = tid < n ? (etag ? etag[tok0 + t0 + tid] : eta_const) : 0.f;
+    auto fetch_eta = [&](int t0, int n) {
+        return tid < n ? (etag ? etag[tok0 + t0 + tid] : eta_const) : 0.f;
     };
+    // this thread's four float4 of a 64 x 64 fp32 matrix
+    auto fetch_mat = [&](const float* src, float4 (&m4)[4]) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int i = tid + BT * m, row = i >> 4, col = (i & 15) * 4;
+            m4[m] = src ? get4(src + row * BD, col) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    // ... into LDS, with its transpose
+    auto put_mat = [&](float (*M)[LS], float (*MT)[LS], const float4 (&m4)[4]) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int i = tid + BT * m, row = i >> 4, col = (i & 15) * 4;
+            put4(M[row], col, m4[m]);
+            MT[col][row] = m4[m].x;
+            MT[col + 1][row] = m4[m].y;
+            MT[col + 2][row] = m4[m].z;
+            MT[col + 3][row] = m4[m].w;
+        }
+    };
+    // Operands of the next chunk are requested while the current one is
+    // processed; they wait in these registers.
+    float4 pk, pq, pv, pz, pw[4];
+    float pe;
 
     // ---------------- pass 1: chunk-start states ----------------
-    for (int i = tid; i < BD * BD / 4; i += BT) {
-        const int row = i >> 4, col = (i & 15) * 4;
-        put4(sm.W[row], col, get4(W0 + (size_t)unit * BD * BD + row * BD, col));
-    }
+    fetch_mat(W0 + (size_t)unit * BD * BD, pw);
+    put_mat(sm.W, sm.WT, pw);
+    pk = fetch_row(Kg, 0, min(b, N));
+    pv = fetch_row(Vg, 0, min(b, N));
+    pe = fetch_eta(0, min(b, N));
     for (int c = 0; c < C; ++c) {
         const int t0 = c * b, n = min(b, N - t0);
-        load_rows(sm.K, Kg, t0, n);
-        load_rows(sm.V, Vg, t0, n);
-        load_eta(t0, n);
+        put4(sm.K[r], j0, pk);
+        put4(sm.V[r], j0, pv);
+        if (tid < BR) sm.eta[tid] = pe;
+        if (c + 1 < C) {
+            const int t1 = t0 + b, n1 = min(b, N - t1);
+            pk = fetch_row(Kg, t1, n1);
+            pv = fetch_row(Vg, t1, n1);
+            pe = fetch_eta(t1, n1);
+        }
         __syncthreads();
         for (int i = tid; i < BD * BD / 4; i += BT) {
             const int row = i >> 4, col = (i & 15) * 4;
@@ -219,8 +266,8 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
         }
         // H = K W
         {
-            const f32x4 t = tile_mm<BD>([&](int i, int k) { return sm.K[i][k]; },
-                                        [&](int k, int j) { return sm.W[k][16 * w + j]; }, lane);
+            const f32x4 t = tile_mm<BD>([&](int i, int k) { return ROW4(sm.K, i, k); },
+                                        [&](int k, int j) { return ROW4(sm.WT, 16 * w + j, k); }, lane);
             st_tile(&sm.H[0][0], LS, 0, 16 * w, t, lane);
         }
         __syncthreads();
@@ -239,9 +286,10 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
             f32x4 acc = ld_tile(&sm.W[0][0], LS, 16 * w, 16 * tj, lane);
-            acc -= tile_mm<BR>([&](int i, int k) { return sm.K[k][16 * w + i]; },
-                               [&](int k, int j) { return sm.G[k][16 * tj + j]; }, lane);
+            acc -= tile_mm<BR>([&](int i, int k) { return COL4(sm.K, k, 16 * w + i); },
+                               [&](int k, int j) { return COL4(sm.G, k, 16 * tj + j); }, lane);
             st_tile(&sm.W[0][0], LS, 16 * w, 16 * tj, acc, lane);
+            st_tile_t(&sm.WT[0][0], LS, 16 * w, 16 * tj, acc, lane);
         }
         __syncthreads();
     }
@@ -250,40 +298,45 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
     __syncthreads();
 
     // ---------------- pass 2: reverse sweep ----------------
-    for (int i = tid; i < BD * BD / 4; i += BT) {
-        const int row = i >> 4, col = (i & 15) * 4;
-        put4(sm.dW[row], col, dWend ? get4(dWend + (size_t)unit * BD * BD + row * BD, col)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f));
-    }
+    fetch_mat(dWend ? dWend + (size_t)unit * BD * BD : nullptr, pw);
+    put_mat(sm.dW, sm.dWT, pw);
+    auto fetch2 = [&](int c) {
+        const int t0 = c * b, n = min(b, N - t0);
+        pk = fetch_row(Kg, t0, n);
+        pq = fetch_row(Qg, t0, n);
+        pv = fetch_row(Vg, t0, n);
+        pz = r < n ? get4(dZg + (tok0 + t0 + r) * BD, j0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        pe = fetch_eta(t0, n);
+        fetch_mat(ck + (size_t)c * BD * BD, pw);
+    };
+    fetch2(C - 1);
     for (int c = C - 1; c >= 0; --c) {
         const int t0 = c * b, n = min(b, N - t0);
-        // A: operands of the chunk
-        load_rows(sm.K, Kg, t0, n);
-        load_rows(sm.Q, Qg, t0, n);
-        load_rows(sm.V, Vg, t0, n);
-        put4(sm.dZ[r], j0, r < n ? get4(dZg + (tok0 + t0 + r) * BD, j0) : make_float4(0.f, 0.f, 0.f, 0.f));
-        load_eta(t0, n);
-        for (int i = tid; i < BD * BD / 4; i += BT) {
-            const int row = i >> 4, col = (i & 15) * 4;
-            put4(sm.W[row], col, get4(ck + (size_t)c * BD * BD + row * BD, col));
-        }
+        // A: operands of the chunk (requested one chunk ahead)
+        put4(sm.K[r], j0, pk);
+        put4(sm.Q[r], j0, pq);
+        put4(sm.V[r], j0, pv);
+        put4(sm.dZ[r], j0, pz);
+        if (tid < BR) sm.eta[tid] = pe;
+        put_mat(sm.W, sm.WT, pw);
+        if (c > 0) fetch2(c - 1);
         __syncthreads();
         // B: H = K W_c, HQ = Q W_c, KD = K dW_{c+1}, S = Q K^T
         {
             const int cw = 16 * w;
-            st_tile(&sm.H[0][0], LS, 0, cw,
-                    tile_mm<BD>([&](int i, int k) { return sm.K[i][k]; }, [&](int k, int j) { return sm.W[k][cw + j]; },
-                                lane), lane);
-            st_tile(&sm.HQ[0][0], LS, 0, cw,
-                    tile_mm<BD>([&](int i, int k) { return sm.Q[i][k]; }, [&](int k, int j) { return sm.W[k][cw + j]; },
-                                lane), lane);
-            st_tile(&sm.KD[0][0], LS, 0, cw,
-                    tile_mm<BD>([&](int i, int k) { return sm.K[i][k]; }, [&](int k, int j) { return sm.dW[k][cw + j]; },
-                                lane), lane);
+            const f32x4 th = tile_mm<BD>([&](int i, int k) { return ROW4(sm.K, i, k); },
+                                         [&](int k, int j) { return ROW4(sm.WT, cw + j, k); }, lane);
+            const f32x4 tq = tile_mm<BD>([&](int i, int k) { return ROW4(sm.Q, i, k); },
+                                         [&](int k, int j) { return ROW4(sm.WT, cw + j, k); }, lane);
+            const f32x4 tk = tile_mm<BD>([&](int i, int k) { return ROW4(sm.K, i, k); },
+                                         [&](int k, int j) { return ROW4(sm.dWT, cw + j, k); }, lane);
+            st_tile(&sm.H[0][0], LS, 0, cw, th, lane);
+            st_tile(&sm.HQ[0][0], LS, 0, cw, tq, lane);
+            st_tile(&sm.KD[0][0], LS, 0, cw, tk, lane);
             if (w == 0)
                 st_tile(&sm.S[0][0], SS, 0, 0,
-                        tile_mm<BD>([&](int i, int k) { return sm.Q[i][k]; }, [&](int k, int j) { return sm.K[j][k]; },
-                                    lane), lane);
+                        tile_mm<BD>([&](int i, int k) { return ROW4(sm.Q, i, k); },
+                                    [&](int k, int j) { return ROW4(sm.K, j, k); }, lane), lane);
         }
         __syncthreads();
         // C: g_s at W_c
@@ -300,12 +353,17 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
         {
             const int cw = 16 * w;
             f32x4 acc = ld_tile(&sm.HQ[0][0], LS, 0, cw, lane);
-            acc -= tile_mm<BR>([&](int i, int k) { return k <= i ? sm.S[i][k] * sm.eta[k] : 0.f; },
-                               [&](int k, int j) { return sm.G[k][cw + j]; }, lane);
+            acc -= tile_mm<BR>(
+                [&](int i, int k) {
+                    const float4 s4 = ROW4(sm.S, i, k), e4 = *reinterpret_cast<const float4*>(&sm.eta[k]);
+                    return make_float4(k <= i ? s4.x * e4.x : 0.f, k + 1 <= i ? s4.y * e4.y : 0.f,
+                                       k + 2 <= i ? s4.z * e4.z : 0.f, k + 3 <= i ? s4.w * e4.w : 0.f);
+                },
+                [&](int k, int j) { return COL4(sm.G, k, cw + j); }, lane);
             st_tile(&sm.HQ[0][0], LS, 0, cw, acc, lane);
             st_tile(&sm.GD[0][0], LS, 0, cw,
-                    tile_mm<BD>([&](int i, int k) { return sm.G[i][k]; }, [&](int k, int j) { return sm.dW[cw + j][k]; },
-                                lane), lane);
+                    tile_mm<BD>([&](int i, int k) { return ROW4(sm.G, i, k); },
+                                [&](int k, int j) { return ROW4(sm.dW, cw + j, k); }, lane), lane);
         }
         __syncthreads();
         // E: output stage, and the terms of W_{c+1} = W_c - sum_s eta_s k_s^T g_s
@@ -349,17 +407,23 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
         {
             const int cw = 16 * w;
             f32x4 acc = ld_tile(&sm.dQ[0][0], LS, 0, cw, lane);
-            acc += tile_mm<BD>([&](int i, int k) { return sm.dHq[i][k]; }, [&](int k, int j) { return sm.W[cw + j][k]; },
-                               lane);
+            acc += tile_mm<BD>([&](int i, int k) { return ROW4(sm.dHq, i, k); },
+                               [&](int k, int j) { return ROW4(sm.W, cw + j, k); }, lane);
             st_tile(&sm.dQ[0][0], LS, 0, cw, acc, lane);
             f32x4 ag = ld_tile(&sm.dG[0][0], LS, 0, cw, lane);
-            ag -= tile_mm<BR>([&](int i, int k) { return i <= k ? sm.S[k][i] * sm.eta[i] : 0.f; },
-                              [&](int k, int j) { return sm.dHq[k][cw + j]; }, lane);
+            ag -= tile_mm<BR>(
+                [&](int i, int k) {
+                    const float4 s4 = COL4(sm.S, k, i);
+                    const float e = sm.eta[i];
+                    return make_float4(i <= k ? s4.x * e : 0.f, i <= k + 1 ? s4.y * e : 0.f,
+                                       i <= k + 2 ? s4.z * e : 0.f, i <= k + 3 ? s4.w * e : 0.f);
+                },
+                [&](int k, int j) { return COL4(sm.dHq, k, cw + j); }, lane);
             st_tile(&sm.dG[0][0], LS, 0, cw, ag, lane);
             if (w == 0)
                 st_tile(&sm.P[0][0], SS, 0, 0,
-                        tile_mm<BD>([&](int i, int k) { return sm.dHq[i][k]; }, [&](int k, int j) { return sm.G[j][k]; },
-                                    lane), lane);
+                        tile_mm<BD>([&](int i, int k) { return ROW4(sm.dHq, i, k); },
+                                    [&](int k, int j) { return ROW4(sm.G, j, k); }, lane), lane);
         }
         __syncthreads();
         // G: causal-term derivatives, d(a_ts eta_s) = -dhq_t . g_s
@@ -375,12 +439,12 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
         {
             const int cw = 16 * w;
             f32x4 acc = ld_tile(&sm.dQ[0][0], LS, 0, cw, lane);
-            acc += tile_mm<BR>([&](int i, int k) { return sm.DA[i][k]; }, [&](int k, int j) { return sm.K[k][cw + j]; },
-                               lane);
+            acc += tile_mm<BR>([&](int i, int k) { return ROW4(sm.DA, i, k); },
+                               [&](int k, int j) { return COL4(sm.K, k, cw + j); }, lane);
             st_tile(&sm.dQ[0][0], LS, 0, cw, acc, lane);
             f32x4 ak = ld_tile(&sm.dK[0][0], LS, 0, cw, lane);
-            ak += tile_mm<BR>([&](int i, int k) { return sm.DA[k][i]; }, [&](int k, int j) { return sm.Q[k][cw + j]; },
-                              lane);
+            ak += tile_mm<BR>([&](int i, int k) { return COL4(sm.DA, k, i); },
+                              [&](int k, int j) { return COL4(sm.Q, k, cw + j); }, lane);
             st_tile(&sm.dK[0][0], LS, 0, cw, ak, lane);
             if (tid < BR) {
                 float a = 0.f;
@@ -460,16 +524,18 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
         {
             const int cw = 16 * w;
             f32x4 ak = ld_tile(&sm.dK[0][0], LS, 0, cw, lane);
-            ak += tile_mm<BD>([&](int i, int k) { return sm.dh[i][k]; }, [&](int k, int j) { return sm.W[cw + j][k]; },
-                              lane);
+            ak += tile_mm<BD>([&](int i, int k) { return ROW4(sm.dh, i, k); },
+                              [&](int k, int j) { return ROW4(sm.W, cw + j, k); }, lane);
             st_tile(&sm.dK[0][0], LS, 0, cw, ak, lane);
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj) {
                 f32x4 acc = ld_tile(&sm.dW[0][0], LS, cw, 16 * tj, lane);
-                acc += tile_mm<2 * BR>(
-                    [&](int i, int k) { return k < BR ? sm.Q[k][cw + i] : sm.K[k - BR][cw + i]; },
-                    [&](int k, int j) { return k < BR ? sm.dHq[k][16 * tj + j] : sm.dh[k - BR][16 * tj + j]; }, lane);
+                acc += tile_mm<BR>([&](int i, int k) { return COL4(sm.Q, k, cw + i); },
+                                   [&](int k, int j) { return COL4(sm.dHq, k, 16 * tj + j); }, lane);
+                acc += tile_mm<BR>([&](int i, int k) { return COL4(sm.K, k, cw + i); },
+                                   [&](int k, int j) { return COL4(sm.dh, k, 16 * tj + j); }, lane);
                 st_tile(&sm.dW[0][0], LS, cw, 16 * tj, acc, lane);
+                st_tile_t(&sm.dWT[0][0], LS, cw, 16 * tj, acc, lane);
             }
         }
         __syncthreads();
