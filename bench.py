@@ -18,7 +18,9 @@ starting or ending weights) and the single-token decode step of B*H = 768
 TTT-Linear+LN streams (d=64), each against the HBM roofline, and the whole
 layer (projections, key normalisation, inner TTT-Linear+LN, output LayerNorm +
 residual + output projection; B=8 N=2048 D=768 H=12 d=64 b=16) against the
-bf16 MFMA roofline of its GEMM work.
+bf16 MFMA roofline of its GEMM work, and the backward of the b = 16 workload
+(gradients with respect to Q, K, V, eta, W0, gamma, beta) against the fp32
+matrix-core peak.
 
 Prints ONE JSON line (stdout). Diagnostics go to stderr.
 """
@@ -231,6 +233,71 @@ def side_measurement(name: str, steps: int, warmup: int, variant: str):
             "roofline": roof}
 
 
+MFMA_F32_PEAK_TFS = 157.3     # MI355X dense fp32 matrix, TFLOP/s
+
+
+def bwd_algorithmic_flops(wl: wlm.Workload) -> int:
+    """FLOPs of one backward call (ttt_linear_bwd), per chunk of n rows: ten
+    products of an n x d by a d x d matrix (two to recompute the chunk-start
+    state; K W_c, Q W_c, K dW, G dW^T, dHq W^T, dh W^T, Q^T dHq, K^T dh) at
+    2 n d^2 each, and six causal n x n x d products (Q K^T, A G, dHq G^T,
+    A^T dHq, dA K, dA^T Q) at n (n+1) d each."""
+    d = wl.d
+    f = sum(20 * n * d * d + 6 * n * (n + 1) * d for n in chunk_rows(wl.N, wl.b))
+    return f * wl.B * wl.H
+
+
+def bwd_measurement(steps: int, warmup: int):
+    """Backward calls (ttt_linear_bwd) on the b = 16 benchmark workload with
+    seeded upstream gradients; inputs and outputs rotate over ROTATE copies."""
+    import torch
+    from weights_ttt_layer_amd import linear_bwd
+
+    idx = [w.name for w in wlm.WORKLOADS].index(DEFAULT_WORKLOAD)
+    wl = wlm.WORKLOADS[idx]
+    inp = wlm.workload_inputs(idx)
+    dev = torch.device("cuda:0")
+    dz, dw = wlm.upstream_grads(wl, 7)
+    base = wlm.to_device(inp, dev)
+    base["dz"] = torch.from_numpy(dz).to(dev)
+    base["dw"] = torch.from_numpy(dw).to(dev)
+    sets = [base] + [{k: (None if t is None else t.clone()) for k, t in base.items()} for _ in range(ROTATE - 1)]
+    stream = torch.cuda.current_stream()
+    kw = dict(b=wl.b, kind=wl.kind, eta_const=inp.eta_const, ln_eps=wl.ln_eps, stream=stream)
+
+    def step(i):
+        s = sets[i % ROTATE]
+        return linear_bwd(s["q"], s["k"], s["v"], s["w0"], s["dz"], s["eta"], dw_end=s["dw"],
+                          ln_gamma=s["gamma"], ln_beta=s["beta"], **kw)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        out = step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    finite = bool(torch.isfinite(out["dQ"]).all().item())
+    if not finite:
+        log(f"[bench] WARNING: non-finite backward output in {wl.name}")
+    del sets, base, out
+    torch.cuda.empty_cache()
+    sec = ms / 1e3
+    flops = bwd_algorithmic_flops(wl)
+    tokens = wl.B * wl.N
+    roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_F32_PEAK_TFS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    log(f"[bench] {wl.name} backward: {ms*1e3:.1f} us/step, {tokens/sec:.4g} tokens/s, "
+        f"{flops/sec/1e12:.2f} TFLOP/s algorithmic (fp32)")
+    return {"workload": wl.name, "variant": "backward", "value": tokens / sec, "unit": "tokens/s",
+            "ms_per_step": ms, "algorithmic_flops": flops, "dtype": "f32", "roofline": roof}
+
+
 def layer_algorithmic(wl: wlm.LayerWorkload):
     """Compulsory HBM bytes of one whole-layer call (read x, the four projection
     weights, eta, the state and the LayerNorm parameters; write y and the state)
@@ -382,6 +449,7 @@ def main():
             "block_after": side_measurement(LARGE_WORKLOAD, args.steps, args.warmup, "block_after"),
             "decode": side_measurement(DECODE_WORKLOAD, args.steps, args.warmup, "decode"),
             "layer": layer_measurement(args.steps, args.warmup),
+            "backward": bwd_measurement(max(3, args.steps // 5), min(args.warmup, 2)),
         }
 
     if args.copy_calibration:

@@ -49,7 +49,7 @@ KERNEL_SOURCES = {
 
 OUR_KERNELS = ("smallb_linear_kernel", "smallb_mlp_kernel", "lc_gram_kernel", "lc_scan_kernel",
                "lc_chunk_kernel", "lc_apply_kernel", "decode_kernel", "layer_gemm_kernel",
-               "layer_outprep_kernel")
+               "layer_outprep_kernel", "bwd_linear_kernel", "bwd_gamma_beta_kernel")
 
 # kernel-name prefixes launched by one call of each path
 PATH_KERNELS = {
