@@ -72,6 +72,25 @@ constexpr int vmcnt_imm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4
 
 enum { EPI_QKV = 0, EPI_ROWS = 1 };
 
+// Logical tile L -> (token block rt, output tile nt). Token blocks are taken in
+// super-rows of GR; inside one, output tiles in groups of GC, and inside a
+// group every (block, tile) pair. An XCD's contiguous range of logical tiles
+// then keeps a super-row of token rows resident in its L2 while the weight
+// rows stream past one group at a time, instead of the whole weight per block.
+constexpr int GR = 8, GC = 3;
+
+__device__ __forceinline__ void grouped_tile(int L, int row_tiles, int tiles_n, int& rt, int& nt)
+{
+    const int sr = L / (GR * tiles_n);
+    const int rows = min(GR, row_tiles - sr * GR);
+    const int rem = L - sr * GR * tiles_n;
+    const int cg = rem / (rows * GC);
+    const int cols = min(GC, tiles_n - cg * GC);
+    const int rem2 = rem - cg * rows * GC;
+    rt = sr * GR + rem2 / cols;
+    nt = cg * GC + rem2 % cols;
+}
+
 struct GemmArgs {
     int N, H;                    // tokens per sequence, heads
     int K, KW;                   // reduction length, wrap of the weight's k index
@@ -99,8 +118,8 @@ layer_gemm_kernel(GemmArgs g)
     constexpr int SA = TM * GK * 2, SB = TN * GK * 2;    // stage bytes
     __shared__ __attribute__((aligned(16))) char smem[NS * (SA + SB)];
 
-    const int L = xcd_tile(blockIdx.x, g.total);
-    const int nt = L % g.tiles_n, rt = L / g.tiles_n;
+    int rt, nt;
+    grouped_tile(xcd_tile(blockIdx.x, g.total), g.tiles_t * (g.total / (g.tiles_t * g.tiles_n)), g.tiles_n, rt, nt);
     const int bi = rt / g.tiles_t, t0 = (rt % g.tiles_t) * TM, n0 = nt * TN;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int h = lane >> 5, l32 = lane & 31;
