@@ -62,6 +62,8 @@ def case(kind, dtype, B, H, N, b, eta="sigmoid", seed=11):
     ("plain", "bf16", 2, 1, 50, 1, "const"),     # b = 1 (online), eta = NULL
     ("ln", "f32", 1, 1, 16, 16, "const"),        # a single chunk
     ("ln", "bf16", 2, 2, 300, 16, "sigmoid"),
+    ("ln", "f32", 1, 2, 1, 16, "sigmoid"),       # a single token
+    ("plain", "f32", 3, 1, 17, 16, "sigmoid"),   # one full chunk and a one-token tail
 ])
 def test_bwd_shapes(kind, dtype, B, H, N, b, eta):
     inp = case(kind, dtype, B, H, N, b, eta)

@@ -68,6 +68,8 @@ def case(kind, B, N, D, H, b, seed=3):
     ("ln", 3, 37, 64, 1, 5),         # one head, D = 64, short ragged sequences
     ("plain", 1, 300, 512, 8, 1),    # b = 1 (online steps)
     ("ln", 2, 256, 768, 12, 16),     # the model width of the named workload
+    ("ln", 1, 1, 128, 2, 16),        # a single token
+    ("plain", 1, 130, 1024, 16, 16), # H = 16, D = 1024
 ])
 def test_layer_shapes(kind, B, N, D, H, b):
     inp = case(kind, B, N, D, H, b)
