@@ -284,7 +284,8 @@ int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b,
  * on bf16 matrix cores with fp32 accumulation; the LayerNorm output enters W_O's
  * product as two bf16 terms (16 significant bits). Asynchronous on hip_stream;
  * validation on the host before any HIP call.
- * Supported: d = 64, 1 <= b <= 16, D a multiple of 64 (else TTT_ERR_UNSUPPORTED).
+ * Supported: d = 64, 1 <= b <= 16, D a multiple of 64, B*H*N < 2^27 (else
+ * TTT_ERR_UNSUPPORTED).
  */
 int ttt_layer_fwd(int kind, int B, int N, int D, int H, int d, int b,
                   const void* x, const void* Wq, const void* Wk, const void* Wv, const void* Wo,

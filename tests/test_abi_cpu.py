@@ -197,6 +197,7 @@ def test_layer_rejections(lib):
     assert layer_call(lib, d=128) == U
     assert layer_call(lib, b=17) == U
     assert layer_call(lib, D=96) == U
+    assert layer_call(lib, B=1024, N=1 << 20, H=8) == U                # B*H*N*16 beyond a 32-bit grid
     assert layer_call(lib) == binding.TTT_ERR_WORKSPACE_TOO_SMALL
     big = need
     assert layer_call(lib, y=ctypes.c_void_p(A + 64), ws_bytes=big) == E               # y overlaps x

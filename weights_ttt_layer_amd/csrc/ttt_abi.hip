@@ -327,6 +327,8 @@ int ttt_layer_fwd(int kind, int B, int N, int D, int H, int d, int b, const void
         return TTT_ERR_INVALID_ARGUMENT;
     if (d != SMALLB_D || b > SMALLB_MAX_B || D % 64 != 0 || (size_t)H * d * 3 > (size_t)INT32_MAX)
         return TTT_ERR_UNSUPPORTED;
+    // the output-operand kernel gives each (token, head) row 16 threads of a 32-bit grid
+    if ((size_t)B * H * N * 16 > (size_t)INT32_MAX) return TTT_ERR_UNSUPPORTED;
     const size_t region = ttt::layer_workspace_region_bytes(B, N, H);
     if (workspace_bytes < 5 * region) return TTT_ERR_WORKSPACE_TOO_SMALL;
 
