@@ -409,6 +409,77 @@ def cpu_baseline(wl: wlm.Workload, inp: wlm.Inputs, max_units: int, min_wall: fl
     }
 
 
+def _oracle_rate(run, tokens: int, sample: str, min_wall: float = 1.0):
+    """Best rate of `run` (the oracle on a bounded sample) over at least two runs
+    and `min_wall` seconds; `tokens` is what one run processes."""
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    times, total = [], 0.0
+    while len(times) < 2 or total < min_wall:
+        t0 = time.perf_counter()
+        run(threads)
+        times.append(time.perf_counter() - t0)
+        total += times[-1]
+    best = min(times)
+    return {"value": tokens / best, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sample}; best of {len(times)} runs ({best:.3f} s at best, {total:.1f} s wall)"}
+
+
+_LARGE_UNIT0 = None
+
+
+def _large_unit0():
+    """The large-chunk workload's first head, generated once."""
+    global _LARGE_UNIT0
+    if _LARGE_UNIT0 is None:
+        idx = [w.name for w in wlm.WORKLOADS].index(LARGE_WORKLOAD)
+        _LARGE_UNIT0 = (wlm.WORKLOADS[idx], wlm.workload_inputs(idx).unit(0, 0))
+    return _LARGE_UNIT0
+
+
+def cpu_baseline_side(kind: str):
+    """The oracle timed beside one of the side measurements, on a bounded sample
+    of the same workload."""
+    import oracle
+    if kind in ("b2048", "block_before", "block_after"):
+        wl, inp = _large_unit0()
+        mode = {"b2048": oracle.MINIBATCH, "block_before": oracle.BLOCK_BEFORE,
+                "block_after": oracle.BLOCK_AFTER}[kind]
+        args = (inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.eta_f64(), inp.f64("w0"), wl.b)
+        return _oracle_rate(lambda th: oracle.linear(mode, oracle.PLAIN, *args, nthreads=th), wl.N,
+                            f"fp64 oracle ({'mini-batch primal' if kind == 'b2048' else kind}) over one of "
+                            f"{wl.H} heads x {wl.N} tokens")
+    if kind == "decode":
+        idx = [w.name for w in wlm.WORKLOADS].index(DECODE_WORKLOAD)
+        wl = wlm.WORKLOADS[idx]
+        inp = wlm.workload_inputs(idx)
+        args = (inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.eta_f64(), inp.f64("w0"), 1, inp.f64("gamma"),
+                inp.f64("beta"), wl.ln_eps)
+        return _oracle_rate(lambda th: oracle.linear(oracle.ONLINE, oracle.LN, *args, nthreads=th), wl.B,
+                            f"fp64 oracle, one online step for all {wl.B * wl.H} streams")
+    if kind == "layer":
+        li = wlm.layer_workload_inputs(0)
+        wl = li.wl
+        s1 = slice(0, 1)
+        args = (li.f64("x")[s1], li.f64("wq"), li.f64("wk"), li.f64("wv"), li.f64("wo"), li.f64("eta")[s1],
+                li.f64("w0")[s1], wl.b, wl.H, li.f64("gamma"), li.f64("beta"), li.f64("gamma_o"),
+                li.f64("beta_o"), wl.ln_eps)
+        return _oracle_rate(lambda th: oracle.layer(oracle.LN, *args, nthreads=th), wl.N,
+                            f"fp64 oracle (numpy projections + C inner model) over 1 of {wl.B} sequences "
+                            f"x {wl.N} tokens")
+    if kind == "backward":
+        idx = [w.name for w in wlm.WORKLOADS].index(DEFAULT_WORKLOAD)
+        wl = wlm.WORKLOADS[idx]
+        inp = wlm.workload_inputs(idx)
+        dz, dw = wlm.upstream_grads(wl, 7)
+        s1 = slice(0, 1)
+        args = (inp.f64("q")[s1], inp.f64("k")[s1], inp.f64("v")[s1], inp.eta_f64()[s1], inp.f64("w0")[s1], wl.b,
+                dz[s1].astype(np.float64), dw[s1].astype(np.float64), inp.f64("gamma"), inp.f64("beta"),
+                wl.ln_eps)
+        return _oracle_rate(lambda th: oracle.linear_bwd(oracle.LN, *args, nthreads=th), wl.N,
+                            f"fp64 oracle backward over 1 of {wl.B} sequences x {wl.H} heads x {wl.N} tokens")
+    raise ValueError(kind)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -451,6 +522,13 @@ def main():
             "layer": layer_measurement(args.steps, args.warmup),
             "backward": bwd_measurement(max(3, args.steps // 5), min(args.warmup, 2)),
         }
+
+    if not args.no_cpu_baseline and next_rows is not None:
+        b2048["cpu_baseline"] = cpu_baseline_side("b2048")
+        for key in next_rows:
+            next_rows[key]["cpu_baseline"] = cpu_baseline_side(key)
+        log("[bench] side cpu baselines: " + ", ".join(
+            f"{k} {v['cpu_baseline']['value']:.3g}" for k, v in [("b2048", b2048), *next_rows.items()]))
 
     if args.copy_calibration:
         copy_calibration()
