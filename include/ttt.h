@@ -281,8 +281,9 @@ int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b,
  *                   at offsets 0, S, 2S, 3S; the last S bytes are scratch.
  * x and the four weights must be 16-byte aligned. y, W_end and the workspace
  * must not overlap any input or each other (W_end may equal W0). Products run
- * on bf16 matrix cores with fp32 accumulation; the LayerNorm output enters W_O's
- * product as two bf16 terms (16 significant bits). Asynchronous on hip_stream;
+ * on bf16 matrix cores with fp32 accumulation; the projected fp32 streams, the
+ * inner state and its gradients, and the LayerNorm output entering W_O's
+ * product are carried as two bf16 terms (16 significant bits). Asynchronous on hip_stream;
  * validation on the host before any HIP call.
  * Supported: d = 64, 1 <= b <= 16, D a multiple of 64, B*H*N < 2^27 (else
  * TTT_ERR_UNSUPPORTED).

@@ -29,8 +29,10 @@
 //    K^T Gt and (as Gt^T) the A operand of the causal term Gt^T tril(S)^T.
 //  * S^T = K Q^T is computed so that its C layout is exactly the B operand of
 //    Gt^T S^T.
-//  * fp32 operands are split into bf16 terms (2 for bf16 token streams, 3 for
-//    fp32 streams; fp32 token streams use 3 terms too).
+//  * fp32 operands (state, gradient, scores) are split into bf16 terms: 2 next
+//    to bf16 token streams, 3 next to fp32 streams, which use 3 terms too. A
+//    variant carries fp32 streams and fp32 operands in 2 terms (16 significant
+//    bits); the whole-layer path launches it for its projected streams.
 //  * Q/K/V/eta chunks are prefetched PF chunks ahead into a register ring and
 //    staged through double-buffered, row-padded LDS tiles. Per chunk: one
 //    workgroup barrier (plain) or two (LayerNorm: forward statistics together
@@ -68,7 +70,7 @@ __device__ __forceinline__ void store_ln_out(float* __restrict__ Zu, const f32x4
         *reinterpret_cast<float4*>(Zu + (size_t)(c0 + n) * D + fcol) = make_float4(z[0], z[1], z[2], z[3]);
 }
 
-template <int KIND, typename S>
+template <int KIND, typename S, int TIN = Stor<S>::TERMS>
 __global__ void __launch_bounds__(THREADS)
 smallb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __restrict__ Kg,
                      const S* __restrict__ Vg, const float* __restrict__ etag, float eta_const,
@@ -76,8 +78,9 @@ smallb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __r
                      const float* __restrict__ beta, float eps, float* __restrict__ Zg,
                      float* __restrict__ Wend)
 {
-    constexpr int TIN = Stor<S>::TERMS;               // terms of a token-stream operand
-    constexpr int TS = (TIN == 1) ? 2 : 3;            // terms of an fp32 operand
+    // TIN: terms of a token-stream operand; TS: terms of an fp32 operand (state,
+    // gradient, scores): two next to exact bf16 or two-term streams, else three
+    constexpr int TS = (TIN <= 2) ? 2 : 3;
     constexpr int STRIDE = Stor<S>::STRIDE;
     constexpr int PPT = (Pieces<S>::TOTAL + THREADS - 1) / THREADS;
 
@@ -348,11 +351,11 @@ smallb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __r
         for (int i = 0; i < 4; ++i) Wu[(16 * r + 4 * g + i) * D + col] = Wacc[r][i];
 }
 
-template <int KIND, typename S>
+template <int KIND, typename S, int TIN = Stor<S>::TERMS>
 hipError_t launch_typed(const LinearArgs& a, hipStream_t stream)
 {
     const int units = a.B * a.H;
-    hipLaunchKernelGGL((smallb_linear_kernel<KIND, S>), dim3(units), dim3(THREADS), 0, stream, a.H,
+    hipLaunchKernelGGL((smallb_linear_kernel<KIND, S, TIN>), dim3(units), dim3(THREADS), 0, stream, a.H,
                        a.N, a.b, static_cast<const S*>(a.Q), static_cast<const S*>(a.K),
                        static_cast<const S*>(a.V), a.eta, a.eta_const, a.W0, a.gamma, a.beta,
                        a.eps, a.Z, a.W_end);
@@ -366,6 +369,11 @@ hipError_t launch_smallb_linear(const LinearArgs& a, hipStream_t stream)
     if (a.dtype == 1)
         return a.kind == 1 ? launch_typed<1, uint16_t>(a, stream) : launch_typed<0, uint16_t>(a, stream);
     return a.kind == 1 ? launch_typed<1, float>(a, stream) : launch_typed<0, float>(a, stream);
+}
+
+hipError_t launch_smallb_linear_f32x2(const LinearArgs& a, hipStream_t stream)
+{
+    return a.kind == 1 ? launch_typed<1, float, 2>(a, stream) : launch_typed<0, float, 2>(a, stream);
 }
 
 }  // namespace ttt

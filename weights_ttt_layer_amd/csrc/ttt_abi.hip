@@ -380,7 +380,7 @@ int ttt_layer_fwd(int kind, int B, int N, int D, int H, int d, int b, const void
     a.y = y;
     hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
     hipError_t err = ttt::launch_layer_qkv(a, Qf, Kf, Vf, stream);
-    if (err == hipSuccess) err = ttt::launch_smallb_linear(inner, stream);
+    if (err == hipSuccess) err = ttt::launch_smallb_linear_f32x2(inner, stream);
     if (err == hipSuccess) err = ttt::launch_layer_out(a, Zf, Qf, Aext, stream);
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
