@@ -37,27 +37,32 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// sum_k A(i, k) B(k, j) for a 16 x 16 tile, k < KD (a multiple of 16), as four
-// independent accumulation chains. The accessors return four consecutive k:
-// a(i, k) = A(i, k .. k+3), b(k, j) = B(k .. k+3, j). Lane l supplies row / column
-// l % 16 at k = k0 + 4 (l / 16) + u to product u, so an operand stored with k
-// contiguous is one 16-byte read. The result is in the C layout (lane l: rows
-// 4 (l / 16) + r, column l % 16).
-template <int KD, class FA, class FB>
-__device__ __forceinline__ f32x4 tile_mm(FA a, FB b, int lane)
+// acc +/- sum_k A(i, k) B(k, j) for a 16 x 16 tile, k < KD (a multiple of 16).
+// The accessors return four consecutive k: a(i, k) = A(i, k .. k+3),
+// b(k, j) = B(k .. k+3, j). Lane l supplies row / column l % 16 at
+// k = k0 + 4 (l / 16) + u to product u, so an operand stored with k contiguous is
+// one 16-byte read. acc and the result are in the C layout (lane l: rows
+// 4 (l / 16) + r, column l % 16). One accumulation chain: an fp32 16x16x4
+// product keeps the matrix pipe busy for as long as its result takes, so
+// independent chains would add no throughput, only moves and sums.
+template <int KD, bool SUB = false, class FA, class FB>
+__device__ __forceinline__ f32x4 tile_mm(f32x4 acc, FA a, FB b, int lane)
 {
     const int i = lane & 15, kq = lane >> 4;
-    f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, p2 = p0, p3 = p0;
 #pragma unroll
     for (int k0 = 0; k0 < KD; k0 += 16) {
-        const float4 av = a(i, k0 + 4 * kq), bv = b(k0 + 4 * kq, i);
-        p0 = mfma4(av.x, bv.x, p0);
-        p1 = mfma4(av.y, bv.y, p1);
-        p2 = mfma4(av.z, bv.z, p2);
-        p3 = mfma4(av.w, bv.w, p3);
+        float4 av = a(i, k0 + 4 * kq);
+        const float4 bv = b(k0 + 4 * kq, i);
+        if constexpr (SUB) av = make_float4(-av.x, -av.y, -av.z, -av.w);
+        acc = mfma4(av.x, bv.x, acc);
+        acc = mfma4(av.y, bv.y, acc);
+        acc = mfma4(av.z, bv.z, acc);
+        acc = mfma4(av.w, bv.w, acc);
     }
-    return (p0 + p1) + (p2 + p3);
+    return acc;
 }
+
+constexpr f32x4 ZERO4 = {0.f, 0.f, 0.f, 0.f};
 
 // Operand accessors: rows of a row-major tile (k contiguous), or a column of
 // one (k strided).
@@ -103,6 +108,7 @@ struct alignas(16) BwdSmem {
     float dHq[BR][LS];
     float dQ[BR][LS], dK[BR][LS], dV[BR][LS];
     float dh[BR][LS];
+    float dKd[BR][LS];   // direct terms of dK from the preactivation-gradient backward
     float S[BR][SS];     // a_ts = q_t . k_s
     float P[BR][SS];     // dhq_t . g_s
     float DA[BR][SS];    // d a_ts (causal part)
@@ -266,7 +272,7 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
         }
         // H = K W
         {
-            const f32x4 t = tile_mm<BD>([&](int i, int k) { return ROW4(sm.K, i, k); },
+            const f32x4 t = tile_mm<BD>(ZERO4, [&](int i, int k) { return ROW4(sm.K, i, k); },
                                         [&](int k, int j) { return ROW4(sm.WT, 16 * w + j, k); }, lane);
             st_tile(&sm.H[0][0], LS, 0, 16 * w, t, lane);
         }
@@ -286,7 +292,7 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
             f32x4 acc = ld_tile(&sm.W[0][0], LS, 16 * w, 16 * tj, lane);
-            acc -= tile_mm<BR>([&](int i, int k) { return COL4(sm.K, k, 16 * w + i); },
+            acc = tile_mm<BR, true>(acc, [&](int i, int k) { return COL4(sm.K, k, 16 * w + i); },
                                [&](int k, int j) { return COL4(sm.G, k, 16 * tj + j); }, lane);
             st_tile(&sm.W[0][0], LS, 16 * w, 16 * tj, acc, lane);
             st_tile_t(&sm.WT[0][0], LS, 16 * w, 16 * tj, acc, lane);
@@ -324,18 +330,18 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
         // B: H = K W_c, HQ = Q W_c, KD = K dW_{c+1}, S = Q K^T
         {
             const int cw = 16 * w;
-            const f32x4 th = tile_mm<BD>([&](int i, int k) { return ROW4(sm.K, i, k); },
+            const f32x4 th = tile_mm<BD>(ZERO4, [&](int i, int k) { return ROW4(sm.K, i, k); },
                                          [&](int k, int j) { return ROW4(sm.WT, cw + j, k); }, lane);
-            const f32x4 tq = tile_mm<BD>([&](int i, int k) { return ROW4(sm.Q, i, k); },
+            const f32x4 tq = tile_mm<BD>(ZERO4, [&](int i, int k) { return ROW4(sm.Q, i, k); },
                                          [&](int k, int j) { return ROW4(sm.WT, cw + j, k); }, lane);
-            const f32x4 tk = tile_mm<BD>([&](int i, int k) { return ROW4(sm.K, i, k); },
+            const f32x4 tk = tile_mm<BD>(ZERO4, [&](int i, int k) { return ROW4(sm.K, i, k); },
                                          [&](int k, int j) { return ROW4(sm.dWT, cw + j, k); }, lane);
             st_tile(&sm.H[0][0], LS, 0, cw, th, lane);
             st_tile(&sm.HQ[0][0], LS, 0, cw, tq, lane);
             st_tile(&sm.KD[0][0], LS, 0, cw, tk, lane);
             if (w == 0)
                 st_tile(&sm.S[0][0], SS, 0, 0,
-                        tile_mm<BD>([&](int i, int k) { return ROW4(sm.Q, i, k); },
+                        tile_mm<BD>(ZERO4, [&](int i, int k) { return ROW4(sm.Q, i, k); },
                                     [&](int k, int j) { return ROW4(sm.K, j, k); }, lane), lane);
         }
         __syncthreads();
@@ -353,7 +359,7 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
         {
             const int cw = 16 * w;
             f32x4 acc = ld_tile(&sm.HQ[0][0], LS, 0, cw, lane);
-            acc -= tile_mm<BR>(
+            acc = tile_mm<BR, true>(acc, 
                 [&](int i, int k) {
                     const float4 s4 = ROW4(sm.S, i, k), e4 = *reinterpret_cast<const float4*>(&sm.eta[k]);
                     return make_float4(k <= i ? s4.x * e4.x : 0.f, k + 1 <= i ? s4.y * e4.y : 0.f,
@@ -362,7 +368,7 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
                 [&](int k, int j) { return COL4(sm.G, k, cw + j); }, lane);
             st_tile(&sm.HQ[0][0], LS, 0, cw, acc, lane);
             st_tile(&sm.GD[0][0], LS, 0, cw,
-                    tile_mm<BD>([&](int i, int k) { return ROW4(sm.G, i, k); },
+                    tile_mm<BD>(ZERO4, [&](int i, int k) { return ROW4(sm.G, i, k); },
                                 [&](int k, int j) { return ROW4(sm.dW, cw + j, k); }, lane), lane);
         }
         __syncthreads();
@@ -407,11 +413,11 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
         {
             const int cw = 16 * w;
             f32x4 acc = ld_tile(&sm.dQ[0][0], LS, 0, cw, lane);
-            acc += tile_mm<BD>([&](int i, int k) { return ROW4(sm.dHq, i, k); },
+            acc = tile_mm<BD>(acc, [&](int i, int k) { return ROW4(sm.dHq, i, k); },
                                [&](int k, int j) { return ROW4(sm.W, cw + j, k); }, lane);
             st_tile(&sm.dQ[0][0], LS, 0, cw, acc, lane);
             f32x4 ag = ld_tile(&sm.dG[0][0], LS, 0, cw, lane);
-            ag -= tile_mm<BR>(
+            ag = tile_mm<BR, true>(ag, 
                 [&](int i, int k) {
                     const float4 s4 = COL4(sm.S, k, i);
                     const float e = sm.eta[i];
@@ -422,11 +428,13 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
             st_tile(&sm.dG[0][0], LS, 0, cw, ag, lane);
             if (w == 0)
                 st_tile(&sm.P[0][0], SS, 0, 0,
-                        tile_mm<BD>([&](int i, int k) { return ROW4(sm.dHq, i, k); },
+                        tile_mm<BD>(ZERO4, [&](int i, int k) { return ROW4(sm.dHq, i, k); },
                                     [&](int k, int j) { return ROW4(sm.G, j, k); }, lane), lane);
         }
         __syncthreads();
-        // G: causal-term derivatives, d(a_ts eta_s) = -dhq_t . g_s
+        // G: causal-term derivatives, d(a_ts eta_s) = -dhq_t . g_s, and, independent of
+        // them, the backward of g = d l / d h: dh and the direct terms of dK, dV,
+        // dgamma, dbeta
         {
             const int t = tid >> 4, s = tid & 15;
             const bool on = s <= t && t < n;
@@ -434,27 +442,6 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
             sm.DA[t][s] = dcoef * sm.eta[s];
             sm.C2[t][s] = dcoef * sm.S[t][s];
         }
-        __syncthreads();
-        // H: dQ += DA K, dK += DA^T Q; d eta_s += sum_t C2[t][s]
-        {
-            const int cw = 16 * w;
-            f32x4 acc = ld_tile(&sm.dQ[0][0], LS, 0, cw, lane);
-            acc += tile_mm<BR>([&](int i, int k) { return ROW4(sm.DA, i, k); },
-                               [&](int k, int j) { return COL4(sm.K, k, cw + j); }, lane);
-            st_tile(&sm.dQ[0][0], LS, 0, cw, acc, lane);
-            f32x4 ak = ld_tile(&sm.dK[0][0], LS, 0, cw, lane);
-            ak += tile_mm<BR>([&](int i, int k) { return COL4(sm.DA, k, i); },
-                              [&](int k, int j) { return COL4(sm.Q, k, cw + j); }, lane);
-            st_tile(&sm.dK[0][0], LS, 0, cw, ak, lane);
-            if (tid < BR) {
-                float a = 0.f;
-#pragma unroll
-                for (int t = 0; t < BR; ++t) a += sm.C2[t][tid];
-                sm.deta[tid] += a;
-            }
-        }
-        __syncthreads();
-        // I: backward of g = d l / d h: dh, and the direct terms of dK, dV, dgamma, dbeta
         {
             float dg[4], dh[4], dv[4], dkd[4] = {0.f, 0.f, 0.f, 0.f};
             to4(get4(sm.dG[r], j0), dg);
@@ -511,31 +498,40 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
                 for (int e = 0; e < 4; ++e) dh[e] = dc[e] - mdc;
             }
             const bool live = r < n;
-            float dk[4];
-            to4(get4(sm.dK[r], j0), dk);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dk[e] += dkd[e];
-            put4(sm.dK[r], j0, of4(dk));
+            put4(sm.dKd[r], j0, of4(dkd));
             put4(sm.dV[r], j0, live ? of4(dv) : make_float4(0.f, 0.f, 0.f, 0.f));
             put4(sm.dh[r], j0, live ? of4(dh) : make_float4(0.f, 0.f, 0.f, 0.f));
         }
         __syncthreads();
-        // J: dK += dh W_c^T;  dW += Q^T dHq + K^T dh  (wave w: rows 16w .. 16w + 15)
+        // H: dQ += DA K;  dK += DA^T Q + (direct terms) + dh W_c^T;
+        //    dW += Q^T dHq + K^T dh  (wave w: rows 16w .. 16w + 15);  d eta_s += sum_t C2[t][s]
         {
             const int cw = 16 * w;
-            f32x4 ak = ld_tile(&sm.dK[0][0], LS, 0, cw, lane);
-            ak += tile_mm<BD>([&](int i, int k) { return ROW4(sm.dh, i, k); },
-                              [&](int k, int j) { return ROW4(sm.W, cw + j, k); }, lane);
+            f32x4 acc = ld_tile(&sm.dQ[0][0], LS, 0, cw, lane);
+            acc = tile_mm<BR>(acc, [&](int i, int k) { return ROW4(sm.DA, i, k); },
+                              [&](int k, int j) { return COL4(sm.K, k, cw + j); }, lane);
+            st_tile(&sm.dQ[0][0], LS, 0, cw, acc, lane);
+            f32x4 ak = ld_tile(&sm.dK[0][0], LS, 0, cw, lane) + ld_tile(&sm.dKd[0][0], LS, 0, cw, lane);
+            ak = tile_mm<BR>(ak, [&](int i, int k) { return COL4(sm.DA, k, i); },
+                             [&](int k, int j) { return COL4(sm.Q, k, cw + j); }, lane);
+            ak = tile_mm<BD>(ak, [&](int i, int k) { return ROW4(sm.dh, i, k); },
+                             [&](int k, int j) { return ROW4(sm.W, cw + j, k); }, lane);
             st_tile(&sm.dK[0][0], LS, 0, cw, ak, lane);
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj) {
-                f32x4 acc = ld_tile(&sm.dW[0][0], LS, cw, 16 * tj, lane);
-                acc += tile_mm<BR>([&](int i, int k) { return COL4(sm.Q, k, cw + i); },
-                                   [&](int k, int j) { return COL4(sm.dHq, k, 16 * tj + j); }, lane);
-                acc += tile_mm<BR>([&](int i, int k) { return COL4(sm.K, k, cw + i); },
-                                   [&](int k, int j) { return COL4(sm.dh, k, 16 * tj + j); }, lane);
-                st_tile(&sm.dW[0][0], LS, cw, 16 * tj, acc, lane);
-                st_tile_t(&sm.dWT[0][0], LS, cw, 16 * tj, acc, lane);
+                f32x4 aw = ld_tile(&sm.dW[0][0], LS, cw, 16 * tj, lane);
+                aw = tile_mm<BR>(aw, [&](int i, int k) { return COL4(sm.Q, k, cw + i); },
+                                 [&](int k, int j) { return COL4(sm.dHq, k, 16 * tj + j); }, lane);
+                aw = tile_mm<BR>(aw, [&](int i, int k) { return COL4(sm.K, k, cw + i); },
+                                 [&](int k, int j) { return COL4(sm.dh, k, 16 * tj + j); }, lane);
+                st_tile(&sm.dW[0][0], LS, cw, 16 * tj, aw, lane);
+                st_tile_t(&sm.dWT[0][0], LS, cw, 16 * tj, aw, lane);
+            }
+            if (tid < BR) {
+                float a = 0.f;
+#pragma unroll
+                for (int t = 0; t < BR; ++t) a += sm.C2[t][tid];
+                sm.deta[tid] += a;
             }
         }
         __syncthreads();
