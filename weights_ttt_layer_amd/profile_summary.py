@@ -53,14 +53,14 @@ OUR_KERNELS = ("smallb_linear_kernel", "smallb_mlp_kernel", "lc_gram_kernel", "l
 
 # kernel-name prefixes launched by one call of each path
 PATH_KERNELS = {
-    "plain": ("smallb_linear_kernel<0",),
-    "ln": ("smallb_linear_kernel<1, unsigned short>",),
+    "plain": ("smallb_linear_kernel<0,",),
+    "ln": ("smallb_linear_kernel<1, unsigned short",),
     "mlp": ("smallb_mlp_kernel",),
     "large": ("lc_gram_kernel", "lc_scan_kernel", "lc_chunk_kernel"),
     "block_before": ("lc_gram_kernel", "lc_scan_kernel", "lc_apply_kernel<false>"),
     "block_after": ("lc_gram_kernel", "lc_scan_kernel", "lc_apply_kernel<true>"),
     "decode": ("decode_kernel",),
-    "layer": ("layer_gemm_kernel", "layer_outprep_kernel", "smallb_linear_kernel<1, float>"),
+    "layer": ("layer_gemm_kernel", "layer_outprep_kernel", "smallb_linear_kernel<1, float, 2>"),
 }
 
 
