@@ -41,6 +41,7 @@ struct alignas(16) MlpSmem {
     float x2[ROWS * XS];     // GELU(K W1), [token][hidden]
     float x2t[HID * XTS];    // the same, [hidden][token]
     float x2q[ROWS * XS];    // GELU(A_Q), [token][hidden]
+    float d1[ROWS * XS];     // GELU'(A), [token][hidden]
     float g2[ROWS * GS];     // dl/dH at the chunk-start weights (no eta), [token][d]
     float red[3][4][ROWS][2];
 };
@@ -106,16 +107,15 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
     for (int i = 0; i < 4; ++i) et[i] = st.eta[4 * g + i];
 
     // ---- (3) X2 = GELU(A), GELU'(A); publish X2 in both orientations ----
-    float x2[4][4], d1[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x2[t][i] = gelu_f(ak[t][i]);
-            d1[t][i] = gelu_d(ak[t][i]);
+            const float x2 = gelu_f(ak[t][i]);
             const int hcol = 64 * w + 16 * t + n;
-            sm.x2[(4 * g + i) * XS + hcol] = x2[t][i];
-            sm.x2t[hcol * XTS + 4 * g + i] = x2[t][i];
+            sm.x2[(4 * g + i) * XS + hcol] = x2;
+            sm.x2t[hcol * XTS + 4 * g + i] = x2;
+            sm.d1[(4 * g + i) * XS + hcol] = gelu_d(ak[t][i]);
         }
     __syncthreads();
 
@@ -181,7 +181,8 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
         }
         float x[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (4 * g + i < bc) ? -et[i] * acc[i] * d1[t][i] : 0.f;
+        for (int i = 0; i < 4; ++i)
+            x[i] = (4 * g + i < bc) ? -et[i] * acc[i] * sm.d1[(4 * g + i) * XS + 64 * w + 16 * t + n] : 0.f;
         terms4<TS>(x, gb1[t]);
     }
 
@@ -199,6 +200,18 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             sm.x2q[(4 * g + i) * XS + 64 * w + 16 * t + n] = gelu_f(aq[t][i]);
+    }
+    // W1 -= K^T diag(eta) G1 now (A_Q used W1_c above), so the G1 terms die here.
+    // A = K^T tile r: row = feature 16r+n, k = token.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = Stor<S>::f(st.k[(4 * g + j) * STRIDE + 16 * r + n]);
+        bf16x4 kt[TIN];
+        terms4<TIN>(x, kt);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) W1acc[r][t] = mma16_terms<TIN, TS>(W1acc[r][t], kt, gb1[t]);
     }
     __syncthreads();
 
@@ -262,17 +275,6 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
     }
 
     // ---- (11) state updates ----
-    // W1 -= K^T diag(eta) G1   (A = K^T tile r: row = feature 16r+n, k = token)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        float x[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = Stor<S>::f(st.k[(4 * g + j) * STRIDE + 16 * r + n]);
-        bf16x4 kt[TIN];
-        terms4<TIN>(x, kt);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) W1acc[r][t] = mma16_terms<TIN, TS>(W1acc[r][t], kt, gb1[t]);
-    }
     // W2 -= X2^T diag(eta) G2   (A = X2^T tile r: row = hidden 16r+n, k = token)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -295,7 +297,7 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
         for (int t = 0; t < 4; ++t) {
             float y[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = -x2[t][i];
+            for (int i = 0; i < 4; ++i) y[i] = -sm.x2[(4 * g + i) * XS + 64 * w + 16 * t + n];
             bf16x4 xb[TS];
             terms4<TS>(y, xb);
             W2Tacc[r][t] = mma16_terms<TS, TS>(W2Tacc[r][t], ga, xb);
