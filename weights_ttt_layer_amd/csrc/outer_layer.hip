@@ -112,9 +112,9 @@ __global__ void __launch_bounds__(TM * TN / 64)
 layer_gemm_kernel(GemmArgs g)
 {
     constexpr int WR = TM / 64, WC = TN / 64, NW = WR * WC;
-    constexpr int AI = TM / 16, BI = TN / 16;            // DMA instructions per stage (1 KB each)
-    constexpr int PER = (AI + BI) / NW;                  // ... per wave
-    static_assert((AI + BI) % NW == 0, "DMA instructions must split evenly over the waves");
+    constexpr int NIA = TM / 16, NIB = TN / 16;            // DMA instructions per stage (1 KB each)
+    constexpr int PER = (NIA + NIB) / NW;                  // ... per wave
+    static_assert((NIA + NIB) % NW == 0, "DMA instructions must split evenly over the waves");
     constexpr int SA = TM * GK * 2, SB = TN * GK * 2;    // stage bytes
     __shared__ __attribute__((aligned(16))) char smem[NS * (SA + SB)];
 
@@ -135,8 +135,8 @@ layer_gemm_kernel(GemmArgs g)
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int ins = w + NW * j;
-        const bool b = ins >= AI;
-        const int r = (b ? ins - AI : ins) * 16 + (lane >> 2);
+        const bool b = ins >= NIA;
+        const int r = (b ? ins - NIA : ins) * 16 + (lane >> 2);
         const int p = (lane & 3) ^ ((r >> 2) & 3);
         if (!b) {
             const int t = min(t0 + r, g.N - 1);
@@ -151,7 +151,7 @@ layer_gemm_kernel(GemmArgs g)
                 n -= which * g.rows_per_w;
             }
             src[j] = Wt + (size_t)n * g.ldb + p * 8;
-            dst[j] = base + NS * SA + (ins - AI) * 1024;
+            dst[j] = base + NS * SA + (ins - NIA) * 1024;
         }
         isb[j] = b;
     }
