@@ -46,16 +46,41 @@ struct alignas(16) MlpSmem {
     float red[3][4][ROWS][2];
 };
 
-__device__ __forceinline__ float gelu_f(float a)
+// GELU(a) = a Phi(a), Phi(a) = (1 + erf(a / sqrt 2)) / 2, and its derivative
+// Phi(a) + a phi(a). erf comes from Abramowitz & Stegun, "Handbook of
+// Mathematical Functions", formula 7.1.26: for x >= 0,
+//     erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
+//     t = 1 / (1 + p x),   |error| <= 1.5e-7,
+// extended to x < 0 by odd symmetry. Only Phi = (1 + erf) / 2 is used, so the
+// absolute error bound is the one that matters. exp(-x^2) = exp(-a^2 / 2) is
+// also the Gaussian factor of phi, shared by the derivative.
+constexpr float AS_P = 0.3275911f;
+constexpr float AS_A1 = 0.254829592f, AS_A2 = -0.284496736f, AS_A3 = 1.421413741f,
+                AS_A4 = -1.453152027f, AS_A5 = 1.061405429f;
+
+__device__ __forceinline__ float phi_cdf(float a, float& gauss)
 {
-    return 0.5f * a * (1.f + erff(a * 0.70710678118654752f));
+    const float x = fabsf(a) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(AS_P, x, 1.f));
+    gauss = __expf(-x * x);
+    const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, AS_A5, AS_A4), AS_A3), AS_A2), AS_A1);
+    const float erfx = 1.f - poly * gauss;
+    return 0.5f * (1.f + copysignf(erfx, a));
 }
 
-// d/da [a Phi(a)] = Phi(a) + a phi(a)
-__device__ __forceinline__ float gelu_d(float a)
+__device__ __forceinline__ float gelu_f(float a)
 {
-    return 0.5f * (1.f + erff(a * 0.70710678118654752f)) +
-           a * 0.39894228040143267794f * expf(-0.5f * a * a);
+    float gauss;
+    return a * phi_cdf(a, gauss);
+}
+
+// GELU(a) and d/da GELU(a) = Phi(a) + a exp(-a^2/2) / sqrt(2 pi)
+__device__ __forceinline__ void gelu_fd(float a, float& f, float& fd)
+{
+    float gauss;
+    const float c = phi_cdf(a, gauss);
+    f = a * c;
+    fd = fmaf(a * 0.39894228040143267794f, gauss, c);
 }
 
 template <typename S>
@@ -111,11 +136,12 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float x2 = gelu_f(ak[t][i]);
+            float x2, d1;
+            gelu_fd(ak[t][i], x2, d1);
             const int hcol = 64 * w + 16 * t + n;
             sm.x2[(4 * g + i) * XS + hcol] = x2;
             sm.x2t[hcol * XTS + 4 * g + i] = x2;
-            sm.d1[(4 * g + i) * XS + hcol] = gelu_d(ak[t][i]);
+            sm.d1[(4 * g + i) * XS + hcol] = d1;
         }
     __syncthreads();
 
