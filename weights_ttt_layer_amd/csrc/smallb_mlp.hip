@@ -34,14 +34,23 @@ constexpr int HID = 256;
 constexpr int XS = HID + 4;     // row stride of [token][hidden] fp32 tiles
 constexpr int GS = D + 4;       // row stride of [token][d] fp32 tiles
 constexpr int XTS = ROWS + 4;   // row stride of the [hidden][token] fp32 tile
+constexpr int XB = HID + 8;     // row stride of [token][hidden] bf16 term tiles
 
+// terms of an fp32 operand next to token streams of type S
+template <typename S>
+constexpr int fp_terms() { return Stor<S>::TERMS == 1 ? 2 : 3; }
+
+// GELU(A) and GELU(A_Q) are written once, already split into their bf16
+// operand terms, by the wave that owns the hidden slice; the products over the
+// hidden dimension then read ready terms instead of every wave splitting every
+// row again.
 template <typename S>
 struct alignas(16) MlpSmem {
     Stage<S> st[2];
-    float x2[ROWS * XS];     // GELU(K W1), [token][hidden]
-    float x2t[HID * XTS];    // the same, [hidden][token]
-    float x2q[ROWS * XS];    // GELU(A_Q), [token][hidden]
-    float d1[ROWS * XS];     // GELU'(A), [token][hidden]
+    uint16_t x2b[fp_terms<S>()][ROWS * XB];    // GELU(K W1) terms, [token][hidden]
+    float x2t[HID * XTS];                      // GELU(K W1), [hidden][token]
+    uint16_t x2qb[fp_terms<S>()][ROWS * XB];   // GELU(A_Q) terms, [token][hidden]
+    float d1[ROWS * XS];                       // GELU'(A), [token][hidden]
     float g2[ROWS * GS];     // dl/dH at the chunk-start weights (no eta), [token][d]
     float red[3][4][ROWS][2];
 };
@@ -81,6 +90,29 @@ __device__ __forceinline__ void gelu_fd(float a, float& f, float& fd)
     const float c = phi_cdf(a, gauss);
     f = a * c;
     fd = fmaf(a * 0.39894228040143267794f, gauss, c);
+}
+
+// Operand fragment of a pre-split [token][hidden] tile: per term, four entries
+// at row + o and four at row + o + 16 (the k order of load_a8).
+template <int T>
+__device__ __forceinline__ void load_terms8(const uint16_t (*tile)[ROWS * XB], int off, bf16x8 (&out)[T])
+{
+#pragma unroll
+    for (int s = 0; s < T; ++s) {
+        const uint2 a = *reinterpret_cast<const uint2*>(tile[s] + off);
+        const uint2 b = *reinterpret_cast<const uint2*>(tile[s] + off + 16);
+        out[s] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+    }
+}
+
+// Split v into T bf16 terms and store them at tile[s][off].
+template <int T>
+__device__ __forceinline__ void store_terms(uint16_t (*tile)[ROWS * XB], int off, float v)
+{
+    __bf16 t[T];
+    split_terms<T>(v, t);
+#pragma unroll
+    for (int s = 0; s < T; ++s) tile[s][off] = __builtin_bit_cast(uint16_t, t[s]);
 }
 
 template <typename S>
@@ -139,7 +171,7 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
             float x2, d1;
             gelu_fd(ak[t][i], x2, d1);
             const int hcol = 64 * w + 16 * t + n;
-            sm.x2[(4 * g + i) * XS + hcol] = x2;
+            store_terms<TS>(sm.x2b, (4 * g + i) * XB + hcol, x2);
             sm.x2t[hcol * XTS + 4 * g + i] = x2;
             sm.d1[(4 * g + i) * XS + hcol] = d1;
         }
@@ -150,8 +182,7 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         bf16x8 xa[TS], wb[TS];
-        const float* r0 = sm.x2 + n * XS + 32 * p + 4 * g;
-        load_a8<float, TS>(r0, r0 + 16, xa);
+        load_terms8<TS>(sm.x2b, n * XB + 32 * p + 4 * g, xa);
         b8_from_acc<TS>(W2acc[2 * p], W2acc[2 * p + 1], wb);
         hk = mma32_terms<TS, TS>(hk, xa, wb);
     }
@@ -225,7 +256,7 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
         aq[t] = mma16_terms<TS, TS>(aq[t], sa, gb1[t]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            sm.x2q[(4 * g + i) * XS + 64 * w + 16 * t + n] = gelu_f(aq[t][i]);
+            store_terms<TS>(sm.x2qb, (4 * g + i) * XB + 64 * w + 16 * t + n, gelu_f(aq[t][i]));
     }
     // W1 -= K^T diag(eta) G1 now (A_Q used W1_c above), so the G1 terms die here.
     // A = K^T tile r: row = feature 16r+n, k = token.
@@ -246,10 +277,8 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         bf16x8 xa[TS], xq[TS];
-        const float* r0 = sm.x2 + n * XS + 32 * p + 4 * g;
-        const float* r1 = sm.x2q + n * XS + 32 * p + 4 * g;
-        load_a8<float, TS>(r0, r0 + 16, xa);
-        load_a8<float, TS>(r1, r1 + 16, xq);
+        load_terms8<TS>(sm.x2b, n * XB + 32 * p + 4 * g, xa);
+        load_terms8<TS>(sm.x2qb, n * XB + 32 * p + 4 * g, xq);
         s2T = mma32_terms<TS, TS>(s2T, xa, xq);
     }
     // -diag(eta) G2 as B operand
@@ -266,8 +295,7 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         bf16x8 xq[TS], wb[TS];
-        const float* r1 = sm.x2q + n * XS + 32 * p + 4 * g;
-        load_a8<float, TS>(r1, r1 + 16, xq);
+        load_terms8<TS>(sm.x2qb, n * XB + 32 * p + 4 * g, xq);
         b8_from_acc<TS>(W2acc[2 * p], W2acc[2 * p + 1], wb);
         hq = mma32_terms<TS, TS>(hq, xq, wb);
     }
@@ -321,11 +349,16 @@ __device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f3
         (void)x;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            float y[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = -sm.x2[(4 * g + i) * XS + 64 * w + 16 * t + n];
+            // terms of -X2 (the split of a negated value is the negated split)
             bf16x4 xb[TS];
-            terms4<TS>(y, xb);
+#pragma unroll
+            for (int sT = 0; sT < TS; ++sT) {
+                uint32_t u[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    u[i] = (uint32_t)sm.x2b[sT][(4 * g + i) * XB + 64 * w + 16 * t + n] ^ 0x8000u;
+                xb[sT] = __builtin_bit_cast(bf16x4, make_uint2(u[0] | (u[1] << 16), u[2] | (u[3] << 16)));
+            }
             W2Tacc[r][t] = mma16_terms<TS, TS>(W2Tacc[r][t], ga, xb);
         }
     }
