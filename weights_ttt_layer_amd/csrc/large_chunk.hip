@@ -249,7 +249,7 @@ lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
 // holds in slots 8s .. 8s+7 of the same lane, so every wave publishes its
 // tile's two bf16 terms lane by lane in LDS and reads the others' at its own
 // lane index; the A operand comes ready-split from lc_gram in that order.
-// The operands of step c+2 are requested while step c runs. W_0 .. W_C are all
+// The operands of step c+2 are requested as step c finishes. W_0 .. W_C are all
 // published (W_C, the final state, for outputs taken after the last step).
 // ===========================================================================
 struct ScanOps {
@@ -320,17 +320,15 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = W0u[(32 * w + crow(i, h)) * LD + colg];
 
-    ScanOps o0, o1;
-    scan_load(Mg, Bg, unit, C, 0, w, cb, lane, o0);
-    scan_load(Mg, Bg, unit, C, min(1, C - 1), w, cb, lane, o1);
-    for (int c = 0; c < C; ++c) {
+    // One step: publish W_c, then W_{c+1} = W_c - M_c W_c + B_c with the
+    // operands in `o`; afterwards `o` is refilled with step c + 2's operands.
+    // The two operand sets alternate by name (the loop is unrolled by two), so
+    // no register copy makes the compiler wait for a refill before its use.
+    auto step = [&](int c, ScanOps& o) {
         const int buf = c & 1;
         // publish W_c: two bf16 terms, lane by lane in LDS and as W_c^T in the workspace
         publish_state(acc, WT + ((size_t)unit * (C + 1) + c) * 2 * LD * LD, wpub[buf][w], w, lane, h, colg);
         __syncthreads();                                 // one barrier per step: wpub is double-buffered
-        // operands of step c + 2 (clamped: the last steps reload their own)
-        ScanOps o2;
-        scan_load(Mg, Bg, unit, C, min(c + 2, C - 1), w, cb, lane, o2);
         f32x16 t = {};
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -338,19 +336,26 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const uint16_t* __res
             for (int s = 0; s < 2; ++s) {
                 const bf16x8 b0 = wpub[buf][r][0][s][lane];
                 const bf16x8 b1 = wpub[buf][r][1][s][lane];
-                t = mfma_32x32x16(o0.a[r][s][1], b0, t);
-                t = mfma_32x32x16(o0.a[r][s][0], b1, t);
-                t = mfma_32x32x16(o0.a[r][s][0], b0, t);
+                t = mfma_32x32x16(o.a[r][s][1], b0, t);
+                t = mfma_32x32x16(o.a[r][s][0], b1, t);
+                t = mfma_32x32x16(o.a[r][s][0], b0, t);
             }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            acc[4 * q] = (acc[4 * q] - t[4 * q]) + o0.bq[q].x;
-            acc[4 * q + 1] = (acc[4 * q + 1] - t[4 * q + 1]) + o0.bq[q].y;
-            acc[4 * q + 2] = (acc[4 * q + 2] - t[4 * q + 2]) + o0.bq[q].z;
-            acc[4 * q + 3] = (acc[4 * q + 3] - t[4 * q + 3]) + o0.bq[q].w;
+            acc[4 * q] = (acc[4 * q] - t[4 * q]) + o.bq[q].x;
+            acc[4 * q + 1] = (acc[4 * q + 1] - t[4 * q + 1]) + o.bq[q].y;
+            acc[4 * q + 2] = (acc[4 * q + 2] - t[4 * q + 2]) + o.bq[q].z;
+            acc[4 * q + 3] = (acc[4 * q + 3] - t[4 * q + 3]) + o.bq[q].w;
         }
-        o0 = o1;
-        o1 = o2;
+        if (c + 2 < C) scan_load(Mg, Bg, unit, C, c + 2, w, cb, lane, o);
+    };
+
+    ScanOps oA, oB;
+    scan_load(Mg, Bg, unit, C, 0, w, cb, lane, oA);
+    if (C > 1) scan_load(Mg, Bg, unit, C, 1, w, cb, lane, oB);
+    for (int c = 0; c < C; c += 2) {
+        step(c, oA);
+        if (c + 1 < C) step(c + 1, oB);
     }
     // the final state, for outputs taken after the last chunk's step
     publish_state(acc, WT + ((size_t)unit * (C + 1) + C) * 2 * LD * LD, nullptr, w, lane, h, colg);
