@@ -96,7 +96,11 @@ def test_ln_zero_affine_gives_identity(dtype):
 
 @pytest.mark.parametrize("kind", ["plain", "ln"])
 def test_state_passing(kind):
-    """run(N1 + N2) equals run(N1) followed by run(N2) from the returned state."""
+    """run(N1 + N2) equals run(N1) followed by run(N2) from the returned state,
+    up to rounding: an uninterrupted run forms the pre-activation of the chunk
+    after the split as K_c W_{c-1} - (K_c K_{c-1}^T) Gt_{c-1}, a restarted one
+    as K_c W_c. Each run is within ~5e-6 of the oracle (two-term operands,
+    2^-16 per entry), so the two differ by at most the sum of those errors."""
     inp = small(kind, "bf16", 2, 2, 96, 16)
     z, w = gpu_linear(inp)
     N1 = 48
@@ -107,8 +111,8 @@ def test_state_passing(kind):
                     inp.v[:, :, N1:].copy(), inp.eta[:, :, N1:].copy(), inp.eta_const, wa, None,
                     None, inp.gamma, inp.beta)
     zb, wb = gpu_linear(b2)
-    assert rel_err(np.concatenate([za, zb], 2), z) <= 1e-6
-    assert rel_err(wb, w) <= 1e-6
+    assert rel_err(np.concatenate([za, zb], 2), z) <= 2e-5
+    assert rel_err(wb, w) <= 2e-5
 
 
 def test_in_place_state_and_determinism():

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libttt.so")
-SOURCES = ["ttt_abi.hip", "smallb_linear.hip", "smallb_mlp.hip", "large_chunk.hip", "decode.hip",
+SOURCES = ["ttt_abi.hip", "smallb_linear.hip", "smallb_chain.hip", "smallb_mlp.hip", "large_chunk.hip", "decode.hip",
            "outer_layer.hip", "backward.hip"]
 ARCH = "gfx950"
 

@@ -184,4 +184,39 @@ __device__ __forceinline__ float row16_sum(float x)
     return x;
 }
 
+// Sum over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48); every
+// lane gets the total. v_permlane32_swap / v_permlane16_swap pair each lane with
+// its xor-32 / xor-16 partner.
+__device__ __forceinline__ float xrow4_sum(float x)
+{
+    const int xi = __builtin_bit_cast(int, x);
+    auto a = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    x = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
+    const int yi = __builtin_bit_cast(int, x);
+    auto b = __builtin_amdgcn_permlane16_swap(yi, yi, false, false);
+    return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Direct global->LDS loads
+// ---------------------------------------------------------------------------
+// One 16-byte (dma16) or 4-byte (dma4) direct global->LDS load per lane: lane
+// l's bytes land at lds + 16 l (+ 4 l). Issued as assembly so that the compiler
+// does not track them: it cannot tell LDS buffers apart through the loads'
+// addresses and would otherwise wait for a prefetch before every read of
+// another buffer. The caller waits for these loads explicitly (vmcnt) before
+// the barrier that publishes the data. (M0 written by SALU needs one wait
+// state before an LDS-DMA instruction.)
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
 }  // namespace ttt

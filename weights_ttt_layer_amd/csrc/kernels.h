@@ -46,6 +46,8 @@ struct MlpArgs {
 
 // Small-b path: one workgroup per (sequence, head); d = 64, 1 <= b <= 16.
 hipError_t launch_smallb_linear(const LinearArgs& a, hipStream_t stream);
+// bf16 token streams: the chain-on-one-wave kernel (smallb_chain.hip)
+hipError_t launch_smallb_chain(const LinearArgs& a, hipStream_t stream);
 // The same on fp32 streams carried as two bf16 terms (16 significant bits)
 // instead of three; the whole-layer path uses it for its projected streams.
 hipError_t launch_smallb_linear_f32x2(const LinearArgs& a, hipStream_t stream);

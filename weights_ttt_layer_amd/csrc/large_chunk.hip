@@ -68,19 +68,6 @@ __device__ __forceinline__ int rsw(int r) { return ((r & 3) << 1) | ((r >> 2) & 
 // byte offset of piece p of row r
 __device__ __forceinline__ int swz(int r, int p) { return r * 256 + ((p ^ rsw(r)) << 4); }
 
-// One 16-byte direct global->LDS load per lane: lane l's bytes land at
-// lds + 16 l. Issued as assembly so that the compiler does not track it: the
-// compiler cannot tell the two LDS buffers apart through the loads' addresses
-// and would otherwise wait for a prefetch before every read of the other
-// buffer. The caller waits for these loads explicitly (vmcnt) before the
-// barrier that publishes the buffer. (M0 written by SALU needs one wait state
-// before an LDS-DMA instruction.)
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 // ===========================================================================
 // lc_gram: M_c = K^T D K and B_c = K^T D V for one (unit, chunk) per workgroup.

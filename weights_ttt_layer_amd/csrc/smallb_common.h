@@ -175,18 +175,6 @@ __device__ __forceinline__ void b8_from_acc(const f32x4& t0, const f32x4& t1, bf
 namespace ttt {
 namespace smallb {
 
-// Sum over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48); every
-// lane gets the total. v_permlane32_swap / v_permlane16_swap pair each lane with
-// its xor-32 / xor-16 partner.
-__device__ __forceinline__ float xrow4_sum(float x)
-{
-    const int xi = __builtin_bit_cast(int, x);
-    auto a = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
-    x = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
-    const int yi = __builtin_bit_cast(int, x);
-    auto b = __builtin_amdgcn_permlane16_swap(yi, yi, false, false);
-    return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
-}
 
 // A operand (16x16x16) of K^T for feature tile r: lane (g, n) gets
 // K[4g + j][16r + n], j = 0..3, i.e. four consecutive tokens of one feature.
