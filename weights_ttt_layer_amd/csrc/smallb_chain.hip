@@ -21,24 +21,29 @@
 // beside it. (The association is exact in real arithmetic; rounding differs
 // from forming K_{c+1} W_{c+1} directly by the same 2^-16 order.)
 //
-// One workgroup of nine waves per (sequence, head) unit:
+// One workgroup of eleven waves per (sequence, head) unit. Waves are placed on
+// the four SIMDs round-robin, so waves 4 and 8 share the chain's SIMD; they get
+// the light roles.
 //  * wave 0, the chain: X^T = A^T + (-Gt_prev)^T P^T (v_mfma_f32_16x16x16_bf16,
 //    four 16-feature tiles). Its C layout holds ONE token per lane (lane
 //    (g, n): token n, features 16t + 4g + i), so a row statistic is 15 in-lane
 //    adds and two lane swaps. It writes -Gt as two bf16 terms into LDS, where
 //    the transpose read hands it back as the A operand of the next chunk's
-//    product. It runs at raised wave priority and touches no global memory.
-//  * waves 1..4, the state: wave 1 + b keeps W[:, 16b..16b+16) in fp32 MFMA
-//    accumulators (C layout, rows = input features) and per chunk computes
-//    W += K^T (-Gt) (16x16x32, the two terms of Gt stacked along k), the A^T
-//    tile b of the next chunk and the Q W part of H_Q^T tile b (W^T as the A
-//    operand, k in a permuted order that the B operand reads to match).
-//    Wave 1 also issues every global->LDS load of the Q/K/V/eta ring: its
-//    vector-memory counter holds nothing else, so it can be waited on exactly.
-//  * waves 5..8, the outputs: wave 5 + b adds the causal term
-//    -Gt^T tril(S)^T (S^T = K Q^T in its C layout) to H_Q^T tile b, forms the
-//    output rows of its 16 features and the residual input of the chain's next
-//    gradient; wave 5 also forms P^T = K_c K_{c+1}^T.
+//    product. Everything it needs for a chunk except A arrives a chunk early
+//    and is read before the barrier; it runs at raised wave priority and
+//    touches no global memory.
+//  * waves 1, 2, 3, 5, the state: the wave of tile b keeps W[:, 16b..16b+16)
+//    in fp32 MFMA accumulators (C layout, rows = input features) and per chunk
+//    computes W += K^T (-Gt) (16x16x32, the two terms of Gt stacked along k),
+//    the A^T tile b of the next chunk and the Q W part of H_Q^T tile b (W^T as
+//    the A operand, k in a permuted order that the B operand reads to match).
+//  * waves 6, 7, 9, 10, the outputs: the wave of tile b adds the causal term
+//    -Gt^T tril(S)^T (S^T = K Q^T in its C layout) to H_Q^T tile b and forms
+//    the output rows of its 16 features.
+//  * wave 4 issues every global->LDS load of the Q/K/V/eta ring (its
+//    vector-memory counter holds nothing else, so it can be waited on exactly)
+//    and forms P^T = K_c K_{c+1}^T two chunks ahead; wave 8 forms the residual
+//    input of the chain's gradient two chunks ahead.
 // One workgroup barrier per chunk (LDS-only fence: the ring loads stay in
 // flight); every exchanged tile is double-buffered by chunk parity. The output
 // LayerNorm needs all 64 features of a row, so its partial sums cross the
@@ -54,11 +59,11 @@ namespace ttt {
 namespace {
 
 constexpr int D = 64;
-constexpr int NWAVE = 9;
+constexpr int NWAVE = 11;
 constexpr int NTHR = 64 * NWAVE;
 constexpr int RING = 12;     // Q/K/V/eta chunk slots
 constexpr int PFD = 8;       // chunks requested ahead of the one being stepped
-static_assert(RING >= PFD + 3, "a slot is read up to two chunks after its step");
+static_assert(RING >= PFD + 3, "slots of chunks c-2 .. c+2 are read during step c");
 
 // One chunk of the ring: [token][feature] bf16 tiles of 16 rows x 128 bytes,
 // 16-byte piece p of row r stored at slot p ^ (r & 7).
@@ -162,14 +167,52 @@ __device__ __forceinline__ void issue_chunk(ChainSmem& sm, int j, int lane, int 
 // The chain wave
 // ---------------------------------------------------------------------------
 
-// One chain step: -Gt_c from A_c^T, P_c^T, the residual input and -Gt_{c-1}.
-template <int KIND, bool PT>
-__device__ __forceinline__ void chain_step(ChainSmem& sm, int c, int bc, int g, int n, int lane,
-                                           const float (&g2)[16], float eta_const, float eps)
+// What the chain reads for a chunk before that chunk's barrier: -Gt of the
+// previous chunk as A operands, P^T, the residual input and eta.
+struct ChainPre {
+    bf16x4 ga0[4], ga1[4];
+    bf16x4 pb0, pb1;
+    float cp[16];
+    float eta;
+};
+
+template <bool PT>
+__device__ __forceinline__ void chain_prefetch(const ChainSmem& sm, int c, int bc, int g, int n, int lane,
+                                               float eta_const, ChainPre& pre)
+{
+    const int par = c & 1;
+    if (c > 0) {
+        const uint16_t* g0 = sm.gt[par ^ 1][0];
+        const uint16_t* g1 = sm.gt[par ^ 1][1];
+        const int row = 4 * g + (n >> 2);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            pre.ga0[t] = tr4(g0, row, 16 * t + 4 * (n & 3));
+            pre.ga1[t] = tr4(g1, row, 16 * t + 4 * (n & 3));
+        }
+        pre.pb0 = __builtin_bit_cast(bf16x4, sm.xp[par][0][lane]);
+        pre.pb1 = __builtin_bit_cast(bf16x4, sm.xp[par][1][lane]);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float4 r = sm.xc[par][t][lane];
+        pre.cp[4 * t] = r.x;
+        pre.cp[4 * t + 1] = r.y;
+        pre.cp[4 * t + 2] = r.z;
+        pre.cp[4 * t + 3] = r.w;
+    }
+    float eta = eta_const;
+    if constexpr (PT) eta = sm.ring[c % RING].eta[n];
+    pre.eta = (n < bc) ? eta : 0.f;
+}
+
+// One chain step: -Gt_c from A_c^T and the prefetched operands.
+template <int KIND>
+__device__ __forceinline__ void chain_step(ChainSmem& sm, int c, int g, int n, int lane, const ChainPre& pre,
+                                           const float (&g2)[16], float eps)
 {
     const int par = c & 1;
     f32x4 acc[4];
-    float cp[16];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const float4 a = sm.xa[par][t][lane];
@@ -177,35 +220,15 @@ __device__ __forceinline__ void chain_step(ChainSmem& sm, int c, int bc, int g, 
         acc[t][1] = a.y;
         acc[t][2] = a.z;
         acc[t][3] = a.w;
-        const float4 r = sm.xc[par][t][lane];
-        cp[4 * t] = r.x;
-        cp[4 * t + 1] = r.y;
-        cp[4 * t + 2] = r.z;
-        cp[4 * t + 3] = r.w;
     }
-    float eta = eta_const;
-    if constexpr (PT) eta = sm.ring[c % RING].eta[n];
-    eta = (n < bc) ? eta : 0.f;
-
     if (c > 0) {
         // X^T += (-Gt_{c-1})^T P_c^T : A = -Gt^T tile t (k = tokens of c-1), B = P^T
-        const bf16x4 pb0 = __builtin_bit_cast(bf16x4, sm.xp[par][0][lane]);
-        const bf16x4 pb1 = __builtin_bit_cast(bf16x4, sm.xp[par][1][lane]);
-        const uint16_t* g0 = sm.gt[par ^ 1][0];
-        const uint16_t* g1 = sm.gt[par ^ 1][1];
-        const int row = 4 * g + (n >> 2);
-        bf16x4 ga0[4], ga1[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            ga0[t] = tr4(g0, row, 16 * t + 4 * (n & 3));
-            ga1[t] = tr4(g1, row, 16 * t + 4 * (n & 3));
-        }
+        for (int t = 0; t < 4; ++t) acc[t] = mfma_16x16x16(pre.ga1[t], pre.pb0, acc[t]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t] = mfma_16x16x16(ga1[t], pb0, acc[t]);
+        for (int t = 0; t < 4; ++t) acc[t] = mfma_16x16x16(pre.ga0[t], pre.pb1, acc[t]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t] = mfma_16x16x16(ga0[t], pb1, acc[t]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t] = mfma_16x16x16(ga0[t], pb0, acc[t]);
+        for (int t = 0; t < 4; ++t) acc[t] = mfma_16x16x16(pre.ga0[t], pre.pb0, acc[t]);
     }
 
     float ng[16];   // -Gt of token n, features 16t + 4g + i at [4t + i]
@@ -228,23 +251,23 @@ __device__ __forceinline__ void chain_step(ChainSmem& sm, int c, int bc, int g, 
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             xh[j] = fmaf(acc[j >> 2][j & 3], rs, nmr);
-            dx[j] = fmaf(g2[j], xh[j], cp[j]);   // gamma * d loss / d LN
+            dx[j] = fmaf(g2[j], xh[j], pre.cp[j]);   // gamma * d loss / d LN
             u1 += dx[j];
             u2 = fmaf(dx[j], xh[j], u2);
         }
         u1 = xrow4_sum(u1);
         u2 = xrow4_sum(u2);
         // -eta rs (dx - mean(dx) - xh mean(dx xh))
-        const float sc = -eta * rs;
+        const float sc = -pre.eta * rs;
         const float ca = -(u2 * (1.f / D)) * sc;
         const float cb = -(u1 * (1.f / D)) * sc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) ng[j] = fmaf(xh[j], ca, fmaf(dx[j], sc, cb));
     } else {
         // -2 eta (X - V)
-        const float sc = 2.f * eta;
+        const float sc = 2.f * pre.eta;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) ng[j] = (cp[j] - acc[j >> 2][j & 3]) * sc;
+        for (int j = 0; j < 16; ++j) ng[j] = (pre.cp[j] - acc[j >> 2][j & 3]) * sc;
     }
 
     char* gh = reinterpret_cast<char*>(sm.gt[par][0]);
@@ -276,8 +299,14 @@ __device__ __forceinline__ void chain_role(ChainSmem& sm, int lane, int h, int N
     }
     lds_barrier();
     lds_barrier();
+    ChainPre pre;
+    if (C > 0) chain_prefetch<PT>(sm, 0, min(b, N), g, n, lane, eta_const, pre);
     for (int c = 0; c < C + 2; ++c) {
-        if (c < C) chain_step<KIND, PT>(sm, c, min(b, N - c * b), g, n, lane, g2, eta_const, eps);
+        if (c < C) {
+            chain_step<KIND>(sm, c, g, n, lane, pre, g2, eps);
+            // operands of chunk c+1 (its own -Gt_c included: LDS ops of one wave are ordered)
+            if (c + 1 < C) chain_prefetch<PT>(sm, c + 1, min(b, N - (c + 1) * b), g, n, lane, eta_const, pre);
+        }
         lds_barrier();
     }
 }
@@ -322,15 +351,9 @@ __device__ __forceinline__ f32x4 row_dots(const uint16_t* xt, const uint16_t* yt
     return a;
 }
 
-// The state waves. Wave 1 (bt == 0) also carries the ring loads.
-template <bool PT>
-__device__ __forceinline__ void w_role(ChainSmem& sm, int bt, int lane, int N, int b, int C, const uint16_t* Qu,
-                                       const uint16_t* Ku, const uint16_t* Vu, const float* etau,
-                                       const float* W0u, float* Wu)
+__device__ __forceinline__ void w_role(ChainSmem& sm, int bt, int lane, int C, const float* W0u, float* Wu)
 {
-    constexpr int DPC = PT ? 7 : 6;   // ring-load instructions per chunk
     const int g = lane >> 4, n = lane & 15;
-    const bool loader = (bt == 0);
     __builtin_amdgcn_s_setprio(2);
 
     // resident state: Wf[a][i] = W[16a + 4g + i][16b + n]
@@ -341,30 +364,15 @@ __device__ __forceinline__ void w_role(ChainSmem& sm, int bt, int lane, int N, i
         for (int i = 0; i < 4; ++i) Wf[a][i] = W0u[(16 * a + 4 * g + i) * D + 16 * bt + n];
     bf16x8 Wt[2][2];
     split_w(Wf, Wt);
-    // W0 is settled before any ring load is in flight (the compiler's wait for
-    // it would otherwise also wait for the ring)
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) asm volatile("" : "+v"(Wt[p][t]));
 
-    if (loader) {
-        const int npro = min(PFD, C);
-        for (int j = 0; j < npro; ++j) issue_chunk<PT>(sm, j, lane, N, b, Qu, Ku, Vu, etau);
-        if (C >= PFD) wait_vm<DPC * (PFD - 1)>(); else wait_vm<0>();   // chunk 0
-    }
-    lds_barrier();
+    lds_barrier();                       // chunks 0 and 1 in LDS
     if (C > 0) {
         const f32x4 a = wt_rows(Wt, sm.ring[0].k, g, n);
         sm.xa[0][bt][lane] = make_float4(a[0], a[1], a[2], a[3]);
     }
-    if (loader) {
-        if (C >= PFD) wait_vm<DPC * (PFD - 2)>(); else wait_vm<0>();   // chunk 1
-    }
     lds_barrier();
 
     for (int c = 0; c < C + 2; ++c) {
-        if (loader && c < C && c + PFD < C) issue_chunk<PT>(sm, c + PFD, lane, N, b, Qu, Ku, Vu, etau);
         if (c >= 1 && c <= C) {
             // W_c = W_{c-1} + K_{c-1}^T (-Gt_{c-1}); k = 16 tokens x 2 terms stacked
             const uint16_t* kt = sm.ring[(c - 1) % RING].k;
@@ -387,10 +395,6 @@ __device__ __forceinline__ void w_role(ChainSmem& sm, int bt, int lane, int N, i
             const f32x4 q = wt_rows(Wt, sm.ring[c % RING].q, g, n);
             sm.xq[c & 1][bt][lane] = make_float4(q[0], q[1], q[2], q[3]);
         }
-        if (loader) {
-            // chunk c + 2 is read after this barrier
-            if (c + PFD < C) wait_vm<DPC * (PFD - 2)>(); else wait_vm<0>();
-        }
         lds_barrier();
     }
 
@@ -400,37 +404,106 @@ __device__ __forceinline__ void w_role(ChainSmem& sm, int bt, int lane, int N, i
         for (int i = 0; i < 4; ++i) Wu[(16 * a + 4 * g + i) * D + 16 * bt + n] = Wf[a][i];
 }
 
-// The output waves.
+// ---------------------------------------------------------------------------
+// The loader (and P^T) wave and the residual-input wave
+// ---------------------------------------------------------------------------
+
+// P_j^T = K_{j-1} K_j^T as two bf16 terms, for the chain's chunk j.
+__device__ __forceinline__ void publish_p(ChainSmem& sm, int j, int g, int n, int lane)
+{
+    const f32x4 p = row_dots(sm.ring[(j - 1) % RING].k, sm.ring[j % RING].k, g, n);
+    const float x[4] = {p[0], p[1], p[2], p[3]};
+    bf16x4 pt[2];
+    terms4<2>(x, pt);
+    sm.xp[j & 1][0][lane] = __builtin_bit_cast(uint2, pt[0]);
+    sm.xp[j & 1][1][lane] = __builtin_bit_cast(uint2, pt[1]);
+}
+
+template <bool PT>
+__device__ __forceinline__ void loader_role(ChainSmem& sm, int lane, int N, int b, int C, const uint16_t* Qu,
+                                            const uint16_t* Ku, const uint16_t* Vu, const float* etau)
+{
+    constexpr int DPC = PT ? 7 : 6;   // ring-load instructions per chunk
+    const int g = lane >> 4, n = lane & 15;
+    const int npro = min(PFD, C);
+    for (int j = 0; j < npro; ++j) issue_chunk<PT>(sm, j, lane, N, b, Qu, Ku, Vu, etau);
+    if (C >= PFD) wait_vm<DPC * (PFD - 2)>(); else wait_vm<0>();   // chunks 0, 1
+    lds_barrier();
+    if (C > 1) publish_p(sm, 1, g, n, lane);
+    if (C >= PFD) wait_vm<DPC * (PFD - 3)>(); else wait_vm<0>();   // chunk 2
+    lds_barrier();
+    for (int c = 0; c < C + 2; ++c) {
+        if (c + PFD < C) issue_chunk<PT>(sm, c + PFD, lane, N, b, Qu, Ku, Vu, etau);
+        if (c + 2 < C) publish_p(sm, c + 2, g, n, lane);
+        // chunk c + 3 is read after this barrier
+        if (c + PFD < C) wait_vm<DPC * (PFD - 3)>(); else wait_vm<0>();
+        lds_barrier();
+    }
+}
+
+// Residual input of the chain's gradient for chunk j, all four tiles, in the
+// chain's lane order (LN: 2 gamma (K - V + beta); plain: V).
+template <int KIND>
+__device__ __forceinline__ void publish_c(ChainSmem& sm, int j, int g, int n, int lane, const float (&c2g)[16],
+                                          const float (&c2gb)[16])
+{
+    const ChainSlot& s = sm.ring[j % RING];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int f = 16 * t + 4 * g;
+        const float4 vv = unpack4(ld8(s.v, n, f));
+        float4 r = vv;
+        if constexpr (KIND == 1) {
+            const float4 kk = unpack4(ld8(s.k, n, f));
+            r = make_float4(fmaf(kk.x - vv.x, c2g[4 * t], c2gb[4 * t]), fmaf(kk.y - vv.y, c2g[4 * t + 1], c2gb[4 * t + 1]),
+                            fmaf(kk.z - vv.z, c2g[4 * t + 2], c2gb[4 * t + 2]),
+                            fmaf(kk.w - vv.w, c2g[4 * t + 3], c2gb[4 * t + 3]));
+        }
+        sm.xc[j & 1][t][lane] = r;
+    }
+}
+
+template <int KIND>
+__device__ __forceinline__ void resid_role(ChainSmem& sm, int lane, int h, int C, const float* gamma,
+                                           const float* beta)
+{
+    const int g = lane >> 4, n = lane & 15;
+    float c2g[16], c2gb[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int f = 16 * (j >> 2) + 4 * g + (j & 3);
+        const float gm = (KIND == 1) ? gamma[h * D + f] : 0.f;
+        const float bt = (KIND == 1) ? beta[h * D + f] : 0.f;
+        c2g[j] = 2.f * gm;
+        c2gb[j] = 2.f * gm * bt;
+    }
+    lds_barrier();
+    if (C > 0) publish_c<KIND>(sm, 0, g, n, lane, c2g, c2gb);
+    if (C > 1) publish_c<KIND>(sm, 1, g, n, lane, c2g, c2gb);
+    lds_barrier();
+    for (int c = 0; c < C + 2; ++c) {
+        if (c + 2 < C) publish_c<KIND>(sm, c + 2, g, n, lane, c2g, c2gb);
+        lds_barrier();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The output waves
+// ---------------------------------------------------------------------------
+
 template <int KIND>
 __device__ __forceinline__ void out_role(ChainSmem& sm, int bt, int lane, int h, int N, int b, int C,
                                          const float* gamma, const float* beta, float eps, float* Zu)
 {
     const int g = lane >> 4, n = lane & 15;
     const int fo = 16 * bt + 4 * g;   // first of this lane's four output features
-    float gam[4], bet[4], c2g[4], c2gb[4];
+    float gam[4], bet[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         gam[i] = (KIND == 1) ? gamma[h * D + fo + i] : 0.f;
         bet[i] = (KIND == 1) ? beta[h * D + fo + i] : 0.f;
-        c2g[i] = 2.f * gam[i];
-        c2gb[i] = 2.f * gam[i] * bet[i];
     }
-
-    // the residual input of the chain's gradient for chunk j, tile b
-    auto publish_c = [&](int j) {
-        const ChainSlot& s = sm.ring[j % RING];
-        const float4 vv = unpack4(ld8(s.v, n, fo));
-        float4 r = vv;
-        if constexpr (KIND == 1) {
-            const float4 kk = unpack4(ld8(s.k, n, fo));
-            r = make_float4(fmaf(kk.x - vv.x, c2g[0], c2gb[0]), fmaf(kk.y - vv.y, c2g[1], c2gb[1]),
-                            fmaf(kk.z - vv.z, c2g[2], c2gb[2]), fmaf(kk.w - vv.w, c2g[3], c2gb[3]));
-        }
-        sm.xc[j & 1][bt][lane] = r;
-    };
-
-    lds_barrier();                       // chunk 0 in LDS
-    if (C > 0) publish_c(0);
+    lds_barrier();
     lds_barrier();
 
     f32x4 xq2 = {0.f, 0.f, 0.f, 0.f};   // final H_Q^T tile b of chunk c-2
@@ -438,18 +511,6 @@ __device__ __forceinline__ void out_role(ChainSmem& sm, int bt, int lane, int h,
 
     for (int c = 0; c < C + 2; ++c) {
         const int par = c & 1;
-        if (c + 1 < C) {
-            publish_c(c + 1);
-            if (bt == 0) {
-                // P_{c+1}^T = K_c K_{c+1}^T as two bf16 terms
-                const f32x4 p = row_dots(sm.ring[c % RING].k, sm.ring[(c + 1) % RING].k, g, n);
-                const float x[4] = {p[0], p[1], p[2], p[3]};
-                bf16x4 pt[2];
-                terms4<2>(x, pt);
-                sm.xp[(c + 1) & 1][0][lane] = __builtin_bit_cast(uint2, pt[0]);
-                sm.xp[(c + 1) & 1][1][lane] = __builtin_bit_cast(uint2, pt[1]);
-            }
-        }
         f32x4 xq1 = {0.f, 0.f, 0.f, 0.f};
         if (c >= 1 && c <= C) {
             // H_Q^T(c-1) = Q W part + (-Gt_{c-1})^T tril(S_{c-1})^T
@@ -530,14 +591,20 @@ smallb_chain_kernel(int H, int N, int b, const uint16_t* __restrict__ Qg, const 
     const size_t unit = blockIdx.x;
     const int h = (int)(unit % H);
     const int C = (N + b - 1) / b;
+    // roles by wave index (wave w runs on SIMD w % 4; 4 and 8 share the chain's)
     if (w == 0) {
         chain_role<KIND, PT>(sm, lane, h, N, b, C, eta_const, gamma, eps);
-    } else if (w <= 4) {
-        w_role<PT>(sm, w - 1, lane, N, b, C, Qg + unit * (size_t)N * D, Kg + unit * (size_t)N * D,
-                   Vg + unit * (size_t)N * D, PT ? etag + unit * (size_t)N : nullptr, W0 + unit * (size_t)D * D,
-                   Wend + unit * (size_t)D * D);
+    } else if (w == 4) {
+        loader_role<PT>(sm, lane, N, b, C, Qg + unit * (size_t)N * D, Kg + unit * (size_t)N * D,
+                        Vg + unit * (size_t)N * D, PT ? etag + unit * (size_t)N : nullptr);
+    } else if (w == 8) {
+        resid_role<KIND>(sm, lane, h, C, gamma, beta);
+    } else if (w <= 5) {
+        const int bt = (w == 5) ? 3 : w - 1;
+        w_role(sm, bt, lane, C, W0 + unit * (size_t)D * D, Wend + unit * (size_t)D * D);
     } else {
-        out_role<KIND>(sm, w - 5, lane, h, N, b, C, gamma, beta, eps, Zg + unit * (size_t)N * D);
+        const int bt = (w <= 7) ? w - 6 : w - 7;
+        out_role<KIND>(sm, bt, lane, h, N, b, C, gamma, beta, eps, Zg + unit * (size_t)N * D);
     }
 }
 
