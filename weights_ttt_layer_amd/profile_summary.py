@@ -38,7 +38,7 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 # kernel sources behind each path; their digest tags a traffic record
 KERNEL_SOURCES = {
     "plain": ["smallb_linear.hip", "smallb_common.h", "device_common.h"],
-    "ln": ["smallb_linear.hip", "smallb_common.h", "device_common.h"],
+    "ln": ["smallb_chain.hip", "device_common.h"],
     "mlp": ["smallb_mlp.hip", "smallb_common.h", "device_common.h"],
     "large": ["large_chunk.hip", "device_common.h"],
     "block_before": ["large_chunk.hip", "device_common.h"],
@@ -47,14 +47,14 @@ KERNEL_SOURCES = {
     "layer": ["outer_layer.hip", "smallb_linear.hip", "smallb_common.h", "device_common.h"],
 }
 
-OUR_KERNELS = ("smallb_linear_kernel", "smallb_mlp_kernel", "lc_gram_kernel", "lc_scan_kernel",
+OUR_KERNELS = ("smallb_linear_kernel", "smallb_chain_kernel", "smallb_mlp_kernel", "lc_gram_kernel", "lc_scan_kernel",
                "lc_chunk_kernel", "lc_apply_kernel", "decode_kernel", "layer_gemm_kernel",
                "layer_outprep_kernel", "bwd_linear_kernel", "bwd_gamma_beta_kernel")
 
 # kernel-name prefixes launched by one call of each path
 PATH_KERNELS = {
     "plain": ("smallb_linear_kernel<0,",),
-    "ln": ("smallb_linear_kernel<1, unsigned short",),
+    "ln": ("smallb_chain_kernel<1,",),
     "mlp": ("smallb_mlp_kernel",),
     "large": ("lc_gram_kernel", "lc_scan_kernel", "lc_chunk_kernel"),
     "block_before": ("lc_gram_kernel", "lc_scan_kernel", "lc_apply_kernel<false>"),
