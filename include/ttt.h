@@ -277,8 +277,12 @@ int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b,
  *   workspace       device, 256-byte aligned, at least
  *                   ttt_layer_fwd_workspace_bytes(B, N, H, d) bytes = 5 S,
  *                   S = B*H*N*d*4 rounded up to a multiple of 256. On return it
- *                   holds the fp32 [B, H, N, d] arrays Q, K (normalised), V and Z
- *                   at offsets 0, S, 2S, 3S; the last S bytes are scratch.
+ *                   holds Q, K (normalised), V and Z at offsets 0, S, 2S, 3S; the
+ *                   last S bytes are scratch. Q, K and V are each two bf16
+ *                   [B, H, N, d] planes, the second starting B*H*N*d*2 bytes after
+ *                   the first: the RNE rounding of the fp32 value and the rounding
+ *                   of the remainder (their sum carries 16 significant bits); Z is
+ *                   fp32 [B, H, N, d].
  * x and the four weights must be 16-byte aligned. y, W_end and the workspace
  * must not overlap any input or each other (W_end may equal W0). Products run
  * on bf16 matrix cores with fp32 accumulation; the projected fp32 streams, the

@@ -3,7 +3,9 @@ inner TTT-Linear, output LayerNorm + residual + W_O) with the fp64 oracle, on
 identical seeded inputs (bf16 x and projection weights, fp32 state).
 
 Tolerances (max|gpu - ref| / max|ref| per tensor):
-  * Q, K, V: 1e-5 -- exact bf16 products summed in fp32.
+  * Q, K, V: 1e-5 -- exact bf16 products summed in fp32, stored as two bf16
+    terms (RNE rounding and the rounding of the remainder: at most 2^-18
+    relative per entry).
   * Z, W_end: 2e-5 -- the inner model carries the fp32 projected streams, the
     state and the gradients as two bf16 terms (16 significant bits, at most
     2^-16 relative per operand entry), products keeping the term pairs i+j < 2.

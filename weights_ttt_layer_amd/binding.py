@@ -327,12 +327,16 @@ def layer_fwd(x: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor, wv: torch.Ten
 
 
 def layer_parts(workspace: torch.Tensor, B: int, N: int, H: int, d: int) -> dict:
-    """Views of the Q, K, V, Z arrays a ``layer_fwd`` call left in its workspace."""
+    """The Q, K, V, Z arrays a ``layer_fwd`` call left in its workspace, fp32
+    [B, H, N, d]. Q, K, V are stored as two bf16 planes each (hi, then lo) and
+    returned as their sum; Z is a view of the fp32 array."""
     region = int(load_library().ttt_layer_fwd_workspace_bytes(B, N, H, d)) // 5
     n = B * H * N * d
     out = {}
-    for i, name in enumerate("QKVZ"):
-        out[name] = workspace[i * region:i * region + 4 * n].view(torch.float32).view(B, H, N, d)
+    for i, name in enumerate("QKV"):
+        planes = workspace[i * region:i * region + 4 * n].view(torch.bfloat16)
+        out[name] = (planes[:n].float() + planes[n:].float()).view(B, H, N, d)
+    out["Z"] = workspace[3 * region:3 * region + 4 * n].view(torch.float32).view(B, H, N, d)
     return out
 
 

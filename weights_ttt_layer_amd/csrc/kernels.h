@@ -48,9 +48,9 @@ struct MlpArgs {
 hipError_t launch_smallb_linear(const LinearArgs& a, hipStream_t stream);
 // bf16 token streams: the chain-on-one-wave kernel (smallb_chain.hip)
 hipError_t launch_smallb_chain(const LinearArgs& a, hipStream_t stream);
-// The same on fp32 streams carried as two bf16 terms (16 significant bits)
-// instead of three; the whole-layer path uses it for its projected streams.
-hipError_t launch_smallb_linear_f32x2(const LinearArgs& a, hipStream_t stream);
+// The same kernel on two-term streams: Q, K, V each a bf16 hi plane [B,H,N,d]
+// followed directly by its lo plane (the whole layer's projected streams).
+hipError_t launch_smallb_chain_terms2(const LinearArgs& a, hipStream_t stream);
 
 // Large-chunk path (plain f, bf16, d = 128, b % 128 == 0). `outputs` selects the
 // dual-form outputs (causal inside a chunk) or block-causal ones taken with the
@@ -97,10 +97,11 @@ struct LayerArgs {
 };
 // Bytes of one fp32 [B, H, N, 64] workspace array, rounded up to 256.
 size_t layer_workspace_region_bytes(int B, int N, int H);
-// Q, K (unit rows), V as fp32 [B, H, N, 64].
-hipError_t launch_layer_qkv(const LayerArgs& a, float* Q, float* K, float* V, hipStream_t stream);
-// y = W_O (LayerNorm(Z) * out_gamma + out_beta + Q), per head; `aext` is one
-// workspace region that receives the two-term operand.
-hipError_t launch_layer_out(const LayerArgs& a, const float* Z, const float* Q, void* aext, hipStream_t stream);
+// Q, K (unit rows), V, each as two bf16 planes [B, H, N, 64]: the RNE rounding
+// (hi) and the rounding of the remainder (lo), the lo plane right after the hi.
+hipError_t launch_layer_qkv(const LayerArgs& a, uint16_t* Q, uint16_t* K, uint16_t* V, hipStream_t stream);
+// y = W_O (LayerNorm(Z) * out_gamma + out_beta + Q), per head, Q as the two
+// planes above; `aext` is one workspace region that receives the two-term operand.
+hipError_t launch_layer_out(const LayerArgs& a, const float* Z, const uint16_t* Q, void* aext, hipStream_t stream);
 
 }  // namespace ttt

@@ -11,8 +11,9 @@
 //  * layer_gemm_kernel<.., EPI_QKV>: [Q | K | V] = x [W_Q; W_K; W_V]^T on bf16
 //    MFMA with fp32 accumulation. Each wave owns 64 tokens x 64 outputs = one
 //    head of one projection, so the key normalisation is a reduction inside
-//    the wave; Q, K, V leave in fp32, head-major [B, H, N, 64], the layout the
-//    inner kernel reads.
+//    the wave; Q, K, V leave head-major [B, H, N, 64] as two bf16 planes each
+//    (the RNE rounding, then the rounding of the remainder: 16 significant
+//    bits), the form in which the inner kernel consumes two-term streams.
 //  * layer_outprep_kernel: A = LayerNorm(z) * gamma_o + beta_o + q per (token,
 //    head) row, written token-major as two bf16 terms (16 significant bits).
 //  * layer_gemm_kernel<.., EPI_ROWS>: y = [A_hi | A_lo] [W_O | W_O]^T, i.e. the
@@ -32,15 +33,6 @@ constexpr int GT = 256;      // threads per workgroup (four waves)
 
 // Row of a 32x32 C-layout tile held by lane half h = lane / 32 at slot i.
 __device__ __forceinline__ int crow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
-
-// Direct global -> LDS load of 16 bytes per lane to lds + 16 * lane (see
-// large_chunk.hip for why this is assembly and why callers wait explicitly).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 // Logical tile of workgroup x. Workgroups are dealt to the eight XCDs round
 // robin; this gives XCD c a contiguous range of logical tiles.
@@ -102,9 +94,9 @@ struct GemmArgs {
     const uint16_t* W1;
     const uint16_t* W2;
     int rows_per_w;
-    float* out0;                 // EPI_QKV: Q, K, V; EPI_ROWS: y [tokens][n_out]
-    float* out1;
-    float* out2;
+    float* out0;                 // EPI_ROWS: y [tokens][n_out]
+    uint16_t* qkv[3];            // EPI_QKV: Q, K, V hi planes (lo planes `plane` elements later)
+    size_t plane;
 };
 
 template <int TM, int TN, int NS, int EPI>
@@ -209,7 +201,7 @@ layer_gemm_kernel(GemmArgs g)
     if (EPI == EPI_QKV) {
         // The wave's 64 outputs are one head of one projection.
         const int which = nw / g.rows_per_w, head = (nw - which * g.rows_per_w) / HDIM;
-        float* out = which == 0 ? g.out0 : (which == 1 ? g.out1 : g.out2);
+        uint16_t* out = g.qkv[which];
         float scale[2][16];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
@@ -228,16 +220,23 @@ layer_gemm_kernel(GemmArgs g)
                     scale[a][i] = s > 0.f ? 1.f / sqrtf(s) : 0.f;
                 }
         }
-        float* ob = out + ((size_t)bi * g.H + head) * (size_t)g.N * HDIM;
+        uint16_t* ob = out + ((size_t)bi * g.H + head) * (size_t)g.N * HDIM;
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int t = t0 + 64 * wr + 32 * a + crow(i, h);
                 if (t < g.N) {
-                    float* row = ob + (size_t)t * HDIM + l32;
-                    row[0] = acc[a][0][i] * scale[a][i];
-                    row[32] = acc[a][1][i] * scale[a][i];
+                    uint16_t* row = ob + (size_t)t * HDIM + l32;
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        // two bf16 terms: RNE rounding, then the rounding of the remainder
+                        const float v = acc[a][c][i] * scale[a][i];
+                        const __bf16 hi = (__bf16)v;
+                        const __bf16 lo = (__bf16)(v - (float)hi);
+                        row[32 * c] = __builtin_bit_cast(uint16_t, hi);
+                        row[32 * c + g.plane] = __builtin_bit_cast(uint16_t, lo);
+                    }
                 }
             }
     } else {
@@ -266,7 +265,8 @@ layer_gemm_kernel(GemmArgs g)
 constexpr int PT = 256;
 
 __global__ void __launch_bounds__(PT)
-layer_outprep_kernel(int N, int H, int rows, const float* __restrict__ Z, const float* __restrict__ Qf,
+layer_outprep_kernel(int N, int H, int rows, size_t plane, const float* __restrict__ Z,
+                     const uint16_t* __restrict__ Qh,
                      const float* __restrict__ gamma_o, const float* __restrict__ beta_o, float eps,
                      uint32_t* __restrict__ Aext)
 {
@@ -274,7 +274,13 @@ layer_outprep_kernel(int N, int H, int rows, const float* __restrict__ Z, const 
     const int row = gid >> 4, e = (gid & 15) * 4;     // row = (b*H + h)*N + t of the head-major arrays
     if (row >= rows) return;                          // whole DPP rows leave together
     const float4 z = *reinterpret_cast<const float4*>(Z + (size_t)row * HDIM + e);
-    const float4 q = *reinterpret_cast<const float4*>(Qf + (size_t)row * HDIM + e);
+    const uint2 qh = *reinterpret_cast<const uint2*>(Qh + (size_t)row * HDIM + e);
+    const uint2 ql = *reinterpret_cast<const uint2*>(Qh + plane + (size_t)row * HDIM + e);
+    const float4 q = make_float4(
+        __builtin_bit_cast(float, qh.x << 16) + __builtin_bit_cast(float, ql.x << 16),
+        __builtin_bit_cast(float, qh.x & 0xFFFF0000u) + __builtin_bit_cast(float, ql.x & 0xFFFF0000u),
+        __builtin_bit_cast(float, qh.y << 16) + __builtin_bit_cast(float, ql.y << 16),
+        __builtin_bit_cast(float, qh.y & 0xFFFF0000u) + __builtin_bit_cast(float, ql.y & 0xFFFF0000u));
     const int t = row % N, bh = row / N, hh = bh % H, bi = bh / H;
     const float mu = row16_sum(z.x + z.y + z.z + z.w) * (1.f / HDIM);
     const float c0 = z.x - mu, c1 = z.y - mu, c2 = z.z - mu, c3 = z.w - mu;
@@ -307,7 +313,7 @@ size_t layer_workspace_region_bytes(int B, int N, int H)
     return (s + 255) & ~(size_t)255;
 }
 
-hipError_t launch_layer_qkv(const LayerArgs& a, float* Qo, float* Ko, float* Vo, hipStream_t stream)
+hipError_t launch_layer_qkv(const LayerArgs& a, uint16_t* Qo, uint16_t* Ko, uint16_t* Vo, hipStream_t stream)
 {
     GemmArgs g{};
     g.N = a.N;
@@ -325,21 +331,23 @@ hipError_t launch_layer_qkv(const LayerArgs& a, float* Qo, float* Ko, float* Vo,
     g.W0 = static_cast<const uint16_t*>(a.Wq);
     g.W1 = static_cast<const uint16_t*>(a.Wk);
     g.W2 = static_cast<const uint16_t*>(a.Wv);
-    g.out0 = Qo;
-    g.out1 = Ko;
-    g.out2 = Vo;
+    g.qkv[0] = Qo;
+    g.qkv[1] = Ko;
+    g.qkv[2] = Vo;
+    g.plane = (size_t)a.B * a.H * a.N * HDIM;
     hipLaunchKernelGGL((layer_gemm_kernel<P_TM, P_TN, P_NS, EPI_QKV>), dim3(g.total), dim3(P_TM * P_TN / 64), 0,
                        stream, g);
     return hipGetLastError();
 }
 
-hipError_t launch_layer_out(const LayerArgs& a, const float* Z, const float* Qf, void* aext, hipStream_t stream)
+hipError_t launch_layer_out(const LayerArgs& a, const float* Z, const uint16_t* Qh, void* aext, hipStream_t stream)
 {
     const int HD = a.H * HDIM;
     const int rows = a.B * a.H * a.N;
     const size_t threads = (size_t)rows * 16;
     hipLaunchKernelGGL(layer_outprep_kernel, dim3((unsigned)((threads + PT - 1) / PT)), dim3(PT), 0, stream, a.N,
-                       a.H, rows, Z, Qf, a.out_gamma, a.out_beta, a.eps, static_cast<uint32_t*>(aext));
+                       a.H, rows, (size_t)a.B * a.H * a.N * HDIM, Z, Qh, a.out_gamma, a.out_beta, a.eps,
+                       static_cast<uint32_t*>(aext));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     GemmArgs g{};

@@ -1,6 +1,7 @@
 // smallb_chain.hip -- TTT-Linear forward (plain and LayerNorm+residual inner
-// model), d = 64, 1 <= b <= 16, bf16 token streams: the chunk-to-chunk chain
-// on one wave, the state and the outputs on eight more.
+// model), d = 64, 1 <= b <= 16, token streams as one bf16 term (bf16 input) or
+// two (fp32 streams carried as hi + lo planes): the chunk-to-chunk chain on one
+// wave, the state and the outputs on ten more.
 //
 // Method: web page "Test-Time Training: Linear Complexity Beyond Attention",
 // sections "2. The Online Gradient Descent Update Rule", "3. Forward Evaluation
@@ -51,7 +52,8 @@
 //
 // Precision as elsewhere: fp32 operands (state, gradient, scores, P) as two
 // bf16 terms, products keeping the pairs (hi, hi), (hi, lo), (lo, hi); bf16
-// token streams exact in one term; fp32 accumulation.
+// token streams exact in one term, two-term streams as two planes (TIN = 2);
+// fp32 accumulation.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -61,21 +63,27 @@ namespace {
 constexpr int D = 64;
 constexpr int NWAVE = 11;
 constexpr int NTHR = 64 * NWAVE;
-constexpr int RING = 12;     // Q/K/V/eta chunk slots
-constexpr int PFD = 8;       // chunks requested ahead of the one being stepped
-static_assert(RING >= PFD + 3, "slots of chunks c-2 .. c+2 are read during step c");
+// Ring geometry per stream term count: slots, and chunks requested ahead of
+// the one being stepped (slots of chunks c-2 .. c+2 are read during step c).
+template <int TIN> struct RingGeom {
+    static constexpr int SLOTS = TIN == 1 ? 12 : 8;
+    static constexpr int AHEAD = TIN == 1 ? 8 : 5;
+    static_assert(SLOTS >= AHEAD + 3, "slot reuse");
+};
 
-// One chunk of the ring: [token][feature] bf16 tiles of 16 rows x 128 bytes,
-// 16-byte piece p of row r stored at slot p ^ (r & 7).
+// One chunk of the ring: per stream term, [token][feature] bf16 tiles of 16
+// rows x 128 bytes, 16-byte piece p of row r stored at slot p ^ (r & 7).
+template <int TIN>
 struct alignas(16) ChainSlot {
-    uint16_t k[16 * D];
-    uint16_t q[16 * D];
-    uint16_t v[16 * D];
+    uint16_t k[TIN][16 * D];
+    uint16_t q[TIN][16 * D];
+    uint16_t v[TIN][16 * D];
     float eta[64];           // rows 0..15 used
 };
 
+template <int TIN>
 struct alignas(16) ChainSmem {
-    ChainSlot ring[RING];
+    ChainSlot<TIN> ring[RingGeom<TIN>::SLOTS];
     float4 xa[2][4][64];          // A^T of a chunk, tile t, lane order of the chain's C layout
     float4 xq[2][4][64];          // Q W part of H_Q^T of a chunk, same layout
     float4 xc[2][4][64];          // residual input of the gradient (LN: 2 gamma (K - V + beta); plain: V)
@@ -143,24 +151,41 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Ring loads of chunk j (rows j*b .. j*b+15, clamped to the sequence): K, Q, V
-// two 1 KB instructions each, plus one for eta when it is per token.
-template <bool PT>
-__device__ __forceinline__ void issue_chunk(ChainSmem& sm, int j, int lane, int N, int b, const uint16_t* Qu,
-                                            const uint16_t* Ku, const uint16_t* Vu, const float* etau)
+// Ring loads of chunk j (rows j*b .. j*b+15, clamped to the sequence): per
+// stream term, K, Q, V two 1 KB instructions each, plus one for eta when it is
+// per token. Term s of a stream is the plane at element offset s * plane.
+template <int TIN, bool PT>
+__device__ __forceinline__ void issue_chunk(ChainSmem<TIN>& sm, int j, int lane, int N, int b, size_t plane,
+                                            const uint16_t* Qu, const uint16_t* Ku, const uint16_t* Vu,
+                                            const float* etau)
 {
-    ChainSlot& s = sm.ring[j % RING];
+    ChainSlot<TIN>& s = sm.ring[j % RingGeom<TIN>::SLOTS];
     const int t0 = j * b;
 #pragma unroll
     for (int ins = 0; ins < 2; ++ins) {
         const int sl = ins * 64 + lane;
         const int r = sl >> 3, p = (sl & 7) ^ (r & 7);
         const size_t off = (size_t)min(t0 + r, N - 1) * D + p * 8;
-        dma16(Ku + off, __builtin_amdgcn_readfirstlane(lds_addr(s.k) + ins * 1024));
-        dma16(Qu + off, __builtin_amdgcn_readfirstlane(lds_addr(s.q) + ins * 1024));
-        dma16(Vu + off, __builtin_amdgcn_readfirstlane(lds_addr(s.v) + ins * 1024));
+#pragma unroll
+        for (int tm = 0; tm < TIN; ++tm) {
+            dma16(Ku + tm * plane + off, __builtin_amdgcn_readfirstlane(lds_addr(s.k[tm]) + ins * 1024));
+            dma16(Qu + tm * plane + off, __builtin_amdgcn_readfirstlane(lds_addr(s.q[tm]) + ins * 1024));
+            dma16(Vu + tm * plane + off, __builtin_amdgcn_readfirstlane(lds_addr(s.v[tm]) + ins * 1024));
+        }
     }
     if constexpr (PT) dma4(etau + min(t0 + min(lane, 15), N - 1), __builtin_amdgcn_readfirstlane(lds_addr(s.eta)));
+}
+
+// Four consecutive stream elements (row, col .. col+3) as fp32, all terms summed.
+template <int TIN>
+__device__ __forceinline__ float4 stream4(const uint16_t (&t)[TIN][16 * D], int row, int col)
+{
+    float4 v = unpack4(ld8(t[0], row, col));
+    if constexpr (TIN == 2) {
+        const float4 l = unpack4(ld8(t[1], row, col));
+        v = make_float4(v.x + l.x, v.y + l.y, v.z + l.z, v.w + l.w);
+    }
+    return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -176,8 +201,8 @@ struct ChainPre {
     float eta;
 };
 
-template <bool PT>
-__device__ __forceinline__ void chain_prefetch(const ChainSmem& sm, int c, int bc, int g, int n, int lane,
+template <int TIN, bool PT>
+__device__ __forceinline__ void chain_prefetch(const ChainSmem<TIN>& sm, int c, int bc, int g, int n, int lane,
                                                float eta_const, ChainPre& pre)
 {
     const int par = c & 1;
@@ -202,13 +227,13 @@ __device__ __forceinline__ void chain_prefetch(const ChainSmem& sm, int c, int b
         pre.cp[4 * t + 3] = r.w;
     }
     float eta = eta_const;
-    if constexpr (PT) eta = sm.ring[c % RING].eta[n];
+    if constexpr (PT) eta = sm.ring[c % RingGeom<TIN>::SLOTS].eta[n];
     pre.eta = (n < bc) ? eta : 0.f;
 }
 
 // One chain step: -Gt_c from A_c^T and the prefetched operands.
-template <int KIND>
-__device__ __forceinline__ void chain_step(ChainSmem& sm, int c, int g, int n, int lane, const ChainPre& pre,
+template <int KIND, int TIN>
+__device__ __forceinline__ void chain_step(ChainSmem<TIN>& sm, int c, int g, int n, int lane, const ChainPre& pre,
                                            const float (&g2)[16], float eps)
 {
     const int par = c & 1;
@@ -283,9 +308,9 @@ __device__ __forceinline__ void chain_step(ChainSmem& sm, int c, int g, int n, i
     }
 }
 
-template <int KIND, bool PT>
-__device__ __forceinline__ void chain_role(ChainSmem& sm, int lane, int h, int N, int b, int C, float eta_const,
-                                           const float* gamma, float eps)
+template <int KIND, int TIN, bool PT>
+__device__ __forceinline__ void chain_role(ChainSmem<TIN>& sm, int lane, int h, int N, int b, int C,
+                                           float eta_const, const float* gamma, float eps)
 {
     const int g = lane >> 4, n = lane & 15;
     __builtin_amdgcn_s_setprio(3);
@@ -300,12 +325,12 @@ __device__ __forceinline__ void chain_role(ChainSmem& sm, int lane, int h, int N
     lds_barrier();
     lds_barrier();
     ChainPre pre;
-    if (C > 0) chain_prefetch<PT>(sm, 0, min(b, N), g, n, lane, eta_const, pre);
+    if (C > 0) chain_prefetch<TIN, PT>(sm, 0, min(b, N), g, n, lane, eta_const, pre);
     for (int c = 0; c < C + 2; ++c) {
         if (c < C) {
-            chain_step<KIND>(sm, c, g, n, lane, pre, g2, eps);
+            chain_step<KIND, TIN>(sm, c, g, n, lane, pre, g2, eps);
             // operands of chunk c+1 (its own -Gt_c included: LDS ops of one wave are ordered)
-            if (c + 1 < C) chain_prefetch<PT>(sm, c + 1, min(b, N - (c + 1) * b), g, n, lane, eta_const, pre);
+            if (c + 1 < C) chain_prefetch<TIN, PT>(sm, c + 1, min(b, N - (c + 1) * b), g, n, lane, eta_const, pre);
         }
         lds_barrier();
     }
@@ -327,32 +352,49 @@ __device__ __forceinline__ void split_w(const f32x4 (&Wf)[4], bf16x8 (&Wt)[2][2]
     }
 }
 
-// W^T X^T for the 16 rows of a ring tile (X = K or Q): C layout lane (g, n) =
-// row n, output features 16b + 4g + i. B operand in the k order of split_w.
-__device__ __forceinline__ f32x4 wt_rows(const bf16x8 (&Wt)[2][2], const uint16_t* xt, int g, int n)
+// W^T X^T for the 16 rows of a ring tile (X = K or Q, TIN terms): C layout
+// lane (g, n) = row n, output features 16b + 4g + i. B operand in the k order
+// of split_w.
+template <int TIN>
+__device__ __forceinline__ f32x4 wt_rows(const bf16x8 (&Wt)[2][2], const uint16_t (&xt)[TIN][16 * D], int g, int n)
 {
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        const bf16x8 xb = cat8(ld8(xt, n, 32 * p + 4 * g), ld8(xt, n, 32 * p + 16 + 4 * g));
-        a = mfma_16x16x32(Wt[p][1], xb, a);
-        a = mfma_16x16x32(Wt[p][0], xb, a);
+        const bf16x8 x0 = cat8(ld8(xt[0], n, 32 * p + 4 * g), ld8(xt[0], n, 32 * p + 16 + 4 * g));
+        a = mfma_16x16x32(Wt[p][1], x0, a);
+        if constexpr (TIN == 2) {
+            const bf16x8 x1 = cat8(ld8(xt[1], n, 32 * p + 4 * g), ld8(xt[1], n, 32 * p + 16 + 4 * g));
+            a = mfma_16x16x32(Wt[p][0], x1, a);
+        }
+        a = mfma_16x16x32(Wt[p][0], x0, a);
     }
     return a;
 }
 
-// Row products X Y^T of two ring tiles (k = features, natural order): C layout
-// lane (g, n) = X[4g + i] . Y[n].
-__device__ __forceinline__ f32x4 row_dots(const uint16_t* xt, const uint16_t* yt, int g, int n)
+// Row products X Y^T of two ring tiles (k = features, natural order; TIN terms
+// each, pairs (hi, hi), (hi, lo), (lo, hi)): C layout lane (g, n) = X[4g + i] . Y[n].
+template <int TIN>
+__device__ __forceinline__ f32x4 row_dots(const uint16_t (&xt)[TIN][16 * D], const uint16_t (&yt)[TIN][16 * D], int g,
+                                          int n)
 {
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < 2; ++p) a = mfma_16x16x32(ld16(xt, n, 32 * p + 8 * g), ld16(yt, n, 32 * p + 8 * g), a);
+    for (int p = 0; p < 2; ++p) {
+        const bf16x8 x0 = ld16(xt[0], n, 32 * p + 8 * g), y0 = ld16(yt[0], n, 32 * p + 8 * g);
+        if constexpr (TIN == 2) {
+            a = mfma_16x16x32(ld16(xt[1], n, 32 * p + 8 * g), y0, a);
+            a = mfma_16x16x32(x0, ld16(yt[1], n, 32 * p + 8 * g), a);
+        }
+        a = mfma_16x16x32(x0, y0, a);
+    }
     return a;
 }
 
-__device__ __forceinline__ void w_role(ChainSmem& sm, int bt, int lane, int C, const float* W0u, float* Wu)
+template <int TIN>
+__device__ __forceinline__ void w_role(ChainSmem<TIN>& sm, int bt, int lane, int C, const float* W0u, float* Wu)
 {
+    constexpr int SL = RingGeom<TIN>::SLOTS;
     const int g = lane >> 4, n = lane & 15;
     __builtin_amdgcn_s_setprio(2);
 
@@ -367,32 +409,36 @@ __device__ __forceinline__ void w_role(ChainSmem& sm, int bt, int lane, int C, c
 
     lds_barrier();                       // chunks 0 and 1 in LDS
     if (C > 0) {
-        const f32x4 a = wt_rows(Wt, sm.ring[0].k, g, n);
+        const f32x4 a = wt_rows<TIN>(Wt, sm.ring[0].k, g, n);
         sm.xa[0][bt][lane] = make_float4(a[0], a[1], a[2], a[3]);
     }
     lds_barrier();
 
     for (int c = 0; c < C + 2; ++c) {
         if (c >= 1 && c <= C) {
-            // W_c = W_{c-1} + K_{c-1}^T (-Gt_{c-1}); k = 16 tokens x 2 terms stacked
-            const uint16_t* kt = sm.ring[(c - 1) % RING].k;
+            // W_c = W_{c-1} + K_{c-1}^T (-Gt_{c-1}); k = 16 tokens x 2 terms of Gt stacked
+            const auto& kt = sm.ring[(c - 1) % SL].k;
             const uint16_t* gtt = sm.gt[(c - 1) & 1][g >> 1];
             const int row = 8 * (g & 1) + (n >> 2);
             const int cq = 4 * (n & 3);
             const bf16x8 gb = cat8(tr4(gtt, row, 16 * bt + cq), tr4(gtt, row + 4, 16 * bt + cq));
+            bf16x4 gh = {};
+            if constexpr (TIN == 2) gh = tr4(sm.gt[(c - 1) & 1][0], 4 * g + (n >> 2), 16 * bt + cq);
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const bf16x8 ka = cat8(tr4(kt, row, 16 * a + cq), tr4(kt, row + 4, 16 * a + cq));
+                const bf16x8 ka = cat8(tr4(kt[0], row, 16 * a + cq), tr4(kt[0], row + 4, 16 * a + cq));
                 Wf[a] = mfma_16x16x32(ka, gb, Wf[a]);
+                if constexpr (TIN == 2)   // the lo term of K against the hi term of Gt
+                    Wf[a] = mfma_16x16x16(tr4(kt[1], 4 * g + (n >> 2), 16 * a + cq), gh, Wf[a]);
             }
             if (c < C) split_w(Wf, Wt);
         }
         if (c + 1 < C) {
-            const f32x4 a = wt_rows(Wt, sm.ring[(c + 1) % RING].k, g, n);
+            const f32x4 a = wt_rows<TIN>(Wt, sm.ring[(c + 1) % SL].k, g, n);
             sm.xa[(c + 1) & 1][bt][lane] = make_float4(a[0], a[1], a[2], a[3]);
         }
         if (c < C) {
-            const f32x4 q = wt_rows(Wt, sm.ring[c % RING].q, g, n);
+            const f32x4 q = wt_rows<TIN>(Wt, sm.ring[c % SL].q, g, n);
             sm.xq[c & 1][bt][lane] = make_float4(q[0], q[1], q[2], q[3]);
         }
         lds_barrier();
@@ -409,9 +455,11 @@ __device__ __forceinline__ void w_role(ChainSmem& sm, int bt, int lane, int C, c
 // ---------------------------------------------------------------------------
 
 // P_j^T = K_{j-1} K_j^T as two bf16 terms, for the chain's chunk j.
-__device__ __forceinline__ void publish_p(ChainSmem& sm, int j, int g, int n, int lane)
+template <int TIN>
+__device__ __forceinline__ void publish_p(ChainSmem<TIN>& sm, int j, int g, int n, int lane)
 {
-    const f32x4 p = row_dots(sm.ring[(j - 1) % RING].k, sm.ring[j % RING].k, g, n);
+    constexpr int SL = RingGeom<TIN>::SLOTS;
+    const f32x4 p = row_dots<TIN>(sm.ring[(j - 1) % SL].k, sm.ring[j % SL].k, g, n);
     const float x[4] = {p[0], p[1], p[2], p[3]};
     bf16x4 pt[2];
     terms4<2>(x, pt);
@@ -419,42 +467,44 @@ __device__ __forceinline__ void publish_p(ChainSmem& sm, int j, int g, int n, in
     sm.xp[j & 1][1][lane] = __builtin_bit_cast(uint2, pt[1]);
 }
 
-template <bool PT>
-__device__ __forceinline__ void loader_role(ChainSmem& sm, int lane, int N, int b, int C, const uint16_t* Qu,
-                                            const uint16_t* Ku, const uint16_t* Vu, const float* etau)
+template <int TIN, bool PT>
+__device__ __forceinline__ void loader_role(ChainSmem<TIN>& sm, int lane, int N, int b, int C, size_t plane,
+                                            const uint16_t* Qu, const uint16_t* Ku, const uint16_t* Vu,
+                                            const float* etau)
 {
-    constexpr int DPC = PT ? 7 : 6;   // ring-load instructions per chunk
+    constexpr int DPC = 6 * TIN + (PT ? 1 : 0);   // ring-load instructions per chunk
+    constexpr int AH = RingGeom<TIN>::AHEAD;
     const int g = lane >> 4, n = lane & 15;
-    const int npro = min(PFD, C);
-    for (int j = 0; j < npro; ++j) issue_chunk<PT>(sm, j, lane, N, b, Qu, Ku, Vu, etau);
-    if (C >= PFD) wait_vm<DPC * (PFD - 2)>(); else wait_vm<0>();   // chunks 0, 1
+    const int npro = min(AH, C);
+    for (int j = 0; j < npro; ++j) issue_chunk<TIN, PT>(sm, j, lane, N, b, plane, Qu, Ku, Vu, etau);
+    if (C >= AH) wait_vm<DPC * (AH - 2)>(); else wait_vm<0>();   // chunks 0, 1
     lds_barrier();
-    if (C > 1) publish_p(sm, 1, g, n, lane);
-    if (C >= PFD) wait_vm<DPC * (PFD - 3)>(); else wait_vm<0>();   // chunk 2
+    if (C > 1) publish_p<TIN>(sm, 1, g, n, lane);
+    if (C >= AH) wait_vm<DPC * (AH - 3)>(); else wait_vm<0>();   // chunk 2
     lds_barrier();
     for (int c = 0; c < C + 2; ++c) {
-        if (c + PFD < C) issue_chunk<PT>(sm, c + PFD, lane, N, b, Qu, Ku, Vu, etau);
-        if (c + 2 < C) publish_p(sm, c + 2, g, n, lane);
+        if (c + AH < C) issue_chunk<TIN, PT>(sm, c + AH, lane, N, b, plane, Qu, Ku, Vu, etau);
+        if (c + 2 < C) publish_p<TIN>(sm, c + 2, g, n, lane);
         // chunk c + 3 is read after this barrier
-        if (c + PFD < C) wait_vm<DPC * (PFD - 3)>(); else wait_vm<0>();
+        if (c + AH < C) wait_vm<DPC * (AH - 3)>(); else wait_vm<0>();
         lds_barrier();
     }
 }
 
 // Residual input of the chain's gradient for chunk j, all four tiles, in the
 // chain's lane order (LN: 2 gamma (K - V + beta); plain: V).
-template <int KIND>
-__device__ __forceinline__ void publish_c(ChainSmem& sm, int j, int g, int n, int lane, const float (&c2g)[16],
+template <int KIND, int TIN>
+__device__ __forceinline__ void publish_c(ChainSmem<TIN>& sm, int j, int g, int n, int lane, const float (&c2g)[16],
                                           const float (&c2gb)[16])
 {
-    const ChainSlot& s = sm.ring[j % RING];
+    const ChainSlot<TIN>& s = sm.ring[j % RingGeom<TIN>::SLOTS];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int f = 16 * t + 4 * g;
-        const float4 vv = unpack4(ld8(s.v, n, f));
+        const float4 vv = stream4<TIN>(s.v, n, f);
         float4 r = vv;
         if constexpr (KIND == 1) {
-            const float4 kk = unpack4(ld8(s.k, n, f));
+            const float4 kk = stream4<TIN>(s.k, n, f);
             r = make_float4(fmaf(kk.x - vv.x, c2g[4 * t], c2gb[4 * t]), fmaf(kk.y - vv.y, c2g[4 * t + 1], c2gb[4 * t + 1]),
                             fmaf(kk.z - vv.z, c2g[4 * t + 2], c2gb[4 * t + 2]),
                             fmaf(kk.w - vv.w, c2g[4 * t + 3], c2gb[4 * t + 3]));
@@ -463,8 +513,8 @@ __device__ __forceinline__ void publish_c(ChainSmem& sm, int j, int g, int n, in
     }
 }
 
-template <int KIND>
-__device__ __forceinline__ void resid_role(ChainSmem& sm, int lane, int h, int C, const float* gamma,
+template <int KIND, int TIN>
+__device__ __forceinline__ void resid_role(ChainSmem<TIN>& sm, int lane, int h, int C, const float* gamma,
                                            const float* beta)
 {
     const int g = lane >> 4, n = lane & 15;
@@ -478,11 +528,11 @@ __device__ __forceinline__ void resid_role(ChainSmem& sm, int lane, int h, int C
         c2gb[j] = 2.f * gm * bt;
     }
     lds_barrier();
-    if (C > 0) publish_c<KIND>(sm, 0, g, n, lane, c2g, c2gb);
-    if (C > 1) publish_c<KIND>(sm, 1, g, n, lane, c2g, c2gb);
+    if (C > 0) publish_c<KIND, TIN>(sm, 0, g, n, lane, c2g, c2gb);
+    if (C > 1) publish_c<KIND, TIN>(sm, 1, g, n, lane, c2g, c2gb);
     lds_barrier();
     for (int c = 0; c < C + 2; ++c) {
-        if (c + 2 < C) publish_c<KIND>(sm, c + 2, g, n, lane, c2g, c2gb);
+        if (c + 2 < C) publish_c<KIND, TIN>(sm, c + 2, g, n, lane, c2g, c2gb);
         lds_barrier();
     }
 }
@@ -491,10 +541,11 @@ __device__ __forceinline__ void resid_role(ChainSmem& sm, int lane, int h, int C
 // The output waves
 // ---------------------------------------------------------------------------
 
-template <int KIND>
-__device__ __forceinline__ void out_role(ChainSmem& sm, int bt, int lane, int h, int N, int b, int C,
+template <int KIND, int TIN>
+__device__ __forceinline__ void out_role(ChainSmem<TIN>& sm, int bt, int lane, int h, int N, int b, int C,
                                          const float* gamma, const float* beta, float eps, float* Zu)
 {
+    constexpr int SL = RingGeom<TIN>::SLOTS;
     const int g = lane >> 4, n = lane & 15;
     const int fo = 16 * bt + 4 * g;   // first of this lane's four output features
     float gam[4], bet[4];
@@ -530,8 +581,8 @@ __device__ __forceinline__ void out_role(ChainSmem& sm, int bt, int lane, int h,
         bf16x4 sbn[2] = {};
         if (c < C) {
             // S_c^T = K_c Q_c^T, causal part (key 4g + i <= query n)
-            const ChainSlot& s = sm.ring[c % RING];
-            const f32x4 st = row_dots(s.k, s.q, g, n);
+            const ChainSlot<TIN>& s = sm.ring[c % SL];
+            const f32x4 st = row_dots<TIN>(s.k, s.q, g, n);
             float x[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[i] = (4 * g + i <= n) ? st[i] : 0.f;
@@ -562,7 +613,7 @@ __device__ __forceinline__ void out_role(ChainSmem& sm, int bt, int lane, int h,
                 const float S2 = (pa.y + pa.w) + (pb.y + pb.w);
                 const float mu = S1 * (1.f / D);
                 const float rs = __builtin_amdgcn_rsqf(fmaxf(S2 * (1.f / D) - mu * mu, 0.f) + eps);
-                const float4 q = unpack4(ld8(sm.ring[m % RING].q, n, fo));
+                const float4 q = stream4<TIN>(sm.ring[m % SL].q, n, fo);
                 const float qv[4] = {q.x, q.y, q.z, q.w};
                 float z[4];
 #pragma unroll
@@ -578,14 +629,15 @@ __device__ __forceinline__ void out_role(ChainSmem& sm, int bt, int lane, int h,
     }
 }
 
-template <int KIND, bool PT>
+template <int KIND, int TIN, bool PT>
 __global__ void __launch_bounds__(NTHR)
-smallb_chain_kernel(int H, int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
-                    const uint16_t* __restrict__ Vg, const float* __restrict__ etag, float eta_const,
-                    const float* __restrict__ W0, const float* __restrict__ gamma,
-                    const float* __restrict__ beta, float eps, float* __restrict__ Zg, float* __restrict__ Wend)
+smallb_chain_kernel(int H, int N, int b, size_t plane, const uint16_t* __restrict__ Qg,
+                    const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
+                    const float* __restrict__ etag, float eta_const, const float* __restrict__ W0,
+                    const float* __restrict__ gamma, const float* __restrict__ beta, float eps,
+                    float* __restrict__ Zg, float* __restrict__ Wend)
 {
-    __shared__ ChainSmem sm;
+    __shared__ ChainSmem<TIN> sm;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const size_t unit = blockIdx.x;
@@ -593,37 +645,43 @@ smallb_chain_kernel(int H, int N, int b, const uint16_t* __restrict__ Qg, const 
     const int C = (N + b - 1) / b;
     // roles by wave index (wave w runs on SIMD w % 4; 4 and 8 share the chain's)
     if (w == 0) {
-        chain_role<KIND, PT>(sm, lane, h, N, b, C, eta_const, gamma, eps);
+        chain_role<KIND, TIN, PT>(sm, lane, h, N, b, C, eta_const, gamma, eps);
     } else if (w == 4) {
-        loader_role<PT>(sm, lane, N, b, C, Qg + unit * (size_t)N * D, Kg + unit * (size_t)N * D,
-                        Vg + unit * (size_t)N * D, PT ? etag + unit * (size_t)N : nullptr);
+        loader_role<TIN, PT>(sm, lane, N, b, C, plane, Qg + unit * (size_t)N * D, Kg + unit * (size_t)N * D,
+                             Vg + unit * (size_t)N * D, PT ? etag + unit * (size_t)N : nullptr);
     } else if (w == 8) {
-        resid_role<KIND>(sm, lane, h, C, gamma, beta);
+        resid_role<KIND, TIN>(sm, lane, h, C, gamma, beta);
     } else if (w <= 5) {
         const int bt = (w == 5) ? 3 : w - 1;
-        w_role(sm, bt, lane, C, W0 + unit * (size_t)D * D, Wend + unit * (size_t)D * D);
+        w_role<TIN>(sm, bt, lane, C, W0 + unit * (size_t)D * D, Wend + unit * (size_t)D * D);
     } else {
         const int bt = (w <= 7) ? w - 6 : w - 7;
-        out_role<KIND>(sm, bt, lane, h, N, b, C, gamma, beta, eps, Zg + unit * (size_t)N * D);
+        out_role<KIND, TIN>(sm, bt, lane, h, N, b, C, gamma, beta, eps, Zg + unit * (size_t)N * D);
     }
 }
 
-template <int KIND, bool PT>
+template <int KIND, int TIN, bool PT>
 hipError_t launch_typed(const LinearArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((smallb_chain_kernel<KIND, PT>), dim3(a.B * a.H), dim3(NTHR), 0, stream, a.H, a.N, a.b,
-                       static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+    const size_t plane = (size_t)a.B * a.H * a.N * D;
+    hipLaunchKernelGGL((smallb_chain_kernel<KIND, TIN, PT>), dim3(a.B * a.H), dim3(NTHR), 0, stream, a.H, a.N, a.b,
+                       plane, static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.eta, a.eta_const, a.W0, a.gamma, a.beta, a.eps,
                        a.Z, a.W_end);
     return hipGetLastError();
 }
 
+template <int TIN>
+hipError_t launch_terms(const LinearArgs& a, hipStream_t stream)
+{
+    if (a.kind == 1) return a.eta ? launch_typed<1, TIN, true>(a, stream) : launch_typed<1, TIN, false>(a, stream);
+    return a.eta ? launch_typed<0, TIN, true>(a, stream) : launch_typed<0, TIN, false>(a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_smallb_chain(const LinearArgs& a, hipStream_t stream)
-{
-    if (a.kind == 1) return a.eta ? launch_typed<1, true>(a, stream) : launch_typed<1, false>(a, stream);
-    return a.eta ? launch_typed<0, true>(a, stream) : launch_typed<0, false>(a, stream);
-}
+hipError_t launch_smallb_chain(const LinearArgs& a, hipStream_t stream) { return launch_terms<1>(a, stream); }
+
+hipError_t launch_smallb_chain_terms2(const LinearArgs& a, hipStream_t stream) { return launch_terms<2>(a, stream); }
 
 }  // namespace ttt

@@ -1,5 +1,7 @@
 // smallb_linear.hip -- TTT-Linear forward (plain and LayerNorm+residual inner
-// model) for small mini-batches, d = 64, 1 <= b <= 16.
+// model) for small mini-batches, d = 64, 1 <= b <= 16, fp32 token streams.
+// (bf16 and two-term streams run the chain-on-one-wave kernel of
+// smallb_chain.hip.)
 //
 // Method: web page "Test-Time Training: Linear Complexity Beyond Attention",
 // sections "2. The Online Gradient Descent Update Rule", "3. Forward Evaluation
@@ -29,10 +31,9 @@
 //    K^T Gt and (as Gt^T) the A operand of the causal term Gt^T tril(S)^T.
 //  * S^T = K Q^T is computed so that its C layout is exactly the B operand of
 //    Gt^T S^T.
-//  * fp32 operands (state, gradient, scores) are split into bf16 terms: 2 next
-//    to bf16 token streams, 3 next to fp32 streams, which use 3 terms too. A
-//    variant carries fp32 streams and fp32 operands in 2 terms (16 significant
-//    bits); the whole-layer path launches it for its projected streams.
+//  * fp32 operands (state, gradient, scores) are split into bf16 terms: 3 next
+//    to fp32 streams, which use 3 terms too (2 next to bf16 streams, for which
+//    the template is still written).
 //  * Q/K/V/eta chunks are prefetched PF chunks ahead into a register ring and
 //    staged through double-buffered, row-padded LDS tiles. Per chunk: one
 //    workgroup barrier (plain) or two (LayerNorm: forward statistics together
@@ -368,11 +369,6 @@ hipError_t launch_smallb_linear(const LinearArgs& a, hipStream_t stream)
 {
     if (a.dtype == 1) return launch_smallb_chain(a, stream);
     return a.kind == 1 ? launch_typed<1, float>(a, stream) : launch_typed<0, float>(a, stream);
-}
-
-hipError_t launch_smallb_linear_f32x2(const LinearArgs& a, hipStream_t stream)
-{
-    return a.kind == 1 ? launch_typed<1, float, 2>(a, stream) : launch_typed<0, float, 2>(a, stream);
 }
 
 }  // namespace ttt

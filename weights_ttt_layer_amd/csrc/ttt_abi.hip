@@ -352,9 +352,10 @@ int ttt_layer_fwd(int kind, int B, int N, int D, int H, int d, int b, const void
         return TTT_ERR_INVALID_ARGUMENT;
 
     char* ws = static_cast<char*>(workspace);
-    float* Qf = reinterpret_cast<float*>(ws);
-    float* Kf = reinterpret_cast<float*>(ws + region);
-    float* Vf = reinterpret_cast<float*>(ws + 2 * region);
+    // Q, K, V: two bf16 planes each (hi, then lo); Z fp32
+    uint16_t* Qf = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* Kf = reinterpret_cast<uint16_t*>(ws + region);
+    uint16_t* Vf = reinterpret_cast<uint16_t*>(ws + 2 * region);
     float* Zf = reinterpret_cast<float*>(ws + 3 * region);
     void* Aext = ws + 4 * region;
     ttt::LinearArgs inner;
@@ -380,7 +381,7 @@ int ttt_layer_fwd(int kind, int B, int N, int D, int H, int d, int b, const void
     a.y = y;
     hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
     hipError_t err = ttt::launch_layer_qkv(a, Qf, Kf, Vf, stream);
-    if (err == hipSuccess) err = ttt::launch_smallb_linear_f32x2(inner, stream);
+    if (err == hipSuccess) err = ttt::launch_smallb_chain_terms2(inner, stream);
     if (err == hipSuccess) err = ttt::launch_layer_out(a, Zf, Qf, Aext, stream);
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }

@@ -44,7 +44,7 @@ KERNEL_SOURCES = {
     "block_before": ["large_chunk.hip", "device_common.h"],
     "block_after": ["large_chunk.hip", "device_common.h"],
     "decode": ["decode.hip", "device_common.h"],
-    "layer": ["outer_layer.hip", "smallb_linear.hip", "smallb_common.h", "device_common.h"],
+    "layer": ["outer_layer.hip", "smallb_chain.hip", "device_common.h"],
 }
 
 OUR_KERNELS = ("smallb_linear_kernel", "smallb_chain_kernel", "smallb_mlp_kernel", "lc_gram_kernel", "lc_scan_kernel",
@@ -60,7 +60,7 @@ PATH_KERNELS = {
     "block_before": ("lc_gram_kernel", "lc_scan_kernel", "lc_apply_kernel<false>"),
     "block_after": ("lc_gram_kernel", "lc_scan_kernel", "lc_apply_kernel<true>"),
     "decode": ("decode_kernel",),
-    "layer": ("layer_gemm_kernel", "layer_outprep_kernel", "smallb_linear_kernel<1, float, 2>"),
+    "layer": ("layer_gemm_kernel", "layer_outprep_kernel", "smallb_chain_kernel<1, 2,"),
 }
 
 
