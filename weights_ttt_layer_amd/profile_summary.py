@@ -54,7 +54,7 @@ OUR_KERNELS = ("smallb_linear_kernel", "smallb_chain_kernel", "smallb_mlp_kernel
 # kernel-name prefixes launched by one call of each path
 PATH_KERNELS = {
     "plain": ("smallb_linear_kernel<0,",),
-    "ln": ("smallb_chain_kernel<1,",),
+    "ln": ("smallb_chain_kernel<1, 1,",),
     "mlp": ("smallb_mlp_kernel",),
     "large": ("lc_gram_kernel", "lc_scan_kernel", "lc_chunk_kernel"),
     "block_before": ("lc_gram_kernel", "lc_scan_kernel", "lc_apply_kernel<false>"),
