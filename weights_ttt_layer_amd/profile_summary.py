@@ -203,6 +203,65 @@ def traffic(args):
     print("\n".join(lines))
 
 
+def gpu_geometry(d: str):
+    """(SIMDs, XCDs) of the GPU agent in a rocprofv3 output directory."""
+    path = find_one(d, "*agent_info.csv")
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Agent_Type"] == "GPU":
+                return int(r["Simd_Count"]), int(r["Num_Xcc"])
+    raise SystemExit(f"no GPU agent in {path}")
+
+
+def counters(args):
+    """Per-kernel matrix-core and issue counters from two --pmc runs.
+
+    The values are device totals per dispatch. GRBM_GUI_ACTIVE is summed over
+    the XCDs (so / XCDs = active clock cycles of the dispatch);
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over all SIMDs (a 32x32x16 bf16 MFMA
+    keeps its SIMD's matrix pipe busy 32 cycles); SQ_INSTS_VALU_MFMA_MOPS_* x 512
+    is the executed MFMA flops; SQ_WAVE_CYCLES, SQ_ACTIVE_INST_VALU and
+    SQ_WAIT_INST_ANY count in units of four cycles (one VALU instruction of a
+    wave of 64 takes one such unit)."""
+    simds, xcds = gpu_geometry(args.mfma_dir)
+    keys_m = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+              "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE")
+    keys_i = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU",
+              "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT")
+    m = {k: load_counter(args.mfma_dir, k) for k in keys_m}
+    i = {k: load_counter(args.issue_dir, k) for k in keys_i}
+    avg = lambda v: sum(v) / len(v)
+    names = [n for n in m["GRBM_GUI_ACTIVE"] if is_ours(n) and n in i["SQ_WAVES"]]
+    lines = [f"# Matrix-core and issue counters per kernel: {args.title}", "",
+             "Commands (from the repository root):", ""]
+    lines += [f"    {c}" for c in args.cmd]
+    lines += ["", f"GPU: {simds} SIMDs in {xcds} XCDs. Per dispatch (averaged over dispatches):",
+              "cycles = GRBM_GUI_ACTIVE / XCDs; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x cycles);",
+              "MFMA TFLOP/s = executed MFMA flops / (cycles / 2.4 GHz) is at the nominal clock;",
+              "per wave: VALU and LDS instructions, VALU issue and waiting as fractions of the wave's",
+              "cycles, LDS bank-conflict cycles per LDS instruction.", "",
+              "| kernel | dispatches | cycles | MFMA instr | MFMA busy | executed MFMA GFLOP | MFMA TFLOP/s | "
+              "waves | VALU/wave | LDS/wave | VALU issue | waiting | conflict cyc/LDS |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for n in names:
+        cyc = avg(m["GRBM_GUI_ACTIVE"][n]) / xcds
+        busy = avg(m["SQ_VALU_MFMA_BUSY_CYCLES"][n]) / (simds * cyc) if cyc else 0.0
+        flops = (avg(m["SQ_INSTS_VALU_MFMA_MOPS_BF16"][n]) + avg(m["SQ_INSTS_VALU_MFMA_MOPS_F32"][n])) * 512
+        tfs = flops / (cyc / 2.4e9) / 1e12 if cyc else 0.0
+        waves = avg(i["SQ_WAVES"][n])
+        wc = avg(i["SQ_WAVE_CYCLES"][n])
+        lds = avg(i["SQ_INSTS_LDS"][n])
+        lines.append(f"| {n} | {len(m['GRBM_GUI_ACTIVE'][n])} | {cyc:.0f} | {avg(m['SQ_INSTS_MFMA'][n]):.3g} | "
+                     f"{100 * busy:.1f}% | {flops / 1e9:.2f} | {tfs:.0f} | {waves:.0f} | "
+                     f"{avg(i['SQ_INSTS_VALU'][n]) / waves:.0f} | {lds / waves:.0f} | "
+                     f"{100 * avg(i['SQ_ACTIVE_INST_VALU'][n]) / wc:.0f}% | "
+                     f"{100 * avg(i['SQ_WAIT_INST_ANY'][n]) / wc:.0f}% | "
+                     f"{(avg(i['SQ_LDS_BANK_CONFLICT'][n]) / lds if lds else 0):.2f} |")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -218,8 +277,14 @@ def main(argv=None):
     t.add_argument("workload")
     t.add_argument("--variant", default="dual", choices=sorted(KERNEL_SOURCES.keys() - {"plain", "ln", "mlp", "large"}) + ["dual"])
     t.add_argument("--cmd", action="append", default=[])
+    k = sub.add_parser("counters")
+    k.add_argument("mfma_dir")
+    k.add_argument("issue_dir")
+    k.add_argument("out")
+    k.add_argument("--title", default="")
+    k.add_argument("--cmd", action="append", default=[])
     args = ap.parse_args(argv)
-    stats(args) if args.what == "stats" else traffic(args)
+    {"stats": stats, "traffic": traffic, "counters": counters}[args.what](args)
 
 
 if __name__ == "__main__":
