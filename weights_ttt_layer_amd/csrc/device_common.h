@@ -197,6 +197,24 @@ __device__ __forceinline__ float xrow4_sum(float x)
     return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
 }
 
+// Both sums of xrow4_sum for two values at once, in the same order of
+// additions. v_permlane32_swap of (a, b) leaves rows 0-1 of a and b in the
+// first result and rows 2-3 in the second, so their sum holds a's half-sums in
+// lanes 0-31 and b's in lanes 32-63; v_permlane16_swap then completes both, and
+// a last v_permlane32_swap hands every lane both totals.
+__device__ __forceinline__ void xrow4_sum2(float& a, float& b)
+{
+    auto s1 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, a), __builtin_bit_cast(int, b), false, false);
+    const float y = __builtin_bit_cast(float, (int)s1[0]) + __builtin_bit_cast(float, (int)s1[1]);
+    const int yi = __builtin_bit_cast(int, y);
+    auto s2 = __builtin_amdgcn_permlane16_swap(yi, yi, false, false);
+    const float z = __builtin_bit_cast(float, (int)s2[0]) + __builtin_bit_cast(float, (int)s2[1]);
+    const int zi = __builtin_bit_cast(int, z);
+    auto s3 = __builtin_amdgcn_permlane32_swap(zi, zi, false, false);
+    a = __builtin_bit_cast(float, (int)s3[0]);
+    b = __builtin_bit_cast(float, (int)s3[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Direct global->LDS loads
 // ---------------------------------------------------------------------------

@@ -28,7 +28,7 @@
 //  * wave 0, the chain: X^T = A^T + (-Gt_prev)^T P^T (v_mfma_f32_16x16x16_bf16,
 //    four 16-feature tiles). Its C layout holds ONE token per lane (lane
 //    (g, n): token n, features 16t + 4g + i), so a row statistic is 15 in-lane
-//    adds and two lane swaps. It writes -Gt as two bf16 terms into LDS, where
+//    adds and lane swaps (two statistics share three swaps). It writes -Gt as two bf16 terms into LDS, where
 //    the transpose read hands it back as the A operand of the next chunk's
 //    product. Everything it needs for a chunk except A arrives a chunk early
 //    and is read before the barrier; it runs at raised wave priority and
@@ -39,12 +39,14 @@
 //    the A^T tile b of the next chunk and the Q W part of H_Q^T tile b (W^T as
 //    the A operand, k in a permuted order that the B operand reads to match).
 //  * waves 6, 7, 9, 10, the outputs: the wave of tile b adds the causal term
-//    -Gt^T tril(S)^T (S^T = K Q^T in its C layout) to H_Q^T tile b and forms
-//    the output rows of its 16 features.
+//    -Gt^T tril(S)^T to H_Q^T tile b and forms the output rows of its 16
+//    features.
 //  * wave 4 issues every global->LDS load of the Q/K/V/eta ring (its
 //    vector-memory counter holds nothing else, so it can be waited on exactly)
-//    and forms P^T = K_c K_{c+1}^T two chunks ahead; wave 8 forms the residual
-//    input of the chain's gradient two chunks ahead.
+//    and forms, two chunks ahead, P^T = K_c K_{c+1}^T and the causal part of
+//    S^T = K_c Q_c^T (its C layout is the B operand of the causal term), both
+//    as two bf16 terms; wave 8 forms the residual input of the chain's
+//    gradient two chunks ahead.
 // One workgroup barrier per chunk (LDS-only fence: the ring loads stay in
 // flight); every exchanged tile is double-buffered by chunk parity. The output
 // LayerNorm needs all 64 features of a row, so its partial sums cross the
@@ -88,6 +90,7 @@ struct alignas(16) ChainSmem {
     float4 xq[2][4][64];          // Q W part of H_Q^T of a chunk, same layout
     float4 xc[2][4][64];          // residual input of the gradient (LN: 2 gamma (K - V + beta); plain: V)
     uint2 xp[2][2][64];           // P^T of a chunk, two bf16 terms, B-operand lane order
+    uint2 xst[4][2][64];          // tril(S)^T of a chunk (slot c % 4), two bf16 terms, same order
     uint16_t gt[2][2][16 * D];    // -Gt of a chunk, two bf16 terms, [token][feature] tiles
     float2 xs[2][16][4];          // output LayerNorm partial sums [token][state wave]
 };
@@ -266,8 +269,7 @@ __device__ __forceinline__ void chain_step(ChainSmem<TIN>& sm, int c, int g, int
             s1 += x;
             s2 = fmaf(x, x, s2);
         }
-        s1 = xrow4_sum(s1);
-        s2 = xrow4_sum(s2);
+        xrow4_sum2(s1, s2);
         const float mu = s1 * (1.f / D);
         const float rs = __builtin_amdgcn_rsqf(fmaxf(s2 * (1.f / D) - mu * mu, 0.f) + eps);
         const float nmr = -mu * rs;
@@ -280,8 +282,7 @@ __device__ __forceinline__ void chain_step(ChainSmem<TIN>& sm, int c, int g, int
             u1 += dx[j];
             u2 = fmaf(dx[j], xh[j], u2);
         }
-        u1 = xrow4_sum(u1);
-        u2 = xrow4_sum(u2);
+        xrow4_sum2(u1, u2);
         // -eta rs (dx - mean(dx) - xh mean(dx xh))
         const float sc = -pre.eta * rs;
         const float ca = -(u2 * (1.f / D)) * sc;
@@ -467,6 +468,22 @@ __device__ __forceinline__ void publish_p(ChainSmem<TIN>& sm, int j, int g, int 
     sm.xp[j & 1][1][lane] = __builtin_bit_cast(uint2, pt[1]);
 }
 
+// tril(S_j)^T = (K_j Q_j^T) with key 4g + i <= query n, as two bf16 terms, for
+// the output waves' causal term of chunk j.
+template <int TIN>
+__device__ __forceinline__ void publish_s(ChainSmem<TIN>& sm, int j, int g, int n, int lane)
+{
+    const ChainSlot<TIN>& s = sm.ring[j % RingGeom<TIN>::SLOTS];
+    const f32x4 st = row_dots<TIN>(s.k, s.q, g, n);
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (4 * g + i <= n) ? st[i] : 0.f;
+    bf16x4 sb[2];
+    terms4<2>(x, sb);
+    sm.xst[j & 3][0][lane] = __builtin_bit_cast(uint2, sb[0]);
+    sm.xst[j & 3][1][lane] = __builtin_bit_cast(uint2, sb[1]);
+}
+
 template <int TIN, bool PT>
 __device__ __forceinline__ void loader_role(ChainSmem<TIN>& sm, int lane, int N, int b, int C, size_t plane,
                                             const uint16_t* Qu, const uint16_t* Ku, const uint16_t* Vu,
@@ -480,11 +497,16 @@ __device__ __forceinline__ void loader_role(ChainSmem<TIN>& sm, int lane, int N,
     if (C >= AH) wait_vm<DPC * (AH - 2)>(); else wait_vm<0>();   // chunks 0, 1
     lds_barrier();
     if (C > 1) publish_p<TIN>(sm, 1, g, n, lane);
+    if (C > 0) publish_s<TIN>(sm, 0, g, n, lane);
+    if (C > 1) publish_s<TIN>(sm, 1, g, n, lane);
     if (C >= AH) wait_vm<DPC * (AH - 3)>(); else wait_vm<0>();   // chunk 2
     lds_barrier();
     for (int c = 0; c < C + 2; ++c) {
         if (c + AH < C) issue_chunk<TIN, PT>(sm, c + AH, lane, N, b, plane, Qu, Ku, Vu, etau);
-        if (c + 2 < C) publish_p<TIN>(sm, c + 2, g, n, lane);
+        if (c + 2 < C) {
+            publish_p<TIN>(sm, c + 2, g, n, lane);
+            publish_s<TIN>(sm, c + 2, g, n, lane);   // slot (c+2) % 4 was last read at step c-2
+        }
         // chunk c + 3 is read after this barrier
         if (c + AH < C) wait_vm<DPC * (AH - 3)>(); else wait_vm<0>();
         lds_barrier();
@@ -580,13 +602,9 @@ __device__ __forceinline__ void out_role(ChainSmem<TIN>& sm, int bt, int lane, i
         }
         bf16x4 sbn[2] = {};
         if (c < C) {
-            // S_c^T = K_c Q_c^T, causal part (key 4g + i <= query n)
-            const ChainSlot<TIN>& s = sm.ring[c % SL];
-            const f32x4 st = row_dots<TIN>(s.k, s.q, g, n);
-            float x[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (4 * g + i <= n) ? st[i] : 0.f;
-            terms4<2>(x, sbn);
+            // tril(S_c)^T terms, formed by the loader wave two chunks ahead
+            sbn[0] = __builtin_bit_cast(bf16x4, sm.xst[c & 3][0][lane]);
+            sbn[1] = __builtin_bit_cast(bf16x4, sm.xst[c & 3][1][lane]);
         }
         if (c >= 1 && c <= C) {
             const int m = c - 1;
@@ -594,8 +612,7 @@ __device__ __forceinline__ void out_role(ChainSmem<TIN>& sm, int bt, int lane, i
                 // partial output-LayerNorm sums of chunk c-1 over this wave's 16 features
                 float s1 = (xq1[0] + xq1[1]) + (xq1[2] + xq1[3]);
                 float s2 = (xq1[0] * xq1[0] + xq1[1] * xq1[1]) + (xq1[2] * xq1[2] + xq1[3] * xq1[3]);
-                s1 = xrow4_sum(s1);
-                s2 = xrow4_sum(s2);
+                xrow4_sum2(s1, s2);
                 if (g == 0) sm.xs[par][n][bt] = make_float2(s1, s2);
             } else {
                 if (n < min(b, N - m * b))
