@@ -55,6 +55,16 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_f16(const f16x8& a, const f16x8&
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// Logical index of workgroup x of `total`. Workgroups are dealt to the eight
+// XCDs round robin (workgroup x runs on XCD x % 8); this gives XCD c a
+// contiguous range of logical indices, so neighbours in logical order share
+// that XCD's L2.
+__device__ __forceinline__ int xcd_tile(int x, int total)
+{
+    const int per = total >> 3, rem = total & 7, c = x & 7, k = x >> 3;
+    return c < rem ? c * (per + 1) + k : rem * (per + 1) + (c - rem) * per + k;
+}
+
 __device__ __forceinline__ short bf16_bits(__bf16 x) { return __builtin_bit_cast(short, x); }
 __device__ __forceinline__ __bf16 bits_bf16(uint16_t x) { return __builtin_bit_cast(__bf16, x); }
 __device__ __forceinline__ float bf16_to_f32(__bf16 x) { return (float)x; }

@@ -298,7 +298,10 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const uint16_t* __res
     // [buffer][wave][term][s][lane] bf16x8: W_c rows of every wave, lane by lane
     __shared__ __attribute__((aligned(16))) bf16x8 wpub[2][4][2][2][64];
     const int C = (N + b - 1) / b;
-    const int unit = blockIdx.x >> 2, cb = blockIdx.x & 3;
+    // the four column blocks of a unit read the same M_c every step: keep them on
+    // one XCD so three of the four reads hit its L2
+    const int lb = xcd_tile(blockIdx.x, gridDim.x);
+    const int unit = lb >> 2, cb = lb & 3;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int colg = 32 * cb + l32;   // global column of this lane
 
@@ -316,7 +319,16 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const uint16_t* __res
         // publish W_c: two bf16 terms, lane by lane in LDS and as W_c^T in the workspace
         publish_state(acc, WT + ((size_t)unit * (C + 1) + c) * 2 * LD * LD, wpub[buf][w], w, lane, h, colg);
         __syncthreads();                                 // one barrier per step: wpub is double-buffered
-        f32x16 t = {};
+        // t = M_c W_c - B_c: B_c enters as the accumulator's start, so its registers
+        // are free for the refill as soon as the first product has read them
+        f32x16 t;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            t[4 * q] = -o.bq[q].x;
+            t[4 * q + 1] = -o.bq[q].y;
+            t[4 * q + 2] = -o.bq[q].z;
+            t[4 * q + 3] = -o.bq[q].w;
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -328,12 +340,7 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const uint16_t* __res
                 t = mfma_32x32x16(o.a[r][s][0], b0, t);
             }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc[4 * q] = (acc[4 * q] - t[4 * q]) + o.bq[q].x;
-            acc[4 * q + 1] = (acc[4 * q + 1] - t[4 * q + 1]) + o.bq[q].y;
-            acc[4 * q + 2] = (acc[4 * q + 2] - t[4 * q + 2]) + o.bq[q].z;
-            acc[4 * q + 3] = (acc[4 * q + 3] - t[4 * q + 3]) + o.bq[q].w;
-        }
+        for (int i = 0; i < 16; ++i) acc[i] -= t[i];
         if (c + 2 < C) scan_load(Mg, Bg, unit, C, c + 2, w, cb, lane, o);
     };
 

@@ -34,14 +34,6 @@ constexpr int GT = 256;      // threads per workgroup (four waves)
 // Row of a 32x32 C-layout tile held by lane half h = lane / 32 at slot i.
 __device__ __forceinline__ int crow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
-// Logical tile of workgroup x. Workgroups are dealt to the eight XCDs round
-// robin; this gives XCD c a contiguous range of logical tiles.
-__device__ __forceinline__ int xcd_tile(int x, int total)
-{
-    const int per = total >> 3, rem = total & 7, c = x & 7, k = x >> 3;
-    return c < rem ? c * (per + 1) + k : rem * (per + 1) + (c - rem) * per + k;
-}
-
 // ===========================================================================
 // The GEMM core shared by both sides:
 //     C[m][n] = sum_{k < K} A[m][k] * Bw[n][k mod KW]
