@@ -15,7 +15,9 @@ measurement for the large-chunk workload (plain TTT-Linear, bf16, B=1 H=16
 N=32768 d=128 b=2048), whose roofline is the bf16 MFMA peak; and "next_rows":
 the block-causal outputs of that workload (chunk outputs with the chunk's
 starting or ending weights) and the single-token decode step of B*H = 768
-TTT-Linear+LN streams (d=64), each against the HBM roofline, and the whole
+TTT-Linear+LN streams (d=64), each against the HBM roofline (decode steps are
+timed as replays of a captured HIP graph, as a serving token loop runs them,
+with the eager per-call time beside it), and the whole
 layer (projections, key normalisation, inner TTT-Linear+LN, output LayerNorm +
 residual + output projection; B=8 N=2048 D=768 H=12 d=64 b=16) against the
 bf16 MFMA roofline of its GEMM work, and the backward of the b = 16 workload
@@ -141,11 +143,12 @@ def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int, variant:
             outs.append((z, torch.empty_like(s["w0"]), ws))
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    def step(i, st=None):
         s, o = sets[i % ROTATE], outs[i % ROTATE]
         if variant == "decode":
             linear_decode(s["q"], s["k"], s["v"], s["w0"], s["eta"], kind=wl.kind, eta_const=inp.eta_const,
-                          ln_gamma=s["gamma"], ln_beta=s["beta"], ln_eps=wl.ln_eps, z=o[0], stream=stream)
+                          ln_gamma=s["gamma"], ln_beta=s["beta"], ln_eps=wl.ln_eps, z=o[0],
+                          stream=stream if st is None else st)
         elif wl.kind == "mlp":
             mlp_fwd(s["q"], s["k"], s["v"], s["w1"], s["w2"], s["eta"], b=wl.b,
                     eta_const=inp.eta_const, ln_gamma=s["gamma"], ln_beta=s["beta"],
@@ -169,12 +172,33 @@ def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int, variant:
         step(i)
     end.record(stream)
     torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
+    ms_step = start.elapsed_time(end) / steps
+    extra = {}
+    if variant == "decode":
+        # A token loop in serving replays captured decode steps instead of paying
+        # a host call per token: one HIP graph of ROTATE steps (one per input
+        # set), replayed; the eager per-call time is reported beside it.
+        extra["eager_ms_per_step"] = ms_step
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for i in range(ROTATE):
+                step(i, cap)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // ROTATE)
+        start.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_step = start.elapsed_time(end) / (reps * ROTATE)
+        extra["graph_steps_timed"] = reps * ROTATE
     z = outs[(steps - 1) % ROTATE][0]
     finite = bool(torch.isfinite(z).all().item())
     del sets, outs, base
     torch.cuda.empty_cache()
-    return ms_total / steps, finite
+    return ms_step, finite, extra
 
 
 def copy_calibration(reps: int = 3):
@@ -201,7 +225,7 @@ def algorithmic_flops_variant(wl: wlm.Workload, variant: str) -> int:
 
 def measure(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int, variant: str = "dual"):
     """tokens/s and the roofline object of one workload (and output variant)."""
-    ms, finite = run_gpu(wl, inp, steps, warmup, variant)
+    ms, finite, extra = run_gpu(wl, inp, steps, warmup, variant)
     if not finite:
         log(f"[bench] WARNING: non-finite output in {wl.name} {variant}")
     sec = ms / 1e3
@@ -220,17 +244,17 @@ def measure(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int, variant:
     roof["traffic"] = measured_traffic(wl, path_key, variant)
     log(f"[bench] {wl.name} {variant}: {ms*1e3:.1f} us/step, {tokens/sec:.4g} tokens/s, "
         f"{nbytes/sec/1e9:.1f} GB/s algorithmic, {flops/sec/1e12:.2f} TFLOP/s algorithmic")
-    return ms, tokens / sec, nbytes, flops, roof
+    return ms, tokens / sec, nbytes, flops, roof, extra
 
 
 def side_measurement(name: str, steps: int, warmup: int, variant: str):
     """One object of the JSON line for a workload other than the headline one."""
     idx = [w.name for w in wlm.WORKLOADS].index(name)
     wl = wlm.WORKLOADS[idx]
-    ms, val, nbytes, flops, roof = measure(wl, wlm.workload_inputs(idx), steps, warmup, variant)
+    ms, val, nbytes, flops, roof, extra = measure(wl, wlm.workload_inputs(idx), steps, warmup, variant)
     return {"workload": wl.name, "variant": variant, "value": val, "unit": "tokens/s", "ms_per_step": ms,
             "token_heads_per_s": val * wl.H, "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
-            "roofline": roof}
+            "roofline": roof, **extra}
 
 
 MFMA_F32_PEAK_TFS = 157.3     # MI355X dense fp32 matrix, TFLOP/s
@@ -509,7 +533,7 @@ def main():
     log(f"[bench] workload {wl.name}: generated inputs")
 
     variant = args.variant or ("decode" if wl.name == DECODE_WORKLOAD else "dual")
-    ms, value, nbytes, flops, roof = measure(wl, inp, args.steps, args.warmup, variant)
+    ms, value, nbytes, flops, roof, extra = measure(wl, inp, args.steps, args.warmup, variant)
 
     b2048 = None
     next_rows = None
@@ -559,6 +583,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    rec["config"].update(extra)
     if b2048 is not None:
         rec["b2048"] = b2048
     if next_rows is not None:

@@ -95,3 +95,46 @@ def test_decode_workload_sampled_units():
         ez, ew = rel_err(z[bi, hi], zr[0, 0]), rel_err(w[bi, hi], wr[0, 0])
         say(f"  unit ({bi},{hi}): err z {ez:.2e} W {ew:.2e}")
         assert ez <= TOL["bf16"] and ew <= TOL["bf16"]
+
+
+def test_decode_graph_replay_matches_eager():
+    """Decode steps captured in a HIP graph (as the benchmark times them): each
+    of several replays, with eager work and a synchronisation in between, leaves
+    the same z and state as the same steps run eagerly (bit for bit: the same
+    kernel on the same inputs)."""
+    import torch
+    from weights_ttt_layer_amd import linear_decode
+    inp = dec("ln", "bf16", 4, 6, 3, "sigmoid", seed=21)
+    say(f"case {inp.wl.name} (graph replay)")
+    t = wlm.to_device(inp)
+    wl = inp.wl
+    steps = [(t["q"][:, :, i].contiguous(), t["k"][:, :, i].contiguous(), t["v"][:, :, i].contiguous(),
+              t["eta"][:, :, i].contiguous()) for i in range(wl.N)]
+    kw = dict(kind=wl.kind, eta_const=inp.eta_const, ln_gamma=t["gamma"], ln_beta=t["beta"], ln_eps=wl.ln_eps)
+    reps = 3
+
+    w_e = t["w0"].clone()
+    ref = []
+    for _ in range(reps):
+        zs = [linear_decode(q, k, v, w_e, eta, **kw) for (q, k, v, eta) in steps]
+        ref.append(([z.clone() for z in zs], w_e.clone()))
+    torch.cuda.synchronize()
+
+    w_g = t["w0"].clone()
+    zg = [torch.empty_like(ref[0][0][0]) for _ in steps]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream()
+        for (q, k, v, eta), z in zip(steps, zg):
+            linear_decode(q, k, v, w_g, eta, z=z, stream=cap, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(w_g, t["w0"]), "capture must not run the steps"
+    for r in range(reps):
+        graph.replay()
+        noise = torch.randn(1 << 16, device=w_g.device).square().sum()   # eager work between replays
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(noise))
+        same_z = all(torch.equal(a, b) for a, b in zip(zg, ref[r][0]))
+        same_w = torch.equal(w_g, ref[r][1])
+        say(f"  replay {r}: z identical {same_z}, state identical {same_w}")
+        assert same_z and same_w
