@@ -22,7 +22,9 @@ layer (projections, key normalisation, inner TTT-Linear+LN, output LayerNorm +
 residual + output projection; B=8 N=2048 D=768 H=12 d=64 b=16) against the
 bf16 MFMA roofline of its GEMM work, and the backward of the b = 16 workload
 (gradients with respect to Q, K, V, eta, W0, gamma, beta) against the fp32
-matrix-core peak.
+matrix-core peak. "practical_peaks" gives, beside the published peaks the
+rooflines use, what a plain copy kernel and a bf16 MFMA loop reach on the
+device, with its compute-unit count and clock.
 
 Prints ONE JSON line (stdout). Diagnostics go to stderr.
 """
@@ -186,7 +188,7 @@ def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int, variant:
                 step(i, cap)
         graph.replay()
         torch.cuda.synchronize()
-        reps = max(1, steps // ROTATE)
+        reps = 10 * max(1, steps // ROTATE)      # a few ms: one step is only ~10 us
         start.record(stream)
         for _ in range(reps):
             graph.replay()
@@ -213,6 +215,54 @@ def copy_calibration(reps: int = 3):
     torch.cuda.synchronize()
     del src, dst
     torch.cuda.empty_cache()
+
+
+def practical_peaks():
+    """Beside the published peaks: the HBM rate a plain copy kernel reaches and the
+    dense bf16 rate of an MFMA loop (both built here, libttt_peak.so), and the
+    device's compute units and clock. The rooflines stay against the published
+    peaks."""
+    import torch
+    from weights_ttt_layer_amd.binding import peak_copy, peak_device_info, peak_mfma
+
+    info = peak_device_info(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+
+    src = torch.arange(COPY_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        peak_copy(src, dst, stream)
+    torch.cuda.synchronize()
+    reps = 10
+    start.record(stream)
+    for _ in range(reps):
+        peak_copy(src, dst, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * COPY_BYTES * reps / (start.elapsed_time(end) / 1e3) / 1e9
+    copy_ok = bool(torch.equal(src, dst))
+    del src, dst
+
+    blocks, iters = 2 * info["compute_units"], 20000     # two waves per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    peak_mfma(out, blocks, 100, stream)
+    torch.cuda.synchronize()
+    start.record(stream)
+    flops = peak_mfma(out, blocks, iters, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    mfma_tfs = flops / (start.elapsed_time(end) / 1e3) / 1e12
+    ok = copy_ok and bool(torch.isfinite(out).all().item())
+    del out
+    torch.cuda.empty_cache()
+    log(f"[bench] practical peaks: copy {copy_gbs:.0f} GB/s, bf16 MFMA loop {mfma_tfs:.0f} TFLOP/s, "
+        f"{info['compute_units']} CUs at {info['clock_khz'] / 1e3:.0f} MHz")
+    return {"copy_GBps": copy_gbs, "copy_bytes": COPY_BYTES, "mfma_bf16_TFLOPs": mfma_tfs,
+            "mfma_flops": flops, "checks_ok": ok, **info,
+            "published": {"hbm_GBps": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFS}}
 
 
 def algorithmic_flops_variant(wl: wlm.Workload, variant: str) -> int:
@@ -586,6 +636,7 @@ def main():
     rec["config"].update(extra)
     if b2048 is not None:
         rec["b2048"] = b2048
+        rec["practical_peaks"] = practical_peaks()
     if next_rows is not None:
         rec["next_rows"] = next_rows
     print(json.dumps(rec), flush=True)

@@ -384,3 +384,64 @@ def linear_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w0: torch.Tens
     if st != TTT_OK:
         raise TTTError(st, "ttt_linear_bwd")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Calibration library (include/ttt_peak.h): practical device peaks for the
+# measurements; not used by any forward or backward call.
+# ---------------------------------------------------------------------------
+PEAK_LIB_PATH = os.path.join(_HERE, "libttt_peak.so")
+_peak_lib = None
+
+
+def load_peak_library(path: str = PEAK_LIB_PATH) -> ctypes.CDLL:
+    """Load libttt_peak.so once and declare its C signatures."""
+    global _peak_lib
+    if _peak_lib is not None:
+        return _peak_lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m weights_ttt_layer_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, sz, ip = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)
+    lib.ttt_peak_device_info.argtypes = [i, ip, ip, ip]
+    lib.ttt_peak_device_info.restype = i
+    lib.ttt_peak_copy.argtypes = [vp, vp, sz, vp]
+    lib.ttt_peak_copy.restype = i
+    lib.ttt_peak_mfma.argtypes = [vp, i, i, vp]
+    lib.ttt_peak_mfma.restype = i
+    lib.ttt_peak_mfma_flops.argtypes = [i, i]
+    lib.ttt_peak_mfma_flops.restype = ctypes.c_double
+    _peak_lib = lib
+    return lib
+
+
+def peak_device_info(device: int = 0) -> dict:
+    """Compute units, shader clock (kHz) and wavefront width of a device."""
+    lib = load_peak_library()
+    cu, clk, wf = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    st = lib.ttt_peak_device_info(int(device), ctypes.byref(cu), ctypes.byref(clk), ctypes.byref(wf))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_peak_device_info")
+    return {"compute_units": cu.value, "clock_khz": clk.value, "wavefront_size": wf.value}
+
+
+def peak_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """dst <- src through the calibration copy kernel (same byte size, 16-byte multiple)."""
+    lib = load_peak_library()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("peak_copy needs contiguous tensors of the same byte size")
+    st = lib.ttt_peak_copy(_ptr(src), _ptr(dst), nbytes, _stream_ptr(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_peak_copy")
+
+
+def peak_mfma(out: torch.Tensor, blocks: int, iters: int, stream=None) -> float:
+    """Run the MFMA loop (out: >= blocks * 256 fp32); returns the flops it performs."""
+    lib = load_peak_library()
+    if out.dtype != torch.float32 or out.numel() < blocks * 256 or not out.is_contiguous():
+        raise ValueError("peak_mfma needs a contiguous fp32 tensor of at least blocks * 256 elements")
+    st = lib.ttt_peak_mfma(_ptr(out), int(blocks), int(iters), _stream_ptr(stream))
+    if st != TTT_OK:
+        raise TTTError(st, "ttt_peak_mfma")
+    return float(lib.ttt_peak_mfma_flops(int(blocks), int(iters)))

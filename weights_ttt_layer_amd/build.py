@@ -20,6 +20,9 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libttt.so")
 SOURCES = ["ttt_abi.hip", "smallb_linear.hip", "smallb_chain.hip", "smallb_mlp.hip", "large_chunk.hip", "decode.hip",
            "outer_layer.hip", "backward.hip"]
+# the measurement calibration kernels (include/ttt_peak.h), a library of their own
+PEAK_LIB_PATH = os.path.join(HERE, "libttt_peak.so")
+PEAK_SOURCES = ["peak.hip"]
 ARCH = "gfx950"
 
 
@@ -50,19 +53,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link libttt.so. Returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libttt.so (and the calibration
+    library libttt_peak.so). Returns the path of libttt.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PEAK_SOURCES
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB_PATH)
+    _link(objs[len(SOURCES):], PEAK_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PEAK_LIB_PATH}")
     return LIB_PATH
 
 
