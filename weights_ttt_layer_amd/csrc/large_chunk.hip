@@ -170,10 +170,14 @@ lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
         accM[t] = f32x16{};
     }
 
+    // The sums are order-free, so the stages run from the end of the chunk to its
+    // start (stage s holds tokens of block nstage - 1 - s): the chunk's first
+    // tokens are then the most recently read when lc_chunk, which must walk the
+    // chunk from its start, reads them again, and the memory-side cache can serve them.
     const int nstage = nt / GR_TOK;
 #pragma unroll
     for (int s = 0; s < GR_NST - 1; ++s)
-        if (s < nstage) gram_dma(sm, s, s, w, lane, Ku, Vu);
+        if (s < nstage) gram_dma(sm, s, nstage - 1 - s, w, lane, Ku, Vu);
     for (int s = 0; s < nstage; ++s) {
         // stage s is this wave's oldest outstanding group of loads
         const int later = min(GR_NST - 2, nstage - 1 - s);
@@ -181,12 +185,13 @@ lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
         else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(OPS));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();                                 // stage s landed everywhere; stage s-1 consumed
-        if (s + GR_NST - 1 < nstage) gram_dma(sm, (s + GR_NST - 1) % GR_NST, s + GR_NST - 1, w, lane, Ku, Vu);
+        if (s + GR_NST - 1 < nstage)
+            gram_dma(sm, (s + GR_NST - 1) % GR_NST, nstage - s - GR_NST, w, lane, Ku, Vu);
         const uint16_t* kt = sm.k[s % GR_NST];
         const uint16_t* vt = sm.v[s % GR_NST];
 #pragma unroll
         for (int ks = 0; ks < GR_TOK / 16; ++ks) {
-            const float* er = PER_TOKEN ? etau + s * GR_TOK + 16 * ks + 8 * h : nullptr;
+            const float* er = PER_TOKEN ? etau + (nstage - 1 - s) * GR_TOK + 16 * ks + 8 * h : nullptr;
             bf16x8 aw[TA];
             scaled_frag<PER_TOKEN, TA>(tok_major_frag(kt, 16 * ks, w, lane), er, aw);
 #pragma unroll
