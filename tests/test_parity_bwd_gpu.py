@@ -72,6 +72,16 @@ def test_bwd_shapes(kind, dtype, B, H, N, b, eta):
     compare(gpu_bwd(inp, dz, dw), oracle_bwd(inp, dz, dw))
 
 
+@pytest.mark.parametrize("b", [2, 3, 7, 9, 12, 14])
+@pytest.mark.parametrize("kind,dtype", [("ln", "bf16"), ("plain", "f32")])
+def test_bwd_chunk_sizes(kind, dtype, b):
+    """Chunk sizes between the cases above: three full chunks and a ragged tail."""
+    inp = case(kind, dtype, 1, 2, 3 * b + b // 2 + 1, b, "sigmoid", seed=300 + b)
+    dz, dw = wlm.upstream_grads(inp.wl, 5)
+    say(f"case {inp.wl.name}")
+    compare(gpu_bwd(inp, dz, dw), oracle_bwd(inp, dz, dw))
+
+
 def test_bwd_without_state_gradient():
     """dW_end = NULL is a zero upstream state gradient."""
     inp = case("ln", "f32", 1, 2, 40, 16)

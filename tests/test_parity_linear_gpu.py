@@ -55,6 +55,18 @@ def test_edge_shapes(kind, dtype, B, H, N, b):
     check(inp)
 
 
+@pytest.mark.parametrize("b", range(1, 17))
+@pytest.mark.parametrize("kind,dtype", [("plain", "bf16"), ("ln", "bf16"), ("plain", "f32"), ("ln", "f32")])
+def test_every_chunk_size(kind, dtype, b):
+    """Every chunk size the small-b path takes (1 <= b <= 16), on both kernels
+    (bf16 and fp32 streams): three full chunks and a ragged tail of b // 2 + 1
+    tokens (a full chunk when b = 1), two units, per-token eta."""
+    N = 3 * b + b // 2 + 1
+    inp = small(kind, dtype, 1, 2, N, b, seed=100 + b)
+    say(f"case {inp.wl.name}")
+    check(inp)
+
+
 @pytest.mark.parametrize("index", [1, 2])
 def test_workload_ln_bf16_sampled_units(index):
     """Full-size LN workloads (B=8 H=12 N=2048; B=16 H=12 N=8192), launched whole

@@ -37,6 +37,15 @@ def test_mlp_edge_shapes(dtype, B, H, N, b):
     check(inp)
 
 
+@pytest.mark.parametrize("b", [2, 3, 5, 8, 11, 13, 15])
+def test_mlp_chunk_sizes(b):
+    """Chunk sizes between the edge cases above, bf16 streams: three full chunks
+    and a ragged tail, two units."""
+    inp = small("bf16", 1, 2, 3 * b + b // 2 + 1, b, seed=200 + b)
+    say(f"case {inp.wl.name}")
+    check(inp)
+
+
 def test_mlp_workload_sampled_units():
     """Full-size TTT-MLP workload (B=4 H=12 N=4096), launched whole; a spread of
     units compared with the oracle run on those units alone."""
