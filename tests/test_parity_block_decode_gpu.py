@@ -30,6 +30,8 @@ def lc(B, H, N, b, eta="const", eta_const=0.01, seed=5):
     (1, 1, 640, 256, "const"),       # short last chunk (128 tokens)
     (1, 2, 2048, 512, "const"),
     (1, 1, 256, 256, "const"),       # a single chunk
+    (1, 1, 1152, 384, "sigmoid"),    # three blocks per chunk
+    (1, 1, 2560, 1024, "sigmoid"),   # last chunk half as long
 ])
 def test_block_shapes(apply, B, H, N, b, eta):
     inp = lc(B, H, N, b, eta)

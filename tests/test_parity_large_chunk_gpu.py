@@ -34,6 +34,9 @@ def check(inp):
     (1, 1, 640, 256, "const"),       # short last chunk (128 tokens)
     (1, 2, 2048, 512, "const"),      # 4 blocks per chunk
     (1, 1, 256, 256, "const"),       # a single chunk
+    (1, 1, 1152, 384, "sigmoid"),    # b a multiple of 128 but not of 256: three blocks per chunk
+    (1, 1, 2560, 1024, "sigmoid"),   # b = 1024, last chunk half as long
+    (1, 1, 4096, 2048, "const"),     # the benchmark chunk size, every output compared
 ])
 def test_large_chunk_shapes(B, H, N, b, eta):
     inp = lc(B, H, N, b, eta)
