@@ -85,6 +85,19 @@ def test_decode_steps_match_online(kind, dtype, eta):
     assert ez <= TOL[dtype] and ew <= TOL[dtype]
 
 
+@pytest.mark.parametrize("B,H", [(1, 1), (7, 3), (2, 12)])
+@pytest.mark.parametrize("kind,dtype", [("ln", "bf16"), ("plain", "f32")])
+def test_decode_stream_counts(kind, dtype, B, H):
+    """Stream counts from one to a few dozen (one wave each), constant eta."""
+    inp = dec(kind, dtype, B, H, 4, "const", seed=40 + B * H)
+    say(f"case {inp.wl.name}")
+    z, w = gpu_decode(inp)
+    zr, wr = oracle_linear(inp, oracle.ONLINE)
+    ez, ew = rel_err(z, zr), rel_err(w, wr)
+    say(f"  err Z {ez:.2e}  W {ew:.2e}  (tol {TOL[dtype]:.0e})")
+    assert ez <= TOL[dtype] and ew <= TOL[dtype]
+
+
 def test_decode_workload_sampled_units():
     """The decode workload (B=64 H=12 d=64, LN, bf16), one step for all 768
     streams; sampled streams compared with the oracle run on them alone."""

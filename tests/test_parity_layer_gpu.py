@@ -73,6 +73,9 @@ def case(kind, B, N, D, H, b, seed=3):
     ("ln", 2, 256, 768, 12, 16),     # the model width of the named workload
     ("ln", 1, 1, 128, 2, 16),        # a single token
     ("plain", 1, 130, 1024, 16, 16), # H = 16, D = 1024
+    ("ln", 1, 77, 256, 4, 3),        # b = 3, ragged tail of 2
+    ("plain", 2, 90, 256, 4, 8),     # b = 8
+    ("ln", 1, 140, 384, 6, 11),      # b = 11, D = 384 (six heads)
 ])
 def test_layer_shapes(kind, B, N, D, H, b):
     inp = case(kind, B, N, D, H, b)
