@@ -48,10 +48,19 @@ from weights_ttt_layer_amd.profile_summary import COPY_BYTES, source_digest  # n
 DEFAULT_WORKLOAD = "linear_ln_bf16_B8H12N2048_d64_b16"
 LARGE_WORKLOAD = "linear_bf16_B1H16N32768_d128_b2048"
 DECODE_WORKLOAD = "decode_ln_bf16_B64H12_d64"
+OTHER_CONFIGS = ["linear_f32_B1H1N256_d64_b16", "linear_ln_bf16_B16H12N8192_d64_b16", "mlp_bf16_B4H12N4096_d64_b16"]
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 ROTATE = 4
+# Distinct input sets a timed loop walks through: at least ROTATE, and enough
+# that their bytes exceed twice the 256 MB Infinity Cache, so repeated steps
+# cannot be served from it (capped for the tiny single-unit workload, which is
+# latency bound).
+MALL_BYTES = 256 * 1024 * 1024
+MAX_ROTATE = 64
 METRIC = "TTT layer fwd tokens/sec"
+# Worker threads of the CPU baseline: the host's CPU share that goes with one GPU.
+CPU_THREADS_CAP = 16
 
 
 def log(*a):
@@ -94,6 +103,31 @@ def algorithmic_flops(wl: wlm.Workload) -> int:
     return f * wl.B * wl.H
 
 
+def rotation(set_bytes: int) -> int:
+    """Number of distinct input/output sets for a loop whose sets are `set_bytes` each."""
+    need = -(-2 * MALL_BYTES // max(1, set_bytes))
+    return int(min(MAX_ROTATE, max(ROTATE, need)))
+
+
+def cpu_threads() -> int:
+    return min(len(os.sched_getaffinity(0)), CPU_THREADS_CAP)
+
+
+def timed(stream, steps: int, step):
+    """Launch `steps` steps with a HIP event recorded on `stream` before each and
+    after the last. Returns (mean ms over the whole bracket, median ms of the
+    per-step intervals)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[steps]) / steps, float(np.median(per))
+
+
 def measured_traffic(wl: wlm.Workload, path_key: str, variant: str = "dual"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when there is none for this workload or the kernel source changed since."""
@@ -124,9 +158,15 @@ def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int, variant:
 
     dev = torch.device("cuda:0")
     base = wlm.to_device(inp, dev)
-    sets = [base] + [{k: (None if t is None else t.clone()) for k, t in base.items()}
-                     for _ in range(ROTATE - 1)]
     B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
+    if variant == "decode":      # the set is one token of every stream and the state
+        set_bytes = (base["w0"].numel() * 4 + 3 * B * H * d * base["q"].element_size() + B * H * d * 4)
+    else:
+        set_bytes += B * H * N * d * 4
+    nrot = rotation(set_bytes)
+    sets = [base] + [{k: (None if t is None else t.clone()) for k, t in base.items()}
+                     for _ in range(nrot - 1)]
     outs = []
     for s in sets:
         if variant == "decode":
@@ -146,7 +186,7 @@ def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int, variant:
     stream = torch.cuda.current_stream()
 
     def step(i, st=None):
-        s, o = sets[i % ROTATE], outs[i % ROTATE]
+        s, o = sets[i % nrot], outs[i % nrot]
         if variant == "decode":
             linear_decode(s["q"], s["k"], s["v"], s["w0"], s["eta"], kind=wl.kind, eta_const=inp.eta_const,
                           ln_gamma=s["gamma"], ln_beta=s["beta"], ln_eps=wl.ln_eps, z=o[0],
@@ -167,36 +207,27 @@ def run_gpu(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int, variant:
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / steps
-    extra = {}
+    ms_step, med = timed(stream, steps, step)
+    extra = {"median_ms_per_step": med, "input_sets": nrot, "input_set_bytes": set_bytes}
     if variant == "decode":
         # A token loop in serving replays captured decode steps instead of paying
-        # a host call per token: one HIP graph of ROTATE steps (one per input
-        # set), replayed; the eager per-call time is reported beside it.
+        # a host call per token: one HIP graph of one step per input set (their
+        # states together exceed twice the Infinity Cache), replayed; the eager
+        # per-call time is reported beside it.
         extra["eager_ms_per_step"] = ms_step
+        extra["eager_median_ms_per_step"] = med
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             cap = torch.cuda.current_stream()
-            for i in range(ROTATE):
+            for i in range(nrot):
                 step(i, cap)
         graph.replay()
         torch.cuda.synchronize()
-        reps = 10 * max(1, steps // ROTATE)      # a few ms: one step is only ~10 us
-        start.record(stream)
-        for _ in range(reps):
-            graph.replay()
-        end.record(stream)
-        torch.cuda.synchronize()
-        ms_step = start.elapsed_time(end) / (reps * ROTATE)
-        extra["graph_steps_timed"] = reps * ROTATE
-    z = outs[(steps - 1) % ROTATE][0]
+        reps = max(3, (10 * steps) // nrot)
+        ms_rep, med_rep = timed(stream, reps, lambda i: graph.replay())
+        ms_step, extra["median_ms_per_step"] = ms_rep / nrot, med_rep / nrot
+        extra["graph_steps_timed"] = reps * nrot
+    z = outs[(steps - 1) % nrot][0]
     finite = bool(torch.isfinite(z).all().item())
     del sets, outs, base
     torch.cuda.empty_cache()
@@ -285,13 +316,16 @@ def measure(wl: wlm.Workload, inp: wlm.Inputs, steps: int, warmup: int, variant:
     path_key = "large" if wl.b >= 256 else wl.kind
     if variant != "dual":
         path_key = variant
-    if wl.b >= 256 and variant == "dual":
-        roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_BF16_PEAK_TFS,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    mfma = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
+    hbm = {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    for r in (mfma, hbm):
+        r["frac"] = r["achieved"] / r["peak"]
+    # large chunks and the MLP (arithmetic intensity at or above the ridge) are
+    # priced against the matrix cores, the rest against HBM; the MLP reports both
+    roof = mfma if ((wl.b >= 256 and variant == "dual") or wl.kind == "mlp") else hbm
     roof["traffic"] = measured_traffic(wl, path_key, variant)
+    if wl.kind == "mlp":
+        extra = dict(extra, roofline_hbm=dict(hbm, traffic=roof["traffic"]))
     log(f"[bench] {wl.name} {variant}: {ms*1e3:.1f} us/step, {tokens/sec:.4g} tokens/s, "
         f"{nbytes/sec/1e9:.1f} GB/s algorithmic, {flops/sec/1e12:.2f} TFLOP/s algorithmic")
     return ms, tokens / sec, nbytes, flops, roof, extra
@@ -308,6 +342,18 @@ def side_measurement(name: str, steps: int, warmup: int, variant: str):
 
 
 MFMA_F32_PEAK_TFS = 157.3     # MI355X dense fp32 matrix, TFLOP/s
+
+
+def bwd_algorithmic_bytes(wl: wlm.Workload) -> int:
+    """Compulsory HBM bytes of one backward call: read Q, K, V, eta, W0, gamma,
+    beta and the upstream dZ, dW_end; write dQ, dK, dV, deta, dW0, dgamma, dbeta."""
+    es = 2 if wl.dtype == "bf16" else 4
+    tok = wl.B * wl.H * wl.N
+    state = wl.B * wl.H * wl.d * wl.d * 4
+    hv = wl.H * wl.d * 4 if wl.kind == "ln" else 0
+    read = 3 * tok * wl.d * es + tok * 4 + state + 2 * hv + tok * wl.d * 4 + state
+    write = 3 * tok * wl.d * 4 + tok * 4 + state + 2 * hv
+    return read + write
 
 
 def bwd_algorithmic_flops(wl: wlm.Workload) -> int:
@@ -347,14 +393,13 @@ def bwd_measurement(steps: int, warmup: int):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        out = step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    last = {}
+
+    def keep(i):
+        last["out"] = step(i)
+
+    ms, med = timed(stream, steps, keep)
+    out = last["out"]
     finite = bool(torch.isfinite(out["dQ"]).all().item())
     if not finite:
         log(f"[bench] WARNING: non-finite backward output in {wl.name}")
@@ -365,11 +410,12 @@ def bwd_measurement(steps: int, warmup: int):
     tokens = wl.B * wl.N
     roof = {"bound": "mfma", "achieved": flops / sec / 1e12, "peak": MFMA_F32_PEAK_TFS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(wl, "backward", "backward")
     log(f"[bench] {wl.name} backward: {ms*1e3:.1f} us/step, {tokens/sec:.4g} tokens/s, "
         f"{flops/sec/1e12:.2f} TFLOP/s algorithmic (fp32)")
     return {"workload": wl.name, "variant": "backward", "value": tokens / sec, "unit": "tokens/s",
-            "ms_per_step": ms, "algorithmic_flops": flops, "dtype": "f32", "roofline": roof}
+            "ms_per_step": ms, "median_ms_per_step": med, "algorithmic_flops": flops, "dtype": "f32",
+            "roofline": roof}
 
 
 def layer_algorithmic(wl: wlm.LayerWorkload):
@@ -414,14 +460,7 @@ def layer_measurement(steps: int, warmup: int):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    ms, med = timed(stream, steps, step)
     finite = bool(torch.isfinite(outs[(steps - 1) % ROTATE][0]).all().item())
     if not finite:
         log(f"[bench] WARNING: non-finite output in {wl.name}")
@@ -436,7 +475,8 @@ def layer_measurement(steps: int, warmup: int):
     log(f"[bench] {wl.name}: {ms*1e3:.1f} us/step, {tokens/sec:.4g} tokens/s, "
         f"{flops/sec/1e12:.2f} TFLOP/s algorithmic")
     return {"workload": wl.name, "variant": "layer", "value": tokens / sec, "unit": "tokens/s",
-            "ms_per_step": ms, "algorithmic_bytes": nbytes, "algorithmic_flops": flops, "roofline": roof}
+            "ms_per_step": ms, "median_ms_per_step": med, "algorithmic_bytes": nbytes,
+            "algorithmic_flops": flops, "roofline": roof}
 
 
 # ---------------------------------------------------------------------------
@@ -448,7 +488,7 @@ def cpu_baseline(wl: wlm.Workload, inp: wlm.Inputs, max_units: int, min_wall: fl
     one untimed run, then repeated runs until `min_wall` seconds have passed (at
     least three); the best run gives the rate."""
     import oracle
-    threads = min(len(os.sched_getaffinity(0)), 16)
+    threads = cpu_threads()
     nb = max(1, min(wl.B, max_units // wl.H))
     sl = slice(0, nb)
     q, k, v = inp.f64("q")[sl], inp.f64("k")[sl], inp.f64("v")[sl]
@@ -486,7 +526,7 @@ def cpu_baseline(wl: wlm.Workload, inp: wlm.Inputs, max_units: int, min_wall: fl
 def _oracle_rate(run, tokens: int, sample: str, min_wall: float = 1.0):
     """Best rate of `run` (the oracle on a bounded sample) over at least two runs
     and `min_wall` seconds; `tokens` is what one run processes."""
-    threads = min(len(os.sched_getaffinity(0)), 16)
+    threads = cpu_threads()
     times, total = [], 0.0
     while len(times) < 2 or total < min_wall:
         t0 = time.perf_counter()
@@ -563,6 +603,9 @@ def main():
     ap.add_argument("--variant", default=None, choices=["dual", "block_before", "block_after", "decode"],
                     help="outputs to measure (default: decode for the decode workload, else dual)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the fp32 single-unit, long-context and TTT-MLP workloads that accompany "
+                         "the default workload")
     ap.add_argument("--no-b2048", action="store_true",
                     help="skip the large-chunk measurement that accompanies the default workload")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -587,6 +630,10 @@ def main():
 
     b2048 = None
     next_rows = None
+    configs = None
+    if wl.name == DEFAULT_WORKLOAD and variant == "dual" and not args.no_configs:
+        # the other forward workloads: fp32 single unit, long context, TTT-MLP
+        configs = {name: side_measurement(name, args.steps, args.warmup, "dual") for name in OTHER_CONFIGS}
     if wl.name == DEFAULT_WORKLOAD and variant == "dual" and not args.no_b2048:
         b2048 = side_measurement(LARGE_WORKLOAD, args.steps, args.warmup, "dual")
         next_rows = {
@@ -603,6 +650,13 @@ def main():
             next_rows[key]["cpu_baseline"] = cpu_baseline_side(key)
         log("[bench] side cpu baselines: " + ", ".join(
             f"{k} {v['cpu_baseline']['value']:.3g}" for k, v in [("b2048", b2048), *next_rows.items()]))
+
+    if not args.no_cpu_baseline and configs is not None:
+        for name, obj in configs.items():
+            idx = [w.name for w in wlm.WORKLOADS].index(name)
+            obj["cpu_baseline"] = cpu_baseline(wlm.WORKLOADS[idx], wlm.workload_inputs(idx), args.cpu_units)
+        log("[bench] config cpu baselines: " + ", ".join(
+            f"{k} {v['cpu_baseline']['value']:.3g}" for k, v in configs.items()))
 
     if args.copy_calibration:
         copy_calibration()
@@ -634,6 +688,8 @@ def main():
         "cpu_baseline": cpu,
     }
     rec["config"].update(extra)
+    if configs is not None:
+        rec["configs"] = configs
     if b2048 is not None:
         rec["b2048"] = b2048
         rec["practical_peaks"] = practical_peaks()

@@ -97,8 +97,11 @@ typedef enum {
  *   W_end       device [B,H,d,d] fp32 output, the state after the last token;
  *               may equal W0
  *   workspace   device scratch of at least ttt_linear_fwd_workspace_bytes(...)
- *               bytes, 256-byte aligned (may be NULL when that size is 0)
+ *               bytes, 256-byte aligned (may be NULL when that size is 0); it
+ *               must not overlap any input or output
  *   hip_stream  hipStream_t to launch on
+ * Alignment: Q, K, V, Z and eta 16 bytes; W0, W_end 4 bytes (else
+ * TTT_ERR_INVALID_ARGUMENT).
  *
  * Supported (else TTT_ERR_UNSUPPORTED):
  *   small-b path  : kind PLAIN or LN, dtype F32 or BF16, d = 64, 1 <= b <= 16
@@ -224,8 +227,11 @@ size_t ttt_linear_bwd_workspace_bytes(int kind, int qkv_dtype, int B, int H, int
 int ttt_linear_fwd_path(int kind, int qkv_dtype, int d, int b);
 
 /*
- * ttt_mlp_fwd -- TTT-MLP forward, f(x) = x + LN(GELU(x W1) W2), no biases, exact
- * erf GELU. The page "How to Master Test-Time Training for Infinite Context
+ * ttt_mlp_fwd -- TTT-MLP forward, f(x) = x + LN(GELU(x W1) W2), no biases,
+ * GELU(a) = a Phi(a) with the Gaussian CDF Phi = (1 + erf(a / sqrt 2)) / 2 (the
+ * erf form, not the tanh approximation). The kernel evaluates erf with
+ * Abramowitz & Stegun, "Handbook of Mathematical Functions", formula 7.1.26
+ * (|error| <= 1.5e-7, i.e. at most 7.5e-8 in Phi). The page "How to Master Test-Time Training for Infinite Context
  * LLMs" (section "The Math and Architecture of TTT Layers") names a small
  * multi-layer perceptron as the inner model. The dual form is applied to both
  * layers: with A = K W1_c, X2 = GELU(A) and the loss gradients G2 (at the

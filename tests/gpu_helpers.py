@@ -19,6 +19,36 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return num if den == 0.0 else num / den
 
 
+def unit_errs(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """rel_err of every (sequence, head) unit of [B, H, ...] arrays: the maximum
+    absolute difference over the unit's outputs divided by the unit's max |ref|."""
+    B, H = ref.shape[:2]
+    diff = np.abs(got.astype(np.float64) - ref).reshape(B, H, -1).max(axis=2)
+    den = np.abs(ref).reshape(B, H, -1).max(axis=2)
+    return np.where(den > 0, diff / np.where(den > 0, den, 1.0), diff)
+
+
+def check_all_units(name: str, pairs, tol: float):
+    """Assert every unit of every (label, got, ref) pair is within tol; print the
+    worst unit of each."""
+    worst = {}
+    for label, got, ref in pairs:
+        e = unit_errs(got, ref)
+        bi, hi = np.unravel_index(int(np.argmax(e)), e.shape)
+        worst[label] = (float(e.max()), (int(bi), int(hi)))
+        say(f"  {name} {label}: all {e.size} units, worst {e.max():.2e} at unit ({bi},{hi}), "
+            f"median {np.median(e):.2e} (tol {tol:.0e})")
+    for label, (e, u) in worst.items():
+        assert e <= tol, f"{name} {label}: unit {u} error {e:.2e} > {tol:.0e}"
+
+
+def row_mean_ratio(x: np.ndarray, w: np.ndarray) -> float:
+    """Median over the rows of h = x W of |mean(h)| / std(h), x [B,H,T,d] and
+    W [B,H,d,e] in fp64: how far a LayerNorm input's mean sits above its spread."""
+    h = np.einsum("bhtd,bhde->bhte", x, w)
+    return float(np.median(np.abs(h.mean(-1)) / h.std(-1)))
+
+
 def say(msg: str):
     print(msg, flush=True)
     sys.stdout.flush()

@@ -92,6 +92,10 @@ def test_rejects_invalid_arguments(lib):
     assert lin_call(lib, Z=ctypes.c_void_p(A + 8)) == E
     # W_end partially overlapping W0 (equal is allowed, see below)
     assert lin_call(lib, We=ctypes.c_void_p(A + 3 * (1 << 30) + 64)) == E
+    # Z and per-token eta are accessed with 16-byte vectors
+    assert lin_call(lib, Z=ctypes.c_void_p(A + 6 * (1 << 30) + 4)) == E
+    assert lin_call(lib, eta=ctypes.c_void_p(A + 8 * (1 << 30) + 4)) == E
+    assert lin_call(lib, eta=ctypes.c_void_p(A + 8 * (1 << 30) + 16)) != E
 
 
 def test_rejects_unsupported(lib):
@@ -105,6 +109,42 @@ def test_rejects_unsupported(lib):
 def test_large_chunk_workspace_checked_before_launch(lib):
     rc = lin_call(lib, B=1, H=16, N=32768, d=128, b=2048, ws=None, wsb=0)
     assert rc == binding.TTT_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_large_chunk_workspace_must_not_overlap_eta(lib):
+    # the large path writes its workspace while other workgroups still read eta
+    need = lib.ttt_linear_fwd_workspace_bytes(0, 1, 1, 16, 32768, 128, 2048)
+    assert need > 0
+    rc = lin_call(lib, B=1, H=16, N=32768, d=128, b=2048, eta=ctypes.c_void_p(A + 9 * (1 << 30) + 256),
+                  ws=9, wsb=need)
+    assert rc == binding.TTT_ERR_INVALID_ARGUMENT
+    rc = lin_call(lib, B=1, H=16, N=32768, d=128, b=2048, eta=8, ws=9, wsb=need)
+    assert rc != binding.TTT_ERR_INVALID_ARGUMENT
+
+
+def test_binding_checks_mlp_outputs_before_launch(monkeypatch):
+    """mlp_fwd validates caller-supplied outputs (shape, dtype, contiguity) before
+    the library is called: a wrong-shape z must raise, not reach the kernel."""
+    import torch
+
+    class NoLaunch:
+        def __getattr__(self, name):
+            raise AssertionError(f"{name} called despite an invalid output")
+
+    monkeypatch.setattr(binding, "load_library", lambda *a, **k: NoLaunch())
+    monkeypatch.setattr(binding, "_on_device", lambda t: True)
+    B, H, N, d, hid = 1, 2, 8, 64, 256
+    q = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+    w1 = torch.zeros((B, H, d, hid))
+    w2 = torch.zeros((B, H, hid, d))
+    g = torch.ones((H, d))
+    kw = dict(b=4, ln_gamma=g, ln_beta=g)
+    with pytest.raises(ValueError, match="z has shape"):
+        binding.mlp_fwd(q, q, q, w1, w2, z=torch.zeros((B, H, N, d + 1)), **kw)
+    with pytest.raises(TypeError, match="w1_end must be"):
+        binding.mlp_fwd(q, q, q, w1, w2, w1_end=torch.zeros((B, H, d, hid), dtype=torch.float64), **kw)
+    with pytest.raises(ValueError, match="w2_end must be contiguous"):
+        binding.mlp_fwd(q, q, q, w1, w2, w2_end=torch.zeros((B, H, d, hid)).transpose(2, 3), **kw)
 
 
 def test_mlp_rejections(lib):

@@ -10,7 +10,8 @@ import pytest
 import oracle
 from weights_ttt_layer_amd import workloads as wlm
 
-from gpu_helpers import TOL, gpu_decode, gpu_linear_block, oracle_linear, rel_err, sample_units, say
+from gpu_helpers import (TOL, check_all_units, gpu_decode, gpu_linear_block, oracle_linear, rel_err,
+                         row_mean_ratio, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,18 +53,14 @@ def test_block_before_first_chunk_is_q_w0():
 
 
 @pytest.mark.parametrize("apply", ["before", "after"])
-def test_block_workload_sampled_units(apply):
+def test_block_workload_all_units(apply):
     """The full large-chunk workload (B=1 H=16 N=32768 d=128 b=2048), launched
-    whole; two heads compared with the oracle run on them alone."""
+    whole; every head compared with the oracle run over the whole input."""
     inp = wlm.workload_inputs(4)
-    say(f"case {inp.wl.name} block apply={apply} (full launch, sampled units)")
+    say(f"case {inp.wl.name} block apply={apply} (full launch, every unit)")
     z, w = gpu_linear_block(inp, apply)
-    assert np.all(np.isfinite(z)) and np.all(np.isfinite(w))
-    for (bi, hi) in sample_units(inp.wl, 2, seed=5):
-        zr, wr = oracle_linear(inp.unit(bi, hi), MODES[apply])
-        ez, ew = rel_err(z[bi, hi], zr[0, 0]), rel_err(w[bi, hi], wr[0, 0])
-        say(f"  unit ({bi},{hi}): err Z {ez:.2e} W_end {ew:.2e}")
-        assert ez <= TOL["bf16"] and ew <= TOL["bf16"]
+    zr, wr = oracle_linear(inp, MODES[apply])
+    check_all_units(f"{inp.wl.name} {apply}", [("Z", z, zr), ("W_end", w, wr)], TOL["bf16"])
 
 
 def dec(kind, dtype, B, H, N, eta, seed):
@@ -98,18 +95,33 @@ def test_decode_stream_counts(kind, dtype, B, H):
     assert ez <= TOL[dtype] and ew <= TOL[dtype]
 
 
-def test_decode_workload_sampled_units():
+def test_decode_workload_all_streams():
     """The decode workload (B=64 H=12 d=64, LN, bf16), one step for all 768
-    streams; sampled streams compared with the oracle run on them alone."""
+    streams; every stream compared with the oracle."""
     idx = [w.name for w in wlm.WORKLOADS].index("decode_ln_bf16_B64H12_d64")
     inp = wlm.workload_inputs(idx)
-    say(f"case {inp.wl.name}")
+    say(f"case {inp.wl.name} (every stream)")
     z, w = gpu_decode(inp)
-    for (bi, hi) in sample_units(inp.wl, 6, seed=3):
-        zr, wr = oracle_linear(inp.unit(bi, hi), oracle.ONLINE)
-        ez, ew = rel_err(z[bi, hi], zr[0, 0]), rel_err(w[bi, hi], wr[0, 0])
-        say(f"  unit ({bi},{hi}): err z {ez:.2e} W {ew:.2e}")
-        assert ez <= TOL["bf16"] and ew <= TOL["bf16"]
+    zr, wr = oracle_linear(inp, oracle.ONLINE)
+    check_all_units(inp.wl.name, [("z", z, zr), ("W", w, wr)], TOL["bf16"])
+
+
+@pytest.mark.parametrize("kind,dtype", [("ln", "bf16"), ("ln", "f32")])
+def test_decode_large_row_mean(kind, dtype):
+    """LayerNorm inputs whose row mean is 30-40 times their spread (the state
+    offset by a constant): the decode step's centred variance must still match.
+    (The step forms h = k W in fp32 from the state as given, so its absolute
+    rounding grows with the row mean; at 1e-5 this holds up to a ratio of ~100.)"""
+    inp = dec(kind, dtype, 2, 3, 5, "sigmoid", seed=23)
+    inp.w0 = (inp.w0.astype(np.float64) + 6.0).astype(np.float32)
+    ratio = row_mean_ratio(inp.f64("k"), inp.f64("w0"))
+    say(f"case {inp.wl.name} (offset state): median |mean|/std of k W0 rows {ratio:.0f}")
+    assert ratio >= 30.0
+    z, w = gpu_decode(inp)
+    zr, wr = oracle_linear(inp, oracle.ONLINE)
+    ez, ew = rel_err(z, zr), rel_err(w, wr)
+    say(f"  err Z {ez:.2e}  W {ew:.2e}  (tol {TOL[dtype]:.0e})")
+    assert ez <= TOL[dtype] and ew <= TOL[dtype]
 
 
 def test_decode_graph_replay_matches_eager():

@@ -11,7 +11,7 @@ import pytest
 import oracle
 from weights_ttt_layer_amd import workloads as wlm
 
-from gpu_helpers import rel_err, say
+from gpu_helpers import check_all_units, rel_err, row_mean_ratio, say
 
 pytestmark = pytest.mark.gpu
 
@@ -89,17 +89,29 @@ def test_bwd_without_state_gradient():
     compare(gpu_bwd(inp, dz, None, with_dw=False), oracle_bwd(inp, dz, None))
 
 
-def test_bwd_named_workload_sampled():
+def test_bwd_named_workload_all_units():
     """The benchmark workload (TTT-Linear+LN, bf16, B=8 H=12 N=2048 b=16) in full
-    on the GPU; four (sequence, head) units checked against the oracle on their
-    own (every output but dgamma/dbeta belongs to one unit)."""
+    on the GPU; every output of every (sequence, head) unit compared with the
+    oracle over the whole input, dgamma/dbeta (summed over the batch) whole."""
     inp = wlm.workload_inputs(1)
     dz, dw = wlm.upstream_grads(inp.wl, 7)
+    say(f"case {inp.wl.name} backward (every unit)")
     g = gpu_bwd(inp, dz, dw)
-    say(f"case {inp.wl.name}")
-    for bi, hi in ((0, 0), (3, 7), (5, 2), (7, 11)):
-        sub = inp.unit(bi, hi)
-        ref = oracle_bwd(sub, dz[bi:bi + 1, hi:hi + 1], dw[bi:bi + 1, hi:hi + 1])
-        got = {k: g[k][bi:bi + 1, hi:hi + 1] for k in ("dQ", "dK", "dV", "deta", "dW0")}
-        say(f"  unit ({bi},{hi})")
-        compare(got, ref, ("dQ", "dK", "dV", "deta", "dW0"))
+    ref = oracle_bwd(inp, dz, dw)
+    check_all_units(inp.wl.name, [(k, g[k], ref[k]) for k in ("dQ", "dK", "dV", "deta", "dW0")], TOL)
+    compare(g, ref, ("dgamma", "dbeta"))
+
+
+def test_bwd_large_row_mean():
+    """LayerNorm inputs whose row mean is 30-40 times their spread (W0 offset by
+    a constant, so every key and query pre-activation row gets a large shift).
+    The backward recomputes K W from the state as given in fp32, so its
+    absolute rounding grows with the row mean; at 1e-5 this holds up to a ratio
+    of ~100."""
+    inp = case("ln", "f32", 1, 2, 40, 16, "sigmoid", seed=12)
+    inp.w0 = (inp.w0.astype(np.float64) + 7.0).astype(np.float32)
+    ratio = row_mean_ratio(inp.f64("k"), inp.f64("w0"))
+    dz, dw = wlm.upstream_grads(inp.wl, 8)
+    say(f"case {inp.wl.name} (offset state): median |mean|/std of k W0 rows {ratio:.0f}")
+    assert ratio >= 30.0
+    compare(gpu_bwd(inp, dz, dw), oracle_bwd(inp, dz, dw))

@@ -9,7 +9,7 @@ import pytest
 
 from weights_ttt_layer_amd import workloads as wlm
 
-from gpu_helpers import TOL, gpu_linear, oracle_linear, rel_err, sample_units, say
+from gpu_helpers import TOL, check_all_units, gpu_linear, oracle_linear, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -59,18 +59,15 @@ def test_large_chunk_single_chunk_is_causal_linear_attention():
     assert rel_err(w[0, 0], wc) <= TOL["bf16"]
 
 
-def test_large_chunk_workload_sampled_units():
+def test_large_chunk_workload_all_units():
     """The full large-chunk workload (B=1 H=16 N=32768 d=128 b=2048, eta = 0.01),
-    launched whole; two heads compared with the oracle run on them alone."""
+    launched whole (the 16-step scan of every head on its XCD-mapped grid); every
+    head compared with the oracle run over the whole input."""
     inp = wlm.workload_inputs(4)
-    say(f"case {inp.wl.name} (full launch, sampled units)")
+    say(f"case {inp.wl.name} (full launch, every unit)")
     z, w = gpu_linear(inp)
-    assert np.all(np.isfinite(z)) and np.all(np.isfinite(w))
-    for (bi, hi) in sample_units(inp.wl, 2, seed=4):
-        zr, wr = oracle_linear(inp.unit(bi, hi))
-        ez, ew = rel_err(z[bi, hi], zr[0, 0]), rel_err(w[bi, hi], wr[0, 0])
-        say(f"  unit ({bi},{hi}): err Z {ez:.2e} W_end {ew:.2e}")
-        assert ez <= TOL["bf16"] and ew <= TOL["bf16"]
+    zr, wr = oracle_linear(inp)
+    check_all_units(inp.wl.name, [("Z", z, zr), ("W_end", w, wr)], TOL["bf16"])
 
 
 def test_large_chunk_state_passing():

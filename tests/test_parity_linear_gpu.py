@@ -10,7 +10,7 @@ import pytest
 import oracle
 from weights_ttt_layer_amd import workloads as wlm
 
-from gpu_helpers import TOL, gpu_linear, oracle_linear, rel_err, sample_units, say
+from gpu_helpers import TOL, check_all_units, gpu_linear, oracle_linear, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -68,20 +68,43 @@ def test_every_chunk_size(kind, dtype, b):
 
 
 @pytest.mark.parametrize("index", [1, 2])
-def test_workload_ln_bf16_sampled_units(index):
+def test_workload_ln_bf16_all_units(index):
     """Full-size LN workloads (B=8 H=12 N=2048; B=16 H=12 N=8192), launched whole
-    exactly as the benchmark launches them; every output of a spread of units is
-    compared with the oracle run on those units alone."""
+    exactly as the benchmark launches them; every output of every unit is
+    compared with the oracle run over the whole input."""
     inp = wlm.workload_inputs(index)
-    say(f"case {inp.wl.name} (full launch, sampled units)")
+    say(f"case {inp.wl.name} (full launch, every unit)")
     z, w = gpu_linear(inp)
-    assert np.all(np.isfinite(z)) and np.all(np.isfinite(w))
-    for (bi, hi) in sample_units(inp.wl, 4 if index == 1 else 3, seed=index):
-        u = inp.unit(bi, hi)
-        zr, wr = oracle_linear(u)
-        ez, ew = rel_err(z[bi, hi], zr[0, 0]), rel_err(w[bi, hi], wr[0, 0])
-        say(f"  unit ({bi},{hi}): err Z {ez:.2e} W_end {ew:.2e}")
-        assert ez <= TOL["bf16"] and ew <= TOL["bf16"]
+    zr, wr = oracle_linear(inp)
+    check_all_units(inp.wl.name, [("Z", z, zr), ("W_end", w, wr)], TOL["bf16"])
+
+
+def offset_state(inp, c: float):
+    """Add c to every entry of W0: each pre-activation row k W0 gains c * sum(k),
+    a row mean far above the row's spread (LayerNorm's cancellation case)."""
+    inp.w0 = (inp.w0.astype(np.float64) + c).astype(np.float32)
+    return inp
+
+
+def mean_to_spread(inp):
+    """Median and 10th percentile over the first chunk's key rows of
+    |mean(k W0)| / std(k W0) (the ratio the offset cases aim at)."""
+    h = np.einsum("bhtd,bhde->bhte", inp.f64("k")[:, :, :inp.wl.b], inp.f64("w0"))
+    r = np.abs(h.mean(-1)) / h.std(-1)
+    return float(np.median(r)), float(np.percentile(r, 10))
+
+
+@pytest.mark.parametrize("dtype,c", [("bf16", 6.0), ("bf16", 60.0), ("f32", 6.0), ("f32", 60.0)])
+def test_ln_large_row_mean(dtype, c):
+    """LayerNorm inputs whose row mean is 30-300 times their spread: the state is
+    offset by a constant c, so every pre-activation row (keys and queries) gets a
+    large common shift. A variance formed as E[h^2] - mu^2 would cancel
+    catastrophically here; the kernels must still match the oracle."""
+    inp = offset_state(small("ln", dtype, 2, 3, 90, 16, seed=31), c)
+    med, p10 = mean_to_spread(inp)
+    say(f"case {inp.wl.name} offset {c}: |mean|/std of k W0 rows: median {med:.0f}, 10th pct {p10:.0f}")
+    assert med >= 30.0
+    check(inp)
 
 
 @pytest.mark.parametrize("kind,dtype", [("plain", "f32"), ("ln", "bf16")])

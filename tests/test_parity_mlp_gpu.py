@@ -9,9 +9,17 @@ import pytest
 
 from weights_ttt_layer_amd import workloads as wlm
 
-from gpu_helpers import TOL, gpu_mlp, oracle_mlp, rel_err, sample_units, say
+from gpu_helpers import TOL, check_all_units, gpu_mlp, oracle_mlp, rel_err, say
 
 pytestmark = pytest.mark.gpu
+
+
+def within_recompose(w2, w2_0) -> bool:
+    """W2_end = (W2_0 - m) + m in fp32 with m the row mean: two roundings, each at
+    most half a unit in the last place of a value no larger than |W2_0| + |m|."""
+    w0 = w2_0.astype(np.float64)
+    m = np.abs(w0.mean(axis=-1, keepdims=True))
+    return bool(np.all(np.abs(w2.astype(np.float64) - w0) <= np.spacing((np.abs(w0) + m).astype(np.float32))))
 
 
 def small(dtype, B, H, N, b, eta="sigmoid", seed=11):
@@ -46,19 +54,36 @@ def test_mlp_chunk_sizes(b):
     check(inp)
 
 
-def test_mlp_workload_sampled_units():
-    """Full-size TTT-MLP workload (B=4 H=12 N=4096), launched whole; a spread of
-    units compared with the oracle run on those units alone."""
+def test_mlp_workload_all_units():
+    """Full-size TTT-MLP workload (B=4 H=12 N=4096), launched whole; every output
+    of every unit compared with the oracle run over the whole input."""
     inp = wlm.workload_inputs(3)
-    say(f"case {inp.wl.name} (full launch, sampled units)")
+    say(f"case {inp.wl.name} (full launch, every unit)")
     z, w1, w2 = gpu_mlp(inp)
-    assert np.all(np.isfinite(z))
-    for (bi, hi) in sample_units(inp.wl, 3, seed=3):
-        zr, w1r, w2r = oracle_mlp(inp.unit(bi, hi))
-        errs = (rel_err(z[bi, hi], zr[0, 0]), rel_err(w1[bi, hi], w1r[0, 0]),
-                rel_err(w2[bi, hi], w2r[0, 0]))
-        say(f"  unit ({bi},{hi}): err Z {errs[0]:.2e} W1 {errs[1]:.2e} W2 {errs[2]:.2e}")
-        assert max(errs) <= TOL["bf16"]
+    zr, w1r, w2r = oracle_mlp(inp)
+    check_all_units(inp.wl.name, [("Z", z, zr), ("W1_end", w1, w1r), ("W2_end", w2, w2r)], TOL["bf16"])
+
+
+def mean_to_spread(inp):
+    """Median over the first chunk's key rows of |mean(h)| / std(h), h = GELU(k W1) W2."""
+    from scipy.special import erf
+    a = np.einsum("bhtd,bhdf->bhtf", inp.f64("k")[:, :, :inp.wl.b], inp.f64("w1"))
+    x2 = 0.5 * a * (1.0 + erf(a / np.sqrt(2.0)))
+    h = np.einsum("bhtf,bhfd->bhtd", x2, inp.f64("w2"))
+    return float(np.median(np.abs(h.mean(-1)) / h.std(-1)))
+
+
+@pytest.mark.parametrize("dtype,c", [("bf16", 0.5), ("bf16", 5.0), ("f32", 1.5), ("f32", 15.0)])
+def test_mlp_large_row_mean(dtype, c):
+    """LayerNorm inputs whose row mean is far above their spread: W2 is offset by a
+    constant c, so every row of H = GELU(X W1) W2 (keys and queries) gets a large
+    common shift; a variance formed as E[h^2] - mu^2 would cancel here."""
+    inp = small(dtype, 2, 2, 45, 16, seed=41)
+    inp.w2 = (inp.w2.astype(np.float64) + c).astype(np.float32)
+    med = mean_to_spread(inp)
+    say(f"case {inp.wl.name} W2 offset {c}: median |mean|/std of the LayerNorm input rows {med:.0f}")
+    assert med >= 30.0
+    check(inp)
 
 
 def test_mlp_zero_affine_identity():
@@ -68,7 +93,9 @@ def test_mlp_zero_affine_identity():
     inp.beta = np.zeros_like(inp.beta)
     z, w1, w2 = gpu_mlp(inp)
     assert np.array_equal(z, inp.f64("q").astype(np.float32))
-    assert np.array_equal(w1, inp.w1) and np.array_equal(w2, inp.w2)
+    assert np.array_equal(w1, inp.w1)
+    # W2 is carried with its row means removed and added back (one rounding)
+    assert within_recompose(w2, inp.w2)
 
 
 def test_mlp_eta_zero():
@@ -76,6 +103,8 @@ def test_mlp_eta_zero():
     inp = small("bf16", 1, 2, 40, 16, eta="const")
     inp.eta_const = 0.0
     z, w1, w2 = gpu_mlp(inp)
-    assert np.array_equal(w1, inp.w1) and np.array_equal(w2, inp.w2)
+    # W1 is carried as given; W2 with its row means removed and added back at the end
+    assert np.array_equal(w1, inp.w1)
+    assert within_recompose(w2, inp.w2)
     zr, _, _ = oracle_mlp(inp)
     assert rel_err(z, zr) <= TOL["bf16"]

@@ -97,10 +97,14 @@ def _qkv_dtype(t: torch.Tensor) -> int:
     raise TypeError(f"Q/K/V must be bfloat16 or float32, got {t.dtype}")
 
 
+def _on_device(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
 def _check(t: torch.Tensor, name: str, shape, dtype=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
+    if not _on_device(t):
         raise ValueError(f"{name} must be a device (HIP) tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -254,9 +258,18 @@ def mlp_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tensor,
         _check(eta, "eta", (B, H, N), torch.float32)
     _check(ln_gamma, "ln_gamma", (H, d), torch.float32)
     _check(ln_beta, "ln_beta", (H, d), torch.float32)
-    z = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if z is None else z
-    w1_end = torch.empty_like(w1) if w1_end is None else w1_end
-    w2_end = torch.empty_like(w2) if w2_end is None else w2_end
+    if z is None:
+        z = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    else:
+        _check(z, "z", (B, H, N, d), torch.float32)
+    if w1_end is None:
+        w1_end = torch.empty_like(w1)
+    else:
+        _check(w1_end, "w1_end", (B, H, d, hid), torch.float32)
+    if w2_end is None:
+        w2_end = torch.empty_like(w2)
+    else:
+        _check(w2_end, "w2_end", (B, H, hid, d), torch.float32)
     st = lib.ttt_mlp_fwd(dt, B, H, N, d, hid, int(b), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                          float(eta_const), _ptr(w1), _ptr(w2), _ptr(ln_gamma), _ptr(ln_beta),
                          float(ln_eps), _ptr(z), _ptr(w1_end), _ptr(w2_end), _stream_ptr(stream))

@@ -250,6 +250,21 @@ bwd_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
 
     // ---------------- pass 1: chunk-start states ----------------
     fetch_mat(W0 + (size_t)unit * BD * BD, pw);
+    if constexpr (KIND == 1) {
+        // LN kind: the recomputed states carry each row's mean over the output
+        // features removed. The forward is unchanged by it (LayerNorm ignores a
+        // constant added to a whole row, and the LayerNorm gradient of every
+        // token sums to zero over the features, so the update never moves the
+        // row means), and so is every gradient: the products with W^T
+        // (dH_Q W^T, dh W^T) take row-gradients that also sum to zero over the
+        // features. Without the means those products do not cancel a large
+        // common part in fp32. A row's 64 entries sit in one 16-lane DPP row.
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float mean = row16_sum((pw[m].x + pw[m].y) + (pw[m].z + pw[m].w)) * (1.f / BD);
+            pw[m] = make_float4(pw[m].x - mean, pw[m].y - mean, pw[m].z - mean, pw[m].w - mean);
+        }
+    }
     put_mat(sm.W, sm.WT, pw);
     pk = fetch_row(Kg, 0, min(b, N));
     pv = fetch_row(Vg, 0, min(b, N));

@@ -93,6 +93,7 @@ struct alignas(16) ChainSmem {
     uint2 xst[4][2][64];          // tril(S)^T of a chunk (slot c % 4), two bf16 terms, same order
     uint16_t gt[2][2][16 * D];    // -Gt of a chunk, two bf16 terms, [token][feature] tiles
     float2 xs[2][16][4];          // output LayerNorm partial sums [token][state wave]
+    float wrow[4][D];             // LN kind: partial row sums of W0 over each state wave's 16 columns
 };
 
 // Byte offset of element col (a multiple of 4) of row r in a ring/gradient tile.
@@ -392,7 +393,7 @@ __device__ __forceinline__ f32x4 row_dots(const uint16_t (&xt)[TIN][16 * D], con
     return a;
 }
 
-template <int TIN>
+template <int KIND, int TIN>
 __device__ __forceinline__ void w_role(ChainSmem<TIN>& sm, int bt, int lane, int C, const float* W0u, float* Wu)
 {
     constexpr int SL = RingGeom<TIN>::SLOTS;
@@ -405,10 +406,38 @@ __device__ __forceinline__ void w_role(ChainSmem<TIN>& sm, int bt, int lane, int
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) Wf[a][i] = W0u[(16 * a + 4 * g + i) * D + 16 * bt + n];
-    bf16x8 Wt[2][2];
-    split_w(Wf, Wt);
+    // LN kind: the state is carried with each row's mean over the output
+    // features removed. LayerNorm ignores a constant added to a whole row, so
+    // K W' and K W have the same LayerNorm and gradient; and the LayerNorm
+    // gradient of every token sums to zero over the features, so the update
+    // K^T Gt never changes the row means. The removed means are added back to
+    // W_end. With it, pre-activation rows have a near-zero mean whatever W0
+    // holds, so the one-pass variance and the two-term operands keep their
+    // relative precision.
+    float wmean[4][4] = {};
+    if constexpr (KIND == 1) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float s = row16_sum(Wf[a][i]);
+                if (n == 0) sm.wrow[bt][16 * a + 4 * g + i] = s;
+            }
+    }
 
     lds_barrier();                       // chunks 0 and 1 in LDS
+    if constexpr (KIND == 1) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * a + 4 * g + i;
+                wmean[a][i] = ((sm.wrow[0][r] + sm.wrow[1][r]) + (sm.wrow[2][r] + sm.wrow[3][r])) * (1.f / D);
+                Wf[a][i] -= wmean[a][i];
+            }
+    }
+    bf16x8 Wt[2][2];
+    split_w(Wf, Wt);
     if (C > 0) {
         const f32x4 a = wt_rows<TIN>(Wt, sm.ring[0].k, g, n);
         sm.xa[0][bt][lane] = make_float4(a[0], a[1], a[2], a[3]);
@@ -445,10 +474,21 @@ __device__ __forceinline__ void w_role(ChainSmem<TIN>& sm, int bt, int lane, int
         lds_barrier();
     }
 
+    // W_end = W0 + (accumulated change): W0 - mean is formed again with the
+    // rounding it had at the start, so a state that never moved comes back bit
+    // for bit. (W_end may be W0: every entry is read and written by one lane.)
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Wu[(16 * a + 4 * g + i) * D + 16 * bt + n] = Wf[a][i];
+        for (int i = 0; i < 4; ++i) {
+            const size_t o = (size_t)(16 * a + 4 * g + i) * D + 16 * bt + n;
+            float v = Wf[a][i];
+            if constexpr (KIND == 1) {
+                const float w0 = W0u[o];
+                v = w0 + (v - (w0 - wmean[a][i]));
+            }
+            Wu[o] = v;
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -670,7 +710,7 @@ smallb_chain_kernel(int H, int N, int b, size_t plane, const uint16_t* __restric
         resid_role<KIND, TIN>(sm, lane, h, C, gamma, beta);
     } else if (w <= 5) {
         const int bt = (w == 5) ? 3 : w - 1;
-        w_role<TIN>(sm, bt, lane, C, W0 + unit * (size_t)D * D, Wend + unit * (size_t)D * D);
+        w_role<KIND, TIN>(sm, bt, lane, C, W0 + unit * (size_t)D * D, Wend + unit * (size_t)D * D);
     } else {
         const int bt = (w <= 7) ? w - 6 : w - 7;
         out_role<KIND, TIN>(sm, bt, lane, h, N, b, C, gamma, beta, eps, Zg + unit * (size_t)N * D);

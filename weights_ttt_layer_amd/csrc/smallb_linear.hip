@@ -52,6 +52,7 @@ struct alignas(16) Smem {
     float red1[ROWS][4][4];         // [token][wave]: sum h, sum h^2 (chunk c), sum hq, sum hq^2 (chunk c-1)
     float red2[ROWS][4][2];         // [token][wave]: LayerNorm-backward sums
     float tp[4][ROWS][ROWS + 4];    // per-wave transpose tile [wave][feature][token]
+    float wrow[4][D];               // LN kind: partial row sums of W0 over each wave's 16 columns
 };
 
 // Output stage of the LayerNorm kind for one chunk: Z = Q + LN(H_Q).
@@ -136,6 +137,32 @@ smallb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __r
     for (int j = 1; j <= PF; ++j)
         if (j < nchunks)
             load_chunk<S, PPT>(pf[j % PF], pe[j % PF], j, b, N, tid, Qu, Ku, Vu, etau, eta_const);
+
+    // LN kind: the state is carried with each row's mean over the output
+    // features removed (LayerNorm ignores a constant added to a whole row, and
+    // its gradient sums to zero over the features, so the update never changes
+    // the row means); the means are added back to W_end. Pre-activation rows
+    // then have a near-zero mean whatever W0 holds, so the one-pass variance
+    // keeps its relative precision.
+    float wmean[4][4] = {};
+    if constexpr (KIND == 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float s = row16_sum(Wacc[r][i]);
+                if (n == 0) sm.wrow[w][16 * r + 4 * g + i] = s;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * r + 4 * g + i;
+                wmean[r][i] = ((sm.wrow[0][row] + sm.wrow[1][row]) + (sm.wrow[2][row] + sm.wrow[3][row])) * (1.f / D);
+                Wacc[r][i] -= wmean[r][i];
+            }
+    }
 
     // W_c as B-operand terms, permuted k order
     bf16x8 Wb[2][TS];
@@ -345,11 +372,23 @@ smallb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __r
         store_ln_out(Zu, hq_prev, q_prev, S3, S4, gam, bet, eps, c0_prev, bc_prev, n, fcol);
     }
 
+    // W_end = W0 + (accumulated change): W0 - mean is formed again with the
+    // rounding it had at the start, so a state that never moved comes back bit
+    // for bit. (W_end may be W0: every entry is read and written by one lane.)
     float* Wu = Wend + unit * (size_t)D * D;
+    const float* W0u = W0 + unit * (size_t)D * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Wu[(16 * r + 4 * g + i) * D + col] = Wacc[r][i];
+        for (int i = 0; i < 4; ++i) {
+            const size_t o = (size_t)(16 * r + 4 * g + i) * D + col;
+            float v = Wacc[r][i];
+            if constexpr (KIND == 1) {
+                const float w0 = W0u[o];
+                v = w0 + (v - (w0 - wmean[r][i]));
+            }
+            Wu[o] = v;
+        }
 }
 
 template <int KIND, typename S, int TIN = Stor<S>::TERMS>

@@ -3,7 +3,8 @@
 //
 // Inner model: a small multi-layer perceptron (page "How to Master Test-Time
 // Training for Infinite Context LLMs", section "The Math and Architecture of
-// TTT Layers"), no biases, exact erf GELU, LayerNorm + residual on its output.
+// TTT Layers"), no biases, GELU in its erf form (erf evaluated with Abramowitz &
+// Stegun 7.1.26, |error| <= 1.5e-7), LayerNorm + residual on its output.
 // The mini-batch dual form (page "Test-Time Training: Linear Complexity Beyond
 // Attention", section "4. Mini-Batch Parallelism (Dual Formulation)") applied
 // to both layers, per chunk with chunk-start weights W1, W2:
@@ -53,6 +54,7 @@ struct alignas(16) MlpSmem {
     float d1[ROWS * XS];                       // GELU'(A), [token][hidden]
     float g2[ROWS * GS];     // dl/dH at the chunk-start weights (no eta), [token][d]
     float red[3][4][ROWS][2];
+    float w2mean[HID];       // row means of W2_0 (removed from the carried state)
 };
 
 // GELU(a) = a Phi(a), Phi(a) = (1 + erf(a / sqrt 2)) / 2, and its derivative
@@ -408,6 +410,31 @@ smallb_mlp_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
     const float gam = gamma[h * D + 16 * w + n];
     const float bet = beta[h * D + 16 * w + n];
 
+    // W2 is carried with each row's mean over the output features removed.
+    // LayerNorm ignores a constant added to a whole row of H = X2 W2, and its
+    // gradient G2 sums to zero over the features, so neither the update
+    // X2^T Gt2 nor the product G2 W2^T sees the means, and they never change;
+    // they are added back to W2_end. Rows of H then have a near-zero mean
+    // whatever W2_0 holds, so the one-pass variance keeps its precision.
+    // Wave w holds hidden rows 64w + 16t + n of W2^T in full (columns 16r + 4g + i).
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s += (W2Tacc[r][t][0] + W2Tacc[r][t][1]) + (W2Tacc[r][t][2] + W2Tacc[r][t][3]);
+        s = xrow4_sum(s) * (1.f / D);
+        if (g == 0) sm.w2mean[64 * w + 16 * t + n] = s;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) W2Tacc[r][t][i] -= s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) W2acc[r][i] -= sm.w2mean[16 * r + 4 * g + i];
+
     const int nchunks = (N + b - 1) / b;
     // one chunk in flight: loaded during the previous chunk's (long) body
     uint4 pf[PPT];
@@ -434,7 +461,8 @@ smallb_mlp_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
 #pragma unroll
     for (int r = 0; r < 16; ++r)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) W2o[(16 * r + 4 * g + i) * D + 16 * w + n] = W2acc[r][i];
+        for (int i = 0; i < 4; ++i)   // the row means added back (one rounding)
+            W2o[(16 * r + 4 * g + i) * D + 16 * w + n] = W2acc[r][i] + sm.w2mean[16 * r + 4 * g + i];
 }
 
 template <typename S>

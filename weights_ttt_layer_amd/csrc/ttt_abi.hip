@@ -86,8 +86,9 @@ int check_linear(int kind, int qkv_dtype, int B, int H, int N, int d, int b, con
     if (!Q || !K || !V || !W0 || !Z || !W_end) return TTT_ERR_INVALID_ARGUMENT;
     if (kind == TTT_LINEAR_LN && (!ln_gamma || !ln_beta || !(ln_eps >= 0.f)))
         return TTT_ERR_INVALID_ARGUMENT;
+    // Z rows leave as 16-byte stores; per-token eta is read in 16-byte vectors
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(W0, 4) ||
-        !aligned(Z, 4) || !aligned(W_end, 4) || (eta && !aligned(eta, 4)))
+        !aligned(Z, 16) || !aligned(W_end, 4) || (eta && !aligned(eta, 16)))
         return TTT_ERR_INVALID_ARGUMENT;
     // size arithmetic in 64 bits; reject overflow of the int32 sizes' products
     const size_t units = (size_t)B * (size_t)H;
@@ -115,7 +116,8 @@ int check_linear(int kind, int qkv_dtype, int B, int H, int N, int d, int b, con
         if (!aligned(workspace, 256)) return TTT_ERR_INVALID_ARGUMENT;
         if (overlaps(workspace, need, Z, z_bytes) || overlaps(workspace, need, W_end, w_bytes) ||
             overlaps(workspace, need, Q, qkv_bytes) || overlaps(workspace, need, K, qkv_bytes) ||
-            overlaps(workspace, need, V, qkv_bytes) || overlaps(workspace, need, W0, w_bytes))
+            overlaps(workspace, need, V, qkv_bytes) || overlaps(workspace, need, W0, w_bytes) ||
+            (eta && overlaps(workspace, need, eta, tok * 4)))
             return TTT_ERR_INVALID_ARGUMENT;
     }
 

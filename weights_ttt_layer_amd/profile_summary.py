@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "block_after": ["large_chunk.hip", "device_common.h"],
     "decode": ["decode.hip", "device_common.h"],
     "layer": ["outer_layer.hip", "smallb_chain.hip", "device_common.h"],
+    "backward": ["backward.hip", "device_common.h"],
 }
 
 OUR_KERNELS = ("smallb_linear_kernel", "smallb_chain_kernel", "smallb_mlp_kernel", "lc_gram_kernel", "lc_scan_kernel",
@@ -61,6 +62,7 @@ PATH_KERNELS = {
     "block_after": ("lc_gram_kernel", "lc_scan_kernel", "lc_apply_kernel<true>"),
     "decode": ("decode_kernel",),
     "layer": ("layer_gemm_kernel", "layer_outprep_kernel", "smallb_chain_kernel<1, 2,"),
+    "backward": ("bwd_linear_kernel", "bwd_gamma_beta_kernel"),
 }
 
 
@@ -134,7 +136,7 @@ def load_counter(d: str, counter: str):
 def traffic(args):
     sys.path.insert(0, ROOT)
     from weights_ttt_layer_amd import workloads as wlm
-    from bench import algorithmic_bytes, layer_algorithmic
+    from bench import algorithmic_bytes, bwd_algorithmic_bytes, layer_algorithmic
 
     layers = {w.name: w for w in wlm.LAYER_WORKLOADS}
     if args.workload in layers:
@@ -144,7 +146,7 @@ def traffic(args):
     else:
         wl = wlm.BY_NAME[args.workload]
         path_key = "large" if wl.b >= 256 else wl.kind
-        alg = algorithmic_bytes(wl)
+        alg = bwd_algorithmic_bytes(wl) if args.variant == "backward" else algorithmic_bytes(wl)
     if args.variant != "dual":
         path_key = args.variant
     suffix = "" if args.variant == "dual" else f"_{args.variant}"
