@@ -120,6 +120,35 @@ int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b,
  * small-b path). Returns 0 as well for unsupported or invalid combinations. */
 size_t ttt_linear_fwd_workspace_bytes(int kind, int qkv_dtype, int B, int H, int N, int d, int b);
 
+/* Size of the library's static device scratch array used by
+ * ttt_linear_fwd_noalloc (64 MiB). */
+#define TTT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * ttt_linear_fwd_noalloc -- ttt_linear_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). The arguments, results, supported combinations and
+ * errors are those of ttt_linear_fwd without the workspace: the large-chunk
+ * path puts its workspace in a file-scope device array of
+ * TTT_NOALLOC_SCRATCH_BYTES inside the library (one per device, created when
+ * the library's code is loaded on that device and kept until the process
+ * ends; its address is looked up once per device, on the first call made with
+ * that device current). The call allocates nothing and frees nothing.
+ *   Returns TTT_ERR_WORKSPACE_TOO_SMALL, before any HIP call, when
+ *   ttt_linear_fwd_workspace_bytes(...) exceeds TTT_NOALLOC_SCRATCH_BYTES
+ *   (at d = 128: when B*H*(3*ceil(N/b) + 1) exceeds 1024).
+ *   Every call on one device shares that device's array and leaves its last
+ *   contents there (every byte a call reads it has written first); calls that
+ *   overlap in time on one device, on different streams or host threads,
+ *   race on it and must be serialised by the caller.
+ * The small-b path needs no workspace and runs exactly as ttt_linear_fwd.
+ */
+int ttt_linear_fwd_noalloc(int kind, int qkv_dtype, int B, int H, int N, int d, int b,
+                           const void* Q, const void* K, const void* V,
+                           const float* eta, float eta_const, const float* W0,
+                           const float* ln_gamma, const float* ln_beta, float ln_eps,
+                           float* Z, float* W_end, void* hip_stream);
+
 typedef enum {
     TTT_APPLY_BEFORE_STEP = 0,  /* chunk outputs use the chunk's starting weights W_c */
     TTT_APPLY_AFTER_STEP = 1    /* chunk outputs use the weights after its step, W_{c+1} */

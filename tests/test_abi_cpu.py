@@ -279,3 +279,18 @@ def test_bwd_rejections(lib):
     assert bwd_call(lib, dk=addr(7), ws_bytes=need) == E                          # dK equals dQ
     assert bwd_call(lib, ws=addr(11), ws_bytes=need) == E                         # workspace over dW0
     assert bwd_call(lib, dwe=ctypes.c_void_p(A + 11 * (1 << 30) + 512), ws_bytes=need) == E   # dW0 over dW_end
+
+
+def test_noalloc_validates_on_the_host(lib):
+    """ttt_linear_fwd_noalloc refuses, before any HIP call, a problem whose
+    workspace exceeds the static scratch array, and bad arguments as
+    ttt_linear_fwd does."""
+    f = lib.ttt_linear_fwd_noalloc
+
+    def call(B=1, H=16, N=32768, d=128, b=2048, Z=6):
+        return f(0, 1, B, H, N, d, b, addr(0), addr(1), addr(2), None, 0.01, addr(3), None, None, 1e-6,
+                 addr(Z), addr(7), None)
+    assert lib.ttt_linear_fwd_workspace_bytes(0, 1, 1, 21, 32768, 128, 2048) > (64 << 20)
+    assert call(H=21) == binding.TTT_ERR_WORKSPACE_TOO_SMALL
+    assert call(Z=0) == binding.TTT_ERR_INVALID_ARGUMENT          # Z overlaps Q
+    assert call(d=96) == binding.TTT_ERR_UNSUPPORTED

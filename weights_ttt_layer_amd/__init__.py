@@ -9,6 +9,8 @@
 ``layer_fwd`` runs the whole layer: projections, key normalisation, the inner
 TTT-Linear model, output LayerNorm + residual and the output projection.
 ``linear_bwd`` is the backward of ``linear_fwd`` (small-b combinations).
+``linear_fwd_noalloc`` is ``linear_fwd`` for callers that cannot allocate: its
+large-chunk workspace is a static device array inside the library.
 Build the library first with ``python -m weights_ttt_layer_amd.build``.
 """
 from .binding import (  # noqa: F401
@@ -20,6 +22,7 @@ from .binding import (  # noqa: F401
     linear_decode,
     linear_fwd,
     linear_fwd_block,
+    linear_fwd_noalloc,
     linear_path,
     linear_workspace_bytes,
     load_library,
@@ -28,5 +31,5 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = ["TTTError", "layer_fwd", "layer_parts", "layer_workspace_bytes", "linear_bwd",
-           "linear_decode", "linear_fwd", "linear_fwd_block", "linear_path",
+           "linear_decode", "linear_fwd", "linear_fwd_block", "linear_fwd_noalloc", "linear_path",
            "linear_workspace_bytes", "load_library", "mlp_fwd", "status_string"]

@@ -45,6 +45,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_linear_fwd.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, fp, f, fp, fp, fp, f, fp, fp, vp,
                                    sz, vp]
     lib.ttt_linear_fwd.restype = i
+    lib.ttt_linear_fwd_noalloc.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, fp, f, fp, fp, fp, f, fp, fp, vp]
+    lib.ttt_linear_fwd_noalloc.restype = i
     lib.ttt_linear_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.ttt_linear_fwd_workspace_bytes.restype = sz
     lib.ttt_linear_fwd_path.argtypes = [i, i, i, i]
@@ -127,7 +129,7 @@ APPLY = {"before": 0, "after": 1}
 
 
 def _linear_call(entry: str, apply: Optional[int], q, k, v, w0, eta, b, kind, eta_const, ln_gamma,
-                 ln_beta, ln_eps, z, w_end, workspace, stream):
+                 ln_beta, ln_eps, z, w_end, workspace, stream, noalloc: bool = False):
     lib = load_library()
     if kind not in KINDS:
         raise ValueError(f"kind must be one of {sorted(KINDS)}")
@@ -152,6 +154,13 @@ def _linear_call(entry: str, apply: Optional[int], q, k, v, w0, eta, b, kind, et
     else:
         _check(w_end, "w_end", (B, H, d, d), torch.float32)
     args = (KINDS[kind], dt, B, H, N, d, int(b))
+    if noalloc:
+        st = lib.ttt_linear_fwd_noalloc(*args, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), float(eta_const), _ptr(w0),
+                                        _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps), _ptr(z), _ptr(w_end),
+                                        _stream_ptr(stream))
+        if st != TTT_OK:
+            raise TTTError(st, entry)
+        return z, w_end
     if apply is None:
         need = int(lib.ttt_linear_fwd_workspace_bytes(*args))
     else:
@@ -186,6 +195,19 @@ def linear_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w0: torch.Tens
     """
     return _linear_call("ttt_linear_fwd", None, q, k, v, w0, eta, b, kind, eta_const, ln_gamma,
                         ln_beta, ln_eps, z, w_end, workspace, stream)
+
+
+def linear_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w0: torch.Tensor,
+                       eta: Optional[torch.Tensor] = None, *, b: int, kind: str = "plain",
+                       eta_const: float = 0.0, ln_gamma: Optional[torch.Tensor] = None,
+                       ln_beta: Optional[torch.Tensor] = None, ln_eps: float = 1e-6,
+                       z: Optional[torch.Tensor] = None, w_end: Optional[torch.Tensor] = None,
+                       stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """``linear_fwd`` through ``ttt_linear_fwd_noalloc``: the large-chunk path
+    uses the library's static device scratch instead of a workspace (outputs the
+    caller does not pass are still allocated here by torch). Returns (Z, W_end)."""
+    return _linear_call("ttt_linear_fwd_noalloc", None, q, k, v, w0, eta, b, kind, eta_const, ln_gamma,
+                        ln_beta, ln_eps, z, w_end, None, stream, noalloc=True)
 
 
 def linear_fwd_block(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w0: torch.Tensor,

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/ttt.h"
 #include "kernels.h"
 
@@ -78,7 +80,7 @@ namespace {
 int check_linear(int kind, int qkv_dtype, int B, int H, int N, int d, int b, const void* Q, const void* K,
                  const void* V, const float* eta, float eta_const, const float* W0, const float* ln_gamma,
                  const float* ln_beta, float ln_eps, float* Z, float* W_end, void* workspace,
-                 size_t workspace_bytes, ttt::LinearArgs& a, int& path)
+                 size_t workspace_bytes, ttt::LinearArgs& a, int& path, bool internal_workspace = false)
 {
     if (kind != TTT_LINEAR_PLAIN && kind != TTT_LINEAR_LN) return TTT_ERR_INVALID_ARGUMENT;
     if (qkv_dtype != TTT_DTYPE_F32 && qkv_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARGUMENT;
@@ -109,8 +111,9 @@ int check_linear(int kind, int qkv_dtype, int B, int H, int N, int d, int b, con
 
     path = linear_path(kind, qkv_dtype, d, b);
     if (path == TTT_PATH_NONE) return TTT_ERR_UNSUPPORTED;
-    if (path == TTT_PATH_LARGE_CHUNK) {
-        if (N % LARGE_B_MULT != 0 || N >= LARGE_MAX_N) return TTT_ERR_UNSUPPORTED;
+    if (path == TTT_PATH_LARGE_CHUNK && N % LARGE_B_MULT != 0) return TTT_ERR_UNSUPPORTED;
+    if (path == TTT_PATH_LARGE_CHUNK && N >= LARGE_MAX_N) return TTT_ERR_UNSUPPORTED;
+    if (path == TTT_PATH_LARGE_CHUNK && !internal_workspace) {
         const size_t need = ttt::large_chunk_workspace_bytes(B, H, N, d, b);
         if (workspace_bytes < need || (need > 0 && !workspace)) return TTT_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned(workspace, 256)) return TTT_ERR_INVALID_ARGUMENT;
@@ -473,3 +476,68 @@ int ttt_linear_bwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b, c
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// ttt_linear_fwd_noalloc: ttt_linear_fwd with its workspace in a file-scope
+// device array instead of a caller buffer, for callers that cannot allocate.
+// ---------------------------------------------------------------------------
+namespace {
+
+// One copy per device, created when the code object is loaded on that device
+// and held until the process ends. In host code `scratch` names a host-side
+// stand-in: its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) char scratch[TTT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+hipError_t scratch_on_current_device(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" int ttt_linear_fwd_noalloc(int kind, int qkv_dtype, int B, int H, int N, int d, int b, const void* Q,
+                                      const void* K, const void* V, const float* eta, float eta_const,
+                                      const float* W0, const float* ln_gamma, const float* ln_beta, float ln_eps,
+                                      float* Z, float* W_end, void* hip_stream)
+{
+    // validation on the host first (the scratch array is never a caller buffer,
+    // so it overlaps none)
+    const size_t need = ttt_linear_fwd_workspace_bytes(kind, qkv_dtype, B, H, N, d, b);
+    if (need > TTT_NOALLOC_SCRATCH_BYTES) return TTT_ERR_WORKSPACE_TOO_SMALL;
+    ttt::LinearArgs a;
+    int path = TTT_PATH_NONE;
+    const int st = check_linear(kind, qkv_dtype, B, H, N, d, b, Q, K, V, eta, eta_const, W0, ln_gamma, ln_beta,
+                                ln_eps, Z, W_end, nullptr, 0, a, path, /*internal_workspace=*/true);
+    if (st != TTT_OK) return st;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    hipError_t err;
+    if (path == TTT_PATH_SMALL_B) {
+        err = ttt::launch_smallb_linear(a, stream);
+    } else {
+        void* ptr = nullptr;
+        err = scratch_on_current_device(&ptr);
+        if (err != hipSuccess) return TTT_ERR_HIP;
+        a.workspace = ptr;
+        a.workspace_bytes = TTT_NOALLOC_SCRATCH_BYTES;
+        err = ttt::launch_large_chunk_linear(a, ttt::LC_OUT_DUAL, stream);
+    }
+    return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
