@@ -104,7 +104,8 @@ typedef enum {
  * TTT_ERR_INVALID_ARGUMENT).
  *
  * Supported (else TTT_ERR_UNSUPPORTED):
- *   small-b path  : kind PLAIN or LN, dtype F32 or BF16, d = 64, 1 <= b <= 16
+ *   small-b path  : kind PLAIN or LN, dtype F32 or BF16, d = 64 or 128,
+ *                   1 <= b <= 64 (one workgroup per unit, the state on chip)
  *   large-chunk   : kind PLAIN, dtype BF16, d = 128, b >= 256, b % 128 == 0,
  *                   N % 128 == 0 and N < 2^22 (needs the workspace).
  * ttt_linear_fwd_path() reports which path a combination takes.

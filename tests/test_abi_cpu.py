@@ -42,7 +42,11 @@ def test_path_selection(lib):
     P = lib.ttt_linear_fwd_path
     assert P(0, 0, 64, 16) == binding.TTT_PATH_SMALL_B
     assert P(1, 1, 64, 1) == binding.TTT_PATH_SMALL_B
-    assert P(1, 1, 64, 17) == binding.TTT_PATH_NONE
+    assert P(1, 1, 64, 17) == binding.TTT_PATH_SMALL_B
+    assert P(0, 0, 64, 64) == binding.TTT_PATH_SMALL_B
+    assert P(1, 0, 128, 1) == binding.TTT_PATH_SMALL_B
+    assert P(1, 1, 128, 64) == binding.TTT_PATH_SMALL_B
+    assert P(1, 1, 64, 65) == binding.TTT_PATH_NONE
     assert P(0, 1, 128, 2048) == binding.TTT_PATH_LARGE_CHUNK
     assert P(1, 1, 128, 2048) == binding.TTT_PATH_NONE       # LN has no large-chunk path
     assert P(0, 1, 128, 2000) == binding.TTT_PATH_NONE       # not a multiple of 128
@@ -101,7 +105,8 @@ def test_rejects_invalid_arguments(lib):
 def test_rejects_unsupported(lib):
     U = binding.TTT_ERR_UNSUPPORTED
     assert lin_call(lib, d=32) == U
-    assert lin_call(lib, b=17) == U
+    assert lin_call(lib, b=65) == U
+    assert lin_call(lib, d=128, b=100) == U
     assert lin_call(lib, kind=1, d=128, b=2048) == U
     assert lin_call(lib, dt=0, d=128, b=2048) == U
 

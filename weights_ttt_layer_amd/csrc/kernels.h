@@ -44,8 +44,11 @@ struct MlpArgs {
     float* W2_end;
 };
 
-// Small-b path: one workgroup per (sequence, head); d = 64, 1 <= b <= 16.
+// Small-b path: one workgroup per (sequence, head); d = 64 or 128, 1 <= b <= 64.
 hipError_t launch_smallb_linear(const LinearArgs& a, hipStream_t stream);
+// The generic small-b kernel (midb_linear.hip): d = 64 with 17 <= b <= 64, d = 128
+// with 1 <= b <= 64, fp32 or bf16 streams.
+hipError_t launch_midb_linear(const LinearArgs& a, hipStream_t stream);
 // bf16 token streams: the chain-on-one-wave kernel (smallb_chain.hip)
 hipError_t launch_smallb_chain(const LinearArgs& a, hipStream_t stream);
 // The same kernel on two-term streams: Q, K, V each a bf16 hi plane [B,H,N,d]

@@ -406,6 +406,7 @@ hipError_t launch_typed(const LinearArgs& a, hipStream_t stream)
 
 hipError_t launch_smallb_linear(const LinearArgs& a, hipStream_t stream)
 {
+    if (a.d != D || a.b > ROWS) return launch_midb_linear(a, stream);
     if (a.dtype == 1) return launch_smallb_chain(a, stream);
     return a.kind == 1 ? launch_typed<1, float>(a, stream) : launch_typed<0, float>(a, stream);
 }

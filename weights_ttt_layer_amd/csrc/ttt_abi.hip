@@ -13,7 +13,9 @@
 namespace {
 
 constexpr int SMALLB_D = 64;
-constexpr int SMALLB_MAX_B = 16;
+constexpr int SMALLB_MAX_B = 16;       // the backward, decode and whole-layer paths
+constexpr int SMALLB_D2 = 128;         // the forward small-b path also takes d = 128
+constexpr int SMALLB_FWD_MAX_B = 64;   // ... and chunks of up to 64 tokens
 constexpr int LARGE_D = 128;
 constexpr int LARGE_MIN_B = 256;
 constexpr int LARGE_B_MULT = 128;
@@ -32,8 +34,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 int linear_path(int kind, int dtype, int d, int b)
 {
     if ((kind == TTT_LINEAR_PLAIN || kind == TTT_LINEAR_LN) &&
-        (dtype == TTT_DTYPE_F32 || dtype == TTT_DTYPE_BF16) && d == SMALLB_D && b >= 1 &&
-        b <= SMALLB_MAX_B)
+        (dtype == TTT_DTYPE_F32 || dtype == TTT_DTYPE_BF16) && (d == SMALLB_D || d == SMALLB_D2) && b >= 1 &&
+        b <= SMALLB_FWD_MAX_B)
         return TTT_PATH_SMALL_B;
     if (kind == TTT_LINEAR_PLAIN && dtype == TTT_DTYPE_BF16 && d == LARGE_D && b >= LARGE_MIN_B &&
         b % LARGE_B_MULT == 0)
