@@ -1,5 +1,5 @@
 // smallb_mlp.hip -- TTT-MLP forward, f(x) = x + LN(GELU(x W1) W2), d = 64,
-// hidden = 256, chunks of 1 <= b <= 16 tokens.
+// hidden = 256, chunks of 1 <= b <= 16 tokens, bf16 or fp32 token streams.
 //
 // Inner model: a small multi-layer perceptron (page "How to Master Test-Time
 // Training for Infinite Context LLMs", section "The Math and Architecture of
@@ -14,15 +14,39 @@
 //     H_Q = X2_Q W2 - tril(X2_Q X2^T) diag(eta) G2,   Z = Q + LN(H_Q)
 //     W1 <- W1 - K^T diag(eta) G1,   W2 <- W2 - X2^T diag(eta) G2
 //
-// Design (gfx950): one workgroup of four waves per (sequence, head). The state
-// stays in MFMA accumulators for the whole scan: wave w holds W1 columns
-// [64w, 64w+64), W2 columns [16w, 16w+16) and, for the backward product
-// G2 W2^T, a second copy W2^T with columns [64w, 64w+64) that receives the
-// same update (K W1 and X2 W2 contract over the state's rows and read the
-// accumulators directly; G2 W2^T contracts over W2's columns, which is the row
-// index of W2^T). Activations that a product needs in another orientation
-// (X2, X2_Q, G2) go through row-padded fp32 LDS tiles. fp32 operands are split
-// into bf16 terms as in the linear kernel.
+// Design (gfx950): one workgroup of four waves per (sequence, head); wave w
+// owns the hidden slice h in [64w, 64w + 64) of both layers and keeps, for the
+// whole scan, in fp32 MFMA accumulator tiles:
+//     W1[:, slice]    rows = input features, columns = hidden
+//     W2[slice, :]    rows = hidden, columns = output features
+//     W2[slice, :]^T  rows = output features, columns = hidden (for G2 W2^T)
+// Every product is taken in the orientation in which its operands are ready:
+//  * A^T = W1^T K^T and A_Q^T (the W1 tiles as A operand) leave one token per
+//    lane; GELU, GELU' and the eta scaling act there in registers.
+//  * H^T = W2^T X2^T takes the W2 tiles as A operand and X2^T straight from the
+//    registers as B operand (the C layout of a transposed product is the B
+//    operand of the next one, up to a fixed permutation of k); its four
+//    slice-partials meet in LDS. Every wave then holds all of H^T and runs the
+//    LayerNorm forward and backward itself (no further exchange).
+//  * G1^T = (W2 G2^T) * GELU'(A)^T and the output-side H_Q^T, S2^T = X2 X2_Q^T
+//    likewise; S2^T's slice-partials meet in LDS with H_Q^T's.
+//  * Products over tokens (the causal terms and the state updates) need the
+//    token index along k: -Gt1, -Gt2 and X2 are written as bf16 terms to
+//    wave-private [token][feature] LDS tiles and read back with the transpose
+//    read ds_read_b64_tr_b16.
+// Two workgroup barriers per chunk (the H and the H_Q/S2 partial sums); the
+// next chunk is staged into the other LDS buffer between them.
+//
+// W2 is carried with each row's mean over the output features removed (a row
+// of W2 belongs to one wave, so the means are wave-local): LayerNorm ignores a
+// constant added to a whole row of H, and G2 sums to zero over the features, so
+// neither G2 W2^T nor the update sees the means and they never change. Rows of
+// H then have a near-zero mean whatever W2_0 holds, so the one-pass variance
+// keeps its precision. W2_end = W2_0 + (accumulated change), bit for bit W2_0
+// when nothing moved.
+//
+// Precision: fp32 operands (state, activations, gradients, scores) as two bf16
+// terms next to bf16 streams, three next to fp32 streams; fp32 accumulation.
 #include "kernels.h"
 #include "smallb_common.h"
 
@@ -32,30 +56,6 @@ namespace {
 using namespace smallb;
 
 constexpr int HID = 256;
-constexpr int XS = HID + 4;     // row stride of [token][hidden] fp32 tiles
-constexpr int GS = D + 4;       // row stride of [token][d] fp32 tiles
-constexpr int XTS = ROWS + 4;   // row stride of the [hidden][token] fp32 tile
-constexpr int XB = HID + 8;     // row stride of [token][hidden] bf16 term tiles
-
-// terms of an fp32 operand next to token streams of type S
-template <typename S>
-constexpr int fp_terms() { return Stor<S>::TERMS == 1 ? 2 : 3; }
-
-// GELU(A) and GELU(A_Q) are written once, already split into their bf16
-// operand terms, by the wave that owns the hidden slice; the products over the
-// hidden dimension then read ready terms instead of every wave splitting every
-// row again.
-template <typename S>
-struct alignas(16) MlpSmem {
-    Stage<S> st[2];
-    uint16_t x2b[fp_terms<S>()][ROWS * XB];    // GELU(K W1) terms, [token][hidden]
-    float x2t[HID * XTS];                      // GELU(K W1), [hidden][token]
-    uint16_t x2qb[fp_terms<S>()][ROWS * XB];   // GELU(A_Q) terms, [token][hidden]
-    float d1[ROWS * XS];                       // GELU'(A), [token][hidden]
-    float g2[ROWS * GS];     // dl/dH at the chunk-start weights (no eta), [token][d]
-    float red[3][4][ROWS][2];
-    float w2mean[HID];       // row means of W2_0 (removed from the carried state)
-};
 
 // GELU(a) = a Phi(a), Phi(a) = (1 + erf(a / sqrt 2)) / 2, and its derivative
 // Phi(a) + a phi(a). erf comes from Abramowitz & Stegun, "Handbook of
@@ -94,277 +94,59 @@ __device__ __forceinline__ void gelu_fd(float a, float& f, float& fd)
     fd = fmaf(a * 0.39894228040143267794f, gauss, c);
 }
 
-// Operand fragment of a pre-split [token][hidden] tile: per term, four entries
-// at row + o and four at row + o + 16 (the k order of load_a8).
+// [16 token][64 column] bf16 tiles with 128-byte rows; the 16-byte piece p of
+// row r sits at slot p ^ (r & 7), which keeps both the 8-byte row writes and
+// the transpose reads of four rows free of bank conflicts.
+__device__ __forceinline__ int toff(int r, int col)
+{
+    return r * 128 + (((col >> 3) ^ (r & 7)) << 4) + (col & 7) * 2;
+}
+
+// Transpose read: lane (g, n) receives column col0 + n of rows 4g .. 4g + 3
+// (called with row = 4g + n/4, col = col0 + 4(n%4)).
+__device__ __forceinline__ bf16x4 tr4(const uint16_t* tile, int row, int col)
+{
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_bf16x4*)(reinterpret_cast<const char*>(tile) + toff(row, col)));
+}
+
+// Four values of one token (columns col .. col + 3) as T bf16 terms, also
+// written to the term tiles at row `r`.
 template <int T>
-__device__ __forceinline__ void load_terms8(const uint16_t (*tile)[ROWS * XB], int off, bf16x8 (&out)[T])
+__device__ __forceinline__ void put4(uint16_t (*tile)[16 * 64], int r, int col, const float (&x)[4], bf16x4 (&t)[T])
 {
+    terms4<T>(x, t);
 #pragma unroll
-    for (int s = 0; s < T; ++s) {
-        const uint2 a = *reinterpret_cast<const uint2*>(tile[s] + off);
-        const uint2 b = *reinterpret_cast<const uint2*>(tile[s] + off + 16);
-        out[s] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
-    }
+    for (int s = 0; s < T; ++s)
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(tile[s]) + toff(r, col)) = t[s];
 }
 
-// Split v into T bf16 terms and store them at tile[s][off].
-template <int T>
-__device__ __forceinline__ void store_terms(uint16_t (*tile)[ROWS * XB], int off, float v)
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b)
 {
-    __bf16 t[T];
-    split_terms<T>(v, t);
-#pragma unroll
-    for (int s = 0; s < T; ++s) tile[s][off] = __builtin_bit_cast(uint16_t, t[s]);
+    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    return __builtin_bit_cast(bf16x8, make_uint4(ua.x, ua.y, ub.x, ub.y));
 }
 
-template <typename S>
-__device__ __forceinline__ void mlp_chunk(const Stage<S>& st, MlpSmem<S>& sm, f32x4 (&W1acc)[4][4],
-                                          f32x4 (&W2acc)[16], f32x4 (&W2Tacc)[4][4], int c0, int bc,
-                                          float gam, float bet, float eps, float* __restrict__ Zu,
-                                          int w, int g, int n)
+__device__ __forceinline__ void wave_lds_sync()
 {
-    constexpr int TIN = Stor<S>::TERMS;
-    constexpr int TS = (TIN == 1) ? 2 : 3;
-    constexpr int STRIDE = Stor<S>::STRIDE;
-    const int col = 16 * w + n;
-
-    // ---- (1) A = K W1 and Q W1 for this wave's four hidden tiles ----
-    f32x4 ak[4], aq[4];
-    {
-        bf16x8 ka[2][TIN], qa[2][TIN];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int o0 = n * STRIDE + 32 * p + 4 * g;
-            load_a8<S, TIN>(st.k + o0, st.k + o0 + 16, ka[p]);
-            load_a8<S, TIN>(st.q + o0, st.q + o0 + 16, qa[p]);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            ak[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            aq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                bf16x8 wb[TS];
-                b8_from_acc<TS>(W1acc[2 * p][t], W1acc[2 * p + 1][t], wb);
-                ak[t] = mma32_terms<TIN, TS>(ak[t], ka[p], wb);
-                aq[t] = mma32_terms<TIN, TS>(aq[t], qa[p], wb);
-            }
-        }
-    }
-    // ---- (2) S^T = K Q^T: lane (g, n) holds S[n][4g+i] = q_n . k_{4g+i} ----
-    f32x4 sT = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        bf16x8 ka[TIN], qb[TIN];
-        const int o = n * STRIDE + 32 * p + 8 * g;
-        load_a8<S, TIN>(st.k + o, st.k + o + 4, ka);
-        load_a8<S, TIN>(st.q + o, st.q + o + 4, qb);
-        sT = mma32_terms<TIN, TIN>(sT, ka, qb);
-    }
-    float et[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) et[i] = st.eta[4 * g + i];
-
-    // ---- (3) X2 = GELU(A), GELU'(A); publish X2 in both orientations ----
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float x2, d1;
-            gelu_fd(ak[t][i], x2, d1);
-            const int hcol = 64 * w + 16 * t + n;
-            store_terms<TS>(sm.x2b, (4 * g + i) * XB + hcol, x2);
-            sm.x2t[hcol * XTS + 4 * g + i] = x2;
-            sm.d1[(4 * g + i) * XS + hcol] = d1;
-        }
-    __syncthreads();
-
-    // ---- (4) H = X2 W2 for columns [16w, 16w+16) ----
-    f32x4 hk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        bf16x8 xa[TS], wb[TS];
-        load_terms8<TS>(sm.x2b, n * XB + 32 * p + 4 * g, xa);
-        b8_from_acc<TS>(W2acc[2 * p], W2acc[2 * p + 1], wb);
-        hk = mma32_terms<TS, TS>(hk, xa, wb);
-    }
-
-    // ---- (5) LayerNorm forward and backward: G2 = dl/dH ----
-    float g2[4];
-    {
-        float s1[4], s2[4], mu[4], rs[4], xh[4], dxh[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s1[i] = hk[i];
-            s2[i] = hk[i] * hk[i];
-        }
-        xwave_row_sums(s1, s2, sm.red[0], w, g, n);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            mu[i] = s1[i] * (1.f / D);
-            const float var = fmaxf(s2[i] * (1.f / D) - mu[i] * mu[i], 0.f);
-            rs[i] = 1.f / sqrtf(var + eps);
-            xh[i] = (hk[i] - mu[i]) * rs[i];
-            const float kk = Stor<S>::f(st.k[(4 * g + i) * STRIDE + col]);
-            const float vv = Stor<S>::f(st.v[(4 * g + i) * STRIDE + col]);
-            dxh[i] = 2.f * (kk + gam * xh[i] + bet - vv) * gam;
-            s1[i] = dxh[i];
-            s2[i] = dxh[i] * xh[i];
-        }
-        xwave_row_sums(s1, s2, sm.red[1], w, g, n);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            g2[i] = rs[i] * (dxh[i] - s1[i] * (1.f / D) - xh[i] * (s2[i] * (1.f / D)));
-            if (4 * g + i >= bc) g2[i] = 0.f;
-            sm.g2[(4 * g + i) * GS + col] = g2[i];
-        }
-    }
-    __syncthreads();
-
-    // ---- (6) G1 = (G2 W2^T) * GELU'(A) for this wave's hidden tiles ----
-    bf16x8 g2a[2][TS];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const float* r0 = sm.g2 + n * GS + 32 * p + 4 * g;
-        load_a8<float, TS>(r0, r0 + 16, g2a[p]);
-    }
-    bf16x4 gb1[4][TS];   // -diag(eta) G1, B operand (k = token)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            bf16x8 wb[TS];
-            b8_from_acc<TS>(W2Tacc[2 * p][t], W2Tacc[2 * p + 1][t], wb);
-            acc = mma32_terms<TS, TS>(acc, g2a[p], wb);
-        }
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            x[i] = (4 * g + i < bc) ? -et[i] * acc[i] * sm.d1[(4 * g + i) * XS + 64 * w + 16 * t + n] : 0.f;
-        terms4<TS>(x, gb1[t]);
-    }
-
-    // ---- (7) A_Q = Q W1 - tril(S) diag(eta) G1; X2_Q = GELU(A_Q) ----
-    bf16x4 sa[TS];
-    {
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (4 * g + i <= n) ? sT[i] : 0.f;
-        terms4<TS>(x, sa);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        aq[t] = mma16_terms<TS, TS>(aq[t], sa, gb1[t]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            store_terms<TS>(sm.x2qb, (4 * g + i) * XB + 64 * w + 16 * t + n, gelu_f(aq[t][i]));
-    }
-    // W1 -= K^T diag(eta) G1 now (A_Q used W1_c above), so the G1 terms die here.
-    // A = K^T tile r: row = feature 16r+n, k = token.
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        float x[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = Stor<S>::f(st.k[(4 * g + j) * STRIDE + 16 * r + n]);
-        bf16x4 kt[TIN];
-        terms4<TIN>(x, kt);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) W1acc[r][t] = mma16_terms<TIN, TS>(W1acc[r][t], kt, gb1[t]);
-    }
-    __syncthreads();
-
-    // ---- (8) S2^T = X2 X2_Q^T: lane (g, n) holds S2[n][4g+i] ----
-    f32x4 s2T = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        bf16x8 xa[TS], xq[TS];
-        load_terms8<TS>(sm.x2b, n * XB + 32 * p + 4 * g, xa);
-        load_terms8<TS>(sm.x2qb, n * XB + 32 * p + 4 * g, xq);
-        s2T = mma32_terms<TS, TS>(s2T, xa, xq);
-    }
-    // -diag(eta) G2 as B operand
-    bf16x4 gb2[TS];
-    {
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = -et[i] * g2[i];
-        terms4<TS>(x, gb2);
-    }
-
-    // ---- (9) H_Q = X2_Q W2 - tril(S2) diag(eta) G2 ----
-    f32x4 hq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        bf16x8 xq[TS], wb[TS];
-        load_terms8<TS>(sm.x2qb, n * XB + 32 * p + 4 * g, xq);
-        b8_from_acc<TS>(W2acc[2 * p], W2acc[2 * p + 1], wb);
-        hq = mma32_terms<TS, TS>(hq, xq, wb);
-    }
-    {
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (4 * g + i <= n) ? s2T[i] : 0.f;
-        bf16x4 s2a[TS];
-        terms4<TS>(x, s2a);
-        hq = mma16_terms<TS, TS>(hq, s2a, gb2);
-    }
-
-    // ---- (10) Z = Q + LN(H_Q) ----
-    {
-        float s1[4], s2[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s1[i] = hq[i];
-            s2[i] = hq[i] * hq[i];
-        }
-        xwave_row_sums(s1, s2, sm.red[2], w, g, n);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float mu = s1[i] * (1.f / D);
-            const float var = fmaxf(s2[i] * (1.f / D) - mu * mu, 0.f);
-            const float rs = 1.f / sqrtf(var + eps);
-            const float qq = Stor<S>::f(st.q[(4 * g + i) * STRIDE + col]);
-            const float z = qq + gam * ((hq[i] - mu) * rs) + bet;
-            if (4 * g + i < bc) Zu[(size_t)(c0 + 4 * g + i) * D + col] = z;
-        }
-    }
-
-    // ---- (11) state updates ----
-    // W2 -= X2^T diag(eta) G2   (A = X2^T tile r: row = hidden 16r+n, k = token)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const float4 v = *reinterpret_cast<const float4*>(sm.x2t + (16 * r + n) * XTS + 4 * g);
-        float x[4] = {v.x, v.y, v.z, v.w};
-        bf16x4 xa[TS];
-        terms4<TS>(x, xa);
-        W2acc[r] = mma16_terms<TS, TS>(W2acc[r], xa, gb2);
-    }
-    // W2^T -= diag(eta)-scaled G2^T X2   (A = G2^T tile r: row = feature 16r+n, k = token)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        float x[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = et[j] * sm.g2[(4 * g + j) * GS + 16 * r + n];
-        bf16x4 ga[TS];
-        terms4<TS>(x, ga);
-        (void)x;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            // terms of -X2 (the split of a negated value is the negated split)
-            bf16x4 xb[TS];
-#pragma unroll
-            for (int sT = 0; sT < TS; ++sT) {
-                uint32_t u[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    u[i] = (uint32_t)sm.x2b[sT][(4 * g + i) * XB + 64 * w + 16 * t + n] ^ 0x8000u;
-                xb[sT] = __builtin_bit_cast(bf16x4, make_uint2(u[0] | (u[1] << 16), u[2] | (u[3] << 16)));
-            }
-            W2Tacc[r][t] = mma16_terms<TS, TS>(W2Tacc[r][t], ga, xb);
-        }
-    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+template <typename S, int TS>
+struct alignas(16) MlpSmem {
+    Stage<S> st[2];
+    float4 hp[4][4][64];            // H^T slice-partials [wave][output tile][lane]
+    float4 hqp[4][4][64];           // H_Q^T slice-partials
+    float4 s2p[4][64];              // S2^T slice-partials
+    uint16_t x2t[4][TS][16 * 64];   // per wave: X2 terms, [token][hidden of the slice]
+    uint16_t g1t[4][TS][16 * 64];   // per wave: -Gt1 terms, [token][hidden of the slice]
+    uint16_t g2t[4][TS][16 * 64];   // per wave: -Gt2 terms, [token][output feature]
+    float w2m[4][64];               // row means of W2_0 over the output features
+    float4 gb[2][4][4];             // LayerNorm gamma, beta: [which][output tile][g]
+};
 
 template <typename S>
 __global__ void __launch_bounds__(THREADS)
@@ -374,8 +156,11 @@ smallb_mlp_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
                   const float* __restrict__ gamma, const float* __restrict__ beta, float eps,
                   float* __restrict__ Zg, float* __restrict__ W1e, float* __restrict__ W2e)
 {
+    constexpr int TIN = Stor<S>::TERMS;
+    constexpr int TS = (TIN == 1) ? 2 : 3;
+    constexpr int STRIDE = Stor<S>::STRIDE;
     constexpr int PPT = (Pieces<S>::TOTAL + THREADS - 1) / THREADS;
-    __shared__ MlpSmem<S> sm;
+    __shared__ MlpSmem<S, TS> sm;
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -392,63 +177,356 @@ smallb_mlp_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
     float* Zu = Zg + unit * (size_t)N * D;
     const float* W1u = W1g + unit * (size_t)D * HID;
     const float* W2u = W2g + unit * (size_t)HID * D;
+    const int hs = 64 * w;   // first hidden index of this wave's slice
 
-    f32x4 W1acc[4][4], W2acc[16], W2Tacc[4][4];
+    // ---- resident state ----
+    f32x4 W1[4][4];    // W1[r][t][i]  = W1[16r + 4g + i][hs + 16t + n]
+    f32x4 W2[4][4];    // W2[a][o][i]  = W2[hs + 16a + 4g + i][16o + n]
+    f32x4 W2T[4][4];   // W2T[r][t][i] = W2[hs + 16t + n][16r + 4g + i]
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                W1acc[r][t][i] = W1u[(16 * r + 4 * g + i) * HID + 64 * w + 16 * t + n];
-                W2Tacc[r][t][i] = W2u[(64 * w + 16 * t + n) * D + 16 * r + 4 * g + i];
+                W1[r][t][i] = W1u[(16 * r + 4 * g + i) * HID + hs + 16 * t + n];
+                W2[r][t][i] = W2u[(hs + 16 * r + 4 * g + i) * D + 16 * t + n];
+                W2T[r][t][i] = W2u[(hs + 16 * t + n) * D + 16 * r + 4 * g + i];
             }
+    // W2's row means (hidden rows of this wave's slice), removed from both copies
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) W2acc[r][i] = W2u[(16 * r + 4 * g + i) * D + 16 * w + n];
-    const float gam = gamma[h * D + 16 * w + n];
-    const float bet = beta[h * D + 16 * w + n];
-
-    // W2 is carried with each row's mean over the output features removed.
-    // LayerNorm ignores a constant added to a whole row of H = X2 W2, and its
-    // gradient G2 sums to zero over the features, so neither the update
-    // X2^T Gt2 nor the product G2 W2^T sees the means, and they never change;
-    // they are added back to W2_end. Rows of H then have a near-zero mean
-    // whatever W2_0 holds, so the one-pass variance keeps its precision.
-    // Wave w holds hidden rows 64w + 16t + n of W2^T in full (columns 16r + 4g + i).
+        for (int i = 0; i < 4; ++i) {
+            const float s = row16_sum((W2[a][0][i] + W2[a][1][i]) + (W2[a][2][i] + W2[a][3][i]));
+            if (n == 0) sm.w2m[w][16 * a + 4 * g + i] = s * (1.f / D);
+        }
+    wave_lds_sync();
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float m = sm.w2m[w][16 * a + 4 * g + i];
+#pragma unroll
+            for (int o = 0; o < 4; ++o) W2[a][o][i] -= m;
+        }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        float s = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s += (W2Tacc[r][t][0] + W2Tacc[r][t][1]) + (W2Tacc[r][t][2] + W2Tacc[r][t][3]);
-        s = xrow4_sum(s) * (1.f / D);
-        if (g == 0) sm.w2mean[64 * w + 16 * t + n] = s;
+        const float m = sm.w2m[w][16 * t + n];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) W2Tacc[r][t][i] -= s;
+            for (int i = 0; i < 4; ++i) W2T[r][t][i] -= m;
     }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) W2acc[r][i] -= sm.w2mean[16 * r + 4 * g + i];
+
+    // LayerNorm parameters, read from LDS where used: gb[0][o][g] holds gamma of
+    // output features 16o + 4g .. 16o + 4g + 3, gb[1] beta
+    if (tid < 32) {
+        const int which = tid >> 4, o = (tid >> 2) & 3, gg = tid & 3;
+        const float* src = (which ? beta : gamma) + h * D + 16 * o + 4 * gg;
+        sm.gb[which][o][gg] = make_float4(src[0], src[1], src[2], src[3]);
+    }
 
     const int nchunks = (N + b - 1) / b;
-    // one chunk in flight: loaded during the previous chunk's (long) body
     uint4 pf[PPT];
     float pe = 0.f;
     load_chunk<S, PPT>(pf, pe, 0, b, N, tid, Qu, Ku, Vu, etau, eta_const);
+    store_chunk<S, PPT>(sm.st[0], pf, pe, tid, min(b, N));
+    if (nchunks > 1) load_chunk<S, PPT>(pf, pe, 1, b, N, tid, Qu, Ku, Vu, etau, eta_const);
+    __syncthreads();
+
     for (int c = 0; c < nchunks; ++c) {
-        const int c0 = c * b;
-        const int bc = min(b, N - c0);
-        store_chunk<S, PPT>(sm.st[c & 1], pf, pe, tid, bc);
-        if (c + 1 < nchunks) load_chunk<S, PPT>(pf, pe, c + 1, b, N, tid, Qu, Ku, Vu, etau, eta_const);
+        const Stage<S>& st = sm.st[c & 1];
+        const int bc = min(b, N - c * b);
+
+        // ================= phase 1: first layer, H^T partial =================
+        // K and Q rows of token n as operands over the input features (permuted k)
+        bf16x8 ka[2][TIN], qa[2][TIN];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int o0 = n * STRIDE + 32 * p + 4 * g;
+            load_a8<S, TIN>(st.k + o0, st.k + o0 + 16, ka[p]);
+            load_a8<S, TIN>(st.q + o0, st.q + o0 + 16, qa[p]);
+        }
+        // A^T, A_Q0^T: lane (g, n) = token n, hidden hs + 16t + 4g + i
+        f32x4 aT[4], aqT[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            aT[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            aqT[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                bf16x8 wb[TS];
+                b8_from_acc<TS>(W1[2 * p][t], W1[2 * p + 1][t], wb);
+                aT[t] = mma32_terms<TS, TIN>(aT[t], wb, ka[p]);
+                aqT[t] = mma32_terms<TS, TIN>(aqT[t], wb, qa[p]);
+            }
+        }
+        // X2 = GELU(A) and GELU'(A); X2 terms to the LDS tile (for the W2 updates)
+        // and, in registers, as the k = hidden operand of H^T and S2^T
+        float d1[4][4];
+        bf16x4 x2q4[4][TS];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gelu_fd(aT[t][i], x[i], d1[t][i]);
+            put4<TS>(sm.x2t[w], n, 16 * t + 4 * g, x, x2q4[t]);
+        }
+        bf16x8 x2b[2][TS];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int s = 0; s < TS; ++s) x2b[p][s] = cat8(x2q4[2 * p][s], x2q4[2 * p + 1][s]);
+        // H^T slice-partial (the W2 tiles as A operand: row = output feature, k =
+        // hidden): lane = token n, output features 16o + 4g + i
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                bf16x8 wb[TS];
+                b8_from_acc<TS>(W2[2 * p][o], W2[2 * p + 1][o], wb);
+                acc = mma32_terms<TS, TS>(acc, wb, x2b[p]);
+            }
+            sm.hp[w][o][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
         __syncthreads();
-        mlp_chunk<S>(sm.st[c & 1], sm, W1acc, W2acc, W2Tacc, c0, bc, gam, bet, eps, Zu, w, g, n);
+
+        // ================= phase 2: LayerNorm gradient, G1, the query side =================
+        // the next chunk into the other buffer (its last reader finished before the barrier)
+        if (c + 1 < nchunks) {
+            store_chunk<S, PPT>(sm.st[(c + 1) & 1], pf, pe, tid, min(b, N - (c + 1) * b));
+            if (c + 2 < nchunks) load_chunk<S, PPT>(pf, pe, c + 2, b, N, tid, Qu, Ku, Vu, etau, eta_const);
+        }
+        const float eta_n = st.eta[n];
+        // H^T (all output features) and the LayerNorm forward / backward of token n
+        float g2[4][4];
+        {
+            float hv[4][4];
+#pragma unroll
+            for (int o = 0; o < 4; ++o) {
+                float4 s = sm.hp[0][o][lane];
+#pragma unroll
+                for (int ww = 1; ww < 4; ++ww) {
+                    const float4 u = sm.hp[ww][o][lane];
+                    s = make_float4(s.x + u.x, s.y + u.y, s.z + u.z, s.w + u.w);
+                }
+                hv[o][0] = s.x;
+                hv[o][1] = s.y;
+                hv[o][2] = s.z;
+                hv[o][3] = s.w;
+            }
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int o = 0; o < 4; ++o)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s1 += hv[o][i];
+                    s2 = fmaf(hv[o][i], hv[o][i], s2);
+                }
+            xrow4_sum2(s1, s2);
+            const float mu = s1 * (1.f / D);
+            const float rs = __builtin_amdgcn_rsqf(fmaxf(s2 * (1.f / D) - mu * mu, 0.f) + eps);
+            float xh[4][4], dx[4][4], u1 = 0.f, u2 = 0.f;
+#pragma unroll
+            for (int o = 0; o < 4; ++o) {
+                const float4 kk = load4_f32<S>(st.k + n * STRIDE + 16 * o + 4 * g);
+                const float4 vv = load4_f32<S>(st.v + n * STRIDE + 16 * o + 4 * g);
+                const float4 ga = sm.gb[0][o][g], be = sm.gb[1][o][g];
+                const float kv[4] = {kk.x - vv.x, kk.y - vv.y, kk.z - vv.z, kk.w - vv.w};
+                const float gam[4] = {ga.x, ga.y, ga.z, ga.w}, bet[4] = {be.x, be.y, be.z, be.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xh[o][i] = (hv[o][i] - mu) * rs;
+                    dx[o][i] = 2.f * gam[i] * (kv[i] + gam[i] * xh[o][i] + bet[i]);
+                    u1 += dx[o][i];
+                    u2 = fmaf(dx[o][i], xh[o][i], u2);
+                }
+            }
+            xrow4_sum2(u1, u2);
+            const float m1 = u1 * (1.f / D), m2 = u2 * (1.f / D);
+#pragma unroll
+            for (int o = 0; o < 4; ++o)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) g2[o][i] = (n < bc) ? rs * (dx[o][i] - m1 - xh[o][i] * m2) : 0.f;
+        }
+        // G2^T as the k = output-feature operand; -Gt2 terms to this wave's tile
+        bf16x8 g2b[2][TS];
+        {
+            bf16x4 q4[4][TS];
+#pragma unroll
+            for (int o = 0; o < 4; ++o) {
+                const float x[4] = {g2[o][0], g2[o][1], g2[o][2], g2[o][3]};
+                terms4<TS>(x, q4[o]);
+                const float y[4] = {-eta_n * g2[o][0], -eta_n * g2[o][1], -eta_n * g2[o][2], -eta_n * g2[o][3]};
+                bf16x4 tmp[TS];
+                put4<TS>(sm.g2t[w], n, 16 * o + 4 * g, y, tmp);
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int s = 0; s < TS; ++s) g2b[p][s] = cat8(q4[2 * p][s], q4[2 * p + 1][s]);
+        }
+        // -Gt1^T = -eta (W2 G2^T) * GELU'(A)^T; its terms to this wave's tile
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                bf16x8 wt[TS];
+                b8_from_acc<TS>(W2T[2 * p][t], W2T[2 * p + 1][t], wt);
+                acc = mma32_terms<TS, TS>(acc, wt, g2b[p]);
+            }
+            const float x[4] = {-eta_n * acc[0] * d1[t][0], -eta_n * acc[1] * d1[t][1], -eta_n * acc[2] * d1[t][2],
+                                -eta_n * acc[3] * d1[t][3]};
+            bf16x4 tmp[TS];
+            put4<TS>(sm.g1t[w], n, 16 * t + 4 * g, x, tmp);
+        }
+        wave_lds_sync();
+        // -Gt1[token 4g + j][hidden hs + 16t + n]: A operand of the causal term, B of the W1 update
+        bf16x4 g1n[4][TS];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int s = 0; s < TS; ++s) g1n[t][s] = tr4(sm.g1t[w][s], 4 * g + (n >> 2), 16 * t + 4 * (n & 3));
+        // tril(S)^T, S^T = K Q^T: lane (g, n) holds S[query n][key 4g + i]
+        bf16x4 sb[TS];
+        {
+            f32x4 sT = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                bf16x8 kn[TIN], qn[TIN];
+                const int o = n * STRIDE + 32 * p + 8 * g;
+                load_a8<S, TIN>(st.k + o, st.k + o + 4, kn);
+                load_a8<S, TIN>(st.q + o, st.q + o + 4, qn);
+                sT = mma32_terms<TIN, TIN>(sT, kn, qn);
+            }
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = (4 * g + i <= n) ? sT[i] : 0.f;
+            terms4<TS>(x, sb);
+        }
+        // A_Q^T = A_Q0^T - Gt1^T tril(S)^T; X2_Q = GELU(A_Q), as the k = hidden operand
+        bf16x8 x2qb[2][TS];
+        {
+            bf16x4 q4[4][TS];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                aqT[t] = mma16_terms<TS, TS>(aqT[t], g1n[t], sb);
+                float x[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = gelu_f(aqT[t][i]);
+                terms4<TS>(x, q4[t]);
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int s = 0; s < TS; ++s) x2qb[p][s] = cat8(q4[2 * p][s], q4[2 * p + 1][s]);
+        }
+        // H_Q^T and S2^T = X2 X2_Q^T slice-partials
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                bf16x8 wb[TS];
+                b8_from_acc<TS>(W2[2 * p][o], W2[2 * p + 1][o], wb);
+                acc = mma32_terms<TS, TS>(acc, wb, x2qb[p]);
+            }
+            sm.hqp[w][o][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+        {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 2; ++p) acc = mma32_terms<TS, TS>(acc, x2b[p], x2qb[p]);
+            sm.s2p[w][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+        // W1 += K^T (-Gt1) for this wave's columns
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            bf16x4 kt[TIN];
+            load_kT_tile<S, TIN>(st.k, r, g, n, kt);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) W1[r][t] = mma16_terms<TIN, TS>(W1[r][t], kt, g1n[t]);
+        }
+        __syncthreads();
+
+        // ================= phase 3: H_Q, Z, the W2 updates =================
+        bf16x4 g2n[4][TS];   // -Gt2[token 4g + j][output feature 16o + n]
+#pragma unroll
+        for (int o = 0; o < 4; ++o)
+#pragma unroll
+            for (int s = 0; s < TS; ++s) g2n[o][s] = tr4(sm.g2t[w][s], 4 * g + (n >> 2), 16 * o + 4 * (n & 3));
+        bf16x4 s2b[TS];
+        {
+            float4 s = sm.s2p[0][lane];
+#pragma unroll
+            for (int ww = 1; ww < 4; ++ww) {
+                const float4 u = sm.s2p[ww][lane];
+                s = make_float4(s.x + u.x, s.y + u.y, s.z + u.z, s.w + u.w);
+            }
+            const float sv[4] = {s.x, s.y, s.z, s.w};
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = (4 * g + i <= n) ? sv[i] : 0.f;
+            terms4<TS>(x, s2b);
+        }
+        {
+            f32x4 hq[4];
+#pragma unroll
+            for (int o = 0; o < 4; ++o) {
+                float4 s = sm.hqp[0][o][lane];
+#pragma unroll
+                for (int ww = 1; ww < 4; ++ww) {
+                    const float4 u = sm.hqp[ww][o][lane];
+                    s = make_float4(s.x + u.x, s.y + u.y, s.z + u.z, s.w + u.w);
+                }
+                hq[o] = f32x4{s.x, s.y, s.z, s.w};
+                hq[o] = mma16_terms<TS, TS>(hq[o], g2n[o], s2b);   // - Gt2^T tril(S2)^T
+            }
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int o = 0; o < 4; ++o)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s1 += hq[o][i];
+                    s2 = fmaf(hq[o][i], hq[o][i], s2);
+                }
+            xrow4_sum2(s1, s2);
+            const float mu = s1 * (1.f / D);
+            const float rs = __builtin_amdgcn_rsqf(fmaxf(s2 * (1.f / D) - mu * mu, 0.f) + eps);
+            // wave w writes output features 16w .. 16w + 15
+#pragma unroll
+            for (int o = 0; o < 4; ++o)
+                if (o == w && n < bc) {
+                    const float4 qq = load4_f32<S>(st.q + n * STRIDE + 16 * o + 4 * g);
+                    const float4 ga = sm.gb[0][o][g], be = sm.gb[1][o][g];
+                    const float qv[4] = {qq.x, qq.y, qq.z, qq.w};
+                    const float gam[4] = {ga.x, ga.y, ga.z, ga.w}, bet[4] = {be.x, be.y, be.z, be.w};
+                    float z[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) z[i] = qv[i] + gam[i] * ((hq[o][i] - mu) * rs) + bet[i];
+                    *reinterpret_cast<float4*>(Zu + (size_t)(c * b + n) * D + 16 * o + 4 * g) =
+                        make_float4(z[0], z[1], z[2], z[3]);
+                }
+        }
+        // W2 += X2^T (-Gt2),  W2^T += (-Gt2)^T X2  (X2[token 4g + j][hidden hs + 16a + n])
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            bf16x4 x2n[TS];
+#pragma unroll
+            for (int s = 0; s < TS; ++s) x2n[s] = tr4(sm.x2t[w][s], 4 * g + (n >> 2), 16 * a + 4 * (n & 3));
+#pragma unroll
+            for (int o = 0; o < 4; ++o) {
+                W2[a][o] = mma16_terms<TS, TS>(W2[a][o], x2n, g2n[o]);
+                W2T[o][a] = mma16_terms<TS, TS>(W2T[o][a], g2n[o], x2n);
+            }
+        }
+        wave_lds_sync();   // this wave's tiles are rewritten by the next chunk
     }
 
+    // ---- final state ----
     float* W1o = W1e + unit * (size_t)D * HID;
     float* W2o = W2e + unit * (size_t)HID * D;
 #pragma unroll
@@ -456,13 +534,21 @@ smallb_mlp_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                W1o[(16 * r + 4 * g + i) * HID + 64 * w + 16 * t + n] = W1acc[r][t][i];
+            for (int i = 0; i < 4; ++i) W1o[(16 * r + 4 * g + i) * HID + hs + 16 * t + n] = W1[r][t][i];
+    // W2_end = W2_0 + (accumulated change): W2_0 - mean is formed with the rounding
+    // it had at the start (W2_end may be W2_0: each entry is read and written by one lane)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)   // the row means added back (one rounding)
-            W2o[(16 * r + 4 * g + i) * D + 16 * w + n] = W2acc[r][i] + sm.w2mean[16 * r + 4 * g + i];
+        for (int i = 0; i < 4; ++i) {
+            const float m = sm.w2m[w][16 * a + 4 * g + i];
+#pragma unroll
+            for (int o = 0; o < 4; ++o) {
+                const size_t idx = (size_t)(hs + 16 * a + 4 * g + i) * D + 16 * o + n;
+                const float w0 = W2u[idx];
+                W2o[idx] = w0 + (W2[a][o][i] - (w0 - m));
+            }
+        }
 }
 
 template <typename S>

@@ -254,8 +254,8 @@ int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b, co
         return TTT_ERR_INVALID_ARGUMENT;
     if (!(ln_eps >= 0.f)) return TTT_ERR_INVALID_ARGUMENT;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(W1_0, 16) ||
-        !aligned(W2_0, 16) || !aligned(Z, 4) || !aligned(W1_end, 16) || !aligned(W2_end, 16) ||
-        (eta && !aligned(eta, 4)))
+        !aligned(W2_0, 16) || !aligned(Z, 16) || !aligned(W1_end, 16) || !aligned(W2_end, 16) ||
+        (eta && !aligned(eta, 16)))
         return TTT_ERR_INVALID_ARGUMENT;
     const size_t units = (size_t)B * (size_t)H;
     const size_t tok = units * (size_t)N;
