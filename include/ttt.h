@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 1
+#define TTT_ABI_VERSION 2
 
 typedef enum {
     TTT_OK = 0,
@@ -259,13 +259,14 @@ int ttt_linear_fwd_path(int kind, int qkv_dtype, int d, int b);
 /*
  * ttt_mlp_fwd -- TTT-MLP forward, f(x) = x + LN(GELU(x W1) W2), no biases,
  * GELU(a) = a Phi(a) with the Gaussian CDF Phi = (1 + erf(a / sqrt 2)) / 2 (the
- * erf form, not the tanh approximation). The kernel evaluates erf with
+ * erf form, not the tanh approximation). The kernels evaluate erf with
  * Abramowitz & Stegun, "Handbook of Mathematical Functions", formula 7.1.26
- * (|error| <= 1.5e-7, i.e. at most 7.5e-8 in Phi). The page "How to Master Test-Time Training for Infinite Context
- * LLMs" (section "The Math and Architecture of TTT Layers") names a small
- * multi-layer perceptron as the inner model. The dual form is applied to both
- * layers: with A = K W1_c, X2 = GELU(A) and the loss gradients G2 (at the
- * second pre-activation) and G1 = (G2 W2_c^T) * GELU'(A),
+ * (|error| <= 1.5e-7, i.e. at most 7.5e-8 in Phi). The page "How to Master
+ * Test-Time Training for Infinite Context LLMs" (section "The Math and
+ * Architecture of TTT Layers") names a small multi-layer perceptron as the
+ * inner model. The dual form is applied to both layers: with A = K W1_c,
+ * X2 = GELU(A) and the loss gradients G2 (at the second pre-activation) and
+ * G1 = (G2 W2_c^T) * GELU'(A),
  *   A_Q = Q W1_c - tril(Q K^T) diag(eta) G1,  X2_Q = GELU(A_Q),
  *   H_Q = X2_Q W2_c - tril(X2_Q X2^T) diag(eta) G2,  Z = Q + LN(H_Q),
  *   W1 <- W1_c - K^T diag(eta) G1,  W2 <- W2_c - X2^T diag(eta) G2.
@@ -273,15 +274,27 @@ int ttt_linear_fwd_path(int kind, int qkv_dtype, int d, int b);
  *   hidden      width of the hidden layer (4*d)
  *   W1_0        device [B,H,d,hidden] fp32;  W2_0 device [B,H,hidden,d] fp32
  *   W1_end, W2_end   outputs of the same shapes; may equal W1_0 / W2_0
+ *   workspace   device, 256-byte aligned, ttt_mlp_fwd_workspace_bytes(...)
+ *               bytes (0, and NULL allowed, for d = 64 with b <= 16, where the
+ *               state stays on chip); it must not overlap any other argument
  *   other arguments as for ttt_linear_fwd (ln_gamma/ln_beta required).
- * Supported: dtype F32 or BF16, d = 64, hidden = 256, 1 <= b <= 16.
+ * Alignment: Q, K, V, Z, eta, the states 16 bytes.
+ * Supported: dtype F32 or BF16, d = 64 or 128, hidden = 4 d, 1 <= b <= 64
+ * (else TTT_ERR_UNSUPPORTED). For d = 64 and b <= 16 the state stays in MFMA
+ * accumulators for the whole scan; otherwise it lives in the workspace (and
+ * W2_end), read and written once per chunk.
  */
 int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b,
                 const void* Q, const void* K, const void* V,
                 const float* eta, float eta_const,
                 const float* W1_0, const float* W2_0,
                 const float* ln_gamma, const float* ln_beta, float ln_eps,
-                float* Z, float* W1_end, float* W2_end, void* hip_stream);
+                float* Z, float* W1_end, float* W2_end,
+                void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes of ttt_mlp_fwd (0 when none is needed, and for unsupported
+ * or invalid input). */
+size_t ttt_mlp_fwd_workspace_bytes(int qkv_dtype, int B, int H, int N, int d, int hidden, int b);
 
 /*
  * ttt_layer_fwd -- the whole TTT layer around TTT-Linear: projections, key

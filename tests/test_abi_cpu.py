@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ttt_abi_version() == 1
+    assert lib.ttt_abi_version() == 2
     for s in range(5):
         assert binding.status_string(s).startswith("TTT_")
     assert binding.status_string(99) == "unknown ttt_status"
@@ -161,14 +161,24 @@ def test_mlp_rejections(lib):
     def call(**kw):
         a = args(**kw)
         return f(a["dt"], a["B"], a["H"], a["N"], a["d"], a["hid"], a["b"], p(0), p(1), p(2), None,
-                 0.1, a.get("W1", p(3)), p(4), a.get("gam", p(5)), p(6), 1e-6, p(7), p(8), p(9), None)
+                 0.1, a.get("W1", p(3)), p(4), a.get("gam", p(5)), p(6), 1e-6, p(7), p(8), p(9),
+                 a.get("ws"), a.get("wsb", 0), None)
+    W = lib.ttt_mlp_fwd_workspace_bytes
     assert call(dt=5) == E
     assert call(hid=0) == E
     assert call(gam=None) == E
     assert call(W1=None) == E
     assert call(d=32, hid=128) == U
     assert call(hid=128) == U
-    assert call(b=32) == U
+    assert call(b=65) == U
+    assert W(1, 1, 1, 64, 64, 256, 16) == 0                # on-chip state
+    need = W(1, 1, 1, 64, 64, 256, 32)
+    assert need > 0 and W(1, 1, 1, 64, 128, 512, 16) > 0
+    assert call(b=32) == binding.TTT_ERR_WORKSPACE_TOO_SMALL
+    assert call(b=32, ws=p(10), wsb=need - 1) == binding.TTT_ERR_WORKSPACE_TOO_SMALL
+    assert call(b=32, ws=ctypes.c_void_p(A + 10 * (1 << 30) + 16), wsb=need) == E   # misaligned
+    assert call(b=32, ws=ctypes.c_void_p(A + 9 * (1 << 30) - 256), wsb=need) == E   # overlaps W2_end
+    assert call(d=128, hid=512, b=16) == binding.TTT_ERR_WORKSPACE_TOO_SMALL
 
 
 def block_call(lib, apply=0, kind=0, dt=1, B=1, H=16, N=32768, d=128, b=2048, ws=None, wsb=0, Z=6):

@@ -110,3 +110,54 @@ def test_mlp_in_place_state():
     torch.cuda.synchronize()
     assert np.array_equal(z.cpu().numpy(), z0)
     assert np.array_equal(w1.cpu().numpy(), w10) and np.array_equal(w2.cpu().numpy(), w20)
+
+
+def case_d(dtype, B, H, N, d, b, eta="sigmoid", seed=31):
+    wl = wlm.Workload(f"mlp_{dtype}_{B}x{H}x{N}_d{d}_b{b}", "mlp", dtype, B, H, N, d, b, eta, 0.05,
+                      qkv_std=1.0 if dtype == "bf16" else 0.125)
+    return wlm.generate(wl, seed)
+
+
+@pytest.mark.parametrize("b", [17, 24, 32, 48, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mlp_chunks_17_to_64(dtype, b):
+    """d = 64, chunks of 17..64 tokens (state and chunk intermediates in the
+    workspace): two full chunks and a ragged tail of b // 2 + 1 tokens."""
+    inp = case_d(dtype, 1, 2, 2 * b + b // 2 + 1, 64, b, seed=700 + b)
+    say(f"case {inp.wl.name}")
+    check(inp)
+
+
+@pytest.mark.parametrize("b", [1, 7, 16, 33, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mlp_d128(dtype, b):
+    """d = 128, hidden = 512, chunks of 1..64 tokens with a ragged tail."""
+    N = 2 * b + b // 2 + 1 if b > 1 else 24
+    inp = case_d(dtype, 1, 2, N, 128, b, seed=800 + b)
+    say(f"case {inp.wl.name}")
+    check(inp)
+
+
+def test_mlp_generic_eta_zero_in_place_and_offset():
+    """The workspace path: eta = 0 leaves both weights bit for bit; in-place
+    state equals separate buffers; a large common shift of H's rows (W2 offset)
+    still matches the oracle."""
+    import torch
+    from weights_ttt_layer_amd import mlp_fwd
+    inp = case_d("bf16", 2, 1, 80, 128, 32, eta="const", seed=41)
+    inp.eta_const = 0.0
+    z, w1, w2 = gpu_mlp(inp)
+    assert np.array_equal(w1, inp.w1) and np.array_equal(w2, inp.w2)
+    zr, _, _ = oracle_mlp(inp)
+    assert rel_err(z, zr) <= TOL["bf16"]
+    inp = case_d("bf16", 2, 1, 80, 64, 40, seed=42)
+    z0, w10, w20 = gpu_mlp(inp)
+    t = wlm.to_device(inp)
+    z1, w11, w21 = mlp_fwd(t["q"], t["k"], t["v"], t["w1"], t["w2"], t["eta"], b=40, ln_gamma=t["gamma"],
+                           ln_beta=t["beta"], ln_eps=inp.wl.ln_eps, w1_end=t["w1"], w2_end=t["w2"])
+    torch.cuda.synchronize()
+    assert np.array_equal(z1.cpu().numpy(), z0)
+    assert np.array_equal(w11.cpu().numpy(), w10) and np.array_equal(w21.cpu().numpy(), w20)
+    inp = case_d("bf16", 1, 2, 70, 128, 32, seed=43)
+    inp.w2 = (inp.w2.astype(np.float64) + 0.5).astype(np.float32)
+    check(inp)

@@ -52,8 +52,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_linear_fwd_path.argtypes = [i, i, i, i]
     lib.ttt_linear_fwd_path.restype = i
     lib.ttt_mlp_fwd.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, fp, f, fp, fp, fp, fp, f, fp, fp, fp,
-                                vp]
+                                vp, sz, vp]
     lib.ttt_mlp_fwd.restype = i
+    lib.ttt_mlp_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.ttt_mlp_fwd_workspace_bytes.restype = sz
     lib.ttt_linear_fwd_block.argtypes = [i] + lib.ttt_linear_fwd.argtypes
     lib.ttt_linear_fwd_block.restype = i
     lib.ttt_linear_fwd_block_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
@@ -265,9 +267,10 @@ def mlp_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tensor,
             eta: Optional[torch.Tensor] = None, *, b: int, ln_gamma: torch.Tensor,
             ln_beta: torch.Tensor, eta_const: float = 0.0, ln_eps: float = 1e-6,
             z: Optional[torch.Tensor] = None, w1_end: Optional[torch.Tensor] = None,
-            w2_end: Optional[torch.Tensor] = None, stream=None
+            w2_end: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None
             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """TTT-MLP forward through ``ttt_mlp_fwd``. Returns (Z, W1_end, W2_end)."""
+    """TTT-MLP forward through ``ttt_mlp_fwd``. Returns (Z, W1_end, W2_end). The
+    workspace (needed beyond d = 64 with b <= 16) is allocated here unless given."""
     lib = load_library()
     B, H, N, d = q.shape
     hid = w1.shape[-1]
@@ -292,9 +295,14 @@ def mlp_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tensor,
         w2_end = torch.empty_like(w2)
     else:
         _check(w2_end, "w2_end", (B, H, hid, d), torch.float32)
+    need = int(lib.ttt_mlp_fwd_workspace_bytes(dt, B, H, N, d, hid, int(b)))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.ttt_mlp_fwd(dt, B, H, N, d, hid, int(b), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                          float(eta_const), _ptr(w1), _ptr(w2), _ptr(ln_gamma), _ptr(ln_beta),
-                         float(ln_eps), _ptr(z), _ptr(w1_end), _ptr(w2_end), _stream_ptr(stream))
+                         float(ln_eps), _ptr(z), _ptr(w1_end), _ptr(w2_end), _ptr(workspace), ws_bytes,
+                         _stream_ptr(stream))
     if st != TTT_OK:
         raise TTTError(st, "ttt_mlp_fwd")
     return z, w1_end, w2_end

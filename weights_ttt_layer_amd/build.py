@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libttt.so")
-SOURCES = ["ttt_abi.hip", "smallb_linear.hip", "smallb_chain.hip", "midb_linear.hip", "smallb_mlp.hip",
+SOURCES = ["ttt_abi.hip", "smallb_linear.hip", "smallb_chain.hip", "midb_linear.hip", "smallb_mlp.hip", "mlp_generic.hip",
            "large_chunk.hip", "decode.hip", "outer_layer.hip", "backward.hip"]
 # the measurement calibration kernels (include/ttt_peak.h), a library of their own
 PEAK_LIB_PATH = os.path.join(HERE, "libttt_peak.so")

@@ -65,8 +65,12 @@ hipError_t launch_large_chunk_linear(const LinearArgs& a, int outputs, hipStream
 // Single-token decode step: one wave per (sequence, head), d = 64.
 hipError_t launch_decode_linear(const LinearArgs& a, hipStream_t stream);
 
-// TTT-MLP small-b path: d = 64, hidden = 256, 1 <= b <= 16.
+// TTT-MLP small-b path: d = 64, hidden = 256, 1 <= b <= 16 (state in registers).
 hipError_t launch_smallb_mlp(const MlpArgs& a, hipStream_t stream);
+// TTT-MLP for d = 64 with 17 <= b <= 64 and d = 128 with 1 <= b <= 64: state
+// and the chunk's intermediates in the caller's workspace (mlp_generic.hip).
+size_t mlp_generic_workspace_bytes(int B, int H, int d, int b);
+hipError_t launch_mlp_generic(const MlpArgs& a, void* workspace, hipStream_t stream);
 
 // Backward of TTT-Linear (plain / LN), d = 64, 1 <= b <= 16. `f` carries the
 // forward's inputs and the workspace (chunk-start states and per-unit partials).

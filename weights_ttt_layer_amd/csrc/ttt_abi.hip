@@ -243,10 +243,21 @@ int ttt_linear_decode(int kind, int qkv_dtype, int B, int H, int d, const void* 
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
+size_t ttt_mlp_fwd_workspace_bytes(int qkv_dtype, int B, int H, int N, int d, int hidden, int b)
+{
+    if (qkv_dtype != TTT_DTYPE_F32 && qkv_dtype != TTT_DTYPE_BF16) return 0;
+    if (B < 1 || H < 1 || N < 1 || b < 1) return 0;
+    if (!((d == 64 || d == 128) && hidden == 4 * d && b <= 64)) return 0;
+    if ((size_t)B * (size_t)H > (size_t)INT32_MAX) return 0;
+    if (d == 64 && b <= 16) return 0;   // the state stays in registers
+    return ttt::mlp_generic_workspace_bytes(B, H, d, b);
+}
+
 int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b, const void* Q,
                 const void* K, const void* V, const float* eta, float eta_const, const float* W1_0,
                 const float* W2_0, const float* ln_gamma, const float* ln_beta, float ln_eps,
-                float* Z, float* W1_end, float* W2_end, void* hip_stream)
+                float* Z, float* W1_end, float* W2_end, void* workspace, size_t workspace_bytes,
+                void* hip_stream)
 {
     if (qkv_dtype != TTT_DTYPE_F32 && qkv_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARGUMENT;
     if (B < 1 || H < 1 || N < 1 || d < 1 || hidden < 1 || b < 1) return TTT_ERR_INVALID_ARGUMENT;
@@ -282,7 +293,17 @@ int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b, co
     if (overlaps(W1_end, w_bytes, W2_0, w_bytes) || overlaps(W2_end, w_bytes, W1_0, w_bytes))
         return TTT_ERR_INVALID_ARGUMENT;
 
-    if (d != 64 || hidden != 4 * d || b > 16) return TTT_ERR_UNSUPPORTED;
+    if (!((d == 64 || d == 128) && hidden == 4 * d && b <= 64)) return TTT_ERR_UNSUPPORTED;
+    const size_t need = ttt_mlp_fwd_workspace_bytes(qkv_dtype, B, H, N, d, hidden, b);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return TTT_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned(workspace, 256)) return TTT_ERR_INVALID_ARGUMENT;
+        const void* others[9] = {Q, K, V, W1_0, W2_0, Z, W1_end, W2_end, eta};
+        const size_t other_bytes[9] = {qkv_bytes, qkv_bytes, qkv_bytes, w_bytes, w_bytes, z_bytes, w_bytes, w_bytes,
+                                       eta ? tok * 4 : 0};
+        for (int i = 0; i < 9; ++i)
+            if (overlaps(workspace, need, others[i], other_bytes[i])) return TTT_ERR_INVALID_ARGUMENT;
+    }
 
     ttt::MlpArgs a;
     a.dtype = qkv_dtype;
@@ -305,7 +326,8 @@ int ttt_mlp_fwd(int qkv_dtype, int B, int H, int N, int d, int hidden, int b, co
     a.Z = Z;
     a.W1_end = W1_end;
     a.W2_end = W2_end;
-    hipError_t err = ttt::launch_smallb_mlp(a, reinterpret_cast<hipStream_t>(hip_stream));
+    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    const hipError_t err = need == 0 ? ttt::launch_smallb_mlp(a, stream) : ttt::launch_mlp_generic(a, workspace, stream);
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
