@@ -106,8 +106,11 @@ typedef enum {
  * Supported (else TTT_ERR_UNSUPPORTED):
  *   small-b path  : kind PLAIN or LN, dtype F32 or BF16, d = 64 or 128,
  *                   1 <= b <= 64 (one workgroup per unit, the state on chip)
- *   large-chunk   : kind PLAIN, dtype BF16, d = 128, b >= 256, b % 128 == 0,
- *                   N % 128 == 0 and N < 2^22 (needs the workspace).
+ *   large-chunk   : kind PLAIN, dtype F32 or BF16, d = 64 or 128, b > 64, any N.
+ *                   With BF16 streams, d = 128, b >= 256, b % 128 == 0,
+ *                   N % 128 == 0 and N < 2^22 the chunk-parallel kernels run
+ *                   (they need the workspace); every other combination runs one
+ *                   workgroup per unit over blocks of 64 tokens (no workspace).
  * ttt_linear_fwd_path() reports which path a combination takes.
  */
 int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b,
@@ -168,9 +171,9 @@ typedef enum {
  *     apply = TTT_APPLY_AFTER_STEP:   Z_c = f(Q_c; W_{c+1})
  * Arguments, layouts, ownership, aliasing and errors are those of
  * ttt_linear_fwd; an invalid `apply` is TTT_ERR_INVALID_ARGUMENT.
- * Supported (else TTT_ERR_UNSUPPORTED): the large-chunk combinations of
- * ttt_linear_fwd (kind PLAIN, BF16, d = 128, b >= 256, b % 128 == 0,
- * N % 128 == 0, N < 2^22), with the workspace below.
+ * Supported (else TTT_ERR_UNSUPPORTED): the combinations of ttt_linear_fwd
+ * that run the chunk-parallel kernels (kind PLAIN, BF16, d = 128, b >= 256,
+ * b % 128 == 0, N % 128 == 0, N < 2^22), with the workspace below.
  */
 int ttt_linear_fwd_block(int apply, int kind, int qkv_dtype, int B, int H, int N, int d, int b,
                          const void* Q, const void* K, const void* V,

@@ -49,7 +49,10 @@ def test_path_selection(lib):
     assert P(1, 1, 64, 65) == binding.TTT_PATH_NONE
     assert P(0, 1, 128, 2048) == binding.TTT_PATH_LARGE_CHUNK
     assert P(1, 1, 128, 2048) == binding.TTT_PATH_NONE       # LN has no large-chunk path
-    assert P(0, 1, 128, 2000) == binding.TTT_PATH_NONE       # not a multiple of 128
+    assert P(1, 0, 64, 65) == binding.TTT_PATH_NONE
+    assert P(0, 1, 128, 2000) == binding.TTT_PATH_LARGE_CHUNK  # any b > 64 for plain f
+    assert P(0, 0, 64, 256) == binding.TTT_PATH_LARGE_CHUNK
+    assert P(0, 1, 64, 65) == binding.TTT_PATH_LARGE_CHUNK
     assert P(0, 1, 32, 16) == binding.TTT_PATH_NONE
     assert P(5, 1, 64, 16) == binding.TTT_PATH_NONE
 
@@ -59,6 +62,10 @@ def test_workspace_sizes(lib):
     assert W(0, 1, 8, 12, 2048, 64, 16) == 0          # small-b path needs none
     assert W(0, 1, 1, 16, 32768, 128, 2048) > 0
     assert W(0, 1, 0, 16, 32768, 128, 2048) == 0      # invalid sizes
+    # combinations outside the chunk-parallel kernels need none
+    assert W(0, 0, 1, 16, 32768, 128, 2048) == 0      # fp32 streams
+    assert W(0, 1, 1, 1, 1000, 64, 256) == 0          # d = 64, ragged N
+    assert W(0, 1, 1, 1, 1000, 128, 256) == 0         # N not a multiple of 128
 
 
 # Fake, never-dereferenced device addresses: every call below must be rejected
@@ -105,10 +112,10 @@ def test_rejects_invalid_arguments(lib):
 def test_rejects_unsupported(lib):
     U = binding.TTT_ERR_UNSUPPORTED
     assert lin_call(lib, d=32) == U
-    assert lin_call(lib, b=65) == U
-    assert lin_call(lib, d=128, b=100) == U
+    assert lin_call(lib, kind=1, b=65) == U
+    assert lin_call(lib, kind=1, d=128, b=100) == U
     assert lin_call(lib, kind=1, d=128, b=2048) == U
-    assert lin_call(lib, dt=0, d=128, b=2048) == U
+    assert lin_call(lib, d=96, b=100) == U
 
 
 def test_large_chunk_workspace_checked_before_launch(lib):
@@ -194,6 +201,8 @@ def test_block_rejections(lib):
     assert block_call(lib, Z=0) == E                              # Z overlaps Q
     assert block_call(lib, d=64, b=16, N=64) == U                 # small-b combinations have no block path
     assert block_call(lib, kind=1) == U
+    assert block_call(lib, d=64, b=256, N=1024) == U              # block outputs: chunk-parallel kernels only
+    assert block_call(lib, N=32040) == U                         # N not a multiple of 128
     assert block_call(lib) == binding.TTT_ERR_WORKSPACE_TOO_SMALL
     Wb = lib.ttt_linear_fwd_block_workspace_bytes
     assert Wb(0, 0, 1, 1, 16, 32768, 128, 2048) == lib.ttt_linear_fwd_workspace_bytes(0, 1, 1, 16, 32768, 128, 2048)

@@ -83,3 +83,44 @@ def test_large_chunk_state_passing():
     zb, wb = gpu_linear(b2)
     assert rel_err(np.concatenate([za, zb], 2), z) <= 1e-6
     assert rel_err(wb, w) <= 1e-6
+
+
+def gen_case(B, H, N, d, b, dtype="bf16", eta="const", eta_const=0.01, seed=9, l2=True):
+    wl = wlm.Workload(f"lcg_{dtype}_{B}x{H}x{N}_d{d}_b{b}_{eta}", "plain", dtype, B, H, N, d, b, eta, eta_const,
+                      l2_rows=l2, qkv_std=1.0 if l2 or dtype == "bf16" else 0.125)
+    return wlm.generate(wl, seed)
+
+
+@pytest.mark.parametrize("B,H,N,d,b,dtype,eta", [
+    (1, 2, 1000, 64, 256, "bf16", "const"),     # d = 64 and N not a multiple of 128 (or of b)
+    (1, 1, 1000, 128, 256, "bf16", "sigmoid"),  # d = 128 with a ragged N: outside the chunk-parallel kernels
+    (2, 1, 700, 64, 256, "f32", "sigmoid"),     # fp32 streams
+    (1, 1, 900, 128, 384, "f32", "const"),
+    (1, 2, 350, 64, 100, "bf16", "sigmoid"),    # b between the small-b limit and 256, blocks of 64 + 36
+    (1, 1, 200, 128, 65, "bf16", "const"),      # one token past the small-b limit
+    (1, 1, 3000, 64, 2048, "bf16", "const"),    # b = 2048 at d = 64, a short last chunk
+])
+def test_large_chunk_generic(B, H, N, d, b, dtype, eta):
+    """Plain TTT-Linear with chunks longer than 64 tokens outside the bf16 d = 128
+    chunk-parallel kernels: the generic kernel in blocks of 64 tokens (the
+    chunk-start state for the gradients, a running state for the outputs)."""
+    inp = gen_case(B, H, N, d, b, dtype, eta)
+    say(f"case {inp.wl.name}")
+    tol = TOL[dtype]
+    z, w = gpu_linear(inp)
+    zr, wr = oracle_linear(inp)
+    ez, ew = rel_err(z, zr), rel_err(w, wr)
+    say(f"  err Z {ez:.2e}  W_end {ew:.2e}  (tol {tol:.0e})")
+    assert ez <= tol and ew <= tol
+
+
+def test_large_chunk_generic_single_chunk_closed_form():
+    """W0 = 0, one chunk of 640 tokens at d = 64: Z = 2 tril(Q K^T) diag(eta) V,
+    W_end = 2 K^T diag(eta) V (unnormalised causal linear attention)."""
+    inp = gen_case(1, 1, 640, 64, 640, "bf16", "const", 0.02, seed=10)
+    inp.w0 = np.zeros_like(inp.w0)
+    z, w = gpu_linear(inp)
+    Q, K, V = (inp.f64(n)[0, 0] for n in ("q", "k", "v"))
+    eta = float(np.float32(0.02))
+    assert rel_err(z[0, 0], 2 * eta * np.tril(Q @ K.T) @ V) <= TOL["bf16"]
+    assert rel_err(w[0, 0], 2 * eta * K.T @ V) <= TOL["bf16"]

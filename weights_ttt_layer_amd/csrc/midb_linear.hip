@@ -83,12 +83,11 @@ struct alignas(16) MidSmem {
 // Global loads of chunk c (rows clamped into the sequence; rows past its end
 // are zeroed when the tile is written to LDS).
 template <int D, int NG, typename S, int PPT>
-__device__ __forceinline__ void mid_load(uint4 (&pf)[PPT], float& pe, int c, int b, int N, int tid, const S* Qu,
+__device__ __forceinline__ void mid_load(uint4 (&pf)[PPT], float& pe, int c0, int N, int tid, const S* Qu,
                                          const S* Ku, const S* Vu, const float* etau, float eta_const)
 {
     using G = MidGeom<D, NG, S>;
     static_assert(PPT == G::PPT, "pieces per thread");
-    const int c0 = c * b;
 #pragma unroll
     for (int k = 0; k < G::PPT; ++k) {
         const int idx = min(tid + k * MB_THREADS, G::TOTAL - 1);
@@ -149,7 +148,13 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int NG, int KIND, typename S>
+// BIG: chunks longer than one block of 16 NG rows (plain f only). A chunk is
+// then a sequence of blocks: every block's gradient is taken at the chunk-start
+// state W_c (kept as a second copy), its outputs use the running state W' that
+// already holds the updates of the chunk's earlier blocks, and W' takes the
+// block's update; W' is W_{c+1} once the chunk ends. (The dual form's causal
+// sum over the chunk, split at block boundaries by associativity.)
+template <int D, int NG, int KIND, typename S, bool BIG>
 __global__ void __launch_bounds__(MB_THREADS)
 midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __restrict__ Kg,
                    const S* __restrict__ Vg, const float* __restrict__ etag, float eta_const,
@@ -157,6 +162,7 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
                    float eps, float* __restrict__ Zg, float* __restrict__ Wend)
 {
     using G = MidGeom<D, NG, S>;
+    static_assert(!BIG || KIND == 0, "blocks of a longer chunk: plain f only");
     constexpr int CT = D / 64;          // column tiles per wave
     constexpr int RT = D / 16;          // row tiles of the state
     constexpr int KS = D / 32;          // 16x16x32 steps over the features
@@ -229,18 +235,32 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
             }
     }
 
-    const int nchunks = (N + b - 1) / b;
+    // Blocks of at most ROWS tokens, in order: chunk c covers rows [c b, c b + b);
+    // a block never crosses a chunk boundary (without BIG, a block is a chunk).
+    auto block_rows = [&](int r0) {            // rows of the block starting at row r0
+        const int cend = min((r0 / b + 1) * b, N);
+        return min(G::ROWS, cend - r0);
+    };
+    f32x4 Wc[BIG ? RT : 1][BIG ? CT : 1];      // BIG: W_c, the chunk-start state
     uint4 pf[G::PPT];
     float pe = 0.f;
-    mid_load<D, NG, S, G::PPT>(pf, pe, 0, b, N, tid, Qu, Ku, Vu, etau, eta_const);
-    mid_store<D, NG, S, G::PPT>(sm, pf, pe, tid, min(b, N));
+    mid_load<D, NG, S, G::PPT>(pf, pe, 0, N, tid, Qu, Ku, Vu, etau, eta_const);
+    mid_store<D, NG, S, G::PPT>(sm, pf, pe, tid, block_rows(0));
     if constexpr (G::PREFETCH)
-        if (nchunks > 1) mid_load<D, NG, S, G::PPT>(pf, pe, 1, b, N, tid, Qu, Ku, Vu, etau, eta_const);
+        if (block_rows(0) < N) mid_load<D, NG, S, G::PPT>(pf, pe, block_rows(0), N, tid, Qu, Ku, Vu, etau, eta_const);
     __syncthreads();
 
-    for (int c = 0; c < nchunks; ++c) {
-        const int c0 = c * b;
-        const int bc = min(b, N - c0);
+    for (int c0 = 0; c0 < N;) {
+        const int bc = block_rows(c0);
+        const int c1 = c0 + bc;                // next block's first row
+        if constexpr (BIG) {
+            if (c0 % b == 0) {
+#pragma unroll
+                for (int r = 0; r < RT; ++r)
+#pragma unroll
+                    for (int t = 0; t < CT; ++t) Wc[r][t] = Wacc[r][t];
+            }
+        }
 
         // ======== products at W_c ========
         // W_c as operand terms: lane (g, n) holds W[32p + 4g + i (+16)][64t + 16w + n]
@@ -249,9 +269,15 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
 #pragma unroll
         for (int t = 0; t < CT; ++t) {
             // column tile t of W_c as operand terms: lane (g, n) holds W[32p + 4g + i (+16)][64t + 16w + n]
+            // (BIG: Wb is the running state W' for the outputs, Wg the chunk-start W_c for the gradient)
             bf16x8 Wb[KS][TS];
 #pragma unroll
             for (int p = 0; p < KS; ++p) b8_from_acc<TS>(Wacc[2 * p][t], Wacc[2 * p + 1][t], Wb[p]);
+            bf16x8 Wg[BIG ? KS : 1][TS];
+            if constexpr (BIG) {
+#pragma unroll
+                for (int p = 0; p < KS; ++p) b8_from_acc<TS>(Wc[2 * p][t], Wc[2 * p + 1][t], Wg[p]);
+            }
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
                 hqT[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -265,6 +291,8 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
                     hqT[j][t] = mma32_terms<TS, TIN>(hqT[j][t], Wb[p], qa);
                     if constexpr (KIND == 1)
                         hk[j][t] = mma32_terms<TS, TIN>(hk[j][t], Wb[p], ka);
+                    else if constexpr (BIG)
+                        hk[j][t] = mma32_terms<TIN, TS>(hk[j][t], ka, Wg[p]);
                     else
                         hk[j][t] = mma32_terms<TIN, TS>(hk[j][t], ka, Wb[p]);
                 }
@@ -459,14 +487,16 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
         }
 
         // ======== the next chunk into the stage ========
-        if (c + 1 < nchunks) {
-            __syncthreads();                       // every wave is done with this chunk's stage
-            if constexpr (!G::PREFETCH) mid_load<D, NG, S, G::PPT>(pf, pe, c + 1, b, N, tid, Qu, Ku, Vu, etau, eta_const);
-            mid_store<D, NG, S, G::PPT>(sm, pf, pe, tid, min(b, N - (c + 1) * b));
+        if (c1 < N) {
+            __syncthreads();                       // every wave is done with this block's stage
+            if constexpr (!G::PREFETCH) mid_load<D, NG, S, G::PPT>(pf, pe, c1, N, tid, Qu, Ku, Vu, etau, eta_const);
+            const int bc1 = block_rows(c1);
+            mid_store<D, NG, S, G::PPT>(sm, pf, pe, tid, bc1);
             if constexpr (G::PREFETCH)
-                if (c + 2 < nchunks) mid_load<D, NG, S, G::PPT>(pf, pe, c + 2, b, N, tid, Qu, Ku, Vu, etau, eta_const);
+                if (c1 + bc1 < N) mid_load<D, NG, S, G::PPT>(pf, pe, c1 + bc1, N, tid, Qu, Ku, Vu, etau, eta_const);
             __syncthreads();
         }
+        c0 = c1;
     }
 
     // W_end = W0 + (accumulated change) for the LN kind (W0 - mean formed with the
@@ -489,19 +519,19 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
             }
 }
 
+template <int D, int NG, int KIND, typename S, bool BIG>
+hipError_t launch_one(const LinearArgs& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((midb_linear_kernel<D, NG, KIND, S, BIG>), dim3(a.B * a.H), dim3(MB_THREADS), 0, stream, a.H,
+                       a.N, a.b, static_cast<const S*>(a.Q), static_cast<const S*>(a.K), static_cast<const S*>(a.V),
+                       a.eta, a.eta_const, a.W0, a.gamma, a.beta, a.eps, a.Z, a.W_end);
+    return hipGetLastError();
+}
+
 template <int D, int NG, typename S>
 hipError_t launch_kind(const LinearArgs& a, hipStream_t stream)
 {
-    const dim3 grid(a.B * a.H), block(MB_THREADS);
-    if (a.kind == 1)
-        hipLaunchKernelGGL((midb_linear_kernel<D, NG, 1, S>), grid, block, 0, stream, a.H, a.N, a.b,
-                           static_cast<const S*>(a.Q), static_cast<const S*>(a.K), static_cast<const S*>(a.V),
-                           a.eta, a.eta_const, a.W0, a.gamma, a.beta, a.eps, a.Z, a.W_end);
-    else
-        hipLaunchKernelGGL((midb_linear_kernel<D, NG, 0, S>), grid, block, 0, stream, a.H, a.N, a.b,
-                           static_cast<const S*>(a.Q), static_cast<const S*>(a.K), static_cast<const S*>(a.V),
-                           a.eta, a.eta_const, a.W0, a.gamma, a.beta, a.eps, a.Z, a.W_end);
-    return hipGetLastError();
+    return a.kind == 1 ? launch_one<D, NG, 1, S, false>(a, stream) : launch_one<D, NG, 0, S, false>(a, stream);
 }
 
 template <int D, typename S>
@@ -515,6 +545,14 @@ hipError_t launch_groups(const LinearArgs& a, hipStream_t stream)
 }
 
 }  // namespace
+
+hipError_t launch_midb_linear_blocks(const LinearArgs& a, hipStream_t stream)
+{
+    if (a.d == 128)
+        return a.dtype == 1 ? launch_one<128, 4, 0, uint16_t, true>(a, stream)
+                            : launch_one<128, 4, 0, float, true>(a, stream);
+    return a.dtype == 1 ? launch_one<64, 4, 0, uint16_t, true>(a, stream) : launch_one<64, 4, 0, float, true>(a, stream);
+}
 
 hipError_t launch_midb_linear(const LinearArgs& a, hipStream_t stream)
 {

@@ -33,14 +33,22 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 
 int linear_path(int kind, int dtype, int d, int b)
 {
-    if ((kind == TTT_LINEAR_PLAIN || kind == TTT_LINEAR_LN) &&
-        (dtype == TTT_DTYPE_F32 || dtype == TTT_DTYPE_BF16) && (d == SMALLB_D || d == SMALLB_D2) && b >= 1 &&
-        b <= SMALLB_FWD_MAX_B)
-        return TTT_PATH_SMALL_B;
-    if (kind == TTT_LINEAR_PLAIN && dtype == TTT_DTYPE_BF16 && d == LARGE_D && b >= LARGE_MIN_B &&
-        b % LARGE_B_MULT == 0)
-        return TTT_PATH_LARGE_CHUNK;
+    const bool kinds = kind == TTT_LINEAR_PLAIN || kind == TTT_LINEAR_LN;
+    const bool dtypes = dtype == TTT_DTYPE_F32 || dtype == TTT_DTYPE_BF16;
+    if (!kinds || !dtypes || (d != SMALLB_D && d != SMALLB_D2) || b < 1) return TTT_PATH_NONE;
+    if (b <= SMALLB_FWD_MAX_B) return TTT_PATH_SMALL_B;
+    if (kind == TTT_LINEAR_PLAIN) return TTT_PATH_LARGE_CHUNK;   // longer chunks: plain f
     return TTT_PATH_NONE;
+}
+
+// The chunk-parallel large-chunk kernels (a workspace, three launches) take bf16
+// streams at d = 128 with b and N multiples of 128; every other large-chunk
+// combination runs the generic kernel's block mode (one workgroup per unit,
+// no workspace).
+bool fast_large(int dtype, int d, int b, int N)
+{
+    return dtype == TTT_DTYPE_BF16 && d == LARGE_D && b >= LARGE_MIN_B && b % LARGE_B_MULT == 0 &&
+           N % LARGE_B_MULT == 0 && N < LARGE_MAX_N;
 }
 
 size_t elem_size(int dtype) { return dtype == TTT_DTYPE_BF16 ? 2 : 4; }
@@ -68,8 +76,7 @@ int ttt_linear_fwd_path(int kind, int qkv_dtype, int d, int b) { return linear_p
 size_t ttt_linear_fwd_workspace_bytes(int kind, int qkv_dtype, int B, int H, int N, int d, int b)
 {
     if (B < 1 || H < 1 || N < 1 || d < 1 || b < 1) return 0;
-    if (linear_path(kind, qkv_dtype, d, b) != TTT_PATH_LARGE_CHUNK || N % LARGE_B_MULT != 0 || N >= LARGE_MAX_N)
-        return 0;
+    if (linear_path(kind, qkv_dtype, d, b) != TTT_PATH_LARGE_CHUNK || !fast_large(qkv_dtype, d, b, N)) return 0;
     return ttt::large_chunk_workspace_bytes(B, H, N, d, b);
 }
 
@@ -113,9 +120,7 @@ int check_linear(int kind, int qkv_dtype, int B, int H, int N, int d, int b, con
 
     path = linear_path(kind, qkv_dtype, d, b);
     if (path == TTT_PATH_NONE) return TTT_ERR_UNSUPPORTED;
-    if (path == TTT_PATH_LARGE_CHUNK && N % LARGE_B_MULT != 0) return TTT_ERR_UNSUPPORTED;
-    if (path == TTT_PATH_LARGE_CHUNK && N >= LARGE_MAX_N) return TTT_ERR_UNSUPPORTED;
-    if (path == TTT_PATH_LARGE_CHUNK && !internal_workspace) {
+    if (path == TTT_PATH_LARGE_CHUNK && fast_large(qkv_dtype, d, b, N) && !internal_workspace) {
         const size_t need = ttt::large_chunk_workspace_bytes(B, H, N, d, b);
         if (workspace_bytes < need || (need > 0 && !workspace)) return TTT_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned(workspace, 256)) return TTT_ERR_INVALID_ARGUMENT;
@@ -164,8 +169,13 @@ int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b, c
                                 ln_eps, Z, W_end, workspace, workspace_bytes, a, path);
     if (st != TTT_OK) return st;
     hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-    const hipError_t err = path == TTT_PATH_SMALL_B ? ttt::launch_smallb_linear(a, stream)
-                                                    : ttt::launch_large_chunk_linear(a, ttt::LC_OUT_DUAL, stream);
+    hipError_t err;
+    if (path == TTT_PATH_SMALL_B)
+        err = ttt::launch_smallb_linear(a, stream);
+    else if (fast_large(qkv_dtype, d, b, N))
+        err = ttt::launch_large_chunk_linear(a, ttt::LC_OUT_DUAL, stream);
+    else
+        err = ttt::launch_midb_linear_blocks(a, stream);
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
@@ -186,7 +196,7 @@ int ttt_linear_fwd_block(int apply, int kind, int qkv_dtype, int B, int H, int N
     const int st = check_linear(kind, qkv_dtype, B, H, N, d, b, Q, K, V, eta, eta_const, W0, ln_gamma, ln_beta,
                                 ln_eps, Z, W_end, workspace, workspace_bytes, a, path);
     if (st != TTT_OK) return st;
-    if (path != TTT_PATH_LARGE_CHUNK) return TTT_ERR_UNSUPPORTED;
+    if (path != TTT_PATH_LARGE_CHUNK || !fast_large(qkv_dtype, d, b, N)) return TTT_ERR_UNSUPPORTED;
     const hipError_t err = ttt::launch_large_chunk_linear(
         a, apply == TTT_APPLY_BEFORE_STEP ? ttt::LC_OUT_BEFORE : ttt::LC_OUT_AFTER,
         reinterpret_cast<hipStream_t>(hip_stream));
@@ -555,6 +565,8 @@ extern "C" int ttt_linear_fwd_noalloc(int kind, int qkv_dtype, int B, int H, int
     hipError_t err;
     if (path == TTT_PATH_SMALL_B) {
         err = ttt::launch_smallb_linear(a, stream);
+    } else if (!fast_large(qkv_dtype, d, b, N)) {
+        err = ttt::launch_midb_linear_blocks(a, stream);
     } else {
         void* ptr = nullptr;
         err = scratch_on_current_device(&ptr);
