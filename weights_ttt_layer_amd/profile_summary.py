@@ -39,7 +39,7 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 KERNEL_SOURCES = {
     "plain": ["smallb_linear.hip", "smallb_common.h", "device_common.h"],
     "ln": ["smallb_chain.hip", "device_common.h"],
-    "mlp": ["smallb_mlp.hip", "smallb_common.h", "device_common.h"],
+    "mlp": ["smallb_mlp.hip", "gelu.h", "smallb_common.h", "device_common.h"],
     "large": ["large_chunk.hip", "device_common.h"],
     "block_before": ["large_chunk.hip", "device_common.h"],
     "block_after": ["large_chunk.hip", "device_common.h"],
@@ -48,9 +48,10 @@ KERNEL_SOURCES = {
     "backward": ["backward.hip", "device_common.h"],
 }
 
-OUR_KERNELS = ("smallb_linear_kernel", "smallb_chain_kernel", "smallb_mlp_kernel", "lc_gram_kernel", "lc_scan_kernel",
-               "lc_chunk_kernel", "lc_apply_kernel", "decode_kernel", "layer_gemm_kernel",
-               "layer_outprep_kernel", "bwd_linear_kernel", "bwd_gamma_beta_kernel")
+OUR_KERNELS = ("smallb_linear_kernel", "smallb_chain_kernel", "smallb_mlp_kernel", "midb_linear_kernel",
+               "mlp_generic_kernel", "lc_gram_kernel", "lc_scan_kernel", "lc_chunk_kernel", "lc_apply_kernel",
+               "decode_kernel", "layer_gemm_kernel", "layer_outprep_kernel", "bwd_linear_kernel",
+               "bwd_gamma_beta_kernel")
 
 # kernel-name prefixes launched by one call of each path
 PATH_KERNELS = {
