@@ -171,9 +171,11 @@ typedef enum {
  *     apply = TTT_APPLY_AFTER_STEP:   Z_c = f(Q_c; W_{c+1})
  * Arguments, layouts, ownership, aliasing and errors are those of
  * ttt_linear_fwd; an invalid `apply` is TTT_ERR_INVALID_ARGUMENT.
- * Supported (else TTT_ERR_UNSUPPORTED): the combinations of ttt_linear_fwd
- * that run the chunk-parallel kernels (kind PLAIN, BF16, d = 128, b >= 256,
- * b % 128 == 0, N % 128 == 0, N < 2^22), with the workspace below.
+ * Supported (else TTT_ERR_UNSUPPORTED): the large-chunk combinations of
+ * ttt_linear_fwd (kind PLAIN, b > 64, d in {64, 128}, fp32 or bf16 streams, any
+ * N). Those that run the chunk-parallel kernels (BF16, d = 128, b >= 256,
+ * b % 128 == 0, N % 128 == 0, N < 2^22) take the workspace below; the others
+ * need none (ttt_linear_fwd_block_workspace_bytes returns 0 for them).
  */
 int ttt_linear_fwd_block(int apply, int kind, int qkv_dtype, int B, int H, int N, int d, int b,
                          const void* Q, const void* K, const void* V,

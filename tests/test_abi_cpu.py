@@ -190,7 +190,7 @@ def test_mlp_rejections(lib):
 
 def block_call(lib, apply=0, kind=0, dt=1, B=1, H=16, N=32768, d=128, b=2048, ws=None, wsb=0, Z=6):
     return lib.ttt_linear_fwd_block(apply, kind, dt, B, H, N, d, b, addr(0), addr(1), addr(2), None, 0.1,
-                                    addr(3), addr(4), addr(5), 1e-6, addr(Z), addr(7),
+                                    addr(3), addr(4), addr(5), 1e-6, None if Z is None else addr(Z), addr(7),
                                     None if ws is None else addr(ws), wsb, None)
 
 
@@ -201,8 +201,11 @@ def test_block_rejections(lib):
     assert block_call(lib, Z=0) == E                              # Z overlaps Q
     assert block_call(lib, d=64, b=16, N=64) == U                 # small-b combinations have no block path
     assert block_call(lib, kind=1) == U
-    assert block_call(lib, d=64, b=256, N=1024) == U              # block outputs: chunk-parallel kernels only
-    assert block_call(lib, N=32040) == U                         # N not a multiple of 128
+    # other large-chunk shapes run the generic kernel's block mode: no workspace
+    # (not called here: a valid call launches)
+    assert lib.ttt_linear_fwd_block_workspace_bytes(0, 0, 1, 1, 16, 32040, 128, 2048) == 0
+    assert lib.ttt_linear_fwd_block_workspace_bytes(1, 0, 0, 2, 3, 1000, 64, 256) == 0
+    assert block_call(lib, d=64, b=256, N=1024, Z=None) == E     # validation still comes first
     assert block_call(lib) == binding.TTT_ERR_WORKSPACE_TOO_SMALL
     Wb = lib.ttt_linear_fwd_block_workspace_bytes
     assert Wb(0, 0, 1, 1, 16, 32768, 128, 2048) == lib.ttt_linear_fwd_workspace_bytes(0, 1, 1, 16, 32768, 128, 2048)

@@ -63,6 +63,30 @@ def test_block_workload_all_units(apply):
     check_all_units(f"{inp.wl.name} {apply}", [("Z", z, zr), ("W_end", w, wr)], TOL["bf16"])
 
 
+@pytest.mark.parametrize("apply", ["before", "after"])
+@pytest.mark.parametrize("dtype,d,B,H,N,b,eta", [
+    ("bf16", 64, 1, 2, 1000, 256, "sigmoid"),    # d = 64, ragged N
+    ("f32", 128, 1, 1, 700, 256, "const"),       # fp32 streams
+    ("f32", 64, 2, 1, 300, 100, "sigmoid"),      # b not a multiple of 16, blocks of 64 + 36
+    ("bf16", 128, 1, 1, 32040, 2048, "const"),   # the benchmark's b with N not a multiple of 128
+    ("bf16", 128, 1, 2, 400, 1000, "sigmoid"),   # a single, partial chunk
+    ("f32", 64, 1, 1, 65, 65, "const"),          # the shortest large chunk, one token past a block
+])
+def test_block_generic_shapes(apply, dtype, d, B, H, N, b, eta):
+    """Large-chunk shapes outside the chunk-parallel kernels run the generic
+    kernel's block mode; the block-causal outputs against the oracle."""
+    std = 1.0 / np.sqrt(d) if dtype == "f32" else 1.0
+    wl = wlm.Workload(f"blkg_{dtype}_d{d}_{B}x{H}x{N}_b{b}_{eta}", "plain", dtype, B, H, N, d, b, eta, 0.01,
+                      qkv_std=std, l2_rows=(dtype == "bf16"))
+    inp = wlm.generate(wl, 17)
+    say(f"case {wl.name} apply={apply}")
+    z, w = gpu_linear_block(inp, apply)
+    zr, wr = oracle_linear(inp, MODES[apply])
+    ez, ew = rel_err(z, zr), rel_err(w, wr)
+    say(f"  err Z {ez:.2e}  W_end {ew:.2e}  (tol {TOL[dtype]:.0e})")
+    assert ez <= TOL[dtype] and ew <= TOL[dtype]
+
+
 def dec(kind, dtype, B, H, N, eta, seed):
     wl = wlm.Workload(f"dec_{kind}_{dtype}_{B}x{H}x{N}_{eta}", kind, dtype, B, H, N, 64, 1, eta, 0.1)
     return wlm.generate(wl, seed)

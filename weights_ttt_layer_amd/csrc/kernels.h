@@ -50,8 +50,9 @@ hipError_t launch_smallb_linear(const LinearArgs& a, hipStream_t stream);
 // with 1 <= b <= 64, fp32 or bf16 streams.
 hipError_t launch_midb_linear(const LinearArgs& a, hipStream_t stream);
 // Plain f with chunks longer than 64 tokens, d = 64 or 128, fp32 or bf16 streams,
-// any N: the same kernel in blocks of 64 tokens (no workspace).
-hipError_t launch_midb_linear_blocks(const LinearArgs& a, hipStream_t stream);
+// any N: the same kernel in blocks of 64 tokens (no workspace). `outputs` is an
+// LC_OUT_* value (below): the dual form's outputs or a block-causal mode.
+hipError_t launch_midb_linear_blocks(const LinearArgs& a, int outputs, hipStream_t stream);
 // bf16 token streams: the chain-on-one-wave kernel (smallb_chain.hip)
 hipError_t launch_smallb_chain(const LinearArgs& a, hipStream_t stream);
 // The same kernel on two-term streams: Q, K, V each a bf16 hi plane [B,H,N,d]

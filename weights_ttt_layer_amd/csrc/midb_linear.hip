@@ -154,7 +154,14 @@ __device__ __forceinline__ void wave_lds_sync()
 // already holds the updates of the chunk's earlier blocks, and W' takes the
 // block's update; W' is W_{c+1} once the chunk ends. (The dual form's causal
 // sum over the chunk, split at block boundaries by associativity.)
-template <int D, int NG, int KIND, typename S, bool BIG>
+// APPLY (BIG only): the block-causal outputs of page "Test-Time Training Done
+// Right" (abstract) instead of the dual form's: every output of chunk c is
+// f(Q; W_c) (APPLY_BEFORE: the products with Q take W_c, no causal term) or
+// f(Q; W_{c+1}) (APPLY_AFTER: once the chunk's last block has stepped the
+// state, its Q rows are read again, block by block, against W_{c+1}).
+enum { APPLY_DUAL = 0, APPLY_BEFORE = 1, APPLY_AFTER = 2 };
+
+template <int D, int NG, int KIND, typename S, bool BIG, int APPLY>
 __global__ void __launch_bounds__(MB_THREADS)
 midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __restrict__ Kg,
                    const S* __restrict__ Vg, const float* __restrict__ etag, float eta_const,
@@ -163,6 +170,7 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
 {
     using G = MidGeom<D, NG, S>;
     static_assert(!BIG || KIND == 0, "blocks of a longer chunk: plain f only");
+    static_assert(APPLY == APPLY_DUAL || BIG, "block-causal outputs: blocks of a longer chunk");
     constexpr int CT = D / 64;          // column tiles per wave
     constexpr int RT = D / 16;          // row tiles of the state
     constexpr int KS = D / 32;          // 16x16x32 steps over the features
@@ -270,9 +278,11 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
         for (int t = 0; t < CT; ++t) {
             // column tile t of W_c as operand terms: lane (g, n) holds W[32p + 4g + i (+16)][64t + 16w + n]
             // (BIG: Wb is the running state W' for the outputs, Wg the chunk-start W_c for the gradient)
-            bf16x8 Wb[KS][TS];
+            bf16x8 Wb[APPLY == APPLY_DUAL ? KS : 1][TS];
+            if constexpr (APPLY == APPLY_DUAL) {
 #pragma unroll
-            for (int p = 0; p < KS; ++p) b8_from_acc<TS>(Wacc[2 * p][t], Wacc[2 * p + 1][t], Wb[p]);
+                for (int p = 0; p < KS; ++p) b8_from_acc<TS>(Wacc[2 * p][t], Wacc[2 * p + 1][t], Wb[p]);
+            }
             bf16x8 Wg[BIG ? KS : 1][TS];
             if constexpr (BIG) {
 #pragma unroll
@@ -288,13 +298,16 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
                     bf16x8 qa[TIN], ka[TIN];
                     load_a8<S, TIN>(sm.q + o, sm.q + o + 16, qa);
                     load_a8<S, TIN>(sm.k + o, sm.k + o + 16, ka);
-                    hqT[j][t] = mma32_terms<TS, TIN>(hqT[j][t], Wb[p], qa);
+                    if constexpr (APPLY == APPLY_DUAL)
+                        hqT[j][t] = mma32_terms<TS, TIN>(hqT[j][t], Wb[p], qa);
+                    else if constexpr (APPLY == APPLY_BEFORE)
+                        hqT[j][t] = mma32_terms<TS, TIN>(hqT[j][t], Wg[p], qa);
                     if constexpr (KIND == 1)
                         hk[j][t] = mma32_terms<TS, TIN>(hk[j][t], Wb[p], ka);
                     else if constexpr (BIG)
                         hk[j][t] = mma32_terms<TIN, TS>(hk[j][t], ka, Wg[p]);
                     else
-                        hk[j][t] = mma32_terms<TIN, TS>(hk[j][t], ka, Wb[p]);
+                        hk[j][t] = mma32_terms<TIN, TS>(hk[j][t], ka, Wb[APPLY == APPLY_DUAL ? p : 0]);
                 }
             }
         }
@@ -405,7 +418,7 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
 
         // ======== causal term: H_Q^T(group jq) -= sum_{jk <= jq} Gt_jk^T tril(S)^T ========
 #pragma unroll
-        for (int jq = 0; jq < NG; ++jq)
+        for (int jq = 0; jq < (APPLY == APPLY_DUAL ? NG : 0); ++jq)
 #pragma unroll
             for (int jk = 0; jk <= jq; ++jk) {
                 // S^T block: lane (g, n) holds S[query 16jq + n][key 16jk + 4g + i] = q . k
@@ -440,7 +453,46 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
             }
 
         // ======== outputs ========
-        if constexpr (KIND == 0) {
+        if constexpr (APPLY == APPLY_AFTER) {
+            // the chunk's outputs once its last block has stepped the state
+            if (c1 % b == 0 || c1 == N) {
+                __syncthreads();                   // every wave is done with this block's stage
+                const int cs = (c0 / b) * b;       // the chunk's first row
+                for (int r0 = cs; r0 < c1; r0 += G::ROWS) {
+                    const int rows = min(G::ROWS, c1 - r0);
+                    for (int idx = tid; idx < G::ROWS * G::PIECES; idx += MB_THREADS) {
+                        const int row = idx / G::PIECES, piece = idx - row * G::PIECES;
+                        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+                        if (row < rows)
+                            val = *reinterpret_cast<const uint4*>(Qu + (size_t)(r0 + row) * D +
+                                                                  piece * (16 / (int)sizeof(S)));
+                        *reinterpret_cast<uint4*>(sm.q + row * G::STRIDE + piece * (16 / (int)sizeof(S))) = val;
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int t = 0; t < CT; ++t) {
+                        bf16x8 Wn[KS][TS];         // W_{c+1}
+#pragma unroll
+                        for (int p = 0; p < KS; ++p) b8_from_acc<TS>(Wacc[2 * p][t], Wacc[2 * p + 1][t], Wn[p]);
+#pragma unroll
+                        for (int j = 0; j < NG; ++j) {
+                            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int p = 0; p < KS; ++p) {
+                                const int o = (16 * j + n) * ST + 32 * p + 4 * g;
+                                bf16x8 qa[TIN];
+                                load_a8<S, TIN>(sm.q + o, sm.q + o + 16, qa);
+                                acc = mma32_terms<TS, TIN>(acc, Wn[p], qa);
+                            }
+                            if (16 * j + n < rows)
+                                *reinterpret_cast<float4*>(Zu + (size_t)(r0 + 16 * j + n) * D + 64 * t + 16 * w +
+                                                           4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                        }
+                    }
+                    __syncthreads();               // the stage's Q rows are read again
+                }
+            }
+        } else if constexpr (KIND == 0) {
 #pragma unroll
             for (int j = 0; j < NG; ++j)
                 if (16 * j + n < bc)
@@ -519,10 +571,11 @@ midb_linear_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __res
             }
 }
 
-template <int D, int NG, int KIND, typename S, bool BIG>
+template <int D, int NG, int KIND, typename S, bool BIG, int APPLY = APPLY_DUAL>
 hipError_t launch_one(const LinearArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((midb_linear_kernel<D, NG, KIND, S, BIG>), dim3(a.B * a.H), dim3(MB_THREADS), 0, stream, a.H,
+    hipLaunchKernelGGL((midb_linear_kernel<D, NG, KIND, S, BIG, APPLY>), dim3(a.B * a.H), dim3(MB_THREADS), 0, stream,
+                       a.H,
                        a.N, a.b, static_cast<const S*>(a.Q), static_cast<const S*>(a.K), static_cast<const S*>(a.V),
                        a.eta, a.eta_const, a.W0, a.gamma, a.beta, a.eps, a.Z, a.W_end);
     return hipGetLastError();
@@ -544,14 +597,23 @@ hipError_t launch_groups(const LinearArgs& a, hipStream_t stream)
     return launch_kind<D, 4, S>(a, stream);
 }
 
-}  // namespace
-
-hipError_t launch_midb_linear_blocks(const LinearArgs& a, hipStream_t stream)
+template <int APPLY>
+hipError_t launch_blocks(const LinearArgs& a, hipStream_t stream)
 {
     if (a.d == 128)
-        return a.dtype == 1 ? launch_one<128, 4, 0, uint16_t, true>(a, stream)
-                            : launch_one<128, 4, 0, float, true>(a, stream);
-    return a.dtype == 1 ? launch_one<64, 4, 0, uint16_t, true>(a, stream) : launch_one<64, 4, 0, float, true>(a, stream);
+        return a.dtype == 1 ? launch_one<128, 4, 0, uint16_t, true, APPLY>(a, stream)
+                            : launch_one<128, 4, 0, float, true, APPLY>(a, stream);
+    return a.dtype == 1 ? launch_one<64, 4, 0, uint16_t, true, APPLY>(a, stream)
+                        : launch_one<64, 4, 0, float, true, APPLY>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_midb_linear_blocks(const LinearArgs& a, int outputs, hipStream_t stream)
+{
+    if (outputs == LC_OUT_BEFORE) return launch_blocks<APPLY_BEFORE>(a, stream);
+    if (outputs == LC_OUT_AFTER) return launch_blocks<APPLY_AFTER>(a, stream);
+    return launch_blocks<APPLY_DUAL>(a, stream);
 }
 
 hipError_t launch_midb_linear(const LinearArgs& a, hipStream_t stream)

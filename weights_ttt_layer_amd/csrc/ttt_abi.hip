@@ -175,7 +175,7 @@ int ttt_linear_fwd(int kind, int qkv_dtype, int B, int H, int N, int d, int b, c
     else if (fast_large(qkv_dtype, d, b, N))
         err = ttt::launch_large_chunk_linear(a, ttt::LC_OUT_DUAL, stream);
     else
-        err = ttt::launch_midb_linear_blocks(a, stream);
+        err = ttt::launch_midb_linear_blocks(a, ttt::LC_OUT_DUAL, stream);
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
@@ -196,10 +196,11 @@ int ttt_linear_fwd_block(int apply, int kind, int qkv_dtype, int B, int H, int N
     const int st = check_linear(kind, qkv_dtype, B, H, N, d, b, Q, K, V, eta, eta_const, W0, ln_gamma, ln_beta,
                                 ln_eps, Z, W_end, workspace, workspace_bytes, a, path);
     if (st != TTT_OK) return st;
-    if (path != TTT_PATH_LARGE_CHUNK || !fast_large(qkv_dtype, d, b, N)) return TTT_ERR_UNSUPPORTED;
-    const hipError_t err = ttt::launch_large_chunk_linear(
-        a, apply == TTT_APPLY_BEFORE_STEP ? ttt::LC_OUT_BEFORE : ttt::LC_OUT_AFTER,
-        reinterpret_cast<hipStream_t>(hip_stream));
+    if (path != TTT_PATH_LARGE_CHUNK) return TTT_ERR_UNSUPPORTED;
+    const int outputs = apply == TTT_APPLY_BEFORE_STEP ? ttt::LC_OUT_BEFORE : ttt::LC_OUT_AFTER;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    const hipError_t err = fast_large(qkv_dtype, d, b, N) ? ttt::launch_large_chunk_linear(a, outputs, stream)
+                                                          : ttt::launch_midb_linear_blocks(a, outputs, stream);
     return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
@@ -566,7 +567,7 @@ extern "C" int ttt_linear_fwd_noalloc(int kind, int qkv_dtype, int B, int H, int
     if (path == TTT_PATH_SMALL_B) {
         err = ttt::launch_smallb_linear(a, stream);
     } else if (!fast_large(qkv_dtype, d, b, N)) {
-        err = ttt::launch_midb_linear_blocks(a, stream);
+        err = ttt::launch_midb_linear_blocks(a, ttt::LC_OUT_DUAL, stream);
     } else {
         void* ptr = nullptr;
         err = scratch_on_current_device(&ptr);
