@@ -24,7 +24,9 @@
 //
 // One workgroup of eleven waves per (sequence, head) unit. Waves are placed on
 // the four SIMDs round-robin, so waves 4 and 8 share the chain's SIMD; they get
-// the light roles.
+// the light roles. A state wave issues more per chunk than an output wave, so
+// SIMD 3 (waves 3, 7) takes two state waves and SIMDs 1, 2 one state and two
+// output waves each.
 //  * wave 0, the chain: X^T = A^T + (-Gt_prev)^T P^T (v_mfma_f32_16x16x16_bf16,
 //    four 16-feature tiles). Its C layout holds ONE token per lane (lane
 //    (g, n): token n, features 16t + 4g + i), so a row statistic is 15 in-lane
@@ -33,12 +35,12 @@
 //    product. Everything it needs for a chunk except A arrives a chunk early
 //    and is read before the barrier; it runs at raised wave priority and
 //    touches no global memory.
-//  * waves 1, 2, 3, 5, the state: the wave of tile b keeps W[:, 16b..16b+16)
+//  * waves 1, 2, 3, 7, the state: the wave of tile b keeps W[:, 16b..16b+16)
 //    in fp32 MFMA accumulators (C layout, rows = input features) and per chunk
 //    computes W += K^T (-Gt) (16x16x32, the two terms of Gt stacked along k),
 //    the A^T tile b of the next chunk and the Q W part of H_Q^T tile b (W^T as
 //    the A operand, k in a permuted order that the B operand reads to match).
-//  * waves 6, 7, 9, 10, the outputs: the wave of tile b adds the causal term
+//  * waves 5, 6, 9, 10, the outputs: the wave of tile b adds the causal term
 //    -Gt^T tril(S)^T to H_Q^T tile b and forms the output rows of its 16
 //    features.
 //  * wave 4 issues every global->LDS load of the Q/K/V/eta ring (its
@@ -708,11 +710,11 @@ smallb_chain_kernel(int H, int N, int b, size_t plane, const uint16_t* __restric
                              Vg + unit * (size_t)N * D, PT ? etag + unit * (size_t)N : nullptr);
     } else if (w == 8) {
         resid_role<KIND, TIN>(sm, lane, h, C, gamma, beta);
-    } else if (w <= 5) {
-        const int bt = (w == 5) ? 3 : w - 1;
+    } else if (w <= 3 || w == 7) {
+        const int bt = (w == 7) ? 3 : w - 1;
         w_role<KIND, TIN>(sm, bt, lane, C, W0 + unit * (size_t)D * D, Wend + unit * (size_t)D * D);
     } else {
-        const int bt = (w <= 7) ? w - 6 : w - 7;
+        const int bt = (w <= 6) ? w - 5 : w - 7;
         out_role<KIND, TIN>(sm, bt, lane, h, N, b, C, gamma, beta, eps, Zg + unit * (size_t)N * D);
     }
 }
