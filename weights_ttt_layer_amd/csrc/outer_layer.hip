@@ -10,10 +10,12 @@
 // Three kernels:
 //  * layer_gemm_kernel<.., EPI_QKV>: [Q | K | V] = x [W_Q; W_K; W_V]^T on bf16
 //    MFMA with fp32 accumulation. Each wave owns 64 tokens x 64 outputs = one
-//    head of one projection, so the key normalisation is a reduction inside
-//    the wave; Q, K, V leave head-major [B, H, N, 64] as two bf16 planes each
-//    (the RNE rounding, then the rounding of the remainder: 16 significant
-//    bits), the form in which the inner kernel consumes two-term streams.
+//    head of one projection, taken as the transposed tile (a lane holds
+//    consecutive outputs of one token), so the key normalisation is an in-lane
+//    sum plus one lane swap; Q, K, V leave head-major [B, H, N, 64] as two bf16
+//    planes each (the RNE rounding, then the rounding of the remainder: 16
+//    significant bits), the form in which the inner kernel consumes two-term
+//    streams, staged through LDS so that every store writes whole head rows.
 //  * layer_outprep_kernel: A = LayerNorm(z) * gamma_o + beta_o + q per (token,
 //    head) row, written token-major as two bf16 terms (16 significant bits).
 //  * layer_gemm_kernel<.., EPI_ROWS>: y = [A_hi | A_lo] [W_O | W_O]^T, i.e. the
@@ -119,7 +121,8 @@ layer_gemm_kernel(GemmArgs g)
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int ins = w + NW * j;
-        const bool b = ins >= NIA;
+        // with NIA a multiple of NW, whether instruction j loads the weight does not depend on w
+        const bool b = (NIA % NW == 0) ? (NW * j >= NIA) : (ins >= NIA);
         const int r = (b ? ins - NIA : ins) * 16 + (lane >> 2);
         const int p = (lane & 3) ^ ((r >> 2) & 3);
         if (!b) {
@@ -181,57 +184,72 @@ layer_gemm_kernel(GemmArgs g)
 #pragma unroll
             for (int c = 0; c < 2; ++c)
                 bv[c] = *reinterpret_cast<const bf16x8*>(Bt + psw(64 * wc + 32 * c + l32, p));
+            // EPI_QKV takes the transposed tiles (rows = outputs, columns = tokens), so
+            // a lane holds consecutive outputs of one token
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
-                for (int c = 0; c < 2; ++c) acc[a][c] = mfma_32x32x16(av[a], bv[c], acc[a][c]);
+                for (int c = 0; c < 2; ++c)
+                    acc[a][c] = EPI == EPI_QKV ? mfma_32x32x16(bv[c], av[a], acc[a][c])
+                                               : mfma_32x32x16(av[a], bv[c], acc[a][c]);
         }
     }
 
-    const int nw = n0 + 64 * wc;                 // this wave's first output
-    if (nw >= g.n_out) return;
+    const int nw = n0 + 64 * wc;                 // this wave's first output (n_out is a multiple of 64)
     if (EPI == EPI_QKV) {
-        // The wave's 64 outputs are one head of one projection.
+        // acc[a][c] slot 4q + j: token 64 wr + 32 a + l32 of the tile, output nw + 32 c + 8 q + 4 h + j.
+        // The wave's 64 outputs are one head of one projection. Each plane of its
+        // 64 x 64 block goes through an 8 KB LDS buffer of its own ([token][output],
+        // 16-byte pieces swizzled by token), so that the global stores are whole
+        // 128-byte head rows, eight per instruction.
+        static_assert(NS * (SA + SB) >= NW * 8192, "the stage buffers hold the output staging");
+        __syncthreads();                             // every wave is done with the stage buffers
+        if (nw >= g.n_out) return;
         const int which = nw / g.rows_per_w, head = (nw - which * g.rows_per_w) / HDIM;
-        uint16_t* out = g.qkv[which];
-        float scale[2][16];
+        uint16_t* ob = g.qkv[which] + ((size_t)bi * g.H + head) * (size_t)g.N * HDIM;
+        // per 32-token half a: both planes of the half through the wave's 8 KB
+        // (high terms at 0, low terms at 4 KB)
+        char* wb = smem + w * 8192;
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a) {
+            float sc = 1.f;
+            if (which == 1) {
+                // k / ||k||: this lane holds 32 of the row's 64 entries, lane l ^ 32 the rest
+                float s = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) scale[a][i] = 1.f;
-        if (which == 1) {
-            // k / ||k||: the row's 64 entries sit in the 32 lanes of this half
-            // (two column tiles per lane).
+                for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+                    for (int i = 0; i < 16; ++i) s = fmaf(acc[a][c][i], acc[a][c][i], s);
+                s += __shfl_xor(s, 32, 64);
+                sc = s > 0.f ? 1.f / sqrtf(s) : 0.f;
+            }
+            const int r = l32;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float s = acc[a][0][i] * acc[a][0][i] + acc[a][1][i] * acc[a][1][i];
-                    s = row16_sum(s);
-                    s += __shfl_xor(s, 16, 64);
-                    scale[a][i] = s > 0.f ? 1.f / sqrtf(s) : 0.f;
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // two bf16 terms: RNE rounding, then the rounding of the remainder
+                    uint32_t p01[2], p23[2];
+                    split_pair<2>(acc[a][c][4 * q] * sc, acc[a][c][4 * q + 1] * sc, p01);
+                    split_pair<2>(acc[a][c][4 * q + 2] * sc, acc[a][c][4 * q + 3] * sc, p23);
+                    const int off = r * 128 + (((4 * c + q) ^ (r & 7)) << 4) + 8 * h;
+                    *reinterpret_cast<uint2*>(wb + off) = make_uint2(p01[0], p23[0]);
+                    *reinterpret_cast<uint2*>(wb + 4096 + off) = make_uint2(p01[1], p23[1]);
+                }
+            // the same wave reads back (its LDS operations are ordered): lane L takes
+            // piece L % 8 of token row 8 j + L / 8 of the half, in each plane
+#pragma unroll
+            for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rr = 8 * j + (lane >> 3), k = lane & 7;
+                    const uint4 v = *reinterpret_cast<const uint4*>(wb + 4096 * pl + rr * 128 + ((k ^ (rr & 7)) << 4));
+                    const int t = t0 + 64 * wr + 32 * a + rr;
+                    if (t < g.N) *reinterpret_cast<uint4*>(ob + (pl ? g.plane : 0) + (size_t)t * HDIM + 8 * k) = v;
                 }
         }
-        uint16_t* ob = out + ((size_t)bi * g.H + head) * (size_t)g.N * HDIM;
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = t0 + 64 * wr + 32 * a + crow(i, h);
-                if (t < g.N) {
-                    uint16_t* row = ob + (size_t)t * HDIM + l32;
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        // two bf16 terms: RNE rounding, then the rounding of the remainder
-                        const float v = acc[a][c][i] * scale[a][i];
-                        const __bf16 hi = (__bf16)v;
-                        const __bf16 lo = (__bf16)(v - (float)hi);
-                        row[32 * c] = __builtin_bit_cast(uint16_t, hi);
-                        row[32 * c + g.plane] = __builtin_bit_cast(uint16_t, lo);
-                    }
-                }
-            }
     } else {
+        if (nw >= g.n_out) return;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int n = nw + 32 * c + l32;
