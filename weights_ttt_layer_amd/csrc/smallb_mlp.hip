@@ -26,16 +26,21 @@
 //  * H^T = W2^T X2^T takes the W2 tiles as A operand and X2^T straight from the
 //    registers as B operand (the C layout of a transposed product is the B
 //    operand of the next one, up to a fixed permutation of k); its four
-//    slice-partials meet in LDS. Every wave then holds all of H^T and runs the
-//    LayerNorm forward and backward itself (no further exchange).
+//    slice-partials meet in LDS. Wave w sums them for tokens 4w .. 4w + 3 only,
+//    one token per DPP row of 16 lanes (four features a lane), runs the
+//    LayerNorm forward and backward there and writes G2 and the -eta G2 terms
+//    to LDS; after a barrier every wave reads G2 back in its own layout.
 //  * G1^T = (W2 G2^T) * GELU'(A)^T and the output-side H_Q^T, S2^T = X2 X2_Q^T
-//    likewise; S2^T's slice-partials meet in LDS with H_Q^T's.
+//    likewise; S2^T's slice-partials meet in LDS with H_Q^T's. Wave w completes
+//    H_Q^T tile w (output features 16w .. 16w + 15) and its part of the output
+//    LayerNorm sums; the four parts meet in LDS behind a barrier.
 //  * Products over tokens (the causal terms and the state updates) need the
-//    token index along k: -Gt1, -Gt2 and X2 are written as bf16 terms to
-//    wave-private [token][feature] LDS tiles and read back with the transpose
-//    read ds_read_b64_tr_b16.
-// Two workgroup barriers per chunk (the H and the H_Q/S2 partial sums); the
-// next chunk is staged into the other LDS buffer between them.
+//    token index along k: -Gt1 and X2 are written as bf16 terms to wave-private
+//    [token][feature] LDS tiles, -Gt2 to one shared tile, and read back with
+//    the transpose read ds_read_b64_tr_b16.
+// Four workgroup barriers per chunk (the H partials, G2, the H_Q/S2 partials,
+// the output LayerNorm sums); the next chunk is staged into the other LDS
+// buffer after the first.
 //
 // W2 is carried with each row's mean over the output features removed (a row
 // of W2 belongs to one wave, so the means are wave-local): LayerNorm ignores a
@@ -107,7 +112,9 @@ struct alignas(16) MlpSmem {
     float4 s2p[4][64];              // S2^T slice-partials
     uint16_t x2t[4][TS][16 * 64];   // per wave: X2 terms, [token][hidden of the slice]
     uint16_t g1t[4][TS][16 * 64];   // per wave: -Gt1 terms, [token][hidden of the slice]
-    uint16_t g2t[4][TS][16 * 64];   // per wave: -Gt2 terms, [token][output feature]
+    uint16_t g2t[TS][16 * 64];      // -Gt2 terms, [token][output feature]
+    float4 g2s[16][16];             // G2 (fp32), [token][output features 4j .. 4j + 3]
+    float2 xs[16][4];               // output LayerNorm partial sums [token][wave]
     float w2m[4][64];               // row means of W2_0 over the output features
     float4 gb[2][4][4];             // LayerNorm gamma, beta: [which][output tile][g]
 };
@@ -264,68 +271,63 @@ smallb_mlp_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
             if (c + 2 < nchunks) load_chunk<S, PPT>(pf, pe, c + 2, b, N, tid, Qu, Ku, Vu, etau, eta_const);
         }
         const float eta_n = st.eta[n];
-        // H^T (all output features) and the LayerNorm forward / backward of token n
-        float g2[4][4];
+        // LayerNorm forward / backward of H, four tokens per wave: lane l takes
+        // token tk = 4w + l / 16 and output features f0 .. f0 + 3 (f0 = 4 (l % 16)),
+        // so the 16 lanes of a DPP row hold one token's 64 features. G2 and the
+        // -eta G2 terms go to LDS, from where every wave takes G2 in its layout.
         {
-            float hv[4][4];
+            const int tk = 4 * w + (lane >> 4), f0 = 4 * (lane & 15);
+            const int o = f0 >> 4, gq = (f0 >> 2) & 3;
+            float4 hs = sm.hp[0][o][16 * gq + tk];
 #pragma unroll
-            for (int o = 0; o < 4; ++o) {
-                float4 s = sm.hp[0][o][lane];
-#pragma unroll
-                for (int ww = 1; ww < 4; ++ww) {
-                    const float4 u = sm.hp[ww][o][lane];
-                    s = make_float4(s.x + u.x, s.y + u.y, s.z + u.z, s.w + u.w);
-                }
-                hv[o][0] = s.x;
-                hv[o][1] = s.y;
-                hv[o][2] = s.z;
-                hv[o][3] = s.w;
+            for (int ww = 1; ww < 4; ++ww) {
+                const float4 u = sm.hp[ww][o][16 * gq + tk];
+                hs = make_float4(hs.x + u.x, hs.y + u.y, hs.z + u.z, hs.w + u.w);
             }
-            float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-            for (int o = 0; o < 4; ++o)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    s1 += hv[o][i];
-                    s2 = fmaf(hv[o][i], hv[o][i], s2);
-                }
-            xrow4_sum2(s1, s2);
+            const float hv[4] = {hs.x, hs.y, hs.z, hs.w};
+            float s1 = (hv[0] + hv[1]) + (hv[2] + hv[3]);
+            float s2 = fmaf(hv[0], hv[0], hv[1] * hv[1]) + fmaf(hv[2], hv[2], hv[3] * hv[3]);
+            s1 = row16_sum(s1);
+            s2 = row16_sum(s2);
             const float mu = s1 * (1.f / D);
             const float rs = __builtin_amdgcn_rsqf(fmaxf(s2 * (1.f / D) - mu * mu, 0.f) + eps);
-            float xh[4][4], dx[4][4], u1 = 0.f, u2 = 0.f;
+            const float4 kk = load4_f32<S>(st.k + tk * STRIDE + f0);
+            const float4 vv = load4_f32<S>(st.v + tk * STRIDE + f0);
+            const float4 ga = sm.gb[0][o][gq], be = sm.gb[1][o][gq];
+            const float kv[4] = {kk.x - vv.x, kk.y - vv.y, kk.z - vv.z, kk.w - vv.w};
+            const float gam[4] = {ga.x, ga.y, ga.z, ga.w}, bet[4] = {be.x, be.y, be.z, be.w};
+            float xh[4], dx[4], u1 = 0.f, u2 = 0.f;
 #pragma unroll
-            for (int o = 0; o < 4; ++o) {
-                const float4 kk = load4_f32<S>(st.k + n * STRIDE + 16 * o + 4 * g);
-                const float4 vv = load4_f32<S>(st.v + n * STRIDE + 16 * o + 4 * g);
-                const float4 ga = sm.gb[0][o][g], be = sm.gb[1][o][g];
-                const float kv[4] = {kk.x - vv.x, kk.y - vv.y, kk.z - vv.z, kk.w - vv.w};
-                const float gam[4] = {ga.x, ga.y, ga.z, ga.w}, bet[4] = {be.x, be.y, be.z, be.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    xh[o][i] = (hv[o][i] - mu) * rs;
-                    dx[o][i] = 2.f * gam[i] * (kv[i] + gam[i] * xh[o][i] + bet[i]);
-                    u1 += dx[o][i];
-                    u2 = fmaf(dx[o][i], xh[o][i], u2);
-                }
+            for (int i = 0; i < 4; ++i) {
+                xh[i] = (hv[i] - mu) * rs;
+                dx[i] = 2.f * gam[i] * (kv[i] + gam[i] * xh[i] + bet[i]);
+                u1 += dx[i];
+                u2 = fmaf(dx[i], xh[i], u2);
             }
-            xrow4_sum2(u1, u2);
+            u1 = row16_sum(u1);
+            u2 = row16_sum(u2);
             const float m1 = u1 * (1.f / D), m2 = u2 * (1.f / D);
+            float gv[4], y[4];
+            const float et = st.eta[tk];
 #pragma unroll
-            for (int o = 0; o < 4; ++o)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) g2[o][i] = (n < bc) ? rs * (dx[o][i] - m1 - xh[o][i] * m2) : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                gv[i] = (tk < bc) ? rs * (dx[i] - m1 - xh[i] * m2) : 0.f;
+                y[i] = -et * gv[i];
+            }
+            sm.g2s[tk][f0 >> 2] = make_float4(gv[0], gv[1], gv[2], gv[3]);
+            bf16x4 tmp[TS];
+            put4<TS>(sm.g2t, tk, f0, y, tmp);
         }
-        // G2^T as the k = output-feature operand; -Gt2 terms to this wave's tile
+        __syncthreads();
+        // G2^T as the k = output-feature operand (lane (g, n): token n, features 16o + 4g + i)
         bf16x8 g2b[2][TS];
         {
             bf16x4 q4[4][TS];
 #pragma unroll
             for (int o = 0; o < 4; ++o) {
-                const float x[4] = {g2[o][0], g2[o][1], g2[o][2], g2[o][3]};
+                const float4 v = sm.g2s[n][4 * o + g];
+                const float x[4] = {v.x, v.y, v.z, v.w};
                 terms4<TS>(x, q4[o]);
-                const float y[4] = {-eta_n * g2[o][0], -eta_n * g2[o][1], -eta_n * g2[o][2], -eta_n * g2[o][3]};
-                bf16x4 tmp[TS];
-                put4<TS>(sm.g2t[w], n, 16 * o + 4 * g, y, tmp);
             }
 #pragma unroll
             for (int p = 0; p < 2; ++p)
@@ -421,7 +423,7 @@ smallb_mlp_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
 #pragma unroll
         for (int o = 0; o < 4; ++o)
 #pragma unroll
-            for (int s = 0; s < TS; ++s) g2n[o][s] = tr4(sm.g2t[w][s], 4 * g + (n >> 2), 16 * o + 4 * (n & 3));
+            for (int s = 0; s < TS; ++s) g2n[o][s] = tr4(sm.g2t[s], 4 * g + (n >> 2), 16 * o + 4 * (n & 3));
         bf16x4 s2b[TS];
         {
             float4 s = sm.s2p[0][lane];
@@ -437,43 +439,39 @@ smallb_mlp_kernel(int H, int N, int b, const S* __restrict__ Qg, const S* __rest
             terms4<TS>(x, s2b);
         }
         {
-            f32x4 hq[4];
+            // wave w forms H_Q^T tile w (output features 16w .. 16w + 15) and its
+            // part of the output LayerNorm sums; the four parts meet in LDS
+            const int o = w;
+            float4 sq = sm.hqp[0][o][lane];
 #pragma unroll
-            for (int o = 0; o < 4; ++o) {
-                float4 s = sm.hqp[0][o][lane];
-#pragma unroll
-                for (int ww = 1; ww < 4; ++ww) {
-                    const float4 u = sm.hqp[ww][o][lane];
-                    s = make_float4(s.x + u.x, s.y + u.y, s.z + u.z, s.w + u.w);
-                }
-                hq[o] = f32x4{s.x, s.y, s.z, s.w};
-                hq[o] = mma16_terms<TS, TS>(hq[o], g2n[o], s2b);   // - Gt2^T tril(S2)^T
+            for (int ww = 1; ww < 4; ++ww) {
+                const float4 u = sm.hqp[ww][o][lane];
+                sq = make_float4(sq.x + u.x, sq.y + u.y, sq.z + u.z, sq.w + u.w);
             }
-            float s1 = 0.f, s2 = 0.f;
+            f32x4 hq = f32x4{sq.x, sq.y, sq.z, sq.w};
 #pragma unroll
-            for (int o = 0; o < 4; ++o)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    s1 += hq[o][i];
-                    s2 = fmaf(hq[o][i], hq[o][i], s2);
-                }
-            xrow4_sum2(s1, s2);
+            for (int oo = 0; oo < 4; ++oo)                 // static indices into g2n
+                if (oo == o) hq = mma16_terms<TS, TS>(hq, g2n[oo], s2b);   // - Gt2^T tril(S2)^T
+            float p1 = (hq[0] + hq[1]) + (hq[2] + hq[3]);
+            float p2 = fmaf(hq[0], hq[0], hq[1] * hq[1]) + fmaf(hq[2], hq[2], hq[3] * hq[3]);
+            xrow4_sum2(p1, p2);
+            if (g == 0) sm.xs[n][w] = make_float2(p1, p2);
+            __syncthreads();
+            const float2 x0 = sm.xs[n][0], x1 = sm.xs[n][1], x2 = sm.xs[n][2], x3 = sm.xs[n][3];
+            const float s1 = (x0.x + x1.x) + (x2.x + x3.x), s2 = (x0.y + x1.y) + (x2.y + x3.y);
             const float mu = s1 * (1.f / D);
             const float rs = __builtin_amdgcn_rsqf(fmaxf(s2 * (1.f / D) - mu * mu, 0.f) + eps);
-            // wave w writes output features 16w .. 16w + 15
+            if (n < bc) {
+                const float4 qq = load4_f32<S>(st.q + n * STRIDE + 16 * o + 4 * g);
+                const float4 ga = sm.gb[0][o][g], be = sm.gb[1][o][g];
+                const float qv[4] = {qq.x, qq.y, qq.z, qq.w};
+                const float gam[4] = {ga.x, ga.y, ga.z, ga.w}, bet[4] = {be.x, be.y, be.z, be.w};
+                float z[4];
 #pragma unroll
-            for (int o = 0; o < 4; ++o)
-                if (o == w && n < bc) {
-                    const float4 qq = load4_f32<S>(st.q + n * STRIDE + 16 * o + 4 * g);
-                    const float4 ga = sm.gb[0][o][g], be = sm.gb[1][o][g];
-                    const float qv[4] = {qq.x, qq.y, qq.z, qq.w};
-                    const float gam[4] = {ga.x, ga.y, ga.z, ga.w}, bet[4] = {be.x, be.y, be.z, be.w};
-                    float z[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) z[i] = qv[i] + gam[i] * ((hq[o][i] - mu) * rs) + bet[i];
-                    *reinterpret_cast<float4*>(Zu + (size_t)(c * b + n) * D + 16 * o + 4 * g) =
-                        make_float4(z[0], z[1], z[2], z[3]);
-                }
+                for (int i = 0; i < 4; ++i) z[i] = qv[i] + gam[i] * ((hq[i] - mu) * rs) + bet[i];
+                *reinterpret_cast<float4*>(Zu + (size_t)(c * b + n) * D + 16 * o + 4 * g) =
+                    make_float4(z[0], z[1], z[2], z[3]);
+            }
         }
         // W2 += X2^T (-Gt2),  W2^T += (-Gt2)^T X2  (X2[token 4g + j][hidden hs + 16a + n])
 #pragma unroll
