@@ -32,9 +32,12 @@
 //    (g, n): token n, features 16t + 4g + i), so a row statistic is 15 in-lane
 //    adds and lane swaps (two statistics share three swaps). It writes -Gt as two bf16 terms into LDS, where
 //    the transpose read hands it back as the A operand of the next chunk's
-//    product. Everything it needs for a chunk except A arrives a chunk early
-//    and is read before the barrier; it runs at raised wave priority and
-//    touches no global memory.
+//    product. Everything it needs for a chunk except A arrives a chunk early:
+//    P^T, the residual input and eta are read before it writes -Gt (their
+//    latency hides behind the splits), and the -Gt read-back stays in flight
+//    across the barrier, which waits only for what was issued before those
+//    eight reads. It runs at raised wave priority and touches no global
+//    memory.
 //  * waves 1, 2, 3, 7, the state: the wave of tile b keeps W[:, 16b..16b+16)
 //    in fp32 MFMA accumulators (C layout, rows = input features) and per chunk
 //    computes W += K^T (-Gt) (16x16x32, the two terms of Gt stacked along k),
@@ -208,19 +211,11 @@ struct ChainPre {
 };
 
 template <int TIN, bool PT>
-__device__ __forceinline__ void chain_prefetch(const ChainSmem<TIN>& sm, int c, int bc, int g, int n, int lane,
+__device__ __forceinline__ void chain_read_ops(const ChainSmem<TIN>& sm, int c, int g, int n, int lane,
                                                float eta_const, ChainPre& pre)
 {
     const int par = c & 1;
     if (c > 0) {
-        const uint16_t* g0 = sm.gt[par ^ 1][0];
-        const uint16_t* g1 = sm.gt[par ^ 1][1];
-        const int row = 4 * g + (n >> 2);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            pre.ga0[t] = tr4(g0, row, 16 * t + 4 * (n & 3));
-            pre.ga1[t] = tr4(g1, row, 16 * t + 4 * (n & 3));
-        }
         pre.pb0 = __builtin_bit_cast(bf16x4, sm.xp[par][0][lane]);
         pre.pb1 = __builtin_bit_cast(bf16x4, sm.xp[par][1][lane]);
     }
@@ -232,16 +227,41 @@ __device__ __forceinline__ void chain_prefetch(const ChainSmem<TIN>& sm, int c, 
         pre.cp[4 * t + 2] = r.z;
         pre.cp[4 * t + 3] = r.w;
     }
-    float eta = eta_const;
-    if constexpr (PT) eta = sm.ring[c % RingGeom<TIN>::SLOTS].eta[n];
-    pre.eta = (n < bc) ? eta : 0.f;
+    // rows past the sequence's end are masked where eta is used
+    pre.eta = eta_const;
+    if constexpr (PT) pre.eta = sm.ring[c % RingGeom<TIN>::SLOTS].eta[n];
+}
+
+// -Gt_c (written by the chain itself) as the A operands of step c + 1.
+template <int TIN>
+__device__ __forceinline__ void chain_read_ga(const ChainSmem<TIN>& sm, int c, int g, int n, ChainPre& pre)
+{
+    const uint16_t* g0 = sm.gt[c & 1][0];
+    const uint16_t* g1 = sm.gt[c & 1][1];
+    const int row = 4 * g + (n >> 2);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        pre.ga0[t] = tr4(g0, row, 16 * t + 4 * (n & 3));
+        pre.ga1[t] = tr4(g1, row, 16 * t + 4 * (n & 3));
+    }
+}
+
+// The chain's barrier with its eight -Gt reads in flight: LDS operations of one
+// wave complete in order, so at most eight outstanding means everything before
+// them (its -Gt writes, the other operand reads) is done. The reads only touch
+// the -Gt buffer of this chunk, which no wave writes before the chain itself
+// does two chunks later.
+__device__ __forceinline__ void chain_barrier_ga_pending()
+{
+    asm volatile("s_waitcnt lgkmcnt(8)\n\ts_barrier" ::: "memory");
 }
 
 // One chain step: -Gt_c from A_c^T and the prefetched operands.
-template <int KIND, int TIN>
-__device__ __forceinline__ void chain_step(ChainSmem<TIN>& sm, int c, int g, int n, int lane, const ChainPre& pre,
-                                           const float (&g2)[16], float eps)
+template <int KIND, int TIN, bool PT>
+__device__ __forceinline__ void chain_step(ChainSmem<TIN>& sm, int c, int C, int N, int b, int g, int n, int lane,
+                                           ChainPre& pre, float eta_const, const float (&g2)[16], float eps)
 {
+    const float eta_c = (n < min(b, N - c * b)) ? pre.eta : 0.f;
     const int par = c & 1;
     f32x4 acc[4];
 #pragma unroll
@@ -252,6 +272,7 @@ __device__ __forceinline__ void chain_step(ChainSmem<TIN>& sm, int c, int g, int
         acc[t][2] = a.z;
         acc[t][3] = a.w;
     }
+    __builtin_amdgcn_sched_barrier(0);   // the four reads go out together
     if (c > 0) {
         // X^T += (-Gt_{c-1})^T P_c^T : A = -Gt^T tile t (k = tokens of c-1), B = P^T
 #pragma unroll
@@ -287,18 +308,24 @@ __device__ __forceinline__ void chain_step(ChainSmem<TIN>& sm, int c, int g, int
         }
         xrow4_sum2(u1, u2);
         // -eta rs (dx - mean(dx) - xh mean(dx xh))
-        const float sc = -pre.eta * rs;
+        const float sc = -eta_c * rs;
         const float ca = -(u2 * (1.f / D)) * sc;
         const float cb = -(u1 * (1.f / D)) * sc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) ng[j] = fmaf(xh[j], ca, fmaf(dx[j], sc, cb));
     } else {
         // -2 eta (X - V)
-        const float sc = 2.f * pre.eta;
+        const float sc = 2.f * eta_c;
 #pragma unroll
         for (int j = 0; j < 16; ++j) ng[j] = (pre.cp[j] - acc[j >> 2][j & 3]) * sc;
     }
 
+    // the operands of chunk c + 1 (every use of this chunk's is above); their reads
+    // complete behind the splits and writes below
+    // (read unconditionally: past the last chunk they are in-bounds LDS reads whose
+    // values go unused, and straight-line code keeps the wait counts exact)
+    chain_read_ops<TIN, PT>(sm, c + 1, g, n, lane, eta_const, pre);
+    asm volatile("" ::: "memory");
     char* gh = reinterpret_cast<char*>(sm.gt[par][0]);
     char* gl = reinterpret_cast<char*>(sm.gt[par][1]);
 #pragma unroll
@@ -310,6 +337,8 @@ __device__ __forceinline__ void chain_step(ChainSmem<TIN>& sm, int c, int g, int
         *reinterpret_cast<uint2*>(gh + off) = make_uint2(p01[0], p23[0]);
         *reinterpret_cast<uint2*>(gl + off) = make_uint2(p01[1], p23[1]);
     }
+    // its own -Gt_c back as the next step's A operands (LDS ops of one wave are ordered)
+    chain_read_ga<TIN>(sm, c, g, n, pre);
 }
 
 template <int KIND, int TIN, bool PT>
@@ -329,14 +358,14 @@ __device__ __forceinline__ void chain_role(ChainSmem<TIN>& sm, int lane, int h, 
     lds_barrier();
     lds_barrier();
     ChainPre pre;
-    if (C > 0) chain_prefetch<TIN, PT>(sm, 0, min(b, N), g, n, lane, eta_const, pre);
+    if (C > 0) chain_read_ops<TIN, PT>(sm, 0, g, n, lane, eta_const, pre);
     for (int c = 0; c < C + 2; ++c) {
         if (c < C) {
-            chain_step<KIND, TIN>(sm, c, g, n, lane, pre, g2, eps);
-            // operands of chunk c+1 (its own -Gt_c included: LDS ops of one wave are ordered)
-            if (c + 1 < C) chain_prefetch<TIN, PT>(sm, c + 1, min(b, N - (c + 1) * b), g, n, lane, eta_const, pre);
+            chain_step<KIND, TIN, PT>(sm, c, C, N, b, g, n, lane, pre, eta_const, g2, eps);
+            chain_barrier_ga_pending();
+        } else {
+            lds_barrier();
         }
-        lds_barrier();
     }
 }
 
