@@ -379,7 +379,9 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const uint16_t* __res
 // Wave w owns output features [32w, 32w+32) of everything (Gn, Z, W').
 // Per sub-block and wave (32x32x16 bf16 MFMA, fp32 accumulation):
 //   Z_m    = Q_m W'                 W' split into two bf16 terms on the fly
-//   G_a    = K_a W_c,  P_am = K_a Q_m^T (m >= a)      one pass over k
+//   G_a    = K_a W_c                W_c^T rows of the wave held in registers
+//   P_am   = K_a Q_m^T (m >= a)     the same for every wave: wave t < 3 forms
+//                                   tile t and shares its two bf16 terms in LDS
 //   Gn_a   = D (V_a - G_a)          two bf16 terms; V read by transpose reads
 //   Z_m   += P_am^T Gn_a            P (masked on the diagonal) as two bf16 terms
 //   W'    += K_a^T Gn_a             K^T by transpose reads
@@ -387,10 +389,12 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const uint16_t* __res
 // directly as the B / A operand of the next product: the k index runs over
 // those rows in that order, and the other operand is read to match.
 //
-// LDS: W_c^T (two terms, 64 KB) and two buffers of K, Q, V sub-block tiles
+// LDS: W_c^T (two terms, 64 KB; read into registers at the start, then the
+// shared score tiles, 12 KB) and two buffers of K, Q, V sub-block tiles
 // (48 KB each), filled by direct global->LDS loads issued one sub-block
-// ahead. Z of a sub-block is stored before the W' update, which gives the
-// stores that long to drain before the next barrier's wait.
+// ahead. Two barriers per sub-block (the tiles landed; the score tiles
+// published). Z of a sub-block is stored before the W' update, which gives
+// the stores that long to drain before the next barrier's wait.
 // ===========================================================================
 constexpr int SB = 64;                  // tokens per sub-block
 
@@ -520,7 +524,8 @@ enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_R = 0x020, SG_DS_R = 0x10
 #define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 template <bool PER_TOKEN>
-__device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uint16_t* nxt, int i, f32x16 (&accW)[4])
+__device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uint16_t* nxt, int i, f32x16 (&accW)[4],
+                                           const bf16x8 (&wreg)[LD / 16][2])
 {
     const int w = x.w, lane = x.lane, h = x.h, l32 = x.l32;
     // this wave's loads into `cur` (and its Z stores) are done; after the
@@ -533,80 +538,78 @@ __device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uin
     const char* kt = reinterpret_cast<const char*>(cur);
     const char* qt = kt + SB * LD * 2;
     const char* vt = kt + 2 * SB * LD * 2;
-    const char* wc = reinterpret_cast<const char*>(lc_wc);
-    const int wrow = 32 * w + l32;
 
     // ---- G_a = K_a W_c for both token tiles (two terms of W_c), then the
     // three causal score tiles P^T_am = K_a Q_m^T; operands one k-step ahead
     f32x16 g0 = {}, g1 = {};
     {
-        bf16x8 w0 = ld_piece(wc, wrow, h), w1 = ld_piece(wc + LD * LD * 2, wrow, h);
         bf16x8 k0 = ld_piece(kt, l32, h), k1 = ld_piece(kt, 32 + l32, h);
 #pragma unroll
         for (int ks = 0; ks < LD / 16; ++ks) {
-            bf16x8 w0n = w0, w1n = w1, k0n = k0, k1n = k1;
+            bf16x8 k0n = k0, k1n = k1;
             if (ks + 1 < LD / 16) {
-                w0n = ld_piece(wc, wrow, 2 * ks + 2 + h);
-                w1n = ld_piece(wc + LD * LD * 2, wrow, 2 * ks + 2 + h);
                 k0n = ld_piece(kt, l32, 2 * ks + 2 + h);
                 k1n = ld_piece(kt, 32 + l32, 2 * ks + 2 + h);
             }
-            g0 = mfma_32x32x16(k0, w1, g0);
-            g1 = mfma_32x32x16(k1, w1, g1);
-            g0 = mfma_32x32x16(k0, w0, g0);
-            g1 = mfma_32x32x16(k1, w0, g1);
-            w0 = w0n; w1 = w1n; k0 = k0n; k1 = k1n;
+            g0 = mfma_32x32x16(k0, wreg[ks][1], g0);
+            g1 = mfma_32x32x16(k1, wreg[ks][1], g1);
+            g0 = mfma_32x32x16(k0, wreg[ks][0], g0);
+            g1 = mfma_32x32x16(k1, wreg[ks][0], g1);
+            k0 = k0n; k1 = k1n;
         }
     }
 #pragma unroll
     for (int ks = 0; ks < LD / 16; ++ks) {
-        SCHED_GROUP(SG_DS_R, 4);
+        SCHED_GROUP(SG_DS_R, 2);
         SCHED_GROUP(SG_MFMA, 4);
     }
-    f32x16 p00 = {}, p01 = {}, p11 = {};
-    {
-        bf16x8 k0 = ld_piece(kt, l32, h), k1 = ld_piece(kt, 32 + l32, h);
-        bf16x8 q0 = ld_piece(qt, l32, h), q1 = ld_piece(qt, 32 + l32, h);
+    // The three causal score tiles P^T_am = K_a Q_m^T, (a, m) = (0, 0), (0, 1),
+    // (1, 1), are the same for every wave: wave w < 3 computes tile w and
+    // publishes its two bf16 terms in LDS (the W_c^T region, free once the
+    // state is in registers), from where every wave reads all three.
+    f32x16 pt = {};
+    if (w < 3) {
+        const int a = (w == 2) ? 1 : 0, m = (w == 0) ? 0 : 1;
+        bf16x8 kx = ld_piece(kt, 32 * a + l32, h), qx = ld_piece(qt, 32 * m + l32, h);
 #pragma unroll
         for (int ks = 0; ks < LD / 16; ++ks) {
-            bf16x8 k0n = k0, k1n = k1, q0n = q0, q1n = q1;
+            bf16x8 kxn = kx, qxn = qx;
             if (ks + 1 < LD / 16) {
-                k0n = ld_piece(kt, l32, 2 * ks + 2 + h);
-                k1n = ld_piece(kt, 32 + l32, 2 * ks + 2 + h);
-                q0n = ld_piece(qt, l32, 2 * ks + 2 + h);
-                q1n = ld_piece(qt, 32 + l32, 2 * ks + 2 + h);
+                kxn = ld_piece(kt, 32 * a + l32, 2 * ks + 2 + h);
+                qxn = ld_piece(qt, 32 * m + l32, 2 * ks + 2 + h);
             }
-            p00 = mfma_32x32x16(k0, q0, p00);
-            p01 = mfma_32x32x16(k0, q1, p01);
-            p11 = mfma_32x32x16(k1, q1, p11);
-            k0 = k0n; k1 = k1n; q0 = q0n; q1 = q1n;
+            pt = mfma_32x32x16(kx, qx, pt);
+            kx = kxn; qx = qxn;
         }
     }
-    // Gn_a = D (V_a - G_a) as two bf16 terms (VALU, overlapping the P products)
+    // Gn_a = D (V_a - G_a) as two bf16 terms
     bf16x8 gnb[2][2][2];                                 // [a][s][term]
     grad_terms<PER_TOKEN>(x, vt, i, 0, g0, gnb[0]);
     grad_terms<PER_TOKEN>(x, vt, i, 1, g1, gnb[1]);
+    bf16x8 (*pshare)[2][2][64] = reinterpret_cast<bf16x8 (*)[2][2][64]>(lc_wc);   // [tile][s][term][lane]
+    if (w < 3) {
 #pragma unroll
-    for (int ks = 0; ks < LD / 16; ++ks) {
-        SCHED_GROUP(SG_DS_R, 4);
-        SCHED_GROUP(SG_MFMA, 1);
-        SCHED_GROUP(SG_VALU, 6);
-        SCHED_GROUP(SG_MFMA, 1);
-        SCHED_GROUP(SG_VALU, 6);
-        SCHED_GROUP(SG_MFMA, 1);
-        SCHED_GROUP(SG_VALU, 6);
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 pp[2];
+            pack_p(pt, s, w != 1, h, l32, pp);
+            pshare[w][s][0][lane] = pp[0];
+            pshare[w][s][1][lane] = pp[1];
+        }
     }
+    __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- Z_m = Q_m W' + P_am^T Gn_a ; W' as B operand: k = in-features
     // 32r + crow(8s + j, h), split into two bf16 terms on the fly
     bf16x8 pa00[2][2], pa01[2][2], pa11[2][2];           // [s][term]
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        pack_p(p00, s, true, h, l32, pa00[s]);
-        pack_p(p01, s, false, h, l32, pa01[s]);
-        pack_p(p11, s, true, h, l32, pa11[s]);
-    }
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            pa00[s][t] = pshare[0][s][t][lane];
+            pa01[s][t] = pshare[1][s][t][lane];
+            pa11[s][t] = pshare[2][s][t][lane];
+        }
     f32x16 zacc[2] = {f32x16{}, f32x16{}};
     const int sw = rsw(l32);
 #pragma unroll
@@ -728,9 +731,21 @@ lc_chunk_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* _
             }
     }
 
+    // this wave's rows of W_c^T (both terms) as the B operand of G = K W_c, held
+    // in registers for the whole chunk
+    bf16x8 wreg[LD / 16][2];
+    {
+        const char* wc = reinterpret_cast<const char*>(lc_wc);
+        const int wrow = 32 * x.w + x.l32;
+#pragma unroll
+        for (int ks = 0; ks < LD / 16; ++ks) {
+            wreg[ks][0] = ld_piece(wc, wrow, 2 * ks + x.h);
+            wreg[ks][1] = ld_piece(wc + LD * LD * 2, wrow, 2 * ks + x.h);
+        }
+    }
     for (int i = 0; i < x.nsb; i += 2) {
-        chunk_step<PER_TOKEN>(x, lc_buf0, lc_buf1, i, accW);
-        chunk_step<PER_TOKEN>(x, lc_buf1, lc_buf0, i + 1, accW);
+        chunk_step<PER_TOKEN>(x, lc_buf0, lc_buf1, i, accW, wreg);
+        chunk_step<PER_TOKEN>(x, lc_buf1, lc_buf0, i + 1, accW, wreg);
     }
 }
 
