@@ -388,13 +388,18 @@ lc_scan_kernel(int N, int b, const float* __restrict__ W0, const uint16_t* __res
 // The C layout of G and P (lane = column, rows 8(i/4) + 4h + i%4) is used
 // directly as the B / A operand of the next product: the k index runs over
 // those rows in that order, and the other operand is read to match.
+// W' keeps its rows (in-features) in a permuted order: the transpose reads
+// that form the A operand of its update hand row i of each 32 the feature
+// sigma(i), sigma swapping bits 2 and 3, so that C slots 8s..8s+7 of lane
+// half h hold the contiguous features 32r + 16s + 8h + 0..7, and the Q
+// operand of Q_m W' is one 16-byte row piece.
 //
 // LDS: W_c^T (two terms, 64 KB; read into registers at the start, then the
 // shared score tiles, 12 KB) and two buffers of K, Q, V sub-block tiles
 // (48 KB each), filled by direct global->LDS loads issued one sub-block
-// ahead. Two barriers per sub-block (the tiles landed; the score tiles
-// published). Z of a sub-block is stored before the W' update, which gives
-// the stores that long to drain before the next barrier's wait.
+// ahead and spread over the G products. Two barriers per sub-block (the
+// tiles landed; the score tiles published). The stores of Z go out one
+// after each product of the W' update, in its shadow.
 // ===========================================================================
 constexpr int SB = 64;                  // tokens per sub-block
 
@@ -427,6 +432,20 @@ __device__ __forceinline__ void sub_dma(uint16_t* buf, const uint16_t* Ku, const
     rows_dma<4>(b + 2 * SB * LD * 2, Vu + (size_t)t * LD, w, lane);
 }
 
+// One of the 12 direct-load instructions of sub_dma (J = 4 * tensor + k).
+template <int J>
+__device__ __forceinline__ void sub_dma_one(uint16_t* buf, const uint16_t* Ku, const uint16_t* Qu, const uint16_t* Vu,
+                                            int t, int w, int lane)
+{
+    constexpr int T = J / 4, k = J % 4;
+    const uint16_t* src = (T == 0 ? Ku : T == 1 ? Qu : Vu) + (size_t)t * LD;
+    char* dst = reinterpret_cast<char*>(buf) + T * SB * LD * 2;
+    const int ins = 4 * w + k;
+    const int sl = ins * 64 + lane;
+    const int r = sl >> 4, p = (sl & 15) ^ rsw(r);
+    dma16(src + (size_t)r * LD + p * 8, __builtin_amdgcn_readfirstlane(lds_addr(dst + ins * 1024)));
+}
+
 // Row read: piece p of row r (16 bytes).
 __device__ __forceinline__ bf16x8 ld_piece(const char* tile, int r, int p)
 {
@@ -440,6 +459,18 @@ __device__ __forceinline__ uint2 ld_tr4(const char* tile, int row0, int col0, in
     const int q = lane >> 4, r16 = lane & 15;
     const int row = row0 + 4 * (q >> 1) + (r16 >> 2);
     const int col = col0 + 16 * (q & 1) + 4 * (r16 & 3);
+    const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(tile + swz(row, col >> 3) + (col & 7) * 2));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// As ld_tr4, with the two middle 4-column segments of each 16 swapped: lane
+// (feature) slot c of the result holds column sigma(c), sigma swapping bits 2 and 3.
+__device__ __forceinline__ uint2 ld_tr4s(const char* tile, int row0, int col0, int lane)
+{
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int row = row0 + 4 * (q >> 1) + (r16 >> 2);
+    const int col = col0 + 16 * (q & 1) + 4 * (((r16 & 1) << 1) | ((r16 >> 1) & 1));
     const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(tile + swz(row, col >> 3) + (col & 7) * 2));
     return __builtin_bit_cast(uint2, v);
 }
@@ -469,23 +500,6 @@ struct ChunkCtx {
     __amdgpu_buffer_rsrc_t zr;          // Z rows of the unit (buffer stores: uniform row offsets)
     int c0, nsb, w, lane, h, l32;
 };
-
-// Z rows of sub-block i from the C-layout accumulators: lane stores column
-// 32w + l32 of rows crow(e, h); the row offset is split into a uniform part
-// (8 (e / 4) rows) and an immediate (e % 4 rows).
-__device__ __forceinline__ void store_z(const ChunkCtx& x, const f32x16 (&z)[2], int i)
-{
-    const int voff = ((4 * x.h) * LD + 32 * x.w + x.l32) * 4;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int srow = __builtin_amdgcn_readfirstlane(x.c0 + i * SB + 32 * m + 8 * (e >> 2));
-            const float v = z[m][e];     // (a bit cast of the vector element itself would read element 0)
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), x.zr, voff + (e & 3) * LD * 4,
-                                                  srow * LD * 4, 0);
-        }
-}
 
 // Two bf16 terms of Gn = D (V - G) for one 32-token tile (C layout of G:
 // column = feature 32w + l32, rows = tokens 32a + crow(e, h)), per k-step s.
@@ -532,8 +546,9 @@ __device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uin
     // barrier every wave's are, and no wave still reads `nxt`
     __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
-    if (i + 1 < x.nsb) sub_dma(nxt, x.Ku, x.Qu, x.Vu, x.c0 + (i + 1) * SB, w, lane);
     __builtin_amdgcn_sched_barrier(0);
+    // next sub-block (the last one reloads itself into the idle buffer)
+    const int tn = x.c0 + min(i + 1, x.nsb - 1) * SB;
 
     const char* kt = reinterpret_cast<const char*>(cur);
     const char* qt = kt + SB * LD * 2;
@@ -556,12 +571,22 @@ __device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uin
             g0 = mfma_32x32x16(k0, wreg[ks][0], g0);
             g1 = mfma_32x32x16(k1, wreg[ks][0], g1);
             k0 = k0n; k1 = k1n;
+            SCHED_GROUP(SG_DS_R, 2);
+            SCHED_GROUP(SG_MFMA, 4);
+            __builtin_amdgcn_sched_barrier(0);
+            // the next sub-block's direct loads, spread over the product
+            switch (ks) {
+            case 0: sub_dma_one<0>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); sub_dma_one<8>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); break;
+            case 1: sub_dma_one<1>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); break;
+            case 2: sub_dma_one<2>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); sub_dma_one<9>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); break;
+            case 3: sub_dma_one<3>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); break;
+            case 4: sub_dma_one<4>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); sub_dma_one<10>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); break;
+            case 5: sub_dma_one<5>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); break;
+            case 6: sub_dma_one<6>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); sub_dma_one<11>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); break;
+            default: sub_dma_one<7>(nxt, x.Ku, x.Qu, x.Vu, tn, w, lane); break;
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-    }
-#pragma unroll
-    for (int ks = 0; ks < LD / 16; ++ks) {
-        SCHED_GROUP(SG_DS_R, 2);
-        SCHED_GROUP(SG_MFMA, 4);
     }
     // The three causal score tiles P^T_am = K_a Q_m^T, (a, m) = (0, 0), (0, 1),
     // (1, 1), are the same for every wave: wave w < 3 computes tile w and
@@ -611,30 +636,39 @@ __device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uin
             pa11[s][t] = pshare[2][s][t][lane];
         }
     f32x16 zacc[2] = {f32x16{}, f32x16{}};
-    const int sw = rsw(l32);
+    // k-block it = 2r + s: Q piece 2 it + h and the matching eight W' slots split
+    // into two bf16 terms. Operands of block it + 1 are read and split while the
+    // products of block it run.
+    auto w_ops = [&](int it, bf16x8 (&wb)[2]) {
+        const int r = it >> 1, s = it & 1;
+        float xv[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+        for (int j = 0; j < 8; ++j) xv[j] = accW[r][8 * s + j];
+        terms8<2>(xv, wb);
+    };
+    {
+        bf16x8 qa[2], wb[2];
+        qa[0] = ld_piece(qt, l32, h);
+        qa[1] = ld_piece(qt, 32 + l32, h);
+        w_ops(0, wb);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            float xv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) xv[j] = accW[r][8 * s + j];
-            bf16x8 wb[2];
-            terms8<2>(xv, wb);
-            const int p0 = 4 * r + 2 * s;
-            bf16x8 qa[2];
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const char* row = qt + (32 * m + l32) * 256;
-                const uint2 lo = *reinterpret_cast<const uint2*>(row + ((p0 ^ sw) << 4) + 8 * h);
-                const uint2 hi = *reinterpret_cast<const uint2*>(row + (((p0 + 1) ^ sw) << 4) + 8 * h);
-                qa[m] = cat8(lo, hi);
+        for (int it = 0; it < 8; ++it) {
+            bf16x8 qn[2], wn[2];
+            if (it + 1 < 8) {
+                qn[0] = ld_piece(qt, l32, 2 * it + 2 + h);
+                qn[1] = ld_piece(qt, 32 + l32, 2 * it + 2 + h);
+                w_ops(it + 1, wn);
             }
             zacc[0] = mfma_32x32x16(qa[0], wb[1], zacc[0]);
             zacc[1] = mfma_32x32x16(qa[1], wb[1], zacc[1]);
             zacc[0] = mfma_32x32x16(qa[0], wb[0], zacc[0]);
             zacc[1] = mfma_32x32x16(qa[1], wb[0], zacc[1]);
+            if (it + 1 < 8) {
+                qa[0] = qn[0]; qa[1] = qn[1];
+                wb[0] = wn[0]; wb[1] = wn[1];
+            }
         }
+    }
     // causal pairs (0,0), (0,1), (1,1); two terms each, the pair (lo, lo) dropped
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -648,19 +682,24 @@ __device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uin
         zacc[1] = mfma_32x32x16(pa11[s][0], gnb[1][s][1], zacc[1]);
         zacc[1] = mfma_32x32x16(pa11[s][0], gnb[1][s][0], zacc[1]);
     }
+    SCHED_GROUP(SG_DS_R, 14);                            // the shared score tiles, Q of block 0
+    SCHED_GROUP(SG_VALU, 24);                            // W' slots of block 0
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        SCHED_GROUP(SG_DS_R, 2);
-        SCHED_GROUP(SG_VALU, 12);
-        SCHED_GROUP(SG_MFMA, 2);
-        SCHED_GROUP(SG_VALU, 12);
-        SCHED_GROUP(SG_MFMA, 2);
+    for (int it = 0; it < 8; ++it) {
+        if (it + 1 < 8) SCHED_GROUP(SG_DS_R, 2);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            SCHED_GROUP(SG_MFMA, 1);
+            if (it + 1 < 8) SCHED_GROUP(SG_VALU, 6);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
-    store_z(x, zacc, i);                                 // drains during the W' update
-    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- W' += K_a^T Gn_a ; A = K^T rows 32r + l32, k = tokens 32a + crow(8s + j, h)
+    // ---- W' += K_a^T Gn_a ; A = K^T rows 32r + sigma(l32), k = tokens 32a + crow(8s + j, h).
+    // The 32 stores of Z go out one after each product, in the products' shadow:
+    // lane stores column 32w + l32 of row crow(e, h) of tile m, the row offset
+    // split into a uniform part (8 (e / 4) rows) and an immediate (e % 4 rows).
+    const int voff = ((4 * h) * LD + 32 * w + l32) * 4;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -668,17 +707,20 @@ __device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uin
             bf16x8 ka[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                ka[r] = cat8(ld_tr4(kt, 32 * a + 16 * s, 32 * r, lane), ld_tr4(kt, 32 * a + 16 * s + 8, 32 * r, lane));
+                ka[r] = cat8(ld_tr4s(kt, 32 * a + 16 * s, 32 * r, lane), ld_tr4s(kt, 32 * a + 16 * s + 8, 32 * r, lane));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) accW[r] = mfma_32x32x16(ka[r], gnb[a][s][1], accW[r]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) accW[r] = mfma_32x32x16(ka[r], gnb[a][s][0], accW[r]);
+            for (int jj = 0; jj < 8; ++jj) {
+                const int r = jj & 3;
+                accW[r] = mfma_32x32x16(ka[r], gnb[a][s][jj < 4 ? 1 : 0], accW[r]);
+                __builtin_amdgcn_sched_barrier(0);
+                const int idx = 16 * a + 8 * s + jj, m = idx >> 4, e = idx & 15;
+                const int srow = __builtin_amdgcn_readfirstlane(x.c0 + i * SB + 32 * m + 8 * (e >> 2));
+                const float v = zacc[m][e];
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), x.zr, voff + (e & 3) * LD * 4,
+                                                      srow * LD * 4, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        SCHED_GROUP(SG_DS_R, 8);
-        SCHED_GROUP(SG_MFMA, 8);
-    }
 }
 
 template <bool PER_TOKEN>
@@ -709,8 +751,9 @@ lc_chunk_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* _
     __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
 
-    // W' = W_c in fp32 (hi + lo), C layout: rows = in-features 32r + crow(e, h),
-    // column = output feature 32w + l32
+    // W' = W_c in fp32 (hi + lo), C layout: column = output feature 32w + l32;
+    // slot 4mq + e of accW[r] = in-feature 32r + 16(mq / 2) + 8h + 4(mq % 2) + e
+    // (row order permuted by sigma, as the W' update's transpose reads give it)
     f32x16 accW[4];
     {
         const char* wc = reinterpret_cast<const char*>(lc_wc);
@@ -719,7 +762,7 @@ lc_chunk_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* _
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int mq = 0; mq < 4; ++mq) {
-                const int k0 = 32 * r + 8 * mq + 4 * x.h;
+                const int k0 = 32 * r + 16 * (mq >> 1) + 8 * x.h + 4 * (mq & 1);
                 const int off = swz(n, k0 >> 3) + (k0 & 7) * 2;
                 const uint2 hi = *reinterpret_cast<const uint2*>(wc + off);
                 const uint2 lo = *reinterpret_cast<const uint2*>(wc + LD * LD * 2 + off);
@@ -747,6 +790,7 @@ lc_chunk_kernel(int N, int b, const uint16_t* __restrict__ Qg, const uint16_t* _
         chunk_step<PER_TOKEN>(x, lc_buf0, lc_buf1, i, accW, wreg);
         chunk_step<PER_TOKEN>(x, lc_buf1, lc_buf0, i + 1, accW, wreg);
     }
+    __builtin_amdgcn_s_waitcnt(0x0070);                  // the last reload lands before the LDS is released
 }
 
 // ===========================================================================
