@@ -44,15 +44,18 @@ __device__ __forceinline__ int crow(int i, int h) { return 8 * (i >> 2) + 4 * h 
 // feed the two bf16 terms of its operand as one K = 2 * H*64 reduction
 // against the same W_O rows. A workgroup computes TM tokens of one sequence x
 // TN outputs with (TM/64) * (TN/64) waves, each owning a 64 x 64 block.
-// Operand tiles stream global -> LDS with direct loads, 32-deep stages, NS
-// stages resident (NS - 1 in flight while one is read).
+// Operand tiles stream global -> LDS with direct loads, 64-deep stages, NS
+// stages resident (NS - 1 in flight while one is read). Both GEMMs use
+// 256 x 192 tiles (twelve waves): at the layer's sizes that is a whole number
+// of rounds of workgroups over the chip, and each loaded byte feeds 110 flops
+// (LDS bandwidth, not the matrix cores, bounds smaller tiles here).
 // ===========================================================================
-constexpr int GK = 32;       // reduction depth of one LDS stage
+constexpr int GK = 64;       // reduction depth of one LDS stage
 
-// Tiles hold rows of 32 bf16 (64 bytes = 4 pieces); piece p of row r sits at
-// slot p ^ ((r >> 2) & 3), so 16 consecutive rows read at one piece start on
-// 16 different 4-bank groups.
-__device__ __forceinline__ int psw(int r, int p) { return r * 64 + ((p ^ ((r >> 2) & 3)) << 4); }
+// Tiles hold rows of 64 bf16 (128 bytes = 8 pieces); piece p of row r sits at
+// slot p ^ (r & 7), so 8 consecutive rows read at one piece start on 8
+// different 4-bank groups of their half of the banks.
+__device__ __forceinline__ int psw(int r, int p) { return r * 128 + ((p ^ (r & 7)) << 4); }
 
 constexpr int vmcnt_imm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
 
@@ -98,11 +101,13 @@ __global__ void __launch_bounds__(TM * TN / 64)
 layer_gemm_kernel(GemmArgs g)
 {
     constexpr int WR = TM / 64, WC = TN / 64, NW = WR * WC;
-    constexpr int NIA = TM / 16, NIB = TN / 16;            // DMA instructions per stage (1 KB each)
-    constexpr int PER = (NIA + NIB) / NW;                  // ... per wave
-    static_assert((NIA + NIB) % NW == 0, "DMA instructions must split evenly over the waves");
+    constexpr int NIA = TM / 8, NIB = TN / 8;              // DMA instructions per stage (1 KB = 8 rows each)
+    constexpr int NI = NIA + NIB;
+    constexpr int PER = (NI + NW - 1) / NW;                // ... per wave: waves w < REM issue PER,
+    constexpr int REM = NI % NW;                           // the others PER - 1 (REM = 0: all PER)
     constexpr int SA = TM * GK * 2, SB = TN * GK * 2;    // stage bytes
-    __shared__ __attribute__((aligned(16))) char smem[NS * (SA + SB)];
+    constexpr int SMEM = (EPI == EPI_QKV && NW * 8192 > NS * (SA + SB)) ? NW * 8192 : NS * (SA + SB);
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     int rt, nt;
     grouped_tile(xcd_tile(blockIdx.x, g.total), g.tiles_t * (g.total / (g.tiles_t * g.tiles_n)), g.tiles_n, rt, nt);
@@ -110,8 +115,9 @@ layer_gemm_kernel(GemmArgs g)
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int h = lane >> 5, l32 = lane & 31;
     const int wr = w / WC, wc = w % WC;
+    const bool full = REM == 0 || w < REM;                 // this wave issues PER instructions
 
-    // DMA instruction j of this wave covers 16 tile rows; rows past the
+    // DMA instruction j of this wave covers 8 tile rows; rows past the
     // sequence or past the last output are clamped to a valid row (their
     // results are never stored).
     const uint16_t* src[PER];
@@ -120,11 +126,11 @@ layer_gemm_kernel(GemmArgs g)
     const uint32_t base = lds_addr(smem);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        const int ins = w + NW * j;
+        const int ins = min(w + NW * j, NI - 1);         // (clamped for the waves that skip it)
         // with NIA a multiple of NW, whether instruction j loads the weight does not depend on w
         const bool b = (NIA % NW == 0) ? (NW * j >= NIA) : (ins >= NIA);
-        const int r = (b ? ins - NIA : ins) * 16 + (lane >> 2);
-        const int p = (lane & 3) ^ ((r >> 2) & 3);
+        const int r = (b ? ins - NIA : ins) * 8 + (lane >> 3);
+        const int p = (lane & 7) ^ (r & 7);
         if (!b) {
             const int t = min(t0 + r, g.N - 1);
             src[j] = g.A + ((size_t)bi * g.N + t) * g.lda + p * 8;
@@ -148,8 +154,9 @@ layer_gemm_kernel(GemmArgs g)
         if (kw >= g.KW) kw -= g.KW;
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-            dma16(src[j] + (isb[j] ? kw : ka),
-                  __builtin_amdgcn_readfirstlane(dst[j] + buf * (isb[j] ? SB : SA)));
+            if (j + 1 < PER || full)
+                dma16(src[j] + (isb[j] ? kw : ka),
+                      __builtin_amdgcn_readfirstlane(dst[j] + buf * (isb[j] ? SB : SA)));
     };
 
     f32x16 acc[2][2];
@@ -167,9 +174,15 @@ layer_gemm_kernel(GemmArgs g)
     for (int kb = 0; kb < KB; ++kb) {
         // stage kb has landed once at most the later stages' loads are pending
         const int later = min(KB - 1, kb + NS - 2) - kb;
-        if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
-        else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        if (full) {
+            if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
+            else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        } else {
+            if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (PER - 1)));
+            else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER - 1));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
         __syncthreads();
         if (kb + NS - 1 < KB) issue(kb + NS - 1, (kb + NS - 1) % NS);
         const char* A = smem + (kb % NS) * SA;
@@ -202,7 +215,7 @@ layer_gemm_kernel(GemmArgs g)
         // 64 x 64 block goes through an 8 KB LDS buffer of its own ([token][output],
         // 16-byte pieces swizzled by token), so that the global stores are whole
         // 128-byte head rows, eight per instruction.
-        static_assert(NS * (SA + SB) >= NW * 8192, "the stage buffers hold the output staging");
+        static_assert(EPI != EPI_QKV || SMEM >= NW * 8192, "the stage buffers hold the output staging");
         __syncthreads();                             // every wave is done with the stage buffers
         if (nw >= g.n_out) return;
         const int which = nw / g.rows_per_w, head = (nw - which * g.rows_per_w) / HDIM;
@@ -312,8 +325,8 @@ layer_outprep_kernel(int N, int H, int rows, size_t plane, const float* __restri
 }
 
 // Tile shapes of the two GEMMs
-constexpr int P_TM = 256, P_TN = 128, P_NS = 3;      // projections
-constexpr int O_TM = 256, O_TN = 128, O_NS = 3;      // output projection
+constexpr int P_TM = 256, P_TN = 192, P_NS = 2;      // projections: 3 rounds at B 8, N 2048, D 768
+constexpr int O_TM = 256, O_TN = 192, O_NS = 2;      // output projection: 1 round
 
 }  // namespace
 
