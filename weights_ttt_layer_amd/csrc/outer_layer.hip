@@ -27,6 +27,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace ttt {
 namespace {
 
@@ -109,172 +111,179 @@ layer_gemm_kernel(GemmArgs g)
     constexpr int SMEM = (EPI == EPI_QKV && NW * 8192 > NS * (SA + SB)) ? NW * 8192 : NS * (SA + SB);
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
-    int rt, nt;
-    grouped_tile(xcd_tile(blockIdx.x, g.total), g.tiles_t * (g.total / (g.tiles_t * g.tiles_n)), g.tiles_n, rt, nt);
-    const int bi = rt / g.tiles_t, t0 = (rt % g.tiles_t) * TM, n0 = nt * TN;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int h = lane >> 5, l32 = lane & 31;
     const int wr = w / WC, wc = w % WC;
     const bool full = REM == 0 || w < REM;                 // this wave issues PER instructions
-
-    // DMA instruction j of this wave covers 8 tile rows; rows past the
-    // sequence or past the last output are clamped to a valid row (their
-    // results are never stored).
-    const uint16_t* src[PER];
-    uint32_t dst[PER];
-    bool isb[PER];
     const uint32_t base = lds_addr(smem);
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int ins = min(w + NW * j, NI - 1);         // (clamped for the waves that skip it)
-        // with NIA a multiple of NW, whether instruction j loads the weight does not depend on w
-        const bool b = (NIA % NW == 0) ? (NW * j >= NIA) : (ins >= NIA);
-        const int r = (b ? ins - NIA : ins) * 8 + (lane >> 3);
-        const int p = (lane & 7) ^ (r & 7);
-        if (!b) {
-            const int t = min(t0 + r, g.N - 1);
-            src[j] = g.A + ((size_t)bi * g.N + t) * g.lda + p * 8;
-            dst[j] = base + ins * 1024;
-        } else {
-            int n = min(n0 + r, g.n_out - 1);
-            const uint16_t* Wt = g.W0;
-            if (EPI == EPI_QKV) {
-                const int which = n / g.rows_per_w;
-                Wt = which == 0 ? g.W0 : (which == 1 ? g.W1 : g.W2);
-                n -= which * g.rows_per_w;
+
+    // Persistent (one workgroup per compute unit): a workgroup takes tiles
+    // blockIdx.x, + gridDim.x, ...; no launch between tiles, and the L2 writes
+    // one tile's outputs back while the next tile's products run.
+    for (int L = blockIdx.x; L < g.total; L += gridDim.x) {
+        int rt, nt;
+        grouped_tile(xcd_tile(L, g.total), g.tiles_t * (g.total / (g.tiles_t * g.tiles_n)), g.tiles_n, rt, nt);
+        const int bi = rt / g.tiles_t, t0 = (rt % g.tiles_t) * TM, n0 = nt * TN;
+
+        // DMA instruction j of this wave covers 8 tile rows; rows past the
+        // sequence or past the last output are clamped to a valid row (their
+        // results are never stored).
+        const uint16_t* src[PER];
+        uint32_t dst[PER];
+        bool isb[PER];
+    #pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int ins = min(w + NW * j, NI - 1);         // (clamped for the waves that skip it)
+            // with NIA a multiple of NW, whether instruction j loads the weight does not depend on w
+            const bool b = (NIA % NW == 0) ? (NW * j >= NIA) : (ins >= NIA);
+            const int r = (b ? ins - NIA : ins) * 8 + (lane >> 3);
+            const int p = (lane & 7) ^ (r & 7);
+            if (!b) {
+                const int t = min(t0 + r, g.N - 1);
+                src[j] = g.A + ((size_t)bi * g.N + t) * g.lda + p * 8;
+                dst[j] = base + ins * 1024;
+            } else {
+                int n = min(n0 + r, g.n_out - 1);
+                const uint16_t* Wt = g.W0;
+                if (EPI == EPI_QKV) {
+                    const int which = n / g.rows_per_w;
+                    Wt = which == 0 ? g.W0 : (which == 1 ? g.W1 : g.W2);
+                    n -= which * g.rows_per_w;
+                }
+                src[j] = Wt + (size_t)n * g.ldb + p * 8;
+                dst[j] = base + NS * SA + (ins - NIA) * 1024;
             }
-            src[j] = Wt + (size_t)n * g.ldb + p * 8;
-            dst[j] = base + NS * SA + (ins - NIA) * 1024;
+            isb[j] = b;
         }
-        isb[j] = b;
-    }
-    auto issue = [&](int kb, int buf) {
-        const int ka = kb * GK;
-        int kw = ka;
-        if (kw >= g.KW) kw -= g.KW;
-#pragma unroll
-        for (int j = 0; j < PER; ++j)
-            if (j + 1 < PER || full)
-                dma16(src[j] + (isb[j] ? kw : ka),
-                      __builtin_amdgcn_readfirstlane(dst[j] + buf * (isb[j] ? SB : SA)));
-    };
+        auto issue = [&](int kb, int buf) {
+            const int ka = kb * GK;
+            int kw = ka;
+            if (kw >= g.KW) kw -= g.KW;
+    #pragma unroll
+            for (int j = 0; j < PER; ++j)
+                if (j + 1 < PER || full)
+                    dma16(src[j] + (isb[j] ? kw : ka),
+                          __builtin_amdgcn_readfirstlane(dst[j] + buf * (isb[j] ? SB : SA)));
+        };
 
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[a][c][i] = 0.f;
-
-    const int KB = g.K / GK;
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < KB) issue(s, s);
-    for (int kb = 0; kb < KB; ++kb) {
-        // stage kb has landed once at most the later stages' loads are pending
-        const int later = min(KB - 1, kb + NS - 2) - kb;
-        if (full) {
-            if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
-            else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        } else {
-            if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (PER - 1)));
-            else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER - 1));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        }
-        __syncthreads();
-        if (kb + NS - 1 < KB) issue(kb + NS - 1, (kb + NS - 1) % NS);
-        const char* A = smem + (kb % NS) * SA;
-        const char* Bt = smem + NS * SA + (kb % NS) * SB;
-#pragma unroll
-        for (int ks = 0; ks < GK / 16; ++ks) {
-            const int p = 2 * ks + h;
-            bf16x8 av[2], bv[2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-                av[a] = *reinterpret_cast<const bf16x8*>(A + psw(64 * wr + 32 * a + l32, p));
-#pragma unroll
+        f32x16 acc[2][2];
+    #pragma unroll
+        for (int a = 0; a < 2; ++a)
+    #pragma unroll
             for (int c = 0; c < 2; ++c)
-                bv[c] = *reinterpret_cast<const bf16x8*>(Bt + psw(64 * wc + 32 * c + l32, p));
-            // EPI_QKV takes the transposed tiles (rows = outputs, columns = tokens), so
-            // a lane holds consecutive outputs of one token
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    acc[a][c] = EPI == EPI_QKV ? mfma_32x32x16(bv[c], av[a], acc[a][c])
-                                               : mfma_32x32x16(av[a], bv[c], acc[a][c]);
-        }
-    }
+    #pragma unroll
+                for (int i = 0; i < 16; ++i) acc[a][c][i] = 0.f;
 
-    const int nw = n0 + 64 * wc;                 // this wave's first output (n_out is a multiple of 64)
-    if (EPI == EPI_QKV) {
-        // acc[a][c] slot 4q + j: token 64 wr + 32 a + l32 of the tile, output nw + 32 c + 8 q + 4 h + j.
-        // The wave's 64 outputs are one head of one projection. Each plane of its
-        // 64 x 64 block goes through an 8 KB LDS buffer of its own ([token][output],
-        // 16-byte pieces swizzled by token), so that the global stores are whole
-        // 128-byte head rows, eight per instruction.
-        static_assert(EPI != EPI_QKV || SMEM >= NW * 8192, "the stage buffers hold the output staging");
-        __syncthreads();                             // every wave is done with the stage buffers
-        if (nw >= g.n_out) return;
-        const int which = nw / g.rows_per_w, head = (nw - which * g.rows_per_w) / HDIM;
-        uint16_t* ob = g.qkv[which] + ((size_t)bi * g.H + head) * (size_t)g.N * HDIM;
-        // per 32-token half a: both planes of the half through the wave's 8 KB
-        // (high terms at 0, low terms at 4 KB)
-        char* wb = smem + w * 8192;
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            float sc = 1.f;
-            if (which == 1) {
-                // k / ||k||: this lane holds 32 of the row's 64 entries, lane l ^ 32 the rest
-                float s = 0.f;
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) s = fmaf(acc[a][c][i], acc[a][c][i], s);
-                s += __shfl_xor(s, 32, 64);
-                sc = s > 0.f ? 1.f / sqrtf(s) : 0.f;
+        const int KB = g.K / GK;
+    #pragma unroll
+        for (int s = 0; s < NS - 1; ++s)
+            if (s < KB) issue(s, s);
+        for (int kb = 0; kb < KB; ++kb) {
+            // stage kb has landed once at most the later stages' loads are pending
+            const int later = min(KB - 1, kb + NS - 2) - kb;
+            if (full) {
+                if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
+                else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            } else {
+                if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (PER - 1)));
+                else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER - 1));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
-            const int r = l32;
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // two bf16 terms: RNE rounding, then the rounding of the remainder
-                    uint32_t p01[2], p23[2];
-                    split_pair<2>(acc[a][c][4 * q] * sc, acc[a][c][4 * q + 1] * sc, p01);
-                    split_pair<2>(acc[a][c][4 * q + 2] * sc, acc[a][c][4 * q + 3] * sc, p23);
-                    const int off = r * 128 + (((4 * c + q) ^ (r & 7)) << 4) + 8 * h;
-                    *reinterpret_cast<uint2*>(wb + off) = make_uint2(p01[0], p23[0]);
-                    *reinterpret_cast<uint2*>(wb + 4096 + off) = make_uint2(p01[1], p23[1]);
-                }
-            // the same wave reads back (its LDS operations are ordered): lane L takes
-            // piece L % 8 of token row 8 j + L / 8 of the half, in each plane
-#pragma unroll
-            for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int rr = 8 * j + (lane >> 3), k = lane & 7;
-                    const uint4 v = *reinterpret_cast<const uint4*>(wb + 4096 * pl + rr * 128 + ((k ^ (rr & 7)) << 4));
-                    const int t = t0 + 64 * wr + 32 * a + rr;
-                    if (t < g.N) *reinterpret_cast<uint4*>(ob + (pl ? g.plane : 0) + (size_t)t * HDIM + 8 * k) = v;
-                }
+            __syncthreads();
+            if (kb + NS - 1 < KB) issue(kb + NS - 1, (kb + NS - 1) % NS);
+            const char* A = smem + (kb % NS) * SA;
+            const char* Bt = smem + NS * SA + (kb % NS) * SB;
+    #pragma unroll
+            for (int ks = 0; ks < GK / 16; ++ks) {
+                const int p = 2 * ks + h;
+                bf16x8 av[2], bv[2];
+    #pragma unroll
+                for (int a = 0; a < 2; ++a)
+                    av[a] = *reinterpret_cast<const bf16x8*>(A + psw(64 * wr + 32 * a + l32, p));
+    #pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    bv[c] = *reinterpret_cast<const bf16x8*>(Bt + psw(64 * wc + 32 * c + l32, p));
+                // EPI_QKV takes the transposed tiles (rows = outputs, columns = tokens), so
+                // a lane holds consecutive outputs of one token
+    #pragma unroll
+                for (int a = 0; a < 2; ++a)
+    #pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        acc[a][c] = EPI == EPI_QKV ? mfma_32x32x16(bv[c], av[a], acc[a][c])
+                                                   : mfma_32x32x16(av[a], bv[c], acc[a][c]);
+            }
         }
-    } else {
-        if (nw >= g.n_out) return;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int n = nw + 32 * c + l32;
-            if (n >= g.n_out) continue;
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int t = t0 + 64 * wr + 32 * a + crow(i, h);
-                    if (t < g.N) g.out0[((size_t)bi * g.N + t) * g.n_out + n] = acc[a][c][i];
+
+        const int nw = n0 + 64 * wc;                 // this wave's first output (n_out is a multiple of 64)
+        if (EPI == EPI_QKV) {
+            // acc[a][c] slot 4q + j: token 64 wr + 32 a + l32 of the tile, output nw + 32 c + 8 q + 4 h + j.
+            // The wave's 64 outputs are one head of one projection. Each plane of its
+            // 64 x 64 block goes through an 8 KB LDS buffer of its own ([token][output],
+            // 16-byte pieces swizzled by token), so that the global stores are whole
+            // 128-byte head rows, eight per instruction.
+            static_assert(EPI != EPI_QKV || SMEM >= NW * 8192, "the stage buffers hold the output staging");
+            __syncthreads();                             // every wave is done with the stage buffers
+            if (nw < g.n_out) {
+            const int which = nw / g.rows_per_w, head = (nw - which * g.rows_per_w) / HDIM;
+            uint16_t* ob = g.qkv[which] + ((size_t)bi * g.H + head) * (size_t)g.N * HDIM;
+            // per 32-token half a: both planes of the half through the wave's 8 KB
+            // (high terms at 0, low terms at 4 KB)
+            char* wb = smem + w * 8192;
+    #pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                float sc = 1.f;
+                if (which == 1) {
+                    // k / ||k||: this lane holds 32 of the row's 64 entries, lane l ^ 32 the rest
+                    float s = 0.f;
+    #pragma unroll
+                    for (int c = 0; c < 2; ++c)
+    #pragma unroll
+                        for (int i = 0; i < 16; ++i) s = fmaf(acc[a][c][i], acc[a][c][i], s);
+                    s += __shfl_xor(s, 32, 64);
+                    sc = s > 0.f ? 1.f / sqrtf(s) : 0.f;
                 }
+                const int r = l32;
+    #pragma unroll
+                for (int c = 0; c < 2; ++c)
+    #pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        // two bf16 terms: RNE rounding, then the rounding of the remainder
+                        uint32_t p01[2], p23[2];
+                        split_pair<2>(acc[a][c][4 * q] * sc, acc[a][c][4 * q + 1] * sc, p01);
+                        split_pair<2>(acc[a][c][4 * q + 2] * sc, acc[a][c][4 * q + 3] * sc, p23);
+                        const int off = r * 128 + (((4 * c + q) ^ (r & 7)) << 4) + 8 * h;
+                        *reinterpret_cast<uint2*>(wb + off) = make_uint2(p01[0], p23[0]);
+                        *reinterpret_cast<uint2*>(wb + 4096 + off) = make_uint2(p01[1], p23[1]);
+                    }
+                // the same wave reads back (its LDS operations are ordered): lane L takes
+                // piece L % 8 of token row 8 j + L / 8 of the half, in each plane
+    #pragma unroll
+                for (int pl = 0; pl < 2; ++pl)
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int rr = 8 * j + (lane >> 3), k = lane & 7;
+                        const uint4 v = *reinterpret_cast<const uint4*>(wb + 4096 * pl + rr * 128 + ((k ^ (rr & 7)) << 4));
+                        const int t = t0 + 64 * wr + 32 * a + rr;
+                        if (t < g.N) *reinterpret_cast<uint4*>(ob + (pl ? g.plane : 0) + (size_t)t * HDIM + 8 * k) = v;
+                    }
+            }
+            }
+        } else if (nw < g.n_out) {
+    #pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int n = nw + 32 * c + l32;
+                if (n >= g.n_out) continue;
+    #pragma unroll
+                for (int a = 0; a < 2; ++a)
+    #pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int t = t0 + 64 * wr + 32 * a + crow(i, h);
+                        if (t < g.N) g.out0[((size_t)bi * g.N + t) * g.n_out + n] = acc[a][c][i];
+                    }
+            }
         }
+        __syncthreads();                                 // the LDS is free for the next tile's loads
     }
 }
 
@@ -328,6 +337,19 @@ layer_outprep_kernel(int N, int H, int rows, size_t plane, const float* __restri
 constexpr int P_TM = 256, P_TN = 192, P_NS = 2;      // projections: 3 rounds at B 8, N 2048, D 768
 constexpr int O_TM = 256, O_TN = 192, O_NS = 2;      // output projection: 1 round
 
+// Compute units of the current device (the persistent GEMM grid), cached per device.
+int device_cus()
+{
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] <= 0) {
+        int v = 0;
+        cus[dev] = (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ? v : 256;
+    }
+    return cus[dev];
+}
+
 }  // namespace
 
 size_t layer_workspace_region_bytes(int B, int N, int H)
@@ -358,7 +380,8 @@ hipError_t launch_layer_qkv(const LayerArgs& a, uint16_t* Qo, uint16_t* Ko, uint
     g.qkv[1] = Ko;
     g.qkv[2] = Vo;
     g.plane = (size_t)a.B * a.H * a.N * HDIM;
-    hipLaunchKernelGGL((layer_gemm_kernel<P_TM, P_TN, P_NS, EPI_QKV>), dim3(g.total), dim3(P_TM * P_TN / 64), 0,
+    hipLaunchKernelGGL((layer_gemm_kernel<P_TM, P_TN, P_NS, EPI_QKV>), dim3(std::min(g.total, device_cus())),
+                       dim3(P_TM * P_TN / 64), 0,
                        stream, g);
     return hipGetLastError();
 }
@@ -388,7 +411,8 @@ hipError_t launch_layer_out(const LayerArgs& a, const float* Z, const uint16_t* 
     g.A = static_cast<const uint16_t*>(aext);
     g.W0 = static_cast<const uint16_t*>(a.Wo);
     g.out0 = a.y;
-    hipLaunchKernelGGL((layer_gemm_kernel<O_TM, O_TN, O_NS, EPI_ROWS>), dim3(g.total), dim3(O_TM * O_TN / 64), 0,
+    hipLaunchKernelGGL((layer_gemm_kernel<O_TM, O_TN, O_NS, EPI_ROWS>), dim3(std::min(g.total, device_cus())),
+                       dim3(O_TM * O_TN / 64), 0,
                        stream, g);
     return hipGetLastError();
 }
