@@ -54,10 +54,10 @@ __device__ __forceinline__ int crow(int i, int h) { return 8 * (i >> 2) + 4 * h 
 // ===========================================================================
 constexpr int GK = 64;       // reduction depth of one LDS stage
 
-// Tiles hold rows of 64 bf16 (128 bytes = 8 pieces); piece p of row r sits at
-// slot p ^ (r & 7), so 8 consecutive rows read at one piece start on 8
-// different 4-bank groups of their half of the banks.
-__device__ __forceinline__ int psw(int r, int p) { return r * 128 + ((p ^ (r & 7)) << 4); }
+// Tiles hold rows of 64 bf16 (128 bytes = 8 pieces, half of the 64 banks, the
+// half set by r & 1); piece p of row r sits at slot p ^ ((r >> 1) & 7), so 16
+// consecutive rows read at one piece start on 16 different 4-bank groups.
+__device__ __forceinline__ int psw(int r, int p) { return r * 128 + ((p ^ ((r >> 1) & 7)) << 4); }
 
 constexpr int vmcnt_imm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
 
@@ -137,7 +137,7 @@ layer_gemm_kernel(GemmArgs g)
             // with NIA a multiple of NW, whether instruction j loads the weight does not depend on w
             const bool b = (NIA % NW == 0) ? (NW * j >= NIA) : (ins >= NIA);
             const int r = (b ? ins - NIA : ins) * 8 + (lane >> 3);
-            const int p = (lane & 7) ^ (r & 7);
+            const int p = (lane & 7) ^ ((r >> 1) & 7);
             if (!b) {
                 const int t = min(t0 + r, g.N - 1);
                 src[j] = g.A + ((size_t)bi * g.N + t) * g.lda + p * 8;
