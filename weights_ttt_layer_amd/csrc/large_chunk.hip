@@ -83,6 +83,10 @@ __device__ __forceinline__ int swz(int r, int p) { return r * 256 + ((p ^ rsw(r)
 //  * B_c, fp32, tile (r, cc) lane by lane in its C layout: [tile][q][lane][4]
 //    (slots 4q .. 4q+3).
 // ===========================================================================
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_R = 0x020, SG_DS_R = 0x100 };
+#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 constexpr int GR_TOK = 64;              // tokens per LDS stage
 constexpr int GR_NST = 4;               // LDS stages (three in flight while one is read)
 
@@ -189,19 +193,43 @@ lc_gram_kernel(int N, int b, const uint16_t* __restrict__ Kg, const uint16_t* __
             gram_dma(sm, (s + GR_NST - 1) % GR_NST, nstage - s - GR_NST, w, lane, Ku, Vu);
         const uint16_t* kt = sm.k[s % GR_NST];
         const uint16_t* vt = sm.v[s % GR_NST];
-#pragma unroll
-        for (int ks = 0; ks < GR_TOK / 16; ++ks) {
+        // operands of k-step ks + 1 are read while the products of ks run
+        struct Ops { bf16x8 aw[TA], bv[4], bk[4]; };
+        auto ops = [&](int ks, Ops& o) {
             const float* er = PER_TOKEN ? etau + (nstage - 1 - s) * GR_TOK + 16 * ks + 8 * h : nullptr;
-            bf16x8 aw[TA];
-            scaled_frag<PER_TOKEN, TA>(tok_major_frag(kt, 16 * ks, w, lane), er, aw);
+            scaled_frag<PER_TOKEN, TA>(tok_major_frag(kt, 16 * ks, w, lane), er, o.aw);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const bf16x8 bv = tok_major_frag(vt, 16 * ks, t, lane);
-                const bf16x8 bk = tok_major_frag(kt, 16 * ks, t, lane);
+                o.bv[t] = tok_major_frag(vt, 16 * ks, t, lane);
+                o.bk[t] = tok_major_frag(kt, 16 * ks, t, lane);
+            }
+        };
+        Ops cur;
+        ops(0, cur);
+#pragma unroll
+        for (int ks = 0; ks < GR_TOK / 16; ++ks) {
+            Ops nxt;
+            if (ks + 1 < GR_TOK / 16) ops(ks + 1, nxt);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int s2 = TA - 1; s2 >= 0; --s2) {
-                    accB[t] = mfma_32x32x16(aw[s2], bv, accB[t]);
-                    accM[t] = mfma_32x32x16(aw[s2], bk, accM[t]);
+                    accB[t] = mfma_32x32x16(cur.aw[s2], cur.bv[t], accB[t]);
+                    accM[t] = mfma_32x32x16(cur.aw[s2], cur.bk[t], accM[t]);
+                }
+            if (ks + 1 < GR_TOK / 16) cur = nxt;
+        }
+        if constexpr (!PER_TOKEN) {
+            SCHED_GROUP(SG_DS_R, 18);
+#pragma unroll
+            for (int ks = 0; ks < GR_TOK / 16; ++ks) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    if (ks + 1 < GR_TOK / 16) {
+                        if (k < 2) SCHED_GROUP(SG_DS_R, 3);
+                        else SCHED_GROUP(SG_DS_R, 2);
+                    }
+                    SCHED_GROUP(SG_MFMA, 1);
                 }
             }
         }
@@ -533,9 +561,6 @@ __device__ __forceinline__ void grad_terms(const ChunkCtx& x, const char* vt, in
     }
 }
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_R = 0x020, SG_DS_R = 0x100 };
-#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 template <bool PER_TOKEN>
 __device__ __forceinline__ void chunk_step(const ChunkCtx& x, uint16_t* cur, uint16_t* nxt, int i, f32x16 (&accW)[4],
