@@ -69,6 +69,10 @@ __device__ __forceinline__ int rsw(int r) { return ((r & 3) << 1) | ((r >> 2) & 
 __device__ __forceinline__ int swz(int r, int p) { return r * 256 + ((p ^ rsw(r)) << 4); }
 
 
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_R = 0x020, SG_DS_R = 0x100 };
+#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 // ===========================================================================
 // lc_gram: M_c = K^T D K and B_c = K^T D V for one (unit, chunk) per workgroup.
 // Wave w computes row tile w of both (rows 32w..32w+31, all four column tiles),
@@ -83,10 +87,6 @@ __device__ __forceinline__ int swz(int r, int p) { return r * 256 + ((p ^ rsw(r)
 //  * B_c, fp32, tile (r, cc) lane by lane in its C layout: [tile][q][lane][4]
 //    (slots 4q .. 4q+3).
 // ===========================================================================
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_R = 0x020, SG_DS_R = 0x100 };
-#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
-
 constexpr int GR_TOK = 64;              // tokens per LDS stage
 constexpr int GR_NST = 4;               // LDS stages (three in flight while one is read)
 
